@@ -1,0 +1,336 @@
+"""CPU oracle for the token-choice MoE layer forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke entry point and the CPU-baseline leg of the benchmark
+may import this module.  The product path (the HIP library and its Python
+binding) never calls it and shares no code with it.
+
+Plain, slow, obviously correct: numpy in float64 on inputs decoded exactly,
+one function per step of the layer, each citing the passage it follows.
+Library primitives used as steps: matrix product, ``exp``, stable argsort.
+
+Pages cited (by title, then section / figure):
+  [R&R]  "Mixture-of-experts routing & LLM repeatability" (vincentschmalbach.com; no headings,
+         cited by the paragraph's subject)
+  [BI]   "Why temperature=0 Still Gives Different Answers: Batch Invariance"
+  [RB]   "Route-Block Membership Selects Packed-AWQ Arithmetic"
+  [MIR]  "Mixture-of-Experts Routing at Inference Time"
+
+Readings taken where the pages are silent are marked READING and listed in the
+design notes.  Parity status: every function here is pinned by tests under
+``tests/`` marked ``not gpu`` (brute force, closed forms, library special
+cases, hand-worked fixtures); no function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "decode_bf16", "decode_e4m3", "dequantize_blocks", "router_logits", "rank_experts",
+    "topk_route", "capacity", "capacity_keep", "align", "silu", "swiglu_expert",
+    "expert_ffn", "combine", "routing_stats", "moe_forward",
+]
+
+
+# ---------------------------------------------------------------- input decoding
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64: the top 16 bits of an IEEE binary32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3FN codes (uint8) -> float64, from the format's definition.
+
+    sign = bit 7, exponent = bits 6..3 (bias 7), mantissa = bits 2..0.
+    exponent 0: subnormal m * 2^-9;  exponent 15 with mantissa 7: NaN (no infinities);
+    otherwise (1 + m/8) * 2^(exp-7).  Largest finite value 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ex = (c >> 3) & 0xF
+    man = c & 0x7
+    val = np.where(ex == 0, man * 2.0 ** -9, (1.0 + man / 8.0) * np.exp2(ex - 7.0))
+    val = np.where((ex == 15) & (man == 7), np.nan, val)
+    return sign * val
+
+
+def dequantize_blocks(codes: np.ndarray, scales: np.ndarray, block: int) -> np.ndarray:
+    """w[r, c] = e4m3(codes[r, c]) * scale[r // block, c // block], exactly, in float64.
+
+    READING: "per-128-block bf16 scales" means one scale per 128 x 128 tile of
+    (output row, reduction column); ``scales`` is given already decoded (float64).
+    """
+    q = decode_e4m3(codes)
+    s = np.repeat(np.repeat(np.asarray(scales, np.float64), block, axis=-2), block, axis=-1)
+    return q * s
+
+
+# ---------------------------------------------------------------- routing
+
+def router_logits(h: np.ndarray, w_gate: np.ndarray, bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """One logit per expert: l[t, e] = sum_i h[t, i] * W_g[e, i] (+ bias[e]).
+
+    [MIR] "How sparse routing works": the router is one learned matrix that
+    projects h to N logits; the worked router is a bias-free linear layer whose
+    weight is stored [N, hidden] ("Worked example: a top-k router").  The
+    optional additive bias is the workload's per-expert logit offset.
+    """
+    l = np.asarray(h, np.float64) @ np.asarray(w_gate, np.float64).T
+    if bias is not None:
+        l = l + np.asarray(bias, np.float64)[None, :]
+    return l
+
+
+def rank_experts(logits: np.ndarray) -> np.ndarray:
+    """Per token, all experts in rank order: logit descending, ties to the lower index.
+
+    [R&R] paragraph on the top-k step: the choice is fixed once scores, tie rule
+    and capacity rules are fixed.  READING: the tie rule is "lowest expert index
+    wins"; comparison is IEEE (so -0 == +0); a NaN logit ranks below every
+    number, NaNs among themselves by index.  Ranking is done on logits, which
+    orders experts exactly as the (strictly monotone) softmax does.
+    """
+    l = np.asarray(logits, np.float64) + 0.0  # +0.0 turns -0 into +0
+    # A stable ascending sort of -l puts the largest logit first, keeps equal
+    # values in index order, and sends NaN to the end.
+    return np.argsort(-l, axis=1, kind="stable")
+
+
+def topk_route(logits: np.ndarray, k: int, renormalize: bool = True):
+    """Top-k experts, their gates and the router margin, per token.
+
+    Returns (ids [T, k] int64 in rank order, gates [T, k] float64, margin [T] float64).
+
+    Gates follow [MIR] "How sparse routing works" and the worked TopKRouter:
+    softmax over all N logits, keep the k selected, divide by their sum
+    (renormalize); without renormalization the kept softmax values are the gates.
+    Margin follows [R&R] paragraph on the router margin: the k-th highest score
+    minus the (k+1)-th highest; +inf when every expert is selected (k = N).
+    """
+    l = np.asarray(logits, np.float64)
+    T, N = l.shape
+    order = rank_experts(l)
+    ids = order[:, :k]
+    # READING: a NaN logit carries zero softmax weight (it already ranks last).
+    lw = np.where(np.isnan(l), -np.inf, l)
+    lmax = np.max(lw, axis=1, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = np.exp(lw - lmax)
+        p = p / p.sum(axis=1, keepdims=True)        # softmax over all N experts
+    sel = np.take_along_axis(p, ids, axis=1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        gates = sel / sel.sum(axis=1, keepdims=True) if renormalize else sel
+    if k < N:
+        lk = np.take_along_axis(l, order[:, k - 1:k + 1], axis=1)
+        margin = lk[:, 0] - lk[:, 1]
+    else:
+        margin = np.full(T, np.inf)
+    return ids.astype(np.int64), gates, margin
+
+
+# ---------------------------------------------------------------- capacity and alignment
+
+def capacity(T: int, k: int, N: int, cap_num: int, cap_den: int) -> Optional[int]:
+    """Per-expert capacity, or None for dropless.
+
+    [R&R] paragraph on expert capacity: tokens / experts x capacity factor.
+    [MIR] "Worked example": capacity = int(mean per-expert load x factor), the mean
+    load being T*k/N.  READING: both as floor(T*k*cap_num / (N*cap_den)) in
+    integers, the factor given as the rational cap_num/cap_den; 0/0 = no limit.
+    """
+    if cap_num == 0 and cap_den == 0:
+        return None
+    return (T * k * cap_num) // (N * cap_den)
+
+
+def capacity_keep(ids: np.ndarray, N: int, cap: Optional[int]) -> np.ndarray:
+    """kept[r] for every route r = t*k + j (flattened ids).
+
+    [R&R] paragraph on overflow: an expert over capacity overflows, the overflow
+    skips the expert; a dispatcher that fills capacity in order makes batch
+    position matter.  READING: capacity is filled in ascending route id, so a
+    route is kept iff fewer than ``cap`` earlier routes went to its expert.
+    Ids outside [0, N) are never kept.
+    """
+    flat = np.asarray(ids, np.int64).reshape(-1)
+    kept = np.zeros(flat.shape[0], dtype=bool)
+    used = [0] * N
+    for r, e in enumerate(flat.tolist()):
+        if not (0 <= e < N):
+            continue
+        if cap is None or used[e] < cap:
+            kept[r] = True
+            used[e] += 1
+    return kept
+
+
+def align(ids: np.ndarray, kept: np.ndarray, N: int, B: int):
+    """Group kept routes by expert and pad each group to whole B-row blocks.
+
+    [RB] "The bookkeeping before the matrix multiplication": routed rows are
+    grouped by expert and padded into fixed-size blocks; route-block membership
+    is the set of valid flattened route ids in each block.  [RB] "Stable
+    construction selected a third trajectory": routes ordered by (expert id,
+    flattened route id).  READING: flattened id r = t*k + j; each expert's list
+    is padded to a multiple of B with the sentinel T*k; experts with no routes
+    get no block; the buffers are sized for P_max = T*k + N*(B-1) rows.
+
+    Returns dict with sorted_route_ids [P_max], block_expert [ceil(P_max/B)]
+    (-1 past the end), expert_offsets [N+1], num_padded.
+    """
+    flat = np.asarray(ids, np.int64).reshape(-1)
+    R = flat.shape[0]
+    p_max = R + N * (B - 1)
+    n_blocks = -(-p_max // B)
+    sentinel = R
+    sorted_ids = np.full(p_max, sentinel, dtype=np.int64)
+    block_expert = np.full(n_blocks, -1, dtype=np.int64)
+    offsets = np.zeros(N + 1, dtype=np.int64)
+    pos = 0
+    for e in range(N):
+        members = np.nonzero(np.asarray(kept, bool) & (flat == e))[0]  # ascending route ids
+        padded = -(-len(members) // B) * B
+        sorted_ids[pos:pos + len(members)] = members
+        block_expert[pos // B:(pos + padded) // B] = e
+        pos += padded
+        offsets[e + 1] = pos
+    return {"sorted_route_ids": sorted_ids, "block_expert": block_expert,
+            "expert_offsets": offsets, "num_padded": pos}
+
+
+# ---------------------------------------------------------------- expert FFN and combine
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """silu(x) = x / (1 + e^-x), written so that e^-x never overflows."""
+    x = np.asarray(x, np.float64)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = x[pos] / (1.0 + np.exp(-x[pos]))
+    ex = np.exp(x[~pos])
+    out[~pos] = x[~pos] * ex / (1.0 + ex)
+    return out
+
+
+def swiglu_expert(x: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """One SwiGLU expert on rows x [M, H]: y = W2 (silu(W1 x) * (W3 x)).
+
+    w13 [2I, H]: rows 0..I-1 the gate projection W1, rows I..2I-1 the up
+    projection W3 (the fused first projection "W13" of [RB] "The boundary that
+    mattered"); w2 [H, I] the second projection.
+    """
+    I = w13.shape[0] // 2
+    u = x @ w13[:I].T
+    v = x @ w13[I:].T
+    return (silu(u) * v) @ w2.T
+
+
+def expert_ffn(h: np.ndarray, ids: np.ndarray, kept: np.ndarray, w13_of, w2_of, N: int,
+               routes: Optional[np.ndarray] = None) -> dict:
+    """y_r = expert_{ids[r]}(h_{r // k}) for every kept route r (or the given subset).
+
+    [MIR] "How sparse routing works": only the k selected experts run on a token.
+    ``w13_of(e)`` / ``w2_of(e)`` return expert e's float64 weights.  Rows are
+    grouped by expert only so that each expert's weights are materialised once;
+    every row is computed independently.  Returns {route id: y row [H]}.
+    """
+    flat = np.asarray(ids, np.int64).reshape(-1)
+    k = flat.shape[0] // h.shape[0]
+    todo = np.nonzero(kept)[0] if routes is None else np.asarray([r for r in routes if kept[r]], np.int64)
+    out = {}
+    for e in range(N):
+        rs = todo[flat[todo] == e]
+        if rs.size == 0:
+            continue
+        y = swiglu_expert(np.asarray(h, np.float64)[rs // k], w13_of(e), w2_of(e))
+        for r, row in zip(rs.tolist(), y):
+            out[r] = row
+    return out
+
+
+def combine(y_route: dict, gates: np.ndarray, kept: np.ndarray, T: int, H: int,
+            shared: Optional[np.ndarray] = None, residual: Optional[np.ndarray] = None,
+            tokens: Optional[np.ndarray] = None) -> np.ndarray:
+    """out[t] = residual[t] + shared[t] + sum over kept j of gate[t, j] * y_{t*k+j}.
+
+    [R&R] the simplified layer: output = sum of gate[e] * expert[e](h) over the
+    chosen experts, fed back into the residual stream.  [MIR] "The hard part":
+    a token whose route overflowed gets h plus only its surviving experts
+    (Figure 2, drop branch).  READING: gates are not renormalised after a drop;
+    absent terms are zero.  ``tokens`` restricts the rows computed.
+    """
+    g = np.asarray(gates, np.float64)
+    k = g.shape[1]
+    rows = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    out = np.zeros((rows.shape[0], H), np.float64)
+    for i, t in enumerate(rows.tolist()):
+        acc = np.zeros(H, np.float64)
+        for j in range(k):
+            r = t * k + j
+            if kept[r]:
+                acc = acc + g[t, j] * y_route[r]
+        if shared is not None:
+            acc = acc + shared[i]
+        if residual is not None:
+            acc = acc + np.asarray(residual[t], np.float64)
+        out[i] = acc
+    return out
+
+
+def routing_stats(ids: np.ndarray, kept: np.ndarray, N: int, cap: Optional[int]) -> dict:
+    """Per-pass routing health numbers.
+
+    [MIR] "Worked example": per-expert load is the bincount of the flattened top-k
+    ids; overflow per expert is max(load - capacity, 0) and the dropped count is
+    its sum.  [MIR] "The hard part": max/min load, imbalance = max / mean, drop
+    fraction = dropped / total routed.
+    """
+    flat = np.asarray(ids, np.int64).reshape(-1)
+    valid = (flat >= 0) & (flat < N)
+    load = np.bincount(flat[valid], minlength=N)
+    dropped = int(np.maximum(load - cap, 0).sum()) if cap is not None else 0
+    total = int(load.sum())
+    return {
+        "load": load,
+        "max_expert_load": int(load.max()),
+        "min_expert_load": int(load.min()),
+        "imbalance_ratio": float(load.max() / load.mean()) if total else 0.0,
+        "dropped_tokens": dropped,
+        "kept_routes": int(np.count_nonzero(kept)),
+        "invalid_routes": int(np.count_nonzero(~valid)),
+        "drop_fraction": dropped / total if total else 0.0,
+        "capacity": -1 if cap is None else cap,
+    }
+
+
+def moe_forward(h, w_gate, w13_of, w2_of, *, k: int, B: int, cap_num: int = 0, cap_den: int = 0,
+                renormalize: bool = True, bias=None, residual=None, shared_w13=None, shared_w2=None,
+                logits=None, tokens=None) -> dict:
+    """The whole layer, step after step in the pages' order, all in float64.
+
+    route ([MIR] "How sparse routing works") -> capacity and drops ([R&R], [MIR]
+    "The hard part") -> alignment ([RB]) -> expert FFN on kept routes -> combine.
+    ``logits`` (if given) replaces the projection, for routing from stored logits.
+    ``tokens`` restricts the expert FFN and combine to a sample of token rows.
+    """
+    h = np.asarray(h, np.float64)
+    T, H = h.shape
+    N = (np.asarray(logits).shape[1] if logits is not None else np.asarray(w_gate).shape[0])
+    l = router_logits(h, w_gate, bias) if logits is None else np.asarray(logits, np.float64)
+    ids, gates, margin = topk_route(l, k, renormalize)
+    cap = capacity(T, k, N, cap_num, cap_den)
+    kept = capacity_keep(ids, N, cap)
+    al = align(ids, kept, N, B)
+    rows = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    routes = (rows[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+    y = expert_ffn(h, ids, kept, w13_of, w2_of, N, routes=routes)
+    shared = None
+    if shared_w13 is not None:
+        shared = swiglu_expert(h[rows], shared_w13, shared_w2)
+    out = combine(y, gates, kept, T, H, shared=shared, residual=residual, tokens=rows)
+    return {"logits": l, "ids": ids, "gates": gates, "margin": margin, "cap": cap, "kept": kept,
+            "align": al, "y_route": y, "shared": shared, "out": out, "tokens": rows,
+            "stats": routing_stats(ids, kept, N, cap)}

@@ -1,0 +1,464 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+Nothing here compares the oracle with itself.  Each test uses a hand-worked
+fixture under tests/golden/ (with its citation), brute force on tiny inputs,
+a closed form, an invariant, or a library routine the step reduces to.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import moe_oracle as O
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_fixture(name):
+    d = {}
+    cases = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, val = line.partition(":")
+            if key == "case":
+                cases.append(line[len("case:"):])
+            else:
+                d[key.strip()] = val.strip()
+    return d, cases
+
+
+def _floats(s):
+    return np.array([float(x) for x in s.split()], dtype=np.float64)
+
+
+def _ints(s):
+    return np.array([int(x) for x in s.split()], dtype=np.int64)
+
+
+# ------------------------------------------------------------------ decoding
+
+def test_decode_e4m3_all_256_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.decode_e4m3(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    m = ~np.isnan(ref)
+    assert np.array_equal(ours[m], ref[m])
+    assert np.nanmax(ours) == 448.0 and np.count_nonzero(np.isnan(ours)) == 2
+
+
+def test_decode_bf16_matches_torch():
+    g = torch.Generator().manual_seed(1)
+    x = torch.randn(4096, generator=g) * 1e3
+    b = x.to(torch.bfloat16)
+    ours = O.decode_bf16(b.view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(ours, b.to(torch.float64).numpy())
+
+
+def test_dequantize_blocks_hand_fixture():
+    d, _ = _read_fixture("fp8_blocks.txt")
+    blk = int(d["block"])
+    codes = np.array([[int(c, 16) for c in row.split()] for row in d["codes"].split("|")], np.uint8)
+    scales = np.array([[float(c) for c in row.split()] for row in d["scales"].split("|")])
+    want = np.array([[float(c) for c in row.split()] for row in d["w"].split("|")])
+    assert np.array_equal(O.dequantize_blocks(codes, scales, blk), want)
+
+
+def test_fp8_generator_roundtrip_within_e4m3_step():
+    # The workload encoder plus the oracle decoder reproduce the fp32 weights to within
+    # half an e4m3 step (2^-4 relative) of each block's scale.
+    wl = W.DEEPSEEKV3_FP8.with_(H=256, I=128)
+    wf = W._expert_f32(wl, "w13", 3, "cpu")
+    codes, scales = W.quantize_fp8_blocks(wf, 128)
+    s = O.decode_bf16(scales.view(torch.int16).numpy().view(np.uint16))
+    w = O.dequantize_blocks(codes.numpy(), s, 128)
+    err = np.abs(w - wf.double().numpy())
+    bound = np.repeat(np.repeat(s, 128, 0), 128, 1) * 448 * 2.0 ** -4
+    assert np.all(err <= bound * 1.0001)
+
+
+# ------------------------------------------------------------------ routing
+
+def test_router_logits_against_library_linear():
+    g = torch.Generator().manual_seed(2)
+    h = torch.randn(17, 40, generator=g, dtype=torch.float64)
+    wg = torch.randn(6, 40, generator=g, dtype=torch.float64)
+    bias = torch.randn(6, generator=g, dtype=torch.float64)
+    ref = F.linear(h, wg, bias).numpy()
+    assert np.allclose(O.router_logits(h.numpy(), wg.numpy(), bias.numpy()), ref, rtol=1e-13, atol=1e-13)
+    ref0 = torch.nn.Linear(40, 6, bias=False).double()
+    with torch.no_grad():
+        ref0.weight.copy_(wg)
+        want = ref0(h).numpy()
+    assert np.allclose(O.router_logits(h.numpy(), wg.numpy()), want, rtol=1e-13, atol=1e-13)
+
+
+def _beats(la, a, lb, b):
+    """Pairwise rule: does expert a rank above expert b?"""
+    na, nb = math.isnan(la), math.isnan(lb)
+    if na or nb:
+        if na and nb:
+            return a < b
+        return nb
+    if la != lb:
+        return la > lb
+    return a < b
+
+
+def _brute_rank(row):
+    N = len(row)
+    wins = [sum(_beats(row[a], a, row[b], b) for b in range(N) if b != a) for a in range(N)]
+    order = [None] * N
+    for a, w in enumerate(wins):
+        order[N - 1 - w] = a
+    return order
+
+
+def test_rank_experts_brute_force_with_ties_zeros_and_nan():
+    alphabet = [-1.0, 0.0, -0.0, 1.0, float("nan")]
+    rng = np.random.default_rng(3)
+    for N in range(1, 7):
+        for _ in range(300):
+            row = rng.choice(alphabet, size=N)
+            order = O.rank_experts(row[None, :])[0].tolist()
+            assert order == _brute_rank(row.tolist()), row
+
+
+def test_topk_exhaustive_small_alphabet():
+    # Every logit vector over a 3-value alphabet for N = 5: the selected set dominates
+    # every outsider under the pairwise rule, and is listed in rank order.
+    N = 5
+    for vals in itertools.product([0.0, 1.0, 2.0], repeat=N):
+        row = np.array(vals)
+        for k in range(1, N + 1):
+            ids, _, margin = O.topk_route(row[None, :], k)
+            ids = ids[0].tolist()
+            assert len(set(ids)) == k
+            out = [e for e in range(N) if e not in ids]
+            for a in ids:
+                for b in out:
+                    assert _beats(row[a], a, row[b], b)
+            for a, b in zip(ids, ids[1:]):
+                assert _beats(row[a], a, row[b], b)
+            if k < N:
+                assert margin[0] == row[ids[-1]] - max(row[b] for b in out)
+            else:
+                assert margin[0] == np.inf
+
+
+def test_topk_matches_torch_topk_on_tie_free_inputs():
+    g = torch.Generator().manual_seed(4)
+    l = torch.randn(500, 64, generator=g, dtype=torch.float64)
+    for k in (1, 2, 8):
+        ids, _, _ = O.topk_route(l.numpy(), k)
+        ref = torch.topk(l, k, dim=1, largest=True, sorted=True).indices.numpy()
+        assert np.array_equal(ids, ref)
+        # selecting on softmax probabilities (the pages' worked router) gives the same experts
+        ref_p = torch.topk(torch.softmax(l, dim=1), k, dim=1).indices.numpy()
+        assert np.array_equal(ids, ref_p)
+
+
+def test_golden_margin_and_gates_k4():
+    d, _ = _read_fixture("router_margin_k4.txt")
+    l = _floats(d["logits"])[None, :]
+    ids, gates, margin = O.topk_route(l, int(d["k"]))
+    assert ids[0].tolist() == _ints(d["ids"]).tolist()
+    assert abs(margin[0] - float(d["margin"])) < 1e-15
+    ratio = np.exp(_floats(d["gate_ratio_exponents"]))
+    assert np.allclose(gates[0] / gates[0][0], ratio, rtol=1e-14)
+    assert abs(gates[0].sum() - 1.0) < 1e-15
+
+
+def test_golden_tie_rule():
+    _, cases = _read_fixture("tie_rule_k2.txt")
+    assert len(cases) == 5
+    for c in cases:
+        lg, ids, mg = [p.split(":")[-1].strip() for p in c.split("|")]
+        l = np.array([float(x) for x in lg.split()])[None, :]
+        got_ids, _, got_m = O.topk_route(l, 2)
+        assert got_ids[0].tolist() == [int(x) for x in ids.split()], c
+        want_m = float(mg)
+        assert (math.isnan(want_m) and math.isnan(got_m[0])) or got_m[0] == want_m, c
+
+
+def test_gates_identities():
+    g = torch.Generator().manual_seed(5)
+    l = (torch.randn(300, 16, generator=g, dtype=torch.float64) * 3).numpy()
+    for k in (1, 2, 4, 16):
+        ids, gates, _ = O.topk_route(l, k)
+        assert np.allclose(gates.sum(1), 1.0, atol=1e-14)
+        if k == 1:
+            assert np.all(gates == 1.0)
+        if k == 16:  # N = k: renormalised gates are the full softmax (library routine)
+            p = torch.softmax(torch.from_numpy(l), dim=1).numpy()
+            assert np.allclose(gates, np.take_along_axis(p, ids, 1), rtol=1e-13)
+        sel = np.take_along_axis(l, ids, 1)
+        # softmax over the selected logits alone (library) -- equal to softmax-then-renorm
+        ref = torch.softmax(torch.from_numpy(sel), dim=1).numpy()
+        assert np.allclose(gates, ref, rtol=1e-12, atol=1e-15)
+        # gates are non-increasing in rank (larger logit, larger gate)
+        assert np.all(np.diff(gates, axis=1) <= 1e-15)
+    # without renormalisation the gates are plain softmax probabilities of the selected experts
+    ids, gates, _ = O.topk_route(l, 2, renormalize=False)
+    p = torch.softmax(torch.from_numpy(l), dim=1).numpy()
+    assert np.allclose(gates, np.take_along_axis(p, ids, 1), rtol=1e-13)
+
+
+# ------------------------------------------------------------------ capacity, alignment, stats
+
+def test_capacity_formulas():
+    # Switch-style: tokens / experts x factor, k = 1 (2048 / 16 x 1.25 = 160)
+    assert O.capacity(2048, 1, 16, 5, 4) == 160
+    assert O.capacity(64, 2, 8, 0, 0) is None
+    # The worked example's int(mean(load) x 1.25) with load = bincount of the flattened ids
+    for seed in range(5):
+        ids = W.random_routes(96, 8, 2, seed).long()
+        load = torch.bincount(ids.flatten(), minlength=8)
+        assert O.capacity(96, 2, 8, 5, 4) == int(load.double().mean() * 1.25)
+    assert O.capacity(3, 1, 8, 5, 4) == 0  # small batch: literal formula gives zero
+
+
+def _brute_fill(ids_flat, N, cap):
+    """A dispatcher that walks tokens in batch order and appends each route to its
+    expert's buffer while the buffer has room."""
+    buffers = {e: [] for e in range(N)}
+    kept = []
+    for r, e in enumerate(ids_flat):
+        if len(buffers[e]) < cap:
+            buffers[e].append(r)
+            kept.append(True)
+        else:
+            kept.append(False)
+    return np.array(kept), buffers
+
+
+def test_capacity_keep_brute_force_and_identities():
+    for T, N, k in itertools.product(range(1, 7), range(1, 4), range(1, 3)):
+        if k > N:
+            continue
+        rng = np.random.default_rng(T * 100 + N * 10 + k)
+        for _ in range(20):
+            ids = np.stack([rng.permutation(N)[:k] for _ in range(T)])
+            for cap in range(0, T * k + 2):
+                kept = O.capacity_keep(ids, N, cap)
+                want, _ = _brute_fill(ids.reshape(-1).tolist(), N, cap)
+                assert np.array_equal(kept, want)
+                load = torch.bincount(torch.from_numpy(ids).flatten(), minlength=N)
+                dropped = int((load - cap).clamp(min=0).sum())
+                assert dropped == kept.size - kept.sum()
+            assert O.capacity_keep(ids, N, None).all()
+            assert not O.capacity_keep(ids, N, 0).any()
+
+
+def test_capacity_keep_invalid_ids_never_kept():
+    ids = np.array([[0, 5], [-1, 1], [2, 2]])
+    kept = O.capacity_keep(ids, 3, None)
+    assert kept.tolist() == [True, False, False, True, True, True]
+
+
+def _brute_align(ids_flat, kept, N, B):
+    R = len(ids_flat)
+    keys = sorted((ids_flat[r], r) for r in range(R) if kept[r])
+    seq, blocks, offs = [], [], [0]
+    for e in range(N):
+        mem = [r for (ee, r) in keys if ee == e]
+        pad = (-len(mem)) % B
+        seq += mem + [R] * pad
+        blocks += [e] * ((len(mem) + pad) // B)
+        offs.append(len(seq))
+    return seq, blocks, offs
+
+
+def test_align_golden_fixture():
+    d, _ = _read_fixture("align_capacity_T4_k2_N3_B2.txt")
+    T, k, N, B = (int(d[x]) for x in "TkNB")
+    ids = _ints(d["ids"]).reshape(T, k)
+    for tag, cap in (("dropless", None), ("cf1", O.capacity(T, k, N, 1, 1))):
+        if tag == "cf1":
+            assert cap == int(d["cf1.cap"])
+        kept = O.capacity_keep(ids, N, cap)
+        assert kept.astype(int).tolist() == _ints(d[tag + ".kept"]).tolist()
+        al = O.align(ids, kept, N, B)
+        assert al["sorted_route_ids"].tolist() == _ints(d[tag + ".sorted_route_ids"]).tolist()
+        assert al["block_expert"].tolist() == _ints(d[tag + ".block_expert"]).tolist()
+        assert al["expert_offsets"].tolist() == _ints(d[tag + ".expert_offsets"]).tolist()
+        assert al["num_padded"] == int(d[tag + ".num_padded"])
+    st = O.routing_stats(ids, O.capacity_keep(ids, N, 2), N, 2)
+    assert st["load"].tolist() == _ints(d["load"]).tolist()
+    assert st["dropped_tokens"] == int(d["cf1.dropped"])
+    assert st["max_expert_load"] == int(d["cf1.max_expert_load"])
+    assert st["min_expert_load"] == int(d["cf1.min_expert_load"])
+    assert st["imbalance_ratio"] == float(d["cf1.imbalance_ratio"])
+    assert st["drop_fraction"] == float(d["cf1.drop_fraction"])
+
+
+def test_align_brute_force_and_invariants():
+    for seed in range(60):
+        rng = np.random.default_rng(seed)
+        T, N = int(rng.integers(1, 20)), int(rng.integers(1, 9))
+        k = int(rng.integers(1, N + 1))
+        B = int(rng.choice([1, 2, 4, 8]))
+        ids = np.stack([rng.permutation(N)[:k] for _ in range(T)])
+        cap = None if seed % 3 == 0 else int(rng.integers(0, T + 1))
+        kept = O.capacity_keep(ids, N, cap)
+        al = O.align(ids, kept, N, B)
+        seq, blocks, offs = _brute_align(ids.reshape(-1).tolist(), kept, N, B)
+        R = T * k
+        sr = al["sorted_route_ids"]
+        assert sr.shape[0] == R + N * (B - 1)
+        assert sr[:len(seq)].tolist() == seq and np.all(sr[len(seq):] == R)
+        assert al["block_expert"][:len(blocks)].tolist() == blocks
+        assert np.all(al["block_expert"][len(blocks):] == -1)
+        assert al["expert_offsets"].tolist() == offs and al["num_padded"] == offs[-1]
+        # invariants: a permutation of the kept routes, homogeneous blocks, counts = bincount
+        valid = sr[sr != R]
+        assert sorted(valid.tolist()) == np.nonzero(kept)[0].tolist()
+        flat = ids.reshape(-1)
+        for b, e in enumerate(al["block_expert"].tolist()):
+            rows = sr[b * B:(b + 1) * B]
+            rows = rows[rows != R]
+            assert e >= 0 or rows.size == 0
+            assert np.all(flat[rows] == e)
+        cnt = np.bincount(flat[kept], minlength=N)
+        assert np.array_equal(np.diff(al["expert_offsets"]), -(-cnt // B) * B)
+
+
+# ------------------------------------------------------------------ expert FFN and combine
+
+def test_silu_against_library():
+    x = np.concatenate([np.linspace(-800, 800, 4001), np.linspace(-6, 6, 1001)])
+    ref = F.silu(torch.from_numpy(x)).numpy()
+    assert np.allclose(O.silu(x), ref, rtol=1e-15, atol=1e-300)
+
+
+def _torch_swiglu(x, w13, w2):
+    I = w13.shape[0] // 2
+    gate, up = w13[:I], w13[I:]
+    return F.linear(F.silu(F.linear(x, gate)) * F.linear(x, up), w2)
+
+
+def test_single_expert_top1_is_a_plain_swiglu_ffn():
+    # N = 1, k = 1: the layer is h + FFN(h) (gate exactly 1)
+    g = torch.Generator().manual_seed(6)
+    T, H, I = 9, 24, 40  # H != I so that a transposed operand cannot pass
+    h = torch.randn(T, H, generator=g, dtype=torch.float64)
+    wg = torch.randn(1, H, generator=g, dtype=torch.float64)
+    w13 = torch.randn(1, 2 * I, H, generator=g, dtype=torch.float64) / math.sqrt(H)
+    w2 = torch.randn(1, H, I, generator=g, dtype=torch.float64) / math.sqrt(I)
+    res = O.moe_forward(h.numpy(), wg.numpy(), lambda e: w13[e].numpy(), lambda e: w2[e].numpy(),
+                        k=1, B=4, residual=h.numpy())
+    want = (h + _torch_swiglu(h, w13[0], w2[0])).numpy()
+    assert np.allclose(res["out"], want, rtol=1e-12, atol=1e-12)
+    res0 = O.moe_forward(h.numpy(), wg.numpy(), lambda e: w13[e].numpy(), lambda e: w2[e].numpy(), k=1, B=4)
+    assert np.allclose(res0["out"], _torch_swiglu(h, w13[0], w2[0]).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def _torch_dense_mixture(h, wg, w13, w2, k):
+    """Independent layer: softmax router, torch.topk on probabilities, renormalise, loop experts."""
+    probs = torch.softmax(F.linear(h, wg), dim=-1)
+    gv, gi = probs.topk(k, dim=-1)
+    gv = gv / gv.sum(-1, keepdim=True)
+    out = h.clone()
+    for e in range(wg.shape[0]):
+        y = _torch_swiglu(h, w13[e], w2[e])
+        wgt = (gv * (gi == e)).sum(-1, keepdim=True)
+        out = out + wgt * y
+    return out
+
+
+def test_all_experts_selected_is_a_dense_soft_mixture():
+    g = torch.Generator().manual_seed(7)
+    T, H, I, N = 11, 16, 20, 4
+    h = torch.randn(T, H, generator=g, dtype=torch.float64)
+    wg = torch.randn(N, H, generator=g, dtype=torch.float64)
+    w13 = torch.randn(N, 2 * I, H, generator=g, dtype=torch.float64) / 4
+    w2 = torch.randn(N, H, I, generator=g, dtype=torch.float64) / 4
+    res = O.moe_forward(h.numpy(), wg.numpy(), lambda e: w13[e].numpy(), lambda e: w2[e].numpy(),
+                        k=N, B=2, residual=h.numpy())
+    p = torch.softmax(F.linear(h, wg), -1)
+    want = h + sum(p[:, e:e + 1] * _torch_swiglu(h, w13[e], w2[e]) for e in range(N))
+    assert np.allclose(res["out"], want.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_toy_layer_against_independent_torch_layer():
+    wl = W.TOY_FP32
+    d = W.layer_inputs(wl)
+    h = d["h"].double()
+    wg, w13, w2 = d["w_gate"].double(), d["w13"].double(), d["w2"].double()
+    res = O.moe_forward(h.numpy(), wg.numpy(), lambda e: w13[e].numpy(), lambda e: w2[e].numpy(),
+                        k=wl.k, B=wl.B, residual=h.numpy())
+    want = _torch_dense_mixture(h, wg, w13, w2, wl.k).numpy()
+    rel = np.abs(res["out"] - want).max() / np.abs(want).max()
+    assert rel < 1e-12
+    # the toy batch has no near-ties at fp64 precision, so the torch topk agrees on every route
+    assert res["margin"].min() > 1e-9
+
+
+def test_partial_and_full_drop_give_residual_plus_survivors():
+    d, _ = _read_fixture("align_capacity_T4_k2_N3_B2.txt")
+    T, k, N = 4, 2, 3
+    ids = _ints(d["ids"]).reshape(T, k)
+    g = torch.Generator().manual_seed(8)
+    H, I = 6, 10
+    h = torch.randn(T, H, generator=g, dtype=torch.float64)
+    w13 = torch.randn(N, 2 * I, H, generator=g, dtype=torch.float64)
+    w2 = torch.randn(N, H, I, generator=g, dtype=torch.float64)
+    gates = np.array([[0.75, 0.25]] * T)
+    kept = O.capacity_keep(ids, N, 2)   # r5 (t2, j1) and r7 (t3, j1) dropped
+    y = O.expert_ffn(h.numpy(), ids, kept, lambda e: w13[e].numpy(), lambda e: w2[e].numpy(), N)
+    out = O.combine(y, gates, kept, T, H, residual=h.numpy())
+    for t in (2, 3):
+        e0 = int(ids[t, 0])
+        want = h[t] + 0.75 * _torch_swiglu(h[t:t + 1], w13[e0], w2[e0])[0]
+        assert np.allclose(out[t], want.numpy(), rtol=1e-12, atol=1e-12)
+    # capacity zero: every route dropped, each output row is exactly its residual row
+    none = O.capacity_keep(ids, N, 0)
+    out0 = O.combine({}, gates, none, T, H, residual=h.numpy())
+    assert np.array_equal(out0, h.numpy())
+
+
+def test_shared_expert_adds_a_dense_ffn():
+    g = torch.Generator().manual_seed(9)
+    T, H, I, N = 5, 8, 12, 3
+    h = torch.randn(T, H, generator=g, dtype=torch.float64)
+    wg = torch.randn(N, H, generator=g, dtype=torch.float64)
+    w13 = torch.randn(N, 2 * I, H, generator=g, dtype=torch.float64)
+    w2 = torch.randn(N, H, I, generator=g, dtype=torch.float64)
+    s13 = torch.randn(2 * I, H, generator=g, dtype=torch.float64)
+    s2 = torch.randn(H, I, generator=g, dtype=torch.float64)
+    base = O.moe_forward(h.numpy(), wg.numpy(), lambda e: w13[e].numpy(), lambda e: w2[e].numpy(), k=2, B=2)
+    withs = O.moe_forward(h.numpy(), wg.numpy(), lambda e: w13[e].numpy(), lambda e: w2[e].numpy(), k=2, B=2,
+                          shared_w13=s13.numpy(), shared_w2=s2.numpy())
+    assert np.allclose(withs["out"] - base["out"], _torch_swiglu(h, s13, s2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_fresh_router_load_is_roughly_uniform():
+    # The worked example: a fresh router on 4096 random 512-wide tokens, 8 experts, top-2.
+    g = torch.Generator().manual_seed(10)
+    h = torch.randn(4096, 512, generator=g, dtype=torch.float64)
+    lin = torch.nn.Linear(512, 8, bias=False).double()
+    torch.nn.init.normal_(lin.weight, 0.0, 0.02, generator=g)
+    ids, _, _ = O.topk_route(O.router_logits(h.numpy(), lin.weight.detach().numpy()), 2)
+    load = O.routing_stats(ids, np.ones(ids.size, bool), 8, None)["load"]
+    assert load.sum() == 8192
+    assert load.min() > 0.75 * 1024 and load.max() < 1.25 * 1024
+
+
+def test_sampled_tokens_equal_full_pass():
+    wl = W.TOY_FP32
+    d = W.layer_inputs(wl)
+    args = (d["h"].double().numpy(), d["w_gate"].double().numpy(),
+            lambda e: d["w13"][e].double().numpy(), lambda e: d["w2"][e].double().numpy())
+    full = O.moe_forward(*args, k=wl.k, B=wl.B, residual=d["h"].double().numpy())
+    sub = np.array([3, 17, 40, 63])
+    part = O.moe_forward(*args, k=wl.k, B=wl.B, residual=d["h"].double().numpy(), tokens=sub)
+    # BLAS may block a smaller product differently: equal up to fp64 rounding
+    assert np.allclose(part["out"], full["out"][sub], rtol=1e-13, atol=1e-13)
