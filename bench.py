@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE layer forward pass on one MI355X.
+
+A step is one moe_forward call (router projection, top-k + gates, capacity +
+alignment, grouped W13+SwiGLU and W2 expert GEMMs, combine) over one batch of
+seeded synthetic inputs already resident in HBM.  Default workload: the
+Mixtral-shaped layer (T=4096, H=4096, 8 experts, top-2, SwiGLU I=14336, B=64,
+bf16).  Prints ONE JSON line on stdout; progress goes to stderr.
+
+Besides the headline rate it times every stage on its own with HIP events
+recorded on the stream each kernel is launched on (per launch, averaged), and
+reports the dominant kernel (the W13+SwiGLU grouped GEMM) against the bf16
+MFMA peak, plus the CPU oracle timed on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "routed tokens/sec per MoE layer fwd (1 GPU) + % MFMA/HBM roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _ffn_source_hash() -> str:
+    p = os.path.join(ROOT, "top_routing_expert_router_amd", "csrc", "ffn.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(workload: str, launches_per_unit: float):
+    """HBM bytes per launch of the W13 GEMM from committed rocprofv3 counter runs,
+    if they were taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"gate_up_gemm_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("ffn_source_sha256_16") != _ffn_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_bf16")
+    ap.add_argument("--cpu-sample", type=int, default=128, help="tokens of the workload the CPU oracle runs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timings")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(expert parallelism is a design note); run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import top_routing_expert_router_amd as M
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    M.lib()
+    dev = "cuda"
+    w = W.ALL[args.workload]
+    log(f"[bench] workload {w.name}: generating inputs on the GPU")
+    d = W.layer_inputs(w, device=dev)
+    cfg = M.make_config(w.T, w.H, w.N, w.k, w.I, w.B, cap_num=w.cap_num, cap_den=w.cap_den, n_shared=w.n_shared,
+                        renormalize=w.renormalize, act_dtype=w.act_dtype, expert_dtype=w.expert_dtype,
+                        scale_block=w.scale_block)
+    p_max, n_blocks = M.moe_align_sizes(cfg)
+    act_t = torch.float32 if w.act_dtype == W.F32 else torch.bfloat16
+    asz = 4 if w.act_dtype == W.F32 else 2
+    ws = torch.empty(M.moe_workspace_size(cfg, M.MOE_OP_FORWARD), dtype=torch.uint8, device=dev)
+    out = torch.empty(w.T, w.H, dtype=act_t, device=dev)
+    wts = {k: d.get(k) for k in ("w_gate", "w13", "w2", "w13_scale", "w2_scale", "shared_w13", "shared_w2",
+                                 "shared_w13_scale", "shared_w2_scale")}
+    wts["logit_bias"] = None if d["bias"] is None else d["bias"].to(dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        M.moe_forward(cfg, wts, d["h"], d["residual"], out, None, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    value = w.T / (ms / 1e3)
+    log(f"[bench] forward: {ms:.4f} ms/step, {value:,.0f} tokens/s")
+
+    # ---- per-stage timings through the individual entry points (same buffers)
+    tr = dict(logits=torch.empty(w.T, w.N, device=dev), topk_ids=torch.empty(w.T, w.k, dtype=torch.int32, device=dev),
+              topk_gates=torch.empty(w.T, w.k, device=dev), margin=torch.empty(w.T, device=dev),
+              route_kept=torch.empty(w.T * w.k, dtype=torch.uint8, device=dev),
+              sorted_route_ids=torch.empty(p_max, dtype=torch.int32, device=dev),
+              block_expert=torch.empty(n_blocks, dtype=torch.int32, device=dev),
+              expert_offsets=torch.empty(w.N + 1, dtype=torch.int32, device=dev),
+              num_padded=torch.empty(1, dtype=torch.int32, device=dev),
+              stats=torch.empty(w.N + M.STATS_EXTRA, dtype=torch.int32, device=dev),
+              act=torch.empty(p_max, w.I, dtype=act_t, device=dev),
+              y_route=torch.empty(w.T * w.k, w.H, dtype=act_t, device=dev))
+    M.moe_forward(cfg, wts, d["h"], d["residual"], out, tr, ws, stream=stream)
+    torch.cuda.synchronize()
+    kept_routes = int(tr["route_kept"].sum().item())
+    aws = torch.empty(M.moe_workspace_size(cfg, M.MOE_OP_ALIGN), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)  # larger than L2 + MALL
+
+    def timed(fn, reps, do_flush):
+        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        fn()
+        for a, b in es:
+            if do_flush:
+                flush.fill_(1)
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in es) / reps  # ms per launch
+
+    R, T, H, I, N, k = w.T * w.k, w.T, w.H, w.I, w.N, w.k
+    stages = {}
+    gate_up_flops = 4.0 * kept_routes * H * I
+    ms_gate_up = timed(lambda: M.moe_expert_gate_up(cfg, d["h"], tr["sorted_route_ids"], tr["expert_offsets"],
+                                                    d["w13"], d.get("w13_scale"), tr["act"], stream=stream),
+                       max(args.steps, 5), False)
+    stages["gate_up_gemm"] = {"us": ms_gate_up * 1e3, "TFLOP/s": gate_up_flops / (ms_gate_up * 1e-3) / 1e12}
+    if not args.no_stages:
+        down_flops = 2.0 * kept_routes * H * I
+        ms_down = timed(lambda: M.moe_expert_down(cfg, tr["act"], tr["sorted_route_ids"], tr["expert_offsets"],
+                                                  d["w2"], d.get("w2_scale"), tr["y_route"], stream=stream),
+                        max(args.steps, 5), False)
+        stages["down_gemm"] = {"us": ms_down * 1e3, "TFLOP/s": down_flops / (ms_down * 1e-3) / 1e12}
+        route_bytes = T * H * asz + N * H * asz + T * N * 4 + R * 8 + T * 4
+        ms_route = timed(lambda: M.moe_route(cfg, d["h"], wts["w_gate"], wts["logit_bias"], tr["logits"],
+                                             tr["topk_ids"], tr["topk_gates"], tr["margin"], stream=stream),
+                         max(args.steps, 5), True)
+        stages["route"] = {"us": ms_route * 1e3, "GB/s": route_bytes / (ms_route * 1e-3) / 1e9}
+        align_bytes = R * 4 + R + p_max * 4 + n_blocks * 4
+        ms_align = timed(lambda: M.moe_align(cfg, tr["topk_ids"], tr["route_kept"], tr["sorted_route_ids"],
+                                             tr["block_expert"], tr["expert_offsets"], tr["num_padded"], tr["stats"],
+                                             aws, stream=stream), max(args.steps, 5), True)
+        stages["align"] = {"us": ms_align * 1e3, "GB/s": align_bytes / (ms_align * 1e-3) / 1e9}
+        comb_bytes = kept_routes * H * asz + T * H * asz * 2 + R * 5
+        ms_comb = timed(lambda: M.moe_combine(cfg, tr["y_route"], tr["topk_gates"], tr["route_kept"], None,
+                                              d["residual"], out, stream=stream), max(args.steps, 5), True)
+        stages["combine"] = {"us": ms_comb * 1e3, "GB/s": comb_bytes / (ms_comb * 1e-3) / 1e9}
+        for kname, v in stages.items():
+            log(f"[bench] stage {kname}: " + ", ".join(f"{a} {b:,.2f}" for a, b in v.items()))
+
+    achieved = stages["gate_up_gemm"]["TFLOP/s"]
+    roofline = {"kernel": "ffn_gemm_bf16<W13+SwiGLU>", "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": _traffic(w.name, 1.0), "avg_launch_us": round(ms_gate_up * 1e3, 2),
+                "flops_per_launch": gate_up_flops}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, d, args.cpu_sample)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.act_dtype == W.BF16 else "f32",
+        "data": "synthetic (seeded; Gaussian inits; see DESIGN.md)",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "N": w.N, "k": w.k, "I": w.I, "B": w.B,
+                   "expert_dtype": w.expert_dtype, "capacity": None if w.cap_den == 0 else f"{w.cap_num}/{w.cap_den}",
+                   "n_shared": w.n_shared, "kept_routes": kept_routes, "parallelism": "none (1 GPU)"},
+        "roofline": roofline, "stages": {k: {a: round(b, 3) for a, b in v.items()} for k, v in stages.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(w, d, sample: int):
+    """The oracle (fp64 numpy) on this workload, restricted to a seeded token sample."""
+    import numpy as np
+    import torch
+
+    from oracle import moe_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - informational only
+        threads = 1
+    bits = lambda t: t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+    log(f"[bench] cpu baseline: copying inputs to the host")
+    h_b, wg_b = bits(d["h"]), bits(d["w_gate"])
+    w13_b = d["w13"].to("cpu")
+    w2_b = d["w2"].to("cpu")
+    g = torch.Generator().manual_seed(1234)
+    tokens = torch.randperm(w.T, generator=g)[:sample].sort().values.numpy()
+    t0 = time.perf_counter()
+    h64 = O.decode_bf16(h_b)
+    res = O.moe_forward(h64, O.decode_bf16(wg_b),
+                        lambda e: O.decode_bf16(w13_b[e].view(torch.int16).numpy().view(np.uint16)),
+                        lambda e: O.decode_bf16(w2_b[e].view(torch.int16).numpy().view(np.uint16)),
+                        k=w.k, B=w.B, cap_num=w.cap_num, cap_den=w.cap_den, residual=h64, tokens=tokens)
+    dt = time.perf_counter() - t0
+    assert res["out"].shape[0] == sample
+    log(f"[bench] cpu baseline: {sample} tokens in {dt:.2f} s")
+    return {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "host_cpus": len(os.sched_getaffinity(0)), "seconds": round(dt, 2),
+            "sample": f"{sample} seeded tokens of the {w.T}-token batch: full routing, capacity and alignment "
+                      f"of all tokens, expert FFN (all experts' weights decoded to fp64) and combine for the "
+                      f"sampled tokens"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,271 @@
+/*
+ * moe.h -- C ABI of libmoe_mi355x.so: the token-choice Mixture-of-Experts layer
+ * forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * Per token the layer computes (pages cited by title and section):
+ *   1. router logits  l = h . W_g^T (+ optional per-expert bias)
+ *        "Mixture-of-Experts Routing at Inference Time", "How sparse routing works"
+ *        and "Worked example: a top-k router and the imbalance it produces";
+ *   2. top-k experts by (logit descending, lower expert index on ties), softmax
+ *      gates renormalised over the k chosen, and the router margin (k-th minus
+ *      (k+1)-th logit)
+ *        same page and section; "Mixture-of-experts routing & LLM repeatability",
+ *        paragraphs on the top-k step and on the router margin;
+ *   3. an optional per-expert capacity, filled in route order, whose overflow
+ *      routes are dropped to the residual path
+ *        "Mixture-of-experts routing & LLM repeatability", paragraph on expert
+ *        capacity; "Mixture-of-Experts Routing at Inference Time", "The hard part:
+ *        token dropping is a silent correctness bug", Figure 2;
+ *   4. alignment of kept routes into expert-homogeneous blocks of B rows, ordered
+ *      by (expert id, flattened route id), padded with a sentinel
+ *        "Route-Block Membership Selects Packed-AWQ Arithmetic", sections "The
+ *        bookkeeping before the matrix multiplication" and "Stable construction
+ *        selected a third trajectory";
+ *   5. SwiGLU expert FFNs on the aligned rows: fused first projection W13
+ *      (gate rows, then up rows), silu(gate) * up, second projection W2
+ *        same page, "The boundary that mattered" (W13, activation, W2 surfaces);
+ *   6. gate-weighted combine added to the residual stream
+ *        "Mixture-of-Experts Routing at Inference Time", "How sparse routing
+ *        works" and Figure 2.
+ *
+ * Conventions for every entry point
+ *   - Tensors are dense, row-major, and live in device memory (pointers from
+ *     hipMalloc or a torch CUDA tensor).  Data tensors (h, weights, act, y, out,
+ *     residual, logits) must be 16-byte aligned; int32/float32 index and gate
+ *     arrays 4-byte aligned; byte arrays unaligned.
+ *   - The caller owns and allocates every buffer, including the workspace whose
+ *     size moe_workspace_size reports.  The library allocates nothing, keeps no
+ *     pointer after return and has no global state besides its code object.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  All work is enqueued
+ *     asynchronously on it; buffers must stay alive until it completes.
+ *   - Arguments are validated on the host first.  On any error nothing is
+ *     enqueued and an error code is returned; no exception crosses the ABI.
+ *     A failed kernel launch returns MOE_ERR_HIP.
+ *   - Route id r = t*k + j for token t and rank j (0 = highest).  The padding
+ *     sentinel is T*k.  P_max = T*k + N*(B-1) bounds the padded row count.
+ *   - Every reduction has a fixed split and order that depends only on the
+ *     config (never on T or on other tokens), so each token's logits, ids,
+ *     gates, expert outputs and layer output are bitwise identical whatever
+ *     else is in the batch (dropless configs; with a capacity limit the drop
+ *     decisions themselves depend on the batch, as the pages say).
+ */
+#ifndef MOE_MI355X_H_
+#define MOE_MI355X_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef int32_t moe_status;
+enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+  MOE_ERR_INVALID_CONFIG = 2,      /* config outside the supported envelope */
+  MOE_ERR_UNSUPPORTED = 3,         /* dtype combination or flag not implemented */
+  MOE_ERR_MISALIGNED = 4,          /* pointer alignment rule violated */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 5, /* ws_bytes below moe_workspace_size */
+  MOE_ERR_HIP = 6                  /* a HIP runtime call or kernel launch failed */
+};
+
+/* Element types.  fp8 is OCP E4M3FN (bias 7, max 448, no infinities). */
+enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 };
+
+/* moe_route flags */
+enum {
+  MOE_ROUTE_LOGITS_IN = 1u /* skip the projection: `logits` is an input (stored or replayed logits) */
+};
+
+/* moe_workspace_size operations */
+enum { MOE_OP_ALIGN = 1, MOE_OP_FORWARD = 2 };
+
+/* Offsets into the stats array written by moe_align ([N + MOE_STATS_EXTRA] int32). */
+enum {
+  MOE_STAT_KEPT = 0,      /* routes kept (stats[N + 0]) */
+  MOE_STAT_DROPPED = 1,   /* valid routes dropped by capacity */
+  MOE_STAT_INVALID = 2,   /* routes whose expert id is outside [0, N) (never kept) */
+  MOE_STAT_CAPACITY = 3,  /* per-expert capacity, -1 when dropless */
+  MOE_STAT_MAX_LOAD = 4,  /* max over experts of routed load (before capacity) */
+  MOE_STAT_MIN_LOAD = 5,  /* min over experts of routed load */
+  MOE_STAT_NUM_PADDED = 6,/* padded rows used (same as *num_padded) */
+  MOE_STAT_RESERVED = 7,
+  MOE_STATS_EXTRA = 8
+};
+
+/*
+ * Layer shape and numerics.  Supported envelope:
+ *   1 <= T <= 65536;  H, I multiples of 128, 128 <= H, I <= 32768;
+ *   1 <= N <= 256;  1 <= k <= min(8, N);  B in {8, 16, 32, 64, 128};
+ *   capacity factor cap_num/cap_den > 0, or 0/0 for dropless:
+ *     cap = floor(T*k*cap_num / (N*cap_den))  (may be 0: every route dropped);
+ *   n_shared in {0, 1} (one always-on expert added with gate 1);
+ *   renormalize 1 = gates renormalised over the k chosen, 0 = plain softmax values;
+ *   dtypes: (act F32, expert F32), (act BF16, expert BF16),
+ *           (act BF16, expert FP8_E4M3 with scale_block 128).
+ * act_dtype is the type of h, residual, out, W_g, act and y_route.
+ */
+typedef struct moe_config {
+  uint32_t struct_size; /* sizeof(moe_config) */
+  int32_t T, H, N, k, I, B;
+  int32_t cap_num, cap_den;
+  int32_t n_shared;
+  int32_t renormalize;
+  int32_t act_dtype;
+  int32_t expert_dtype;
+  int32_t scale_block;  /* 128 for fp8 experts, else 0 */
+} moe_config;
+
+/*
+ * Weights for moe_forward / moe_expert_ffn (device pointers).
+ *   w_gate      [N, H] act dtype (router projection, one row per expert)
+ *   logit_bias  [N] float32, nullable (added to the logits)
+ *   w13         [N, 2I, H] expert dtype: rows 0..I-1 gate projection, I..2I-1 up projection
+ *   w2          [N, H, I] expert dtype
+ *   w13_scale   fp8 only: [N, 2I/128, H/128] bf16, w = e4m3(q) * scale of its 128x128 block
+ *   w2_scale    fp8 only: [N, H/128, I/128] bf16
+ *   shared_*    the always-on expert, same layouts without the N dimension (n_shared = 1)
+ */
+typedef struct moe_weights {
+  const void* w_gate;
+  const float* logit_bias;
+  const void* w13;
+  const void* w2;
+  const void* w13_scale;
+  const void* w2_scale;
+  const void* shared_w13;
+  const void* shared_w2;
+  const void* shared_w13_scale;
+  const void* shared_w2_scale;
+} moe_weights;
+
+/*
+ * Optional places for moe_forward's intermediates.  Any non-NULL member is
+ * used instead of the workspace region for that tensor, so the caller can read
+ * it after the stream completes (route traces, replay, debugging).
+ */
+typedef struct moe_trace {
+  float* logits;             /* [T, N] */
+  int32_t* topk_ids;         /* [T, k] */
+  float* topk_gates;         /* [T, k] */
+  float* margin;             /* [T] */
+  uint8_t* route_kept;       /* [T*k] */
+  int32_t* sorted_route_ids; /* [P_max] */
+  int32_t* block_expert;     /* [ceil(P_max / B)] */
+  int32_t* expert_offsets;   /* [N + 1] */
+  int32_t* num_padded;       /* [1] */
+  int32_t* stats;            /* [N + MOE_STATS_EXTRA] */
+  void* act;                 /* [P_max, I] act dtype */
+  void* y_route;             /* [T*k, H] act dtype */
+} moe_trace;
+
+/* ABI version (MOE_ABI_VERSION) of the loaded library. */
+int32_t moe_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* moe_status_str(moe_status s);
+
+/* Host-only check of a config against the supported envelope. */
+moe_status moe_validate_config(const moe_config* cfg);
+
+/* Host-only: P_max = T*k + N*(B-1) and ceil(P_max / B) for a valid config. */
+moe_status moe_align_sizes(const moe_config* cfg, int32_t* p_max, int32_t* n_blocks);
+
+/* Host-only: workspace bytes needed by moe_align (MOE_OP_ALIGN) or moe_forward (MOE_OP_FORWARD). */
+moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes);
+
+/*
+ * Router: projection, top-k, gates, margin.
+ *   h          [T, H] act dtype (ignored with MOE_ROUTE_LOGITS_IN)
+ *   w_gate     [N, H] act dtype (ignored with MOE_ROUTE_LOGITS_IN)
+ *   logit_bias [N] float32, nullable (ignored with MOE_ROUTE_LOGITS_IN)
+ *   logits     [T, N] float32: written, or read with MOE_ROUTE_LOGITS_IN
+ *   topk_ids   [T, k] int32, rank order;  topk_gates [T, k] float32
+ *   margin     [T] float32, nullable: l_(k-1) - l_(k) in rank order, +inf when k = N
+ * Logits are accumulated in fp32 over fixed 32-wide K steps in ascending K.
+ * A NaN logit ranks below every number and carries zero gate weight; -0 == +0.
+ */
+moe_status moe_route(const moe_config* cfg, const void* h, const void* w_gate, const float* logit_bias,
+                     float* logits, int32_t* topk_ids, float* topk_gates, float* margin, uint32_t flags,
+                     void* stream);
+
+/*
+ * Capacity and alignment (deterministic: no atomic decides any order).
+ *   topk_ids         [T*k] int32 (from moe_route, or replayed by the caller)
+ *   route_kept       [T*k] uint8 out: 1 = the route runs its expert, 0 = dropped or invalid id
+ *   sorted_route_ids [P_max] int32 out: per expert (ascending), its kept route ids ascending,
+ *                    padded to a multiple of B with the sentinel T*k; the tail is sentinel
+ *   block_expert     [ceil(P_max/B)] int32 out: expert of each B-row block, -1 past the end
+ *   expert_offsets   [N+1] int32 out: first padded row of each expert; [N] = padded rows used
+ *   num_padded       [1] int32 out
+ *   stats            [N + MOE_STATS_EXTRA] int32 out, nullable: per-expert load, then the
+ *                    MOE_STAT_* counters
+ *   ws, ws_bytes     device workspace of at least moe_workspace_size(MOE_OP_ALIGN) bytes
+ */
+moe_status moe_align(const moe_config* cfg, const int32_t* topk_ids, uint8_t* route_kept,
+                     int32_t* sorted_route_ids, int32_t* block_expert, int32_t* expert_offsets,
+                     int32_t* num_padded, int32_t* stats, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Grouped SwiGLU expert FFN over aligned rows.
+ * Routed mode (sorted_route_ids != NULL): rows p in expert e's segment
+ *   [expert_offsets[e], expert_offsets[e+1]) hold route r = sorted_route_ids[p]
+ *   (token r / k); sentinel rows compute zeros and write no output row.
+ *   w13/w2 (+ scales) are the [N, ...] stacks; act is [P_max, I]; y_out is
+ *   y_route [T*k, H]: row r written for every kept route, other rows untouched.
+ * Identity mode (sorted_route_ids == NULL, expert_offsets ignored): one expert
+ *   (w13 [2I, H], w2 [H, I]) on every token row t; act is [T, I]; y_out is [T, H].
+ * act = silu(h W1^T) * (h W3^T) is stored in the act dtype (fp32 accumulation);
+ * fp8 weights are decoded and scaled to bf16 before the bf16 MFMA.  Every row's
+ * K order is fixed, so a row's results do not depend on the other rows.
+ */
+moe_status moe_expert_ffn(const moe_config* cfg, const void* h, const int32_t* sorted_route_ids,
+                          const int32_t* expert_offsets, const void* w13, const void* w2,
+                          const void* w13_scale, const void* w2_scale, void* act, void* y_out,
+                          void* stream);
+
+/*
+ * The two halves of moe_expert_ffn, for callers that want the surfaces apart
+ * (same row conventions and modes as moe_expert_ffn):
+ *   moe_expert_gate_up: act = silu(x W1^T) * (x W3^T) from the fused W13 projection
+ *                       ("Route-Block Membership Selects Packed-AWQ Arithmetic", "The
+ *                       boundary that mattered": W13 and activation surfaces);
+ *   moe_expert_down:    y rows = act W2^T (the routed second projection surface).
+ */
+moe_status moe_expert_gate_up(const moe_config* cfg, const void* h, const int32_t* sorted_route_ids,
+                              const int32_t* expert_offsets, const void* w13, const void* w13_scale, void* act,
+                              void* stream);
+moe_status moe_expert_down(const moe_config* cfg, const void* act, const int32_t* sorted_route_ids,
+                           const int32_t* expert_offsets, const void* w2, const void* w2_scale, void* y_out,
+                           void* stream);
+
+/*
+ * Combine: out[t] = round( ((sum over kept j ascending of gate[t,j] * y_route[t*k+j])
+ *                           + shared_out[t]) + residual[t] ), fp32 accumulation in exactly
+ * that order, one rounding to the act dtype.  Gates are not renormalised after a drop.
+ * A token with no kept route, no shared expert and a residual outputs its residual bitwise.
+ *   y_route [T*k, H], topk_gates [T, k] float32, route_kept [T*k] uint8,
+ *   shared_out [T, H] nullable, residual [T, H] nullable, out [T, H]; all act dtype but gates.
+ */
+moe_status moe_combine(const moe_config* cfg, const void* y_route, const float* topk_gates,
+                       const uint8_t* route_kept, const void* shared_out, const void* residual,
+                       void* out, void* stream);
+
+/*
+ * The whole layer: moe_route -> moe_align -> moe_expert_ffn (routed, then the shared
+ * expert in identity mode) -> moe_combine, on one stream, with no host synchronisation.
+ *   h [T, H], residual [T, H] nullable (pass h for the usual h + MoE(h)), out [T, H].
+ *   trace nullable (see moe_trace); ws of moe_workspace_size(MOE_OP_FORWARD) bytes.
+ */
+moe_status moe_forward(const moe_config* cfg, const moe_weights* weights, const void* h,
+                       const void* residual, void* out, const moe_trace* trace, void* ws,
+                       size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H_ */

@@ -28,7 +28,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "decode_bf16", "decode_e4m3", "dequantize_blocks", "router_logits", "rank_experts",
+    "decode_bf16", "decode_e4m3", "round_bf16", "dequantize_blocks", "router_logits", "rank_experts",
     "topk_route", "capacity", "capacity_keep", "align", "silu", "swiglu_expert",
     "expert_ffn", "combine", "routing_stats", "moe_forward",
 ]
@@ -56,6 +56,17 @@ def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     val = np.where(ex == 0, man * 2.0 ** -9, (1.0 + man / 8.0) * np.exp2(ex - 7.0))
     val = np.where((ex == 15) & (man == 7), np.nan, val)
     return sign * val
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bfloat16 value (8 significant bits), ties to even.
+
+    Diagnostic only: lets the oracle mimic a pipeline that stores intermediates
+    in bf16, to tell rounding from defects when a tolerance is approached.
+    Normal-range values only (no subnormal or overflow handling).
+    """
+    m, e = np.frexp(np.asarray(x, np.float64))
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)
 
 
 def dequantize_blocks(codes: np.ndarray, scales: np.ndarray, block: int) -> np.ndarray:
@@ -215,21 +226,25 @@ def silu(x: np.ndarray) -> np.ndarray:
     return out
 
 
-def swiglu_expert(x: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
+def swiglu_expert(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, stage_round=None) -> np.ndarray:
     """One SwiGLU expert on rows x [M, H]: y = W2 (silu(W1 x) * (W3 x)).
 
     w13 [2I, H]: rows 0..I-1 the gate projection W1, rows I..2I-1 the up
     projection W3 (the fused first projection "W13" of [RB] "The boundary that
     mattered"); w2 [H, I] the second projection.
+    ``stage_round`` (diagnostic, default off) is applied to the weights, the
+    activation and the output, to mimic a pipeline that stores them rounded.
     """
+    r = stage_round if stage_round is not None else (lambda a: a)
+    w13, w2 = r(w13), r(w2)
     I = w13.shape[0] // 2
     u = x @ w13[:I].T
     v = x @ w13[I:].T
-    return (silu(u) * v) @ w2.T
+    return r(r(silu(u) * v) @ w2.T)
 
 
 def expert_ffn(h: np.ndarray, ids: np.ndarray, kept: np.ndarray, w13_of, w2_of, N: int,
-               routes: Optional[np.ndarray] = None) -> dict:
+               routes: Optional[np.ndarray] = None, stage_round=None) -> dict:
     """y_r = expert_{ids[r]}(h_{r // k}) for every kept route r (or the given subset).
 
     [MIR] "How sparse routing works": only the k selected experts run on a token.
@@ -245,7 +260,7 @@ def expert_ffn(h: np.ndarray, ids: np.ndarray, kept: np.ndarray, w13_of, w2_of, 
         rs = todo[flat[todo] == e]
         if rs.size == 0:
             continue
-        y = swiglu_expert(np.asarray(h, np.float64)[rs // k], w13_of(e), w2_of(e))
+        y = swiglu_expert(np.asarray(h, np.float64)[rs // k], w13_of(e), w2_of(e), stage_round)
         for r, row in zip(rs.tolist(), y):
             out[r] = row
     return out

@@ -1,0 +1,123 @@
+"""C-ABI tests that need no GPU: the library loads, exports every declared entry
+point, and rejects bad arguments on the host before any HIP call.
+
+Every call here is built to fail validation (NULL or misaligned pointers, bad
+configs), so nothing is ever enqueued on a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_routing_expert_router_amd as M
+import workloads as W
+from tests.harness import config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) >= 10
+    L = M.lib()
+    for n in names:
+        assert hasattr(L, n), n
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_abi_version_and_status_strings():
+    assert M.moe_abi_version() == 1
+    for code, name in M.STATUS.items():
+        assert M.moe_status_str(code).startswith(name)
+    assert "unknown" in M.moe_status_str(99)
+
+
+@pytest.mark.parametrize("w", list(W.ALL.values()), ids=list(W.ALL))
+def test_workload_configs_are_valid(w):
+    cfg = config(w)
+    M.moe_validate_config(cfg)
+    p_max, n_blocks = M.moe_align_sizes(cfg)
+    assert p_max == w.T * w.k + w.N * (w.B - 1)
+    assert n_blocks == -(-p_max // w.B)
+    assert M.moe_workspace_size(cfg, M.MOE_OP_ALIGN) > 0
+    fwd = M.moe_workspace_size(cfg, M.MOE_OP_FORWARD)
+    act = 4 if w.act_dtype == W.F32 else 2
+    assert fwd >= p_max * w.I * act + w.T * w.k * w.H * act
+
+
+BAD = [
+    dict(T=0), dict(T=65537), dict(H=100), dict(H=0), dict(I=64), dict(N=0), dict(N=257), dict(k=0),
+    dict(k=9, N=16), dict(k=3, N=2), dict(B=12), dict(B=256), dict(cap_num=5, cap_den=0),
+    dict(cap_num=-1, cap_den=4), dict(n_shared=2), dict(renormalize=2),
+]
+
+
+@pytest.mark.parametrize("bad", BAD, ids=[str(b) for b in BAD])
+def test_invalid_configs_rejected(bad):
+    cfg = config(W.MIXTRAL_BF16, **bad)
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_validate_config(cfg)
+    assert ei.value.name == "MOE_ERR_INVALID_CONFIG"
+
+
+def test_unsupported_dtype_combinations():
+    for act, exp, sb in (("f32", "bf16", 0), ("bf16", "f32", 0), ("f32", "fp8_e4m3", 128), ("bf16", "fp8_e4m3", 64)):
+        cfg = M.make_config(64, 128, 8, 2, 256, 8, act_dtype=act, expert_dtype=exp, scale_block=sb)
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_validate_config(cfg)
+        assert ei.value.name == "MOE_ERR_UNSUPPORTED"
+    cfg = config(W.MIXTRAL_BF16)
+    cfg.struct_size = 8
+    with pytest.raises(M.MoeError):
+        M.moe_validate_config(cfg)
+
+
+def _expect(name, fn, *args, **kw):
+    with pytest.raises(M.MoeError) as ei:
+        fn(*args, **kw)
+    assert ei.value.name == name, ei.value
+
+
+def test_host_validation_of_pointers_and_workspace():
+    cfg = config(W.MIXTRAL_BF16)
+    A, ODD = 4096, 4098  # stand-in addresses: never dereferenced, every call below fails validation
+    s = 0
+    # route
+    _expect("MOE_ERR_NULL_POINTER", M.moe_route, cfg, A, A, None, None, A, A, None, 0, s)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_route, cfg, None, A, None, A, A, A, None, 0, s)
+    _expect("MOE_ERR_MISALIGNED", M.moe_route, cfg, ODD, A, None, A, A, A, None, 0, s)
+    _expect("MOE_ERR_MISALIGNED", M.moe_route, cfg, A, A, None, A + 1, A, A, None, M.MOE_ROUTE_LOGITS_IN, s)
+    _expect("MOE_ERR_UNSUPPORTED", M.moe_route, cfg, A, A, None, A, A, A, None, 0x10, s)
+    # align
+    _expect("MOE_ERR_NULL_POINTER", M.moe_align, cfg, A, A, A, A, A, None, None, A, 1 << 20, s)
+    _expect("MOE_ERR_MISALIGNED", M.moe_align, cfg, A + 2, A, A, A, A, A, None, A, 1 << 20, s)
+    _expect("MOE_ERR_WORKSPACE_TOO_SMALL", M.moe_align, cfg, A, A, A, A, A, A, None, A, 4, s)
+    # expert ffn
+    _expect("MOE_ERR_NULL_POINTER", M.moe_expert_ffn, cfg, A, A, None, A, A, None, None, A, A, s)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_expert_ffn, cfg, A, None, None, None, A, None, None, A, A, s)
+    _expect("MOE_ERR_MISALIGNED", M.moe_expert_ffn, cfg, A, None, None, A, A, None, None, A + 8, A, s)
+    cfg8 = config(W.DEEPSEEKV3_FP8)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_expert_ffn, cfg8, A, None, None, A, A, None, None, A, A, s)
+    # combine
+    _expect("MOE_ERR_NULL_POINTER", M.moe_combine, cfg, A, A, None, None, None, A, s)
+    _expect("MOE_ERR_MISALIGNED", M.moe_combine, cfg, A, A, A, None, ODD, A, s)
+    # forward
+    _expect("MOE_ERR_NULL_POINTER", M.moe_forward, cfg, {"w_gate": A, "w13": A}, A, None, A, None, A, 1 << 40, s)
+    full = {"w_gate": A, "w13": A, "w2": A}
+    _expect("MOE_ERR_WORKSPACE_TOO_SMALL", M.moe_forward, cfg, full, A, None, A, None, A, 1024, s)
+    _expect("MOE_ERR_MISALIGNED", M.moe_forward, cfg, full, A, None, A, None, A + 16, 1 << 40, s)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_forward, cfg8, full, A, None, A, None, A, 1 << 40, s)
+    bad = config(W.MIXTRAL_BF16, k=0)
+    _expect("MOE_ERR_INVALID_CONFIG", M.moe_forward, bad, full, A, None, A, None, A, 1 << 40, s)
+
+
+def test_workspace_op_codes():
+    cfg = config(W.TOY_FP32)
+    _expect("MOE_ERR_INVALID_CONFIG", M.moe_workspace_size, cfg, 7)

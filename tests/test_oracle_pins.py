@@ -63,6 +63,20 @@ def test_decode_bf16_matches_torch():
     assert np.array_equal(ours, b.to(torch.float64).numpy())
 
 
+def test_round_bf16_matches_torch_cast_on_fp32_values():
+    g = torch.Generator().manual_seed(11)
+    x = torch.cat([torch.randn(20000, generator=g) * 10 ** float(p) for p in range(-6, 7)])
+    # include exact ties: values halfway between two bf16 neighbours
+    b = x.to(torch.bfloat16)
+    up = (b.view(torch.int16) + 1).view(torch.bfloat16).float()  # next bf16 away from zero
+    mid = (b.float() + up) / 2                                     # exact in fp32: a rounding tie
+    assert torch.all(mid != b.float())
+    for v in (x, mid):
+        ours = O.round_bf16(v.double().numpy())
+        ref = v.to(torch.bfloat16).double().numpy()
+        assert np.array_equal(ours, ref)
+
+
 def test_dequantize_blocks_hand_fixture():
     d, _ = _read_fixture("fp8_blocks.txt")
     blk = int(d["block"])

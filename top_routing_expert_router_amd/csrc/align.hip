@@ -1,0 +1,223 @@
+// Capacity and alignment: a deterministic stable counting sort of the kept routes
+// by (expert id, flattened route id), padded to whole B-row blocks per expert.
+//
+// "Route-Block Membership Selects Packed-AWQ Arithmetic": routed rows are grouped
+// by expert and padded into fixed-size blocks ("The bookkeeping before the matrix
+// multiplication"); the stable construction orders valid routes by expert id and
+// flattened route id instead of atomic arrival order ("Stable construction
+// selected a third trajectory").  "Mixture-of-experts routing & LLM
+// repeatability", paragraph on expert capacity: capacity = tokens/experts x
+// factor, overflow skips the expert, capacity is filled in order -- here in
+// ascending route id.  "Mixture-of-Experts Routing at Inference Time", "Worked
+// example" and "The hard part": per-expert load = bincount of the flattened ids;
+// dropped = sum of max(load - capacity, 0).
+//
+// Three kernels on one stream:
+//   hist    : per chunk of kChunk routes, per-expert counts (LDS atomics only count;
+//             a count does not depend on the order the increments land in)
+//   scan    : one workgroup: per expert, exclusive prefix of the chunk counts (in
+//             place), capacity, padded segment sizes, expert offsets, block map, stats
+//   scatter : per chunk, each route's position among the routes to its expert is
+//             chunk prefix + the count of earlier routes in the chunk with the same
+//             expert (ballot peer masks, waves in order) -- no atomic decides a slot.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kChunk = 1024;        // routes per chunk (4 waves x 4 steps x 64 lanes)
+constexpr int kThreads = 256;
+constexpr int kStepsPerWave = kChunk / (4 * kWave);
+
+__global__ __launch_bounds__(kThreads) void align_hist(const int32_t* __restrict__ ids, int R, int N,
+                                                       int32_t* __restrict__ counts) {
+  __shared__ int cnt[257];
+  for (int i = threadIdx.x; i <= N; i += kThreads) cnt[i] = 0;
+  __syncthreads();
+  const int r0 = blockIdx.x * kChunk;
+  for (int i = threadIdx.x; i < kChunk; i += kThreads) {
+    const int r = r0 + i;
+    if (r >= R) break;
+    const int e = ids[r];
+    atomicAdd(&cnt[(e >= 0 && e < N) ? e : N], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i <= N; i += kThreads) counts[(size_t)blockIdx.x * (N + 1) + i] = cnt[i];
+}
+
+__global__ __launch_bounds__(kThreads) void align_scan(int32_t* __restrict__ counts, int nchunks, int N, int B,
+                                                       int cap, int n_blocks,
+                                                       int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ num_padded,
+                                                       int32_t* __restrict__ stats, int sentinel) {
+  __shared__ int wave_tot[4];
+  __shared__ int red[4][4];
+  const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+  int load = 0;
+  if (e < N) {
+    for (int c = 0; c < nchunks; ++c) {
+      int32_t* p = counts + (size_t)c * (N + 1) + e;
+      const int v = *p;
+      *p = load;  // exclusive prefix over chunks, in place
+      load += v;
+    }
+  }
+  int invalid = 0;
+  if (e == 0)
+    for (int c = 0; c < nchunks; ++c) invalid += counts[(size_t)c * (N + 1) + N];
+  const int kept = e < N ? (cap < 0 ? load : min(load, cap)) : 0;
+  const int padded = ceil_div(kept, B) * B;
+  // exclusive scan of padded sizes over experts: per wave, then across waves in order
+  const int incl = wave_incl_scan_i32(padded);
+  if (lane == 63) wave_tot[wave] = incl;
+  // per-wave partial stats (kept sum, max load, min load over valid experts)
+  int ksum = wave_sum_i32(kept);
+  int mx = e < N ? load : 0, mn = e < N ? load : 0x7fffffff;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    mx = max(mx, __shfl_xor(mx, m, kWave));
+    mn = min(mn, __shfl_xor(mn, m, kWave));
+  }
+  if (lane == 0) {
+    red[wave][0] = ksum;
+    red[wave][1] = mx;
+    red[wave][2] = mn;
+  }
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wave_tot[w];
+  const int total = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+  const int off = base + incl - padded;
+  if (e < N) {
+    offsets[e] = off;
+    for (int i = off + kept; i < off + padded; ++i) sorted_ids[i] = sentinel;
+    for (int b = off / B; b < (off + padded) / B; ++b) block_expert[b] = e;
+    if (stats) stats[e] = load;
+  }
+  if (e == 0) {
+    offsets[N] = total;
+    *num_padded = total;
+  }
+  for (int b = total / B + threadIdx.x; b < n_blocks; b += kThreads) block_expert[b] = -1;
+  if (stats && e == 0) {
+    int ks = 0, mxx = 0, mnn = 0x7fffffff;
+    for (int w = 0; w < 4; ++w) {
+      ks += red[w][0];
+      mxx = max(mxx, red[w][1]);
+      mnn = min(mnn, red[w][2]);
+    }
+    stats[N + MOE_STAT_KEPT] = ks;
+    stats[N + MOE_STAT_DROPPED] = (sentinel - invalid) - ks;  // valid routes not kept
+    stats[N + MOE_STAT_INVALID] = invalid;
+    stats[N + MOE_STAT_CAPACITY] = cap;
+    stats[N + MOE_STAT_MAX_LOAD] = mxx;
+    stats[N + MOE_STAT_MIN_LOAD] = mnn;
+    stats[N + MOE_STAT_NUM_PADDED] = total;
+    stats[N + MOE_STAT_RESERVED] = 0;
+  }
+}
+
+// Lanes whose keys are equal (keys in [0, 512)).
+__device__ __forceinline__ uint64_t peer_mask(int key) {
+  uint64_t peers = __ballot(1);
+#pragma unroll
+  for (int b = 0; b < 9; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    peers &= bit ? bal : ~bal;
+  }
+  return peers;
+}
+
+__global__ __launch_bounds__(kThreads) void align_scatter(const int32_t* __restrict__ ids, int R, int N, int cap,
+                                                          const int32_t* __restrict__ chunk_base,
+                                                          const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ num_padded, int p_max,
+                                                          uint8_t* __restrict__ kept_out,
+                                                          int32_t* __restrict__ sorted_ids, int sentinel) {
+  __shared__ int run[4][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int i = threadIdx.x; i < 4 * 256; i += kThreads) (&run[0][0])[i] = 0;
+  __syncthreads();
+  const int rw = blockIdx.x * kChunk + wave * (kStepsPerWave * kWave);
+  // pass 1: per-wave counts per expert
+  for (int s = 0; s < kStepsPerWave; ++s) {
+    const int r = rw + s * kWave + lane;
+    const int e = r < R ? ids[r] : -1;
+    const bool valid = e >= 0 && e < N;
+    const int key = valid ? e : 256;
+    const uint64_t peers = peer_mask(key);
+    if (valid && (peers & lt) == 0) run[wave][e] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  // per-wave starting positions: chunk prefix + counts of earlier waves, in wave order
+  for (int e = threadIdx.x; e < N; e += kThreads) {
+    int acc = chunk_base[(size_t)blockIdx.x * (N + 1) + e];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = run[w][e];
+      run[w][e] = acc;
+      acc += c;
+    }
+  }
+  __syncthreads();
+  // pass 2: position of each route among all routes to its expert (route-id order)
+  for (int s = 0; s < kStepsPerWave; ++s) {
+    const int r = rw + s * kWave + lane;
+    const int e = r < R ? ids[r] : -1;
+    const bool valid = e >= 0 && e < N;
+    const int key = valid ? e : 256;
+    const uint64_t peers = peer_mask(key);
+    int pos = 0;
+    if (valid) pos = run[wave][e] + __popcll(peers & lt);
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (peers & lt) == 0) run[wave][e] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+    const bool keep = valid && (cap < 0 || pos < cap);
+    if (keep) sorted_ids[offsets[e] + pos] = r;
+    if (r < R) kept_out[r] = keep ? 1 : 0;
+  }
+  // sentinel tail of the padded row list
+  const int np = *num_padded;
+  for (int i = np + blockIdx.x * kThreads + threadIdx.x; i < p_max; i += gridDim.x * kThreads) sorted_ids[i] = sentinel;
+}
+
+}  // namespace
+
+int align_chunk_routes() { return kChunk; }
+
+size_t align_workspace_bytes(const moe_config& c) {
+  const long R = (long)c.T * c.k;
+  const long nchunks = (R + kChunk - 1) / kChunk;
+  return (size_t)(nchunks * (c.N + 1)) * sizeof(int32_t);
+}
+
+hipError_t launch_align(const moe_config& c, const int32_t* ids, uint8_t* kept, int32_t* sorted_ids,
+                        int32_t* block_expert, int32_t* offsets, int32_t* num_padded, int32_t* stats, void* ws,
+                        hipStream_t s) {
+  const int R = c.T * c.k;
+  const int nchunks = ceil_div(R, kChunk);
+  const int p_max = R + c.N * (c.B - 1);
+  const int n_blocks = ceil_div(p_max, c.B);
+  int cap = -1;
+  if (!(c.cap_num == 0 && c.cap_den == 0)) {
+    const long long cl = ((long long)c.T * c.k * c.cap_num) / ((long long)c.N * c.cap_den);
+    cap = cl > 0x7fffffffLL ? 0x7fffffff : (int)cl;
+  }
+  int32_t* counts = (int32_t*)ws;
+  align_hist<<<nchunks, kThreads, 0, s>>>(ids, R, c.N, counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  align_scan<<<1, kThreads, 0, s>>>(counts, nchunks, c.N, c.B, cap, n_blocks, sorted_ids, block_expert, offsets,
+                                    num_padded, stats, R);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  align_scatter<<<nchunks, kThreads, 0, s>>>(ids, R, c.N, cap, counts, offsets, num_padded, p_max, kept, sorted_ids, R);
+  err = hipGetLastError();
+  return err;
+}
+
+}  // namespace moe

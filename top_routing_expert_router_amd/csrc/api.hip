@@ -1,0 +1,302 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace layout, and the moe_forward composition on one stream.
+// Validation runs before any HIP call, so every error path is host-only.
+#include <string.h>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return MOE_ERR_NULL_POINTER;
+  if (c->struct_size < sizeof(moe_config)) return MOE_ERR_INVALID_CONFIG;
+  if (c->T < 1 || c->T > 65536) return MOE_ERR_INVALID_CONFIG;
+  if (c->H < 128 || c->H > 32768 || c->H % 128) return MOE_ERR_INVALID_CONFIG;
+  if (c->I < 128 || c->I > 32768 || c->I % 128) return MOE_ERR_INVALID_CONFIG;
+  if (c->N < 1 || c->N > 256) return MOE_ERR_INVALID_CONFIG;
+  if (c->k < 1 || c->k > 8 || c->k > c->N) return MOE_ERR_INVALID_CONFIG;
+  if (!(c->B == 8 || c->B == 16 || c->B == 32 || c->B == 64 || c->B == 128)) return MOE_ERR_INVALID_CONFIG;
+  const bool dropless = c->cap_num == 0 && c->cap_den == 0;
+  if (!dropless && (c->cap_num <= 0 || c->cap_den <= 0)) return MOE_ERR_INVALID_CONFIG;
+  if (c->n_shared != 0 && c->n_shared != 1) return MOE_ERR_INVALID_CONFIG;
+  if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_CONFIG;
+  const bool f32 = c->act_dtype == MOE_F32 && c->expert_dtype == MOE_F32 && c->scale_block == 0;
+  const bool bf16 = c->act_dtype == MOE_BF16 && c->expert_dtype == MOE_BF16 && c->scale_block == 0;
+  const bool fp8 = c->act_dtype == MOE_BF16 && c->expert_dtype == MOE_FP8_E4M3 && c->scale_block == 128;
+  if (!(f32 || bf16 || fp8)) {
+    const bool known = (c->act_dtype == MOE_F32 || c->act_dtype == MOE_BF16) &&
+                       (c->expert_dtype >= MOE_F32 && c->expert_dtype <= MOE_FP8_E4M3);
+    return known ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_CONFIG;
+  }
+  return MOE_OK;
+}
+
+size_t act_size(const moe_config& c) { return c.act_dtype == MOE_F32 ? 4 : 2; }
+long p_max_of(const moe_config& c) { return (long)c.T * c.k + (long)c.N * (c.B - 1); }
+long n_blocks_of(const moe_config& c) { return (p_max_of(c) + c.B - 1) / c.B; }
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Regions of the moe_forward workspace, in order, each 256-byte aligned.
+struct FwdLayout {
+  size_t logits, ids, gates, margin, kept, sorted, blocks, offsets, npad, stats, align_ws, act, y, sact, sout, total;
+};
+
+FwdLayout forward_layout(const moe_config& c) {
+  FwdLayout L{};
+  const size_t T = c.T, N = c.N, R = (size_t)c.T * c.k, P = p_max_of(c), a = act_size(c);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round_up(bytes);
+    return at;
+  };
+  L.logits = take(T * N * 4);
+  L.ids = take(R * 4);
+  L.gates = take(R * 4);
+  L.margin = take(T * 4);
+  L.kept = take(R);
+  L.sorted = take(P * 4);
+  L.blocks = take(n_blocks_of(c) * 4);
+  L.offsets = take((N + 1) * 4);
+  L.npad = take(4);
+  L.stats = take((N + MOE_STATS_EXTRA) * 4);
+  L.align_ws = take(align_workspace_bytes(c));
+  L.act = take(P * (size_t)c.I * a);
+  L.y = take(R * (size_t)c.H * a);
+  L.sact = c.n_shared ? take(T * (size_t)c.I * a) : o;
+  L.sout = c.n_shared ? take(T * (size_t)c.H * a) : o;
+  L.total = o;
+  return L;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status check_route_args(const moe_config& c, const void* h, const void* w_gate, const float* bias,
+                            const float* logits, const int32_t* ids, const float* gates, const float* margin,
+                            uint32_t flags) {
+  if (flags & ~(uint32_t)MOE_ROUTE_LOGITS_IN) return MOE_ERR_UNSUPPORTED;
+  const bool in = flags & MOE_ROUTE_LOGITS_IN;
+  if (!logits || !ids || !gates) return MOE_ERR_NULL_POINTER;
+  if (!in && (!h || !w_gate)) return MOE_ERR_NULL_POINTER;
+  if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4) || (margin && !aligned(margin, 4)))
+    return MOE_ERR_MISALIGNED;
+  if (!in && (!aligned(h, 16) || !aligned(w_gate, 16) || (bias && !aligned(bias, 4)))) return MOE_ERR_MISALIGNED;
+  (void)c;
+  return MOE_OK;
+}
+
+moe_status check_align_args(const int32_t* ids, const uint8_t* kept, const int32_t* sorted, const int32_t* blocks,
+                            const int32_t* offsets, const int32_t* npad, const int32_t* stats, const void* ws) {
+  if (!ids || !kept || !sorted || !blocks || !offsets || !npad || !ws) return MOE_ERR_NULL_POINTER;
+  if (!aligned(ids, 4) || !aligned(sorted, 4) || !aligned(blocks, 4) || !aligned(offsets, 4) || !aligned(npad, 4) ||
+      (stats && !aligned(stats, 4)) || !aligned(ws, 16))
+    return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+moe_status check_ffn_args(const moe_config& c, const void* h, const int32_t* sorted, const int32_t* offsets,
+                          const void* w13, const void* w2, const void* s13, const void* s2, const void* act,
+                          const void* y) {
+  if (!h || !w13 || !w2 || !act || !y) return MOE_ERR_NULL_POINTER;
+  if (sorted && !offsets) return MOE_ERR_NULL_POINTER;
+  const bool fp8 = c.expert_dtype == MOE_FP8_E4M3;
+  if (fp8 && (!s13 || !s2)) return MOE_ERR_NULL_POINTER;
+  if (!aligned(h, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(act, 16) || !aligned(y, 16))
+    return MOE_ERR_MISALIGNED;
+  if ((sorted && !aligned(sorted, 4)) || (offsets && !aligned(offsets, 4))) return MOE_ERR_MISALIGNED;
+  if (fp8 && (!aligned(s13, 2) || !aligned(s2, 2))) return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+moe_status check_combine_args(const void* y, const float* gates, const uint8_t* kept, const void* shared,
+                              const void* residual, const void* out) {
+  if (!y || !gates || !kept || !out) return MOE_ERR_NULL_POINTER;
+  if (!aligned(y, 16) || !aligned(gates, 4) || !aligned(out, 16) || (shared && !aligned(shared, 16)) ||
+      (residual && !aligned(residual, 16)))
+    return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL_POINTER: return "MOE_ERR_NULL_POINTER: a required pointer is NULL";
+    case MOE_ERR_INVALID_CONFIG: return "MOE_ERR_INVALID_CONFIG: config outside the supported envelope";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: dtype combination or flag not implemented";
+    case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED: pointer alignment rule violated";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL: workspace below moe_workspace_size";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP runtime call or kernel launch failed";
+    default: return "unknown moe_status";
+  }
+}
+
+moe_status moe_validate_config(const moe_config* cfg) { return check_config(cfg); }
+
+moe_status moe_align_sizes(const moe_config* cfg, int32_t* p_max, int32_t* n_blocks) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!p_max || !n_blocks) return MOE_ERR_NULL_POINTER;
+  *p_max = (int32_t)p_max_of(*cfg);
+  *n_blocks = (int32_t)n_blocks_of(*cfg);
+  return MOE_OK;
+}
+
+moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_NULL_POINTER;
+  if (op == MOE_OP_ALIGN) {
+    *bytes = round_up(align_workspace_bytes(*cfg));
+    return MOE_OK;
+  }
+  if (op == MOE_OP_FORWARD) {
+    *bytes = forward_layout(*cfg).total;
+    return MOE_OK;
+  }
+  return MOE_ERR_INVALID_CONFIG;
+}
+
+moe_status moe_route(const moe_config* cfg, const void* h, const void* w_gate, const float* logit_bias, float* logits,
+                     int32_t* topk_ids, float* topk_gates, float* margin, uint32_t flags, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  st = check_route_args(*cfg, h, w_gate, logit_bias, logits, topk_ids, topk_gates, margin, flags);
+  if (st != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (!(flags & MOE_ROUTE_LOGITS_IN)) {
+    st = hip_status(launch_router_logits(*cfg, h, w_gate, logit_bias, logits, s));
+    if (st != MOE_OK) return st;
+  }
+  return hip_status(launch_topk(*cfg, logits, topk_ids, topk_gates, margin, s));
+}
+
+moe_status moe_align(const moe_config* cfg, const int32_t* topk_ids, uint8_t* route_kept, int32_t* sorted_route_ids,
+                     int32_t* block_expert, int32_t* expert_offsets, int32_t* num_padded, int32_t* stats, void* ws,
+                     size_t ws_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  st = check_align_args(topk_ids, route_kept, sorted_route_ids, block_expert, expert_offsets, num_padded, stats, ws);
+  if (st != MOE_OK) return st;
+  if (ws_bytes < align_workspace_bytes(*cfg)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(launch_align(*cfg, topk_ids, route_kept, sorted_route_ids, block_expert, expert_offsets,
+                                 num_padded, stats, ws, (hipStream_t)stream));
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const void* h, const int32_t* sorted_route_ids,
+                          const int32_t* expert_offsets, const void* w13, const void* w2, const void* w13_scale,
+                          const void* w2_scale, void* act, void* y_out, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  st = check_ffn_args(*cfg, h, sorted_route_ids, expert_offsets, w13, w2, w13_scale, w2_scale, act, y_out);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_expert_ffn(*cfg, h, sorted_route_ids, expert_offsets, w13, w2, w13_scale, w2_scale, act,
+                                      y_out, sorted_route_ids == nullptr, (hipStream_t)stream));
+}
+
+moe_status moe_expert_gate_up(const moe_config* cfg, const void* h, const int32_t* sorted_route_ids,
+                              const int32_t* expert_offsets, const void* w13, const void* w13_scale, void* act,
+                              void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const bool fp8 = cfg->expert_dtype == MOE_FP8_E4M3;
+  if (!h || !w13 || !act || (sorted_route_ids && !expert_offsets) || (fp8 && !w13_scale)) return MOE_ERR_NULL_POINTER;
+  if (!aligned(h, 16) || !aligned(w13, 16) || !aligned(act, 16) || (sorted_route_ids && !aligned(sorted_route_ids, 4)) ||
+      (expert_offsets && !aligned(expert_offsets, 4)) || (fp8 && !aligned(w13_scale, 2)))
+    return MOE_ERR_MISALIGNED;
+  return hip_status(launch_gate_up(*cfg, h, sorted_route_ids, expert_offsets, w13, w13_scale, act,
+                                   sorted_route_ids == nullptr, (hipStream_t)stream));
+}
+
+moe_status moe_expert_down(const moe_config* cfg, const void* act, const int32_t* sorted_route_ids,
+                           const int32_t* expert_offsets, const void* w2, const void* w2_scale, void* y_out,
+                           void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const bool fp8 = cfg->expert_dtype == MOE_FP8_E4M3;
+  if (!act || !w2 || !y_out || (sorted_route_ids && !expert_offsets) || (fp8 && !w2_scale)) return MOE_ERR_NULL_POINTER;
+  if (!aligned(act, 16) || !aligned(w2, 16) || !aligned(y_out, 16) || (sorted_route_ids && !aligned(sorted_route_ids, 4)) ||
+      (expert_offsets && !aligned(expert_offsets, 4)) || (fp8 && !aligned(w2_scale, 2)))
+    return MOE_ERR_MISALIGNED;
+  return hip_status(launch_down(*cfg, act, sorted_route_ids, expert_offsets, w2, w2_scale, y_out,
+                                sorted_route_ids == nullptr, (hipStream_t)stream));
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* y_route, const float* topk_gates, const uint8_t* route_kept,
+                       const void* shared_out, const void* residual, void* out, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  st = check_combine_args(y_route, topk_gates, route_kept, shared_out, residual, out);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_combine(*cfg, y_route, topk_gates, route_kept, shared_out, residual, out,
+                                   (hipStream_t)stream));
+}
+
+moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void* h, const void* residual, void* out,
+                       const moe_trace* trace, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const moe_config& c = *cfg;
+  if (!wt || !h || !out || !ws) return MOE_ERR_NULL_POINTER;
+  if (!wt->w_gate || !wt->w13 || !wt->w2) return MOE_ERR_NULL_POINTER;
+  const bool fp8 = c.expert_dtype == MOE_FP8_E4M3;
+  if (fp8 && (!wt->w13_scale || !wt->w2_scale)) return MOE_ERR_NULL_POINTER;
+  if (c.n_shared && (!wt->shared_w13 || !wt->shared_w2)) return MOE_ERR_NULL_POINTER;
+  if (c.n_shared && fp8 && (!wt->shared_w13_scale || !wt->shared_w2_scale)) return MOE_ERR_NULL_POINTER;
+  if (!aligned(h, 16) || !aligned(out, 16) || (residual && !aligned(residual, 16)) || !aligned(ws, 256) ||
+      !aligned(wt->w_gate, 16) || !aligned(wt->w13, 16) || !aligned(wt->w2, 16) ||
+      (wt->logit_bias && !aligned(wt->logit_bias, 4)) ||
+      (c.n_shared && (!aligned(wt->shared_w13, 16) || !aligned(wt->shared_w2, 16))))
+    return MOE_ERR_MISALIGNED;
+  const FwdLayout L = forward_layout(c);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  char* base = (char*)ws;
+  moe_trace tr{};
+  if (trace) tr = *trace;
+  auto pick = [&](void* user, size_t off) -> void* { return user ? user : (void*)(base + off); };
+  float* logits = (float*)pick(tr.logits, L.logits);
+  int32_t* ids = (int32_t*)pick(tr.topk_ids, L.ids);
+  float* gates = (float*)pick(tr.topk_gates, L.gates);
+  float* margin = (float*)pick(tr.margin, L.margin);
+  uint8_t* kept = (uint8_t*)pick(tr.route_kept, L.kept);
+  int32_t* sorted = (int32_t*)pick(tr.sorted_route_ids, L.sorted);
+  int32_t* blocks = (int32_t*)pick(tr.block_expert, L.blocks);
+  int32_t* offsets = (int32_t*)pick(tr.expert_offsets, L.offsets);
+  int32_t* npad = (int32_t*)pick(tr.num_padded, L.npad);
+  int32_t* stats = (int32_t*)pick(tr.stats, L.stats);
+  void* act = pick(tr.act, L.act);
+  void* y = pick(tr.y_route, L.y);
+  if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4) || !aligned(margin, 4) || !aligned(sorted, 4) ||
+      !aligned(blocks, 4) || !aligned(offsets, 4) || !aligned(npad, 4) || !aligned(stats, 4) || !aligned(act, 16) ||
+      !aligned(y, 16))
+    return MOE_ERR_MISALIGNED;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_router_logits(c, h, wt->w_gate, wt->logit_bias, logits, s);
+  if (e == hipSuccess) e = launch_topk(c, logits, ids, gates, margin, s);
+  if (e == hipSuccess)
+    e = launch_align(c, ids, kept, sorted, blocks, offsets, npad, stats, base + L.align_ws, s);
+  if (e == hipSuccess)
+    e = launch_expert_ffn(c, h, sorted, offsets, wt->w13, wt->w2, wt->w13_scale, wt->w2_scale, act, y, false, s);
+  const void* shared_out = nullptr;
+  if (e == hipSuccess && c.n_shared) {
+    e = launch_expert_ffn(c, h, nullptr, nullptr, wt->shared_w13, wt->shared_w2, wt->shared_w13_scale,
+                          wt->shared_w2_scale, base + L.sact, base + L.sout, true, s);
+    shared_out = base + L.sout;
+  }
+  if (e == hipSuccess) e = launch_combine(c, y, gates, kept, shared_out, residual, out, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,458 @@
+// Grouped SwiGLU expert FFN over aligned rows, on gfx950 bf16 MFMA.
+//
+// "Route-Block Membership Selects Packed-AWQ Arithmetic", "The boundary that
+// mattered": the expert path is the fused first projection W13, the activation,
+// and the routed second projection W2, applied to padded expert blocks.  The
+// FFN form is SwiGLU: act = silu(h W1^T) * (h W3^T), y = act W2^T, with W13 rows
+// 0..I-1 = W1 (gate) and I..2I-1 = W3 (up).
+//
+// Unlike the packed kernel studied on that page, no row's arithmetic depends on
+// the block it lands in: there is no split-K and no schedule class; every output
+// element is one MFMA chain over K in ascending 16-wide steps ("Why
+// temperature=0 Still Gives Different Answers: Batch Invariance", tier 2: one
+// tile configuration, no atomic split-K).  Rows are independent, so permuting
+// routes inside or across blocks leaves each row's bits unchanged.
+//
+// Kernel shape (bf16 / fp8-weight path):
+//   workgroup tile 256 rows x 256 weight rows, K step 64, 4 waves of 128 x 128,
+//   v_mfma_f32_32x32x16_bf16 with weights as the MFMA "A" operand, so each lane
+//   ends with 4 consecutive output columns of one row (8-byte stores);
+//   two LDS stages of (256 x 64) bf16 for each operand, 16-byte chunks XOR-swizzled
+//   by (row & 7) so 8 consecutive rows hit distinct banks;
+//   global -> register -> LDS staging, one barrier per K step;
+//   the A-row gather (route -> token row of h) is fused into the tile load;
+//   W13 tiles hold 128 gate rows and the matching 128 up rows, so SwiGLU is a
+//   register-local epilogue; W2 writes each row straight to its route's y row;
+//   M tiles are 256-row slices of one expert's padded segment (a fixed constant,
+//   decoupled from B); workgroups map to XCDs so each XCD walks a contiguous
+//   run of (n-tile group, m-tile) pairs and shares weight tiles in its L2.
+// fp8 weights: E4M3FN codes are decoded with the hardware converter, multiplied
+// by their 128x128 block's bf16 scale in fp32, and rounded to bf16 on the way into LDS.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kThreads = 256;
+constexpr int kStageBytes = (BM + BN) * BK * 2;  // one stage: A tile + B tile, bf16
+constexpr int kGroupN = 8;                        // n-tiles per raster group
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+struct FfnArgs {
+  const void* x;          // W13: h [T, H];  W2: act [rows, I]
+  const int32_t* sorted;  // routed: sorted_route_ids; identity: nullptr
+  const int32_t* offsets; // routed: expert_offsets [N + 1]
+  const void* w;          // W13: [E, 2I, H];  W2: [E, H, I]
+  const __bf16* wscale;   // fp8 block scales or nullptr
+  void* out;              // W13: act [rows, I];  W2: y [*, H]
+  int T, H, I, N, k;
+  int sentinel;           // T*k: padding row marker; any id outside [0, T*k) is treated as padding
+  int rows;               // rows of the act buffer (P_max routed, T identity): no row index reaches it
+  int mtiles;             // M-tile bound used for the grid
+  int ntiles;
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * (BK * 2) + ((chunk ^ (row & 7)) << 4); }
+
+// Resolve M-tile m to (expert, first row, end row) from the expert offsets.
+// Each expert's padded segment is cut into ceil(len / BM) tiles in expert order.
+__device__ bool resolve_tile(const FfnArgs& a, int m, int& e, int& p0, int& p1, int* sh) {
+  if (a.sorted == nullptr) {
+    e = 0;
+    p0 = m * BM;
+    p1 = min(a.T, p0 + BM);
+    return p0 < a.T;
+  }
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    int cnt[4], beg[4];
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ee = lane * 4 + i;
+      beg[i] = ee < a.N ? a.offsets[ee] : 0;
+      const int end = ee < a.N ? a.offsets[ee + 1] : 0;
+      cnt[i] = ee < a.N ? ceil_div(end - beg[i], BM) : 0;
+      s += cnt[i];
+    }
+    const int incl = wave_incl_scan_i32(s);
+    int before = incl - s;
+    if (lane == 0) sh[0] = -1;
+    __builtin_amdgcn_wave_barrier();
+    if (m >= before && m < incl) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (m >= before && m < before + cnt[i]) {
+          const int ee = lane * 4 + i;
+          sh[0] = ee;
+          sh[1] = beg[i] + (m - before) * BM;
+          sh[2] = min(min(a.offsets[ee + 1], sh[1] + BM), a.rows);
+        }
+        before += cnt[i];
+      }
+    }
+  }
+  __syncthreads();
+  e = sh[0];
+  p0 = sh[1];
+  p1 = sh[2];
+  return e >= 0 && p0 >= 0 && p0 < p1;
+}
+
+template <bool FP8>
+struct WeightStage;
+
+template <>
+struct WeightStage<false> {
+  u32x4 v[8];
+};
+template <>
+struct WeightStage<true> {
+  u32x2 v[8];
+};
+
+// MODE 0: W13 + SwiGLU -> act.  MODE 1: W2 -> y rows.
+template <int MODE, bool FP8>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffn_gemm_bf16(FfnArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
+  __shared__ int tile_sh[4];
+
+  // ---- tile selection: XCD-contiguous logical ids, grouped raster over n-tiles
+  const int G = a.mtiles * a.ntiles;
+  const int bid = blockIdx.x;
+  const int lid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+  if (lid >= G) return;
+  const int group = lid / (kGroupN * a.mtiles);
+  const int gn0 = group * kGroupN;
+  const int gsize = min(kGroupN, a.ntiles - gn0);
+  const int idx = lid - group * kGroupN * a.mtiles;
+  const int mt = idx / gsize, nt = gn0 + idx % gsize;
+  int e, p0, p1;
+  if (!resolve_tile(a, mt, e, p0, p1, tile_sh)) return;
+
+  const int K = MODE == 0 ? a.H : a.I;
+  const int WR = MODE == 0 ? 2 * a.I : a.H;  // weight rows per expert
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = tid & 7, rb = tid >> 3;
+
+  // ---- per-thread source rows for the A (activation) tile: rows rb + 32 i
+  long arow[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int p = p0 + rb + 32 * i;
+    long off = -1;
+    if (p < p1) {
+      if (a.sorted == nullptr) {
+        off = (long)p * K;
+      } else {
+        const int r = a.sorted[p];
+        if ((unsigned)r < (unsigned)a.sentinel) off = MODE == 0 ? (long)(r / a.k) * K : (long)p * K;
+      }
+    }
+    arow[i] = off;
+  }
+  // ---- per-thread weight rows for the B tile
+  const int n0 = MODE == 0 ? nt * (BN / 2) : nt * BN;
+  long wrow[8];
+  bool wok[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = rb + 32 * i;
+    const int r = MODE == 0 ? (j < BN / 2 ? n0 + j : a.I + n0 + (j - BN / 2)) : n0 + j;
+    wok[i] = MODE == 0 ? true : r < a.H;
+    wrow[i] = ((long)e * WR + (wok[i] ? r : 0)) * K;
+  }
+  // fp8: scale rows for the two 128-row halves of the B tile
+  long srow_lo = 0, srow_hi = 0;
+  if constexpr (FP8) {
+    const int kb = K / 128;
+    const int rlo = n0;
+    const int rhi = MODE == 0 ? a.I + n0 : n0 + 128;
+    srow_lo = ((long)e * (WR / 128) + rlo / 128) * kb;
+    srow_hi = ((long)e * (WR / 128) + min(rhi, WR - 1) / 128) * kb;
+  }
+
+  const __bf16* X = (const __bf16*)a.x;
+  u32x4 astage[8];
+  WeightStage<FP8> bstage;
+  float sc_lo = 1.f, sc_hi = 1.f;
+
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      astage[i] = arow[i] >= 0 ? *reinterpret_cast<const u32x4*>(X + arow[i] + k0 + chunk * 8) : u32x4{0, 0, 0, 0};
+    }
+    if constexpr (FP8) {
+      const uint8_t* Wq = (const uint8_t*)a.w;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        bstage.v[i] = wok[i] ? *reinterpret_cast<const u32x2*>(Wq + wrow[i] + k0 + chunk * 8) : u32x2{0, 0};
+      sc_lo = (float)a.wscale[srow_lo + k0 / 128];
+      sc_hi = (float)a.wscale[srow_hi + k0 / 128];
+    } else {
+      const __bf16* Wb = (const __bf16*)a.w;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        bstage.v[i] = wok[i] ? *reinterpret_cast<const u32x4*>(Wb + wrow[i] + k0 + chunk * 8) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&](int stage) {
+    char* sA = lds + stage * kStageBytes;
+    char* sB = sA + BM * BK * 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(sA + swz(rb + 32 * i, chunk)) = astage[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      u32x4 v;
+      if constexpr (FP8) {
+        const u32x2 q = bstage.v[i];
+        const float s = i < 4 ? sc_lo : sc_hi;
+        // bytes 0,1 / 2,3 of each 32-bit word -> two fp32 each (hardware E4M3 decode)
+        const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[0], false);
+        const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[0], true);
+        const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[1], false);
+        const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[1], true);
+        auto pack = [&](float lo, float hi) {
+          return (unsigned)bf16_bits((__bf16)(lo * s)) | ((unsigned)bf16_bits((__bf16)(hi * s)) << 16);
+        };
+        v = u32x4{pack(f0[0], f0[1]), pack(f1[0], f1[1]), pack(f2[0], f2[1]), pack(f3[0], f3[1])};
+      } else {
+        v = bstage.v[i];
+      }
+      *reinterpret_cast<u32x4*>(sB + swz(rb + 32 * i, chunk)) = v;
+    }
+  };
+
+  // ---- wave sub-tile: rows [wm*128, +128); weight rows per MODE
+  const int wm = wave & 1, wn = wave >> 1;
+  int brow[4];
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) {
+    if (MODE == 0)
+      brow[ns] = ns < 2 ? wn * 64 + ns * 32 : BN / 2 + wn * 64 + (ns - 2) * 32;
+    else
+      brow[ns] = wn * 128 + ns * 32;
+  }
+  const int l32 = lane & 31, khalf = lane >> 5;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) acc[ns][ms] = f32x16{};
+
+  const int KT = K / BK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) load_tile((kt + 1) * BK);
+    const char* sA = lds + cur * kStageBytes;
+    const char* sB = sA + BM * BK * 2;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int ch = kk * 2 + khalf;
+      bf16x8 wf[4], xf[4];
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) wf[ns] = *reinterpret_cast<const bf16x8*>(sB + swz(brow[ns] + l32, ch));
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) xf[ms] = *reinterpret_cast<const bf16x8*>(sA + swz(wm * 128 + ms * 32 + l32, ch));
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms)
+          acc[ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ns], xf[ms], acc[ns][ms], 0, 0, 0);
+    }
+    if (kt + 1 < KT) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue.  Lane holds row (lane & 31) of each 32-row sub-tile and, per
+  // register group g, the 4 consecutive columns 8 g + 4 (lane >> 5) + [0, 4).
+  if (MODE == 0) {
+    __bf16* act = (__bf16*)a.out;
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) {
+      const int p = p0 + wm * 128 + ms * 32 + l32;
+      bool ok = p < p1;
+      if (ok && a.sorted != nullptr) ok = (unsigned)a.sorted[p] < (unsigned)a.sentinel;
+      if (!ok) continue;
+#pragma unroll
+      for (int ns = 0; ns < 2; ++ns) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = n0 + wn * 64 + ns * 32 + g * 8 + khalf * 4;
+          bf16x4 o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float gt = acc[ns][ms][g * 4 + q], up = acc[ns + 2][ms][g * 4 + q];
+            o[q] = (__bf16)(silu_f32(gt) * up);
+          }
+          *reinterpret_cast<bf16x4*>(act + (long)p * a.I + col) = o;
+        }
+      }
+    }
+  } else {
+    __bf16* y = (__bf16*)a.out;
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) {
+      const int p = p0 + wm * 128 + ms * 32 + l32;
+      if (p >= p1) continue;
+      int dest = p;
+      if (a.sorted != nullptr) {
+        dest = a.sorted[p];
+        if ((unsigned)dest >= (unsigned)a.sentinel) continue;
+      }
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) {
+        const int cbase = n0 + wn * 128 + ns * 32;
+        if (cbase >= a.H) continue;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = cbase + g * 8 + khalf * 4;
+          bf16x4 o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = (__bf16)acc[ns][ms][g * 4 + q];
+          *reinterpret_cast<bf16x4*>(y + (long)dest * a.H + col) = o;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 path
+// One thread per (row, output column); fmaf over K in ascending order.
+
+__device__ __forceinline__ int expert_of_row(const int32_t* offsets, int N, int p) {
+  int lo = 0, hi = N;  // offsets[lo] <= p < offsets[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (offsets[mid] <= p) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void ffn_w13_f32(FfnArgs a, int rows) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)rows * a.I) return;
+  const int p = (int)(i / a.I), col = (int)(i % a.I);
+  int e = 0;
+  const float* x;
+  if (a.sorted == nullptr) {
+    x = (const float*)a.x + (long)p * a.H;
+  } else {
+    if (p >= a.offsets[a.N]) return;
+    const int r = a.sorted[p];
+    if ((unsigned)r >= (unsigned)a.sentinel) return;
+    e = expert_of_row(a.offsets, a.N, p);
+    x = (const float*)a.x + (long)(r / a.k) * a.H;
+  }
+  const float* w1 = (const float*)a.w + ((long)e * 2 * a.I + col) * a.H;
+  const float* w3 = w1 + (long)a.I * a.H;
+  float u = 0.f, v = 0.f;
+  for (int kk = 0; kk < a.H; ++kk) {
+    u = fmaf(x[kk], w1[kk], u);
+    v = fmaf(x[kk], w3[kk], v);
+  }
+  ((float*)a.out)[(long)p * a.I + col] = silu_f32(u) * v;
+}
+
+__global__ __launch_bounds__(256) void ffn_w2_f32(FfnArgs a, int rows) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)rows * a.H) return;
+  const int p = (int)(i / a.H), col = (int)(i % a.H);
+  int e = 0, dest = p;
+  if (a.sorted != nullptr) {
+    if (p >= a.offsets[a.N]) return;
+    dest = a.sorted[p];
+    if ((unsigned)dest >= (unsigned)a.sentinel) return;
+    e = expert_of_row(a.offsets, a.N, p);
+  }
+  const float* x = (const float*)a.x + (long)p * a.I;
+  const float* w = (const float*)a.w + ((long)e * a.H + col) * a.I;
+  float acc = 0.f;
+  for (int kk = 0; kk < a.I; ++kk) acc = fmaf(x[kk], w[kk], acc);
+  ((float*)a.out)[(long)dest * a.H + col] = acc;
+}
+
+int mtile_bound(const moe_config& c, bool identity) {
+  if (identity) return ceil_div(c.T, BM);
+  const long p_max = (long)c.T * c.k + (long)c.N * (c.B - 1);
+  return (int)((p_max + (long)c.N * (BM - 1)) / BM);
+}
+
+template <int MODE, bool FP8>
+hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
+  const int G = a.mtiles * a.ntiles;
+  const int grid = ceil_div(G, 8) * 8;
+  ffn_gemm_bf16<MODE, FP8><<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+namespace {
+
+FfnArgs base_args(const moe_config& c, const int32_t* sorted_ids, const int32_t* offsets, bool identity) {
+  FfnArgs a{};
+  a.sorted = identity ? nullptr : sorted_ids;
+  a.offsets = identity ? nullptr : offsets;
+  a.T = c.T;
+  a.H = c.H;
+  a.I = c.I;
+  a.N = identity ? 1 : c.N;
+  a.k = c.k;
+  a.sentinel = c.T * c.k;
+  a.mtiles = mtile_bound(c, identity);
+  a.rows = identity ? c.T : c.T * c.k + c.N * (c.B - 1);
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_gate_up(const moe_config& c, const void* h, const int32_t* sorted_ids, const int32_t* offsets,
+                          const void* w13, const void* w13_scale, void* act, bool identity, hipStream_t s) {
+  FfnArgs a = base_args(c, sorted_ids, offsets, identity);
+  a.x = h;
+  a.w = w13;
+  a.wscale = (const __bf16*)w13_scale;
+  a.out = act;
+  if (c.expert_dtype == MOE_F32) {
+    const long n = (long)a.rows * c.I;
+    ffn_w13_f32<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(a, a.rows);
+    return hipGetLastError();
+  }
+  a.ntiles = c.I / (BN / 2);
+  return c.expert_dtype == MOE_FP8_E4M3 ? launch_gemm<0, true>(a, s) : launch_gemm<0, false>(a, s);
+}
+
+hipError_t launch_down(const moe_config& c, const void* act, const int32_t* sorted_ids, const int32_t* offsets,
+                       const void* w2, const void* w2_scale, void* y, bool identity, hipStream_t s) {
+  FfnArgs a = base_args(c, sorted_ids, offsets, identity);
+  a.x = act;
+  a.w = w2;
+  a.wscale = (const __bf16*)w2_scale;
+  a.out = y;
+  if (c.expert_dtype == MOE_F32) {
+    const long n = (long)a.rows * c.H;
+    ffn_w2_f32<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(a, a.rows);
+    return hipGetLastError();
+  }
+  a.ntiles = ceil_div(c.H, BN);
+  return c.expert_dtype == MOE_FP8_E4M3 ? launch_gemm<1, true>(a, s) : launch_gemm<1, false>(a, s);
+}
+
+hipError_t launch_expert_ffn(const moe_config& c, const void* h, const int32_t* sorted_ids, const int32_t* offsets,
+                             const void* w13, const void* w2, const void* w13_scale, const void* w2_scale, void* act,
+                             void* y, bool identity, hipStream_t s) {
+  hipError_t err = launch_gate_up(c, h, sorted_ids, offsets, w13, w13_scale, act, identity, s);
+  if (err != hipSuccess) return err;
+  return launch_down(c, act, sorted_ids, offsets, w2, w2_scale, y, identity, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,40 @@
+// Internal launch entry points between the host layer (api.hip) and the kernels.
+// Every launcher enqueues on `stream` and returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---- routing (route.hip)
+hipError_t launch_router_logits(const moe_config& c, const void* h, const void* w_gate, const float* bias,
+                                float* logits, hipStream_t s);
+hipError_t launch_topk(const moe_config& c, const float* logits, int32_t* ids, float* gates, float* margin,
+                       hipStream_t s);
+
+// ---- alignment (align.hip)
+int align_chunk_routes();                       // routes per alignment chunk
+size_t align_workspace_bytes(const moe_config& c);
+hipError_t launch_align(const moe_config& c, const int32_t* ids, uint8_t* kept, int32_t* sorted_ids,
+                        int32_t* block_expert, int32_t* offsets, int32_t* num_padded, int32_t* stats,
+                        void* ws, hipStream_t s);
+
+// ---- expert FFN (ffn.hip)
+// identity == true: one expert over T token rows (shared expert), offsets ignored.
+hipError_t launch_gate_up(const moe_config& c, const void* h, const int32_t* sorted_ids, const int32_t* offsets,
+                          const void* w13, const void* w13_scale, void* act, bool identity, hipStream_t s);
+hipError_t launch_down(const moe_config& c, const void* act, const int32_t* sorted_ids, const int32_t* offsets,
+                       const void* w2, const void* w2_scale, void* y, bool identity, hipStream_t s);
+hipError_t launch_expert_ffn(const moe_config& c, const void* h, const int32_t* sorted_ids,
+                             const int32_t* offsets, const void* w13, const void* w2, const void* w13_scale,
+                             const void* w2_scale, void* act, void* y, bool identity, hipStream_t s);
+
+// ---- combine (combine.hip)
+hipError_t launch_combine(const moe_config& c, const void* y_route, const float* gates, const uint8_t* kept,
+                          const void* shared_out, const void* residual, void* out, hipStream_t s);
+
+}  // namespace moe
