@@ -36,7 +36,6 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 256;
-constexpr int kStageBytes = (BM + BN) * BK * 2;  // one stage: A tile + B tile, bf16
 constexpr int kGroupN = 8;                        // n-tiles per raster group
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -56,7 +55,13 @@ struct FfnArgs {
   int ntiles;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * (BK * 2) + ((chunk ^ (row & 7)) << 4); }
+// LDS tile layout: row-major 128-byte rows of 8 16-byte chunks, chunk index XORed
+// with (row >> 1) & 7.  A ds_read_b128 serves 16 lanes per cycle from 64 banks;
+// the 32x32 fragment reads put 16 consecutive rows at one logical chunk in those
+// 16 lanes, and this XOR spreads them over all 64 banks (rows r and r+1 differ in
+// the bank half, rows 2m.. in the chunk).
+__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * (BK * 2) + (swz_chunk(row, chunk) << 4); }
 
 // Resolve M-tile m to (expert, first row, end row) from the expert offsets.
 // Each expert's padded segment is cut into ceil(len / BM) tiles in expert order.
@@ -103,22 +108,27 @@ __device__ bool resolve_tile(const FfnArgs& a, int m, int& e, int& p0, int& p1, 
   return e >= 0 && p0 >= 0 && p0 < p1;
 }
 
-template <bool FP8>
-struct WeightStage;
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-template <>
-struct WeightStage<false> {
-  u32x4 v[8];
-};
-template <>
-struct WeightStage<true> {
-  u32x2 v[8];
-};
+// Barrier that publishes LDS written by global->LDS DMA.  The DMA is counted by
+// vmcnt, and a workgroup fence does not wait for it (the compiler treats it as a
+// load), so every wave waits for its own DMA *before* the barrier; only then are
+// all waves' rows in LDS when any wave passes it.  s_waitcnt imm 0x70 =
+// vmcnt(0) expcnt(7) lgkmcnt(0).
+__device__ __forceinline__ void dma_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x70);
+  __syncthreads();
+}
 
 // MODE 0: W13 + SwiGLU -> act.  MODE 1: W2 -> y rows.
 template <int MODE, bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffn_gemm_bf16(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
+  // Two stages, each its own array so the compiler can see that the tile being
+  // filled by DMA never aliases the tile being read.
+  __shared__ __attribute__((aligned(16))) char sA0[BM * BK * 2];
+  __shared__ __attribute__((aligned(16))) char sB0[BN * BK * 2];
+  __shared__ __attribute__((aligned(16))) char sA1[BM * BK * 2];
+  __shared__ __attribute__((aligned(16))) char sB1[BN * BK * 2];
   __shared__ int tile_sh[4];
 
   // ---- tile selection: XCD-contiguous logical ids, grouped raster over n-tiles
@@ -137,81 +147,91 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int K = MODE == 0 ? a.H : a.I;
   const int WR = MODE == 0 ? 2 * a.I : a.H;  // weight rows per expert
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int chunk = tid & 7, rb = tid >> 3;
 
-  // ---- per-thread source rows for the A (activation) tile: rows rb + 32 i
-  long arow[8];
+  // ---- global -> LDS copy plan.  Wave w fills rows [64 w, 64 w + 64) of each tile,
+  // 8 rows (1 KB) per DMA instruction; lane L lands in physical 16-byte chunk L % 8
+  // of tile row 64 w + 8 j + L / 8, so it fetches the logical chunk that the swizzle
+  // puts there (the swizzle is an involution in the chunk index).
+  const int drow = lane >> 3;                    // row within the 8-row group
+  auto dchunk = [&](int j) { return swz_chunk(wave * 64 + j * 8 + drow, lane & 7); };
+  const __bf16* X = (const __bf16*)a.x;
+  const __bf16* arow[8];                         // activation row of each of the lane's 8 rows
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int p = p0 + rb + 32 * i;
-    long off = -1;
+  for (int j = 0; j < 8; ++j) {
+    const int p = p0 + wave * 64 + j * 8 + drow;
+    // rows outside the tile or padding rows read a harmless valid row; their
+    // results are never stored (rows never interact in the product)
+    long row = MODE == 0 ? 0 : p0;
     if (p < p1) {
       if (a.sorted == nullptr) {
-        off = (long)p * K;
+        row = p;
       } else {
         const int r = a.sorted[p];
-        if ((unsigned)r < (unsigned)a.sentinel) off = MODE == 0 ? (long)(r / a.k) * K : (long)p * K;
+        if ((unsigned)r < (unsigned)a.sentinel) row = MODE == 0 ? r / a.k : p;
       }
     }
-    arow[i] = off;
+    arow[j] = X + row * K + dchunk(j) * 8;
   }
-  // ---- per-thread weight rows for the B tile
   const int n0 = MODE == 0 ? nt * (BN / 2) : nt * BN;
-  long wrow[8];
-  bool wok[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int j = rb + 32 * i;
+  // weight rows of the lane's 8 DMA rows (bf16 path) / staging rows (fp8 path)
+  auto weight_row = [&](int j) {  // j = tile row
     const int r = MODE == 0 ? (j < BN / 2 ? n0 + j : a.I + n0 + (j - BN / 2)) : n0 + j;
-    wok[i] = MODE == 0 ? true : r < a.H;
-    wrow[i] = ((long)e * WR + (wok[i] ? r : 0)) * K;
-  }
-  // fp8: scale rows for the two 128-row halves of the B tile
+    return (MODE == 1 && r >= a.H) ? -1 : r;
+  };
+
+  // ---- bf16 weights: DMA like the activations
+  const __bf16* brow[8];
+  // ---- fp8 weights: register staging with decode + scale (rows rb + 32 i)
+  const int chunk = tid & 7, rb = tid >> 3;
+  long wrow8[8];
+  bool wok8[8];
   long srow_lo = 0, srow_hi = 0;
-  if constexpr (FP8) {
-    const int kb = K / 128;
-    const int rlo = n0;
-    const int rhi = MODE == 0 ? a.I + n0 : n0 + 128;
-    srow_lo = ((long)e * (WR / 128) + rlo / 128) * kb;
-    srow_hi = ((long)e * (WR / 128) + min(rhi, WR - 1) / 128) * kb;
-  }
-
-  const __bf16* X = (const __bf16*)a.x;
-  u32x4 astage[8];
-  WeightStage<FP8> bstage;
-  float sc_lo = 1.f, sc_hi = 1.f;
-
-  auto load_tile = [&](int k0) {
+  if constexpr (!FP8) {
+    const __bf16* Wb = (const __bf16*)a.w + (long)e * WR * K;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = weight_row(wave * 64 + j * 8 + drow);
+      brow[j] = Wb + (long)(r < 0 ? 0 : r) * K + dchunk(j) * 8;
+    }
+  } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      astage[i] = arow[i] >= 0 ? *reinterpret_cast<const u32x4*>(X + arow[i] + k0 + chunk * 8) : u32x4{0, 0, 0, 0};
+      const int r = weight_row(rb + 32 * i);
+      wok8[i] = r >= 0;
+      wrow8[i] = ((long)e * WR + (r < 0 ? 0 : r)) * K;
     }
-    if constexpr (FP8) {
+    const int kb = K / 128;
+    const int rhi = MODE == 0 ? a.I + n0 : n0 + 128;
+    srow_lo = ((long)e * (WR / 128) + n0 / 128) * kb;
+    srow_hi = ((long)e * (WR / 128) + min(rhi, WR - 1) / 128) * kb;
+  }
+  u32x2 bq[8];
+  float sc_lo = 1.f, sc_hi = 1.f;
+
+  auto issue_loads = [&](char* sA, char* sB, int k0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_global_load_lds(arow[j] + k0, LDS_PTR(sA + (wave * 8 + j) * 1024), 16, 0, 0);
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        __builtin_amdgcn_global_load_lds(brow[j] + k0, LDS_PTR(sB + (wave * 8 + j) * 1024), 16, 0, 0);
+    } else {
       const uint8_t* Wq = (const uint8_t*)a.w;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        bstage.v[i] = wok[i] ? *reinterpret_cast<const u32x2*>(Wq + wrow[i] + k0 + chunk * 8) : u32x2{0, 0};
+        bq[i] = wok8[i] ? *reinterpret_cast<const u32x2*>(Wq + wrow8[i] + k0 + chunk * 8) : u32x2{0, 0};
       sc_lo = (float)a.wscale[srow_lo + k0 / 128];
       sc_hi = (float)a.wscale[srow_hi + k0 / 128];
-    } else {
-      const __bf16* Wb = (const __bf16*)a.w;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        bstage.v[i] = wok[i] ? *reinterpret_cast<const u32x4*>(Wb + wrow[i] + k0 + chunk * 8) : u32x4{0, 0, 0, 0};
     }
   };
-  auto store_tile = [&](int stage) {
-    char* sA = lds + stage * kStageBytes;
-    char* sB = sA + BM * BK * 2;
+  // fp8 only: decode the staged codes, scale, round to bf16 and write the B tile
+  auto store_fp8 = [&](char* sB) {
+    if constexpr (FP8) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(sA + swz(rb + 32 * i, chunk)) = astage[i];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u32x4 v;
-      if constexpr (FP8) {
-        const u32x2 q = bstage.v[i];
+      for (int i = 0; i < 8; ++i) {
+        const u32x2 q = bq[i];
         const float s = i < 4 ? sc_lo : sc_hi;
-        // bytes 0,1 / 2,3 of each 32-bit word -> two fp32 each (hardware E4M3 decode)
         const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[0], false);
         const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[0], true);
         const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[1], false);
@@ -219,23 +239,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         auto pack = [&](float lo, float hi) {
           return (unsigned)bf16_bits((__bf16)(lo * s)) | ((unsigned)bf16_bits((__bf16)(hi * s)) << 16);
         };
-        v = u32x4{pack(f0[0], f0[1]), pack(f1[0], f1[1]), pack(f2[0], f2[1]), pack(f3[0], f3[1])};
-      } else {
-        v = bstage.v[i];
+        *reinterpret_cast<u32x4*>(sB + swz(rb + 32 * i, chunk)) =
+            u32x4{pack(f0[0], f0[1]), pack(f1[0], f1[1]), pack(f2[0], f2[1]), pack(f3[0], f3[1])};
       }
-      *reinterpret_cast<u32x4*>(sB + swz(rb + 32 * i, chunk)) = v;
     }
   };
 
   // ---- wave sub-tile: rows [wm*128, +128); weight rows per MODE
   const int wm = wave & 1, wn = wave >> 1;
-  int brow[4];
+  int brw[4];
 #pragma unroll
   for (int ns = 0; ns < 4; ++ns) {
     if (MODE == 0)
-      brow[ns] = ns < 2 ? wn * 64 + ns * 32 : BN / 2 + wn * 64 + (ns - 2) * 32;
+      brw[ns] = ns < 2 ? wn * 64 + ns * 32 : BN / 2 + wn * 64 + (ns - 2) * 32;
     else
-      brow[ns] = wn * 128 + ns * 32;
+      brw[ns] = wn * 128 + ns * 32;
   }
   const int l32 = lane & 31, khalf = lane >> 5;
 
@@ -245,32 +263,76 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms) acc[ns][ms] = f32x16{};
 
-  const int KT = K / BK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) load_tile((kt + 1) * BK);
-    const char* sA = lds + cur * kStageBytes;
-    const char* sB = sA + BM * BK * 2;
+  // Fragments of one 16-wide K step: 4 weight sub-tiles and 4 activation sub-tiles.
+  auto load_frags = [&](const char* sA, const char* sB, int kk, bf16x8* wf, bf16x8* xf) {
+    const int ch = kk * 2 + khalf;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int ch = kk * 2 + khalf;
-      bf16x8 wf[4], xf[4];
+    for (int ns = 0; ns < 4; ++ns) wf[ns] = *reinterpret_cast<const bf16x8*>(sB + swz(brw[ns] + l32, ch));
 #pragma unroll
-      for (int ns = 0; ns < 4; ++ns) wf[ns] = *reinterpret_cast<const bf16x8*>(sB + swz(brow[ns] + l32, ch));
+    for (int ms = 0; ms < 4; ++ms) xf[ms] = *reinterpret_cast<const bf16x8*>(sA + swz(wm * 128 + ms * 32 + l32, ch));
+  };
+  auto mfma16 = [&](const bf16x8* wf, const bf16x8* xf) {
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms) xf[ms] = *reinterpret_cast<const bf16x8*>(sA + swz(wm * 128 + ms * 32 + l32, ch));
+    for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
-      for (int ns = 0; ns < 4; ++ns)
+      for (int ms = 0; ms < 4; ++ms)
+        acc[ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ns], xf[ms], acc[ns][ms], 0, 0, 0);
+  };
+  // Software pipeline over fragments.  Four register sets hold the fragments of
+  // the four 16-wide steps of a 64-deep stage.  Every block of 16 MFMAs runs with
+  // the reads of a later step interleaved (one read per two MFMAs), so LDS latency
+  // hides behind the matrix core:
+  //   [MFMA s.0 | read s.2] [MFMA s.1 | read s.3] barrier, DMA(stage s+2)
+  //   [MFMA s.2 | read (s+1).0] [MFMA s.3 | read (s+1).1]
+  // The reads of stage s+1 can start before its half-way barrier because that
+  // barrier of stage s already waited for stage s+1's DMA.
+  bf16x8 fw[4][4], fx[4][4];
+  auto step = [&](int mset, const char* sA, const char* sB, int kk, int lset) {
+    load_frags(sA, sB, kk, fw[lset], fx[lset]);
+    mfma16(fw[mset], fx[mset]);
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
-          acc[ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ns], xf[ms], acc[ns][ms], 0, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     }
-    if (kt + 1 < KT) store_tile(cur ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Stage s of the K loop lives in buffer s & 1.  The DMA of stage s+2 is issued
+  // right after the barrier that ends the reads of stage s.  K is a multiple of
+  // 128, so the stage count is even.  The loop body is one basic block (the DMA is
+  // unconditional: past the end it refetches the last stage into a buffer whose
+  // reads are never used) so the scheduling barriers hold.
+  const int KT = K / BK;
+  issue_loads(sA0, sB0, 0);
+  store_fp8(sB0);
+  issue_loads(sA1, sB1, BK);
+  dma_barrier();
+  load_frags(sA0, sB0, 0, fw[0], fx[0]);
+  load_frags(sA0, sB0, 1, fw[1], fx[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int kt = 0; kt < KT; kt += 2) {
+    step(0, sA0, sB0, 2, 2);
+    step(1, sA0, sB0, 3, 3);
+    store_fp8(sB1);  // fp8: stage kt+1 into buffer 1 (codes fetched a stage earlier)
+    dma_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_loads(sA0, sB0, min(kt + 2, KT - 1) * BK);
+    __builtin_amdgcn_sched_barrier(0);
+    step(2, sA1, sB1, 0, 0);
+    step(3, sA1, sB1, 1, 1);
+    step(0, sA1, sB1, 2, 2);
+    step(1, sA1, sB1, 3, 3);
+    store_fp8(sB0);
+    dma_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_loads(sA1, sB1, min(kt + 3, KT - 1) * BK);
+    __builtin_amdgcn_sched_barrier(0);
+    step(2, sA0, sB0, 0, 0);
+    step(3, sA0, sB0, 1, 1);
   }
+  dma_barrier();  // no DMA may outlive the workgroup's LDS
 
   // ---- epilogue.  Lane holds row (lane & 31) of each 32-row sub-tile and, per
   // register group g, the 4 consecutive columns 8 g + 4 (lane >> 5) + [0, 4).
