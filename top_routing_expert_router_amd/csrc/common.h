@@ -30,8 +30,13 @@ template <typename T> __device__ __forceinline__ T cvt_act(float x);
 template <> __device__ __forceinline__ float cvt_act<float>(float x) { return x; }
 template <> __device__ __forceinline__ __bf16 cvt_act<__bf16>(float x) { return (__bf16)x; }
 
-// silu(x) = x / (1 + e^-x), fp32, accurate expf.
+// silu(x) = x / (1 + e^-x), fp32, accurate expf and IEEE division (fp32 outputs).
 __device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + expf(-x)); }
+
+// silu for results that are rounded to bf16 next: hardware exp2 and reciprocal
+// (each within ~1 fp32 ulp, far below the bf16 rounding that follows).
+// Large negative x: e^-x = inf, rcp(inf) = 0, x * 0 = -0.
+__device__ __forceinline__ float silu_fast(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Order-preserving 32-bit key of a float: larger float -> larger key; -0 and +0
 // share a key; every NaN maps to 0, below -inf.

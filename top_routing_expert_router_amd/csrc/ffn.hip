@@ -208,11 +208,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   u32x2 bq[8];
   float sc_lo = 1.f, sc_hi = 1.f;
 
-  auto issue_loads = [&](char* sA, char* sB, int k0) {
+  // part 0: the 8 activation-row DMAs; part 1: the 8 weight-row DMAs (bf16) or
+  // the 8 weight-code loads into registers (fp8).
+  auto issue_part = [&](char* sA, char* sB, int k0, int part) {
+    if (part == 0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_global_load_lds(arow[j] + k0, LDS_PTR(sA + (wave * 8 + j) * 1024), 16, 0, 0);
-    if constexpr (!FP8) {
+      for (int j = 0; j < 8; ++j)
+        __builtin_amdgcn_global_load_lds(arow[j] + k0, LDS_PTR(sA + (wave * 8 + j) * 1024), 16, 0, 0);
+    } else if constexpr (!FP8) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         __builtin_amdgcn_global_load_lds(brow[j] + k0, LDS_PTR(sB + (wave * 8 + j) * 1024), 16, 0, 0);
@@ -224,6 +227,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       sc_lo = (float)a.wscale[srow_lo + k0 / 128];
       sc_hi = (float)a.wscale[srow_hi + k0 / 128];
     }
+  };
+  auto issue_loads = [&](char* sA, char* sB, int k0) {
+    issue_part(sA, sB, k0, 0);
+    issue_part(sA, sB, k0, 1);
   };
   // fp8 only: decode the staged codes, scale, round to bf16 and write the B tile
   auto store_fp8 = [&](char* sB) {
@@ -298,12 +305,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
     __builtin_amdgcn_sched_barrier(0);
   };
+  // The same, with 8 global loads of a later stage spread through the 16 MFMAs
+  // (a burst of them would stall the wave at issue while the matrix core idles).
+  auto step_dma = [&](int mset, const char* sA, const char* sB, int kk, int lset, char* dA, char* dB, int k0,
+                      int part) {
+    load_frags(sA, sB, kk, fw[lset], fx[lset]);
+    issue_part(dA, dB, k0, part);
+    mfma16(fw[mset], fx[mset]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // global load
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   // Stage s of the K loop lives in buffer s & 1.  The DMA of stage s+2 is issued
-  // right after the barrier that ends the reads of stage s.  K is a multiple of
-  // 128, so the stage count is even.  The loop body is one basic block (the DMA is
-  // unconditional: past the end it refetches the last stage into a buffer whose
-  // reads are never used) so the scheduling barriers hold.
+  // right after the barrier that ends the reads of stage s, spread over the next
+  // 32 MFMAs.  K is a multiple of 128, so the stage count is even.  The loop body
+  // is one basic block (the DMA is unconditional: past the end it refetches the
+  // last stage into a buffer whose reads are never used) so the scheduling
+  // barriers hold.
   const int KT = K / BK;
   issue_loads(sA0, sB0, 0);
   store_fp8(sB0);
@@ -318,19 +342,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     store_fp8(sB1);  // fp8: stage kt+1 into buffer 1 (codes fetched a stage earlier)
     dma_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue_loads(sA0, sB0, min(kt + 2, KT - 1) * BK);
-    __builtin_amdgcn_sched_barrier(0);
-    step(2, sA1, sB1, 0, 0);
-    step(3, sA1, sB1, 1, 1);
+    const int k2 = min(kt + 2, KT - 1) * BK;
+    step_dma(2, sA1, sB1, 0, 0, sA0, sB0, k2, 0);
+    step_dma(3, sA1, sB1, 1, 1, sA0, sB0, k2, 1);
     step(0, sA1, sB1, 2, 2);
     step(1, sA1, sB1, 3, 3);
     store_fp8(sB0);
     dma_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue_loads(sA1, sB1, min(kt + 3, KT - 1) * BK);
-    __builtin_amdgcn_sched_barrier(0);
-    step(2, sA0, sB0, 0, 0);
-    step(3, sA0, sB0, 1, 1);
+    const int k3 = min(kt + 3, KT - 1) * BK;
+    step_dma(2, sA0, sB0, 0, 0, sA1, sB1, k3, 0);
+    step_dma(3, sA0, sB0, 1, 1, sA1, sB1, k3, 1);
   }
   dma_barrier();  // no DMA may outlive the workgroup's LDS
 
@@ -353,7 +375,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float gt = acc[ns][ms][g * 4 + q], up = acc[ns + 2][ms][g * 4 + q];
-            o[q] = (__bf16)(silu_f32(gt) * up);
+            o[q] = (__bf16)(silu_fast(gt) * up);
           }
           *reinterpret_cast<bf16x4*>(act + (long)p * a.I + col) = o;
         }
