@@ -36,7 +36,7 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 256;
-constexpr int kGroupN = 8;                        // n-tiles per raster group
+constexpr int kGroupN = 2;                        // n-tiles per raster group
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
