@@ -139,3 +139,41 @@ def check_ffn_surface(w: W.Workload, got: np.ndarray, exact: np.ndarray, emul, s
         f"elements beyond 2 ulp of the model: {far.mean():.2e}")
     assert err.max() <= max(tol(w), 1.25 * err_model.max()), err.max()
     assert far.mean() <= 1e-3, far.mean()
+
+
+WEIGHT_KEYS = ("w_gate", "w13", "w2", "w13_scale", "w2_scale", "shared_w13", "shared_w2", "shared_w13_scale",
+               "shared_w2_scale")
+
+
+def forward_trace_buffers(cfg, w: W.Workload, T: int = None, dev: str = "cuda") -> dict:
+    T = w.T if T is None else T
+    p_max, n_blocks = M.moe_align_sizes(cfg)
+    act_t = torch.float32 if w.act_dtype == W.F32 else torch.bfloat16
+    return dict(logits=torch.empty(T, w.N, device=dev), topk_ids=torch.empty(T, w.k, dtype=torch.int32, device=dev),
+                topk_gates=torch.empty(T, w.k, device=dev), margin=torch.empty(T, device=dev),
+                route_kept=torch.empty(T * w.k, dtype=torch.uint8, device=dev),
+                sorted_route_ids=torch.empty(p_max, dtype=torch.int32, device=dev),
+                block_expert=torch.empty(n_blocks, dtype=torch.int32, device=dev),
+                expert_offsets=torch.empty(w.N + 1, dtype=torch.int32, device=dev),
+                num_padded=torch.empty(1, dtype=torch.int32, device=dev),
+                stats=torch.empty(w.N + M.STATS_EXTRA, dtype=torch.int32, device=dev),
+                y_route=torch.empty(T * w.k, w.H, dtype=act_t, device=dev))
+
+
+def run_forward(w: W.Workload, dv: dict, h=None, trace: bool = True, ws=None, dev: str = "cuda"):
+    """moe_forward on device inputs ``dv`` (h overridable); returns (out, trace dict)."""
+    h = dv["h"] if h is None else h
+    T = h.shape[0]
+    wT = w.with_(T=T)
+    cfg = config(wT)
+    act_t = torch.float32 if w.act_dtype == W.F32 else torch.bfloat16
+    need = M.moe_workspace_size(cfg, M.MOE_OP_FORWARD)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.empty(T, w.H, dtype=act_t, device=dev)
+    tr = forward_trace_buffers(cfg, wT, T, dev) if trace else None
+    wts = {k: dv.get(k) for k in WEIGHT_KEYS}
+    wts["logit_bias"] = None if dv.get("bias") is None else dv["bias"].to(dev)
+    M.moe_forward(cfg, wts, h, h, out, tr, ws)
+    torch.cuda.synchronize()
+    return out, tr

@@ -175,11 +175,8 @@ moe_status moe_route(const moe_config* cfg, const void* h, const void* w_gate, c
   st = check_route_args(*cfg, h, w_gate, logit_bias, logits, topk_ids, topk_gates, margin, flags);
   if (st != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (!(flags & MOE_ROUTE_LOGITS_IN)) {
-    st = hip_status(launch_router_logits(*cfg, h, w_gate, logit_bias, logits, s));
-    if (st != MOE_OK) return st;
-  }
-  return hip_status(launch_topk(*cfg, logits, topk_ids, topk_gates, margin, s));
+  if (flags & MOE_ROUTE_LOGITS_IN) return hip_status(launch_topk(*cfg, logits, topk_ids, topk_gates, margin, s));
+  return hip_status(launch_router(*cfg, h, w_gate, logit_bias, logits, topk_ids, topk_gates, margin, s));
 }
 
 moe_status moe_align(const moe_config* cfg, const int32_t* topk_ids, uint8_t* route_kept, int32_t* sorted_route_ids,
@@ -283,8 +280,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
     return MOE_ERR_MISALIGNED;
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_router_logits(c, h, wt->w_gate, wt->logit_bias, logits, s);
-  if (e == hipSuccess) e = launch_topk(c, logits, ids, gates, margin, s);
+  hipError_t e = launch_router(c, h, wt->w_gate, wt->logit_bias, logits, ids, gates, margin, s);
   if (e == hipSuccess)
     e = launch_align(c, ids, kept, sorted, blocks, offsets, npad, stats, base + L.align_ws, s);
   if (e == hipSuccess)

@@ -10,6 +10,8 @@
 // The accumulator starts at -0.0 (the IEEE additive identity), so a token with no
 // kept route and no shared expert outputs its residual bit for bit, -0 included.
 // Each thread owns 8 consecutive columns of one token (16-byte bf16 accesses).
+// A route whose kept flag is 0 contributes nothing: its y row (allocated, never
+// written) is loaded but not added.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,37 +29,53 @@ struct Vec8<float> {
   typedef float type __attribute__((ext_vector_type(8)));
 };
 
+constexpr int kColsPerThread = 8;
+constexpr int kThreads = 256;
+constexpr int kColsPerBlock = kColsPerThread * kThreads;
+
+// One workgroup per (token, 2048-column slice): the token's gates and kept flags
+// are uniform (scalar loads); every y row is loaded unconditionally (all rows are
+// allocated) and the kept flag selects whether it enters the sum, so all loads of
+// a thread are in flight together.
 template <typename T>
-__global__ __launch_bounds__(256) void combine_rows(const T* __restrict__ y, const float* __restrict__ gates,
-                                                   const uint8_t* __restrict__ kept, const T* __restrict__ shared,
-                                                   const T* __restrict__ residual, T* __restrict__ out, int Tn, int H,
-                                                   int k) {
+__global__ __launch_bounds__(kThreads) void combine_rows(const T* __restrict__ y, const float* __restrict__ gates,
+                                                          const uint8_t* __restrict__ kept, const T* __restrict__ shared,
+                                                          const T* __restrict__ residual, T* __restrict__ out, int H,
+                                                          int k, int slices) {
   typedef typename Vec8<T>::type V;
-  const int per_row = H / 8;
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long)Tn * per_row) return;
-  const int t = (int)(i / per_row);
-  const long col = (long)(i % per_row) * 8;
+  const int t = blockIdx.x / slices;
+  const long col = (long)(blockIdx.x % slices) * kColsPerBlock + threadIdx.x * kColsPerThread;
+  if (col >= H) return;
+  V yv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < k) yv[j] = *reinterpret_cast<const V*>(y + ((long)t * k + j) * H + col);
+  V sv, rv;
+  if (shared) sv = *reinterpret_cast<const V*>(shared + (long)t * H + col);
+  if (residual) rv = *reinterpret_cast<const V*>(residual + (long)t * H + col);
   float acc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = -0.0f;
-  for (int j = 0; j < k; ++j) {
-    const long r = (long)t * k + j;
-    if (!kept[r]) continue;
-    const float g = gates[r];
-    const V v = *reinterpret_cast<const V*>(y + r * H + col);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, (float)v[q], acc[q]);
+  for (int j = 0; j < 8; ++j) {
+    if (j < k) {
+      const long r = (long)t * k + j;
+      const bool on = kept[r] != 0;
+      const float g = gates[r];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float f = fmaf(g, (float)yv[j][q], acc[q]);
+        acc[q] = on ? f : acc[q];
+      }
+    }
   }
   if (shared) {
-    const V v = *reinterpret_cast<const V*>(shared + (long)t * H + col);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] += (float)v[q];
+    for (int q = 0; q < 8; ++q) acc[q] += (float)sv[q];
   }
   if (residual) {
-    const V v = *reinterpret_cast<const V*>(residual + (long)t * H + col);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] += (float)v[q];
+    for (int q = 0; q < 8; ++q) acc[q] += (float)rv[q];
   }
   V o;
 #pragma unroll
@@ -69,14 +87,14 @@ __global__ __launch_bounds__(256) void combine_rows(const T* __restrict__ y, con
 
 hipError_t launch_combine(const moe_config& c, const void* y_route, const float* gates, const uint8_t* kept,
                           const void* shared_out, const void* residual, void* out, hipStream_t s) {
-  const long n = (long)c.T * (c.H / 8);
-  const dim3 grid((unsigned)((n + 255) / 256));
+  const int slices = ceil_div(c.H, kColsPerBlock);
+  const dim3 grid((unsigned)c.T * slices);
   if (c.act_dtype == MOE_F32) {
-    combine_rows<float><<<grid, 256, 0, s>>>((const float*)y_route, gates, kept, (const float*)shared_out,
-                                             (const float*)residual, (float*)out, c.T, c.H, c.k);
+    combine_rows<float><<<grid, kThreads, 0, s>>>((const float*)y_route, gates, kept, (const float*)shared_out,
+                                                  (const float*)residual, (float*)out, c.H, c.k, slices);
   } else {
-    combine_rows<__bf16><<<grid, 256, 0, s>>>((const __bf16*)y_route, gates, kept, (const __bf16*)shared_out,
-                                              (const __bf16*)residual, (__bf16*)out, c.T, c.H, c.k);
+    combine_rows<__bf16><<<grid, kThreads, 0, s>>>((const __bf16*)y_route, gates, kept, (const __bf16*)shared_out,
+                                                   (const __bf16*)residual, (__bf16*)out, c.H, c.k, slices);
   }
   return hipGetLastError();
 }

@@ -11,8 +11,9 @@
 namespace moe {
 
 // ---- routing (route.hip)
-hipError_t launch_router_logits(const moe_config& c, const void* h, const void* w_gate, const float* bias,
-                                float* logits, hipStream_t s);
+// projection + top-k + gates + margin (fused for bf16)
+hipError_t launch_router(const moe_config& c, const void* h, const void* w_gate, const float* bias, float* logits,
+                         int32_t* ids, float* gates, float* margin, hipStream_t s);
 hipError_t launch_topk(const moe_config& c, const float* logits, int32_t* ids, float* gates, float* margin,
                        hipStream_t s);
 

@@ -9,9 +9,9 @@
 //
 // Batch invariance ("Why temperature=0 Still Gives Different Answers: Batch
 // Invariance", "How do I make LLM inference reproducible?", tier 2): each logit
-// is reduced over fixed 32-wide K steps in ascending order inside a fixed
-// quarter of H per wave, and the four quarters are added in a fixed order.
-// Nothing depends on T or on the other tokens.
+// is reduced in a fixed order that depends only on H (64-wide K chunks dealt to
+// four waves round-robin, each wave in ascending chunk order, then the four wave
+// partials added in wave order).  Nothing depends on T or on the other tokens.
 #include "common.h"
 #include "kernels.h"
 
@@ -19,89 +19,27 @@ namespace moe {
 namespace {
 
 constexpr int kRouterTokens = 16;   // tokens per workgroup (one 16-wide MFMA column block)
-constexpr int kRouterWaves = 4;     // waves per workgroup, each owns a quarter of H
+constexpr int kRouterWaves = 4;     // waves per workgroup; wave w takes K chunks w, w+4, ...
+constexpr int kChunkK = 64;         // K per chunk: lane group q = lane / 16 holds k in [16 q, 16 q + 16)
+constexpr int kUnroll = 4;          // chunks in flight per wave
 
-// bf16 projection on MFMA 16x16x32: D[expert][token] = sum_k W_g[expert][k] * h[token][k].
-template <int NSUB>
-__global__ __launch_bounds__(256) void router_logits_bf16(const __bf16* __restrict__ h,
-                                                           const __bf16* __restrict__ wg,
-                                                           const float* __restrict__ bias,
-                                                           float* __restrict__ logits, int T, int H, int N) {
-  __shared__ float part[kRouterWaves][NSUB * 16][kRouterTokens];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * kRouterTokens;
-  const int col = lane & 15, kq = (lane >> 4) * 8;
-  const int tok = t0 + col;
-  const int kspan = H / kRouterWaves;
-  const int kbeg = wave * kspan;
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 
-  f32x4 acc[NSUB];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const bf16x8 zero8 = bf16x8{};
-  const __bf16* hrow = h + (size_t)(tok < T ? tok : 0) * H + kq;
-  const bool tok_ok = tok < T;
-  for (int k0 = kbeg; k0 < kbeg + kspan; k0 += 32) {
-    bf16x8 xb = tok_ok ? *reinterpret_cast<const bf16x8*>(hrow + k0) : zero8;
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const int e = s * 16 + col;
-      bf16x8 wa = e < N ? *reinterpret_cast<const bf16x8*>(wg + (size_t)e * H + k0 + kq) : zero8;
-      acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xb, acc[s], 0, 0, 0);
-    }
-  }
-  // lane holds token column (lane & 15), expert rows 4*(lane>>4) + r
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) part[wave][s * 16 + (lane >> 4) * 4 + r][col] = acc[s][r];
-  __syncthreads();
-  for (int i = threadIdx.x; i < NSUB * 16 * kRouterTokens; i += blockDim.x) {
-    const int e = i / kRouterTokens, t = i % kRouterTokens;
-    if (e >= N || t0 + t >= T) continue;
-    float v = part[0][e][t];
-    v += part[1][e][t];
-    v += part[2][e][t];
-    v += part[3][e][t];
-    if (bias) v += bias[e];
-    logits[(size_t)(t0 + t) * N + e] = v;
-  }
-}
-
-// fp32 projection: one thread per (token, expert), fmaf over H in ascending order.
-__global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict__ h, const float* __restrict__ wg,
-                                                          const float* __restrict__ bias,
-                                                          float* __restrict__ logits, int T, int H, int N) {
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long)T * N) return;
-  const int t = (int)(i / N), e = (int)(i % N);
-  const float* x = h + (size_t)t * H;
-  const float* w = wg + (size_t)e * H;
-  float acc = 0.f;
-  for (int k = 0; k < H; ++k) acc = fmaf(x[k], w[k], acc);
-  if (bias) acc += bias[e];
-  logits[i] = acc;
-}
-
-// Top-k over one token's N logits per wave.  Each lane holds experts lane + 64*i.
-// k+1 rounds of a wave-wide max over (value, -index) keys give the ranked ids and
-// the (k+1)-th logit for the margin.
-constexpr int kTopkTokensPerBlock = 4;
-
-__global__ __launch_bounds__(256) void topk_gates(const float* __restrict__ logits, int32_t* __restrict__ ids,
-                                                   float* __restrict__ gates, float* __restrict__ margin,
-                                                   int T, int N, int k, int renormalize) {
+// Top-k, gates and margin of one token from its N logits (global or LDS), one wave.
+// Each lane holds experts lane + 64 i.  k+1 rounds of a wave-wide max over
+// (value, -index) keys give the ranked ids and the (k+1)-th logit for the margin.
+// Gate weight_j = exp(l_j - l_0) (0 for a NaN logit); divided by the sum over the
+// k chosen in rank order, or by the sum over all N experts without renormalisation.
+template <typename RowPtr>
+__device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int renormalize, int32_t* __restrict__ ids,
+                                         float* __restrict__ gates, float* __restrict__ margin) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kTopkTokensPerBlock + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* lrow = logits + (size_t)t * N;
   float lv[4];
   uint64_t key[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    lv[i] = e < N ? lrow[e] : 0.f;
+    lv[i] = e < N ? row[e] : 0.f;
     key[i] = e < N ? rank_key(lv[i], e) : 0ull;
   }
   const int rounds = k < N ? k + 1 : k;
@@ -130,8 +68,6 @@ __global__ __launch_bounds__(256) void topk_gates(const float* __restrict__ logi
       }
     }
   }
-  // gates: weight_j = exp(l_j - l_0) (zero for a NaN logit), divided by the sum over
-  // the k chosen in rank order, or by the sum over all N experts without renormalisation.
   const float l0 = sl[0];
   float w[8];
   float s = 0.f;
@@ -168,42 +104,141 @@ __global__ __launch_bounds__(256) void topk_gates(const float* __restrict__ logi
   }
 }
 
+// bf16 router on MFMA 16x16x32, with top-k fused: D[expert][token] = sum_k W_g[expert][k] h[token][k].
+// Per 64-wide K chunk each lane loads 32 contiguous bytes of its token row (a whole
+// 128-byte line per row and instruction) and of its expert row, and issues two MFMAs
+// (the first and second 8 elements of its 16).  Wave w accumulates chunks w, w+4, ...
+// in ascending order; the four wave partials are added in wave order; nothing depends
+// on T or on the other tokens.
+template <int NSUB>
+__global__ __launch_bounds__(256) void router_bf16(const __bf16* __restrict__ h, const __bf16* __restrict__ wg,
+                                                   const float* __restrict__ bias, float* __restrict__ logits,
+                                                   int32_t* __restrict__ ids, float* __restrict__ gates,
+                                                   float* __restrict__ margin, int T, int H, int N, int k,
+                                                   int renormalize) {
+  constexpr int NP = NSUB * 16;
+  __shared__ float part[kRouterWaves][NP][kRouterTokens];
+  __shared__ float lg[kRouterTokens][NP + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kRouterTokens;
+  const int col = lane & 15, kq = (lane >> 4) * 16;
+  const int tok = t0 + col;
+  const bool tok_ok = tok < T;
+  const __bf16* hrow = h + (size_t)(tok_ok ? tok : 0) * H + kq;
+  const int nchunks = H / kChunkK;
+
+  f32x4 acc[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bf16x16 zero16 = bf16x16{};
+  for (int c0 = wave; c0 < nchunks; c0 += kRouterWaves * kUnroll) {
+    bf16x16 hv[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = c0 + u * kRouterWaves;
+      hv[u] = (c < nchunks && tok_ok) ? *reinterpret_cast<const bf16x16*>(hrow + c * kChunkK) : zero16;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = c0 + u * kRouterWaves;
+      if (c >= nchunks) break;
+      const bf16x8 hlo = __builtin_shufflevector(hv[u], hv[u], 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 hhi = __builtin_shufflevector(hv[u], hv[u], 8, 9, 10, 11, 12, 13, 14, 15);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        const int e = s * 16 + col;
+        const bf16x16 wv = e < N ? *reinterpret_cast<const bf16x16*>(wg + (size_t)e * H + c * kChunkK + kq) : zero16;
+        const bf16x8 wlo = __builtin_shufflevector(wv, wv, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 whi = __builtin_shufflevector(wv, wv, 8, 9, 10, 11, 12, 13, 14, 15);
+        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, hlo, acc[s], 0, 0, 0);
+        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, hhi, acc[s], 0, 0, 0);
+      }
+    }
+  }
+  // lane holds token column (lane & 15), expert rows 4*(lane>>4) + r
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[wave][s * 16 + (lane >> 4) * 4 + r][col] = acc[s][r];
+  __syncthreads();
+  for (int i = threadIdx.x; i < NP * kRouterTokens; i += blockDim.x) {
+    const int e = i / kRouterTokens, t = i % kRouterTokens;
+    if (e >= N) continue;
+    float v = part[0][e][t];
+    v += part[1][e][t];
+    v += part[2][e][t];
+    v += part[3][e][t];
+    if (bias) v += bias[e];
+    lg[t][e] = v;
+    if (t0 + t < T) logits[(size_t)(t0 + t) * N + e] = v;
+  }
+  __syncthreads();
+  // fused top-k: wave w ranks tokens 4 w .. 4 w + 3 of this workgroup
+#pragma unroll
+  for (int j = 0; j < kRouterTokens / kRouterWaves; ++j) {
+    const int t = wave * (kRouterTokens / kRouterWaves) + j;
+    if (t0 + t < T) topk_one(&lg[t][0], t0 + t, N, k, renormalize, ids, gates, margin);
+  }
+}
+
+// fp32 projection: one thread per (token, expert), fmaf over H in ascending order.
+__global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict__ h, const float* __restrict__ wg,
+                                                          const float* __restrict__ bias,
+                                                          float* __restrict__ logits, int T, int H, int N) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)T * N) return;
+  const int t = (int)(i / N), e = (int)(i % N);
+  const float* x = h + (size_t)t * H;
+  const float* w = wg + (size_t)e * H;
+  float acc = 0.f;
+  for (int kk = 0; kk < H; ++kk) acc = fmaf(x[kk], w[kk], acc);
+  if (bias) acc += bias[e];
+  logits[i] = acc;
+}
+
+// Standalone top-k over stored logits (fp32 path and routing from given logits).
+constexpr int kTopkTokensPerBlock = 4;
+
+__global__ __launch_bounds__(256) void topk_gates(const float* __restrict__ logits, int32_t* __restrict__ ids,
+                                                   float* __restrict__ gates, float* __restrict__ margin,
+                                                   int T, int N, int k, int renormalize) {
+  const int t = blockIdx.x * kTopkTokensPerBlock + (threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_one(logits + (size_t)t * N, t, N, k, renormalize, ids, gates, margin);
+}
+
 template <int NSUB>
 hipError_t launch_router_bf16(const moe_config& c, const void* h, const void* wg, const float* bias, float* logits,
-                              hipStream_t s) {
+                              int32_t* ids, float* gates, float* margin, hipStream_t s) {
   dim3 grid(ceil_div(c.T, kRouterTokens));
-  router_logits_bf16<NSUB><<<grid, 256, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits, c.T, c.H, c.N);
+  router_bf16<NSUB><<<grid, 256, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits, ids, gates, margin, c.T,
+                                         c.H, c.N, c.k, c.renormalize);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_router_logits(const moe_config& c, const void* h, const void* w_gate, const float* bias,
-                                float* logits, hipStream_t s) {
+hipError_t launch_router(const moe_config& c, const void* h, const void* w_gate, const float* bias, float* logits,
+                         int32_t* ids, float* gates, float* margin, hipStream_t s) {
   if (c.act_dtype == MOE_F32) {
     const long n = (long)c.T * c.N;
     router_logits_f32<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>((const float*)h, (const float*)w_gate, bias,
                                                                         logits, c.T, c.H, c.N);
-    return hipGetLastError();
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_topk(c, logits, ids, gates, margin, s);
   }
+#define MOE_ROUTER_CASE(n) \
+  case n:                  \
+    return launch_router_bf16<n>(c, h, w_gate, bias, logits, ids, gates, margin, s);
   switch (ceil_div(c.N, 16)) {
-    case 1: return launch_router_bf16<1>(c, h, w_gate, bias, logits, s);
-    case 2: return launch_router_bf16<2>(c, h, w_gate, bias, logits, s);
-    case 3: return launch_router_bf16<3>(c, h, w_gate, bias, logits, s);
-    case 4: return launch_router_bf16<4>(c, h, w_gate, bias, logits, s);
-    case 5: return launch_router_bf16<5>(c, h, w_gate, bias, logits, s);
-    case 6: return launch_router_bf16<6>(c, h, w_gate, bias, logits, s);
-    case 7: return launch_router_bf16<7>(c, h, w_gate, bias, logits, s);
-    case 8: return launch_router_bf16<8>(c, h, w_gate, bias, logits, s);
-    case 9: return launch_router_bf16<9>(c, h, w_gate, bias, logits, s);
-    case 10: return launch_router_bf16<10>(c, h, w_gate, bias, logits, s);
-    case 11: return launch_router_bf16<11>(c, h, w_gate, bias, logits, s);
-    case 12: return launch_router_bf16<12>(c, h, w_gate, bias, logits, s);
-    case 13: return launch_router_bf16<13>(c, h, w_gate, bias, logits, s);
-    case 14: return launch_router_bf16<14>(c, h, w_gate, bias, logits, s);
-    case 15: return launch_router_bf16<15>(c, h, w_gate, bias, logits, s);
-    default: return launch_router_bf16<16>(c, h, w_gate, bias, logits, s);
+    MOE_ROUTER_CASE(1) MOE_ROUTER_CASE(2) MOE_ROUTER_CASE(3) MOE_ROUTER_CASE(4) MOE_ROUTER_CASE(5)
+    MOE_ROUTER_CASE(6) MOE_ROUTER_CASE(7) MOE_ROUTER_CASE(8) MOE_ROUTER_CASE(9) MOE_ROUTER_CASE(10)
+    MOE_ROUTER_CASE(11) MOE_ROUTER_CASE(12) MOE_ROUTER_CASE(13) MOE_ROUTER_CASE(14) MOE_ROUTER_CASE(15)
+    default: return launch_router_bf16<16>(c, h, w_gate, bias, logits, ids, gates, margin, s);
   }
+#undef MOE_ROUTER_CASE
 }
 
 hipError_t launch_topk(const moe_config& c, const float* logits, int32_t* ids, float* gates, float* margin,
