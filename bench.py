@@ -173,6 +173,10 @@ def main() -> int:
                 "traffic": _traffic(w.name, 1.0), "avg_launch_us": round(ms_gate_up * 1e3, 2),
                 "flops_per_launch": gate_up_flops}
 
+    ceil = None if args.no_stages else ceilings(stream)
+    if ceil:
+        log("[bench] measured ceilings: " + ", ".join(f"{a} {b:,.1f}" for a, b in ceil.items()))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, d, args.cpu_sample)
@@ -186,10 +190,55 @@ def main() -> int:
                    "expert_dtype": w.expert_dtype, "capacity": None if w.cap_den == 0 else f"{w.cap_num}/{w.cap_den}",
                    "n_shared": w.n_shared, "kept_routes": kept_routes, "parallelism": "none (1 GPU)"},
         "roofline": roofline, "stages": {k: {a: round(b, 3) for a, b in v.items()} for k, v in stages.items()},
+        "measured_ceilings": ceil,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def ceilings(stream):
+    """Measured ceilings on this GPU (libmoe_ceiling.so): 1 GiB copy and read streams,
+    and back-to-back bf16 MFMAs from registers at one and two waves per SIMD."""
+    import ctypes
+
+    import torch
+
+    from top_routing_expert_router_amd.build import CEILING_LIB_PATH
+
+    L = ctypes.CDLL(CEILING_LIB_PATH)
+    P, SZ, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    L.moe_ceiling_copy.argtypes, L.moe_ceiling_copy.restype = [P, P, SZ, P], I32
+    L.moe_ceiling_read.argtypes, L.moe_ceiling_read.restype = [P, SZ, P, P], I32
+    L.moe_ceiling_mfma_bf16.argtypes, L.moe_ceiling_mfma_bf16.restype = [I32, I32, P, P], I32
+    sp = stream.cuda_stream
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4096, dtype=torch.float32, device="cuda")
+
+    def time_ms(fn, reps=5):
+        assert fn() == 0
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            assert fn() == 0
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    out = {}
+    ms = time_ms(lambda: L.moe_ceiling_copy(src.data_ptr(), dst.data_ptr(), nbytes, sp))
+    out["hbm_copy_GB/s"] = 2 * nbytes / (ms * 1e-3) / 1e9
+    ms = time_ms(lambda: L.moe_ceiling_read(src.data_ptr(), nbytes, sink.data_ptr(), sp))
+    out["hbm_read_GB/s"] = nbytes / (ms * 1e-3) / 1e9
+    iters = 20000
+    for wpe in (1, 2):
+        ms = time_ms(lambda: L.moe_ceiling_mfma_bf16(iters, wpe, sink.data_ptr(), sp), reps=3)
+        flops = 256 * 4 * wpe * iters * 8 * 32768.0
+        out[f"mfma_bf16_TFLOP/s_{wpe}wave"] = flops / (ms * 1e-3) / 1e12
+    del src, dst
+    return {k: round(v, 1) for k, v in out.items()}
 
 
 def cpu_baseline(w, d, sample: int):

@@ -17,19 +17,39 @@ from tests.harness import config
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+def _declared_functions(header="moe.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert len(names) >= 10
+    assert len(names) >= 12
     L = M.lib()
     for n in names:
         assert hasattr(L, n), n
         assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_ceiling_library_exports_and_rejects_bad_arguments():
+    from top_routing_expert_router_amd.build import CEILING_LIB_PATH
+    L = ctypes.CDLL(CEILING_LIB_PATH)
+    names = _declared_functions("moe_ceiling.h")
+    assert names == ["moe_ceiling_copy", "moe_ceiling_mfma_bf16", "moe_ceiling_read"]
+    for n in names:
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+    P, SZ, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    L.moe_ceiling_copy.argtypes, L.moe_ceiling_copy.restype = [P, P, SZ, P], I32
+    L.moe_ceiling_read.argtypes, L.moe_ceiling_read.restype = [P, SZ, P, P], I32
+    L.moe_ceiling_mfma_bf16.argtypes, L.moe_ceiling_mfma_bf16.restype = [I32, I32, P, P], I32
+    # every call below fails its host-side argument check; nothing is launched
+    assert L.moe_ceiling_copy(None, 4096, 64, None) == 1
+    assert L.moe_ceiling_copy(4096, 8192, 24, None) == 1
+    assert L.moe_ceiling_copy(4100, 8192, 64, None) == 1
+    assert L.moe_ceiling_read(4096, 0, 4096, None) == 1
+    assert L.moe_ceiling_mfma_bf16(10, 3, 4096, None) == 1
+    assert L.moe_ceiling_mfma_bf16(0, 1, 4096, None) == 1
 
 
 def test_abi_version_and_status_strings():

@@ -10,7 +10,7 @@
 // Batch invariance ("Why temperature=0 Still Gives Different Answers: Batch
 // Invariance", "How do I make LLM inference reproducible?", tier 2): each logit
 // is reduced in a fixed order that depends only on H (64-wide K chunks dealt to
-// four waves round-robin, each wave in ascending chunk order, then the four wave
+// eight waves round-robin, each wave in ascending chunk order, then the eight wave
 // partials added in wave order).  Nothing depends on T or on the other tokens.
 #include "common.h"
 #include "kernels.h"
@@ -19,9 +19,15 @@ namespace moe {
 namespace {
 
 constexpr int kRouterTokens = 16;   // tokens per workgroup (one 16-wide MFMA column block)
-constexpr int kRouterWaves = 4;     // waves per workgroup; wave w takes K chunks w, w+4, ...
+constexpr int kRouterWaves = 8;     // waves per workgroup; wave w takes K chunks w, w+8, ...
+constexpr int kRouterThreads = kRouterWaves * 64;
 constexpr int kChunkK = 64;         // K per chunk: lane group q = lane / 16 holds k in [16 q, 16 q + 16)
-constexpr int kUnroll = 4;          // chunks in flight per wave
+
+// chunks in flight per wave: a CU's whole share of h for small expert counts
+template <int NSUB>
+struct RouterUnroll {
+  static constexpr int value = NSUB <= 1 ? 8 : (NSUB <= 4 ? 4 : 2);
+};
 
 typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 
@@ -108,10 +114,10 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
 // Per 64-wide K chunk each lane loads 32 contiguous bytes of its token row (a whole
 // 128-byte line per row and instruction) and of its expert row, and issues two MFMAs
 // (the first and second 8 elements of its 16).  Wave w accumulates chunks w, w+4, ...
-// in ascending order; the four wave partials are added in wave order; nothing depends
+// in ascending order; the eight wave partials are added in wave order; nothing depends
 // on T or on the other tokens.
 template <int NSUB>
-__global__ __launch_bounds__(256) void router_bf16(const __bf16* __restrict__ h, const __bf16* __restrict__ wg,
+__global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __restrict__ h, const __bf16* __restrict__ wg,
                                                    const float* __restrict__ bias, float* __restrict__ logits,
                                                    int32_t* __restrict__ ids, float* __restrict__ gates,
                                                    float* __restrict__ margin, int T, int H, int N, int k,
@@ -122,37 +128,64 @@ __global__ __launch_bounds__(256) void router_bf16(const __bf16* __restrict__ h,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kRouterTokens;
   const int col = lane & 15, kq = (lane >> 4) * 16;
-  const int tok = t0 + col;
-  const bool tok_ok = tok < T;
-  const __bf16* hrow = h + (size_t)(tok_ok ? tok : 0) * H + kq;
+  // Columns past T and expert rows past N read row 0: their products land only in
+  // accumulator entries that are never written out, so no load needs a branch.
+  const __bf16* hrow = h + (size_t)(t0 + col < T ? t0 + col : 0) * H + kq;
+  const __bf16* wrow[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) wrow[s] = wg + (size_t)(s * 16 + col < N ? s * 16 + col : 0) * H + kq;
   const int nchunks = H / kChunkK;
 
   f32x4 acc[NSUB];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  constexpr int kUnroll = RouterUnroll<NSUB>::value;
+  auto mfma2 = [&](int s, const bf16x16& wv, const bf16x16& hv) {
+    const bf16x8 hlo = __builtin_shufflevector(hv, hv, 0, 1, 2, 3, 4, 5, 6, 7);
+    const bf16x8 hhi = __builtin_shufflevector(hv, hv, 8, 9, 10, 11, 12, 13, 14, 15);
+    const bf16x8 wlo = __builtin_shufflevector(wv, wv, 0, 1, 2, 3, 4, 5, 6, 7);
+    const bf16x8 whi = __builtin_shufflevector(wv, wv, 8, 9, 10, 11, 12, 13, 14, 15);
+    acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, hlo, acc[s], 0, 0, 0);
+    acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, hhi, acc[s], 0, 0, 0);
+  };
   const bf16x16 zero16 = bf16x16{};
   for (int c0 = wave; c0 < nchunks; c0 += kRouterWaves * kUnroll) {
+    // Every load of this round is issued before the first MFMA.  A chunk slot past
+    // the end of H (which slots exist depends on H only) re-reads the last chunk
+    // and has its activations replaced by zeros, adding exact zeros to the sums.
     bf16x16 hv[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int c = c0 + u * kRouterWaves;
-      hv[u] = (c < nchunks && tok_ok) ? *reinterpret_cast<const bf16x16*>(hrow + c * kChunkK) : zero16;
+      const int c = min(c0 + u * kRouterWaves, nchunks - 1);
+      hv[u] = *reinterpret_cast<const bf16x16*>(hrow + c * kChunkK);
     }
+    if constexpr (NSUB <= 4) {
+      bf16x16 wv[kUnroll][NSUB];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int c = c0 + u * kRouterWaves;
-      if (c >= nchunks) break;
-      const bf16x8 hlo = __builtin_shufflevector(hv[u], hv[u], 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 hhi = __builtin_shufflevector(hv[u], hv[u], 8, 9, 10, 11, 12, 13, 14, 15);
+      for (int u = 0; u < kUnroll; ++u) {
+        const int c = min(c0 + u * kRouterWaves, nchunks - 1);
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        const int e = s * 16 + col;
-        const bf16x16 wv = e < N ? *reinterpret_cast<const bf16x16*>(wg + (size_t)e * H + c * kChunkK + kq) : zero16;
-        const bf16x8 wlo = __builtin_shufflevector(wv, wv, 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 whi = __builtin_shufflevector(wv, wv, 8, 9, 10, 11, 12, 13, 14, 15);
-        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, hlo, acc[s], 0, 0, 0);
-        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, hhi, acc[s], 0, 0, 0);
+        for (int s = 0; s < NSUB; ++s) wv[u][s] = *reinterpret_cast<const bf16x16*>(wrow[s] + c * kChunkK);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const bf16x16 x = (c0 + u * kRouterWaves < nchunks) ? hv[u] : zero16;
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) mfma2(s, wv[u][s], x);
+      }
+    } else {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int c = min(c0 + u * kRouterWaves, nchunks - 1);
+        const bf16x16 x = (c0 + u * kRouterWaves < nchunks) ? hv[u] : zero16;
+        bf16x16 wv[NSUB];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) wv[s] = *reinterpret_cast<const bf16x16*>(wrow[s] + c * kChunkK);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) mfma2(s, wv[s], x);
       }
     }
   }
@@ -166,15 +199,14 @@ __global__ __launch_bounds__(256) void router_bf16(const __bf16* __restrict__ h,
     const int e = i / kRouterTokens, t = i % kRouterTokens;
     if (e >= N) continue;
     float v = part[0][e][t];
-    v += part[1][e][t];
-    v += part[2][e][t];
-    v += part[3][e][t];
+#pragma unroll
+    for (int w = 1; w < kRouterWaves; ++w) v += part[w][e][t];
     if (bias) v += bias[e];
     lg[t][e] = v;
     if (t0 + t < T) logits[(size_t)(t0 + t) * N + e] = v;
   }
   __syncthreads();
-  // fused top-k: wave w ranks tokens 4 w .. 4 w + 3 of this workgroup
+  // fused top-k: wave w ranks tokens 2 w, 2 w + 1 of this workgroup
 #pragma unroll
   for (int j = 0; j < kRouterTokens / kRouterWaves; ++j) {
     const int t = wave * (kRouterTokens / kRouterWaves) + j;
@@ -212,7 +244,7 @@ template <int NSUB>
 hipError_t launch_router_bf16(const moe_config& c, const void* h, const void* wg, const float* bias, float* logits,
                               int32_t* ids, float* gates, float* margin, hipStream_t s) {
   dim3 grid(ceil_div(c.T, kRouterTokens));
-  router_bf16<NSUB><<<grid, 256, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits, ids, gates, margin, c.T,
+  router_bf16<NSUB><<<grid, kRouterThreads, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits, ids, gates, margin, c.T,
                                          c.H, c.N, c.k, c.renormalize);
   return hipGetLastError();
 }
