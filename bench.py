@@ -50,6 +50,87 @@ def _traffic(workload: str, launches_per_unit: float):
     return d.get("hbm_bytes_per_launch")
 
 
+# rocprofv3 kernel-name fragments -> stage names used in the counter summary
+_COUNTER_KERNELS = [("ffn_gemm_bf16<0", "gate_up_gemm"), ("ffn_gemm_bf16<1", "down_gemm"),
+                    ("router_bf16", "route"), ("topk_gates", "route_topk"), ("align_hist", "align_hist"),
+                    ("align_scan", "align_scan"), ("align_scatter", "align_scatter"),
+                    ("combine_rows", "combine"), ("copy16", "ceiling_copy_1GiB"), ("read16", "ceiling_read_1GiB"),
+                    ("mfma_loop<1>", "ceiling_mfma_1wave"), ("mfma_loop<2>", "ceiling_mfma_2wave")]
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str) -> int:
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; CSV
+    output) into HBM bytes per launch.  Both counters are in KiB per dispatch; each is
+    scaled by bytes / counter for the 1 GiB copy kernel the same runs launch (it reads
+    and writes exactly 2^30 bytes).  Writes profiles/gate_up_gemm_<workload>_traffic.json
+    (tagged with the hash of the GEMM source it was taken on) and prints a text summary."""
+    import csv
+    import statistics
+
+    def per_kernel(d, counter):
+        path = os.path.join(d, "run_counter_collection.csv")
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            for frag, stage in _COUNTER_KERNELS:
+                if frag in r["Kernel_Name"]:
+                    vals.setdefault(stage, []).append(float(r["Counter_Value"]))
+        return {k: statistics.mean(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+    fetch, nf = per_kernel(fetch_dir, "FETCH_SIZE")
+    write, nw = per_kernel(write_dir, "WRITE_SIZE")
+    copy_bytes = float(1 << 30)
+    f_scale = copy_bytes / (fetch["ceiling_copy_1GiB"] * 1024)
+    w_scale = copy_bytes / (write["ceiling_copy_1GiB"] * 1024)
+    rows = {}
+    for stage in fetch:
+        if stage not in write:
+            continue
+        rb, wb = fetch[stage] * 1024 * f_scale, write[stage] * 1024 * w_scale
+        rows[stage] = {"fetch_KiB": round(fetch[stage], 1), "write_KiB": round(write[stage], 1),
+                       "read_bytes": round(rb), "write_bytes": round(wb), "hbm_bytes": round(rb + wb),
+                       "dispatches": nf[stage]}
+    out = {"workload": workload, "ffn_source_sha256_16": _ffn_source_hash(),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "hbm_bytes_per_launch": rows["gate_up_gemm"]["hbm_bytes"], "kernels": rows}
+    path = os.path.join(ROOT, "profiles", f"gate_up_gemm_{workload}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(f"counter calibration: FETCH_SIZE x{f_scale:.4f}, WRITE_SIZE x{w_scale:.4f} "
+          f"(1 GiB copy kernel: {fetch['ceiling_copy_1GiB']:.0f} / {write['ceiling_copy_1GiB']:.0f} KiB)")
+    print(f"{'kernel':<20}{'FETCH KiB':>14}{'WRITE KiB':>14}{'read GB':>10}{'write GB':>10}{'HBM GB':>10}")
+    for k, v in rows.items():
+        print(f"{k:<20}{v['fetch_KiB']:>14,.0f}{v['write_KiB']:>14,.0f}{v['read_bytes'] / 1e9:>10.4f}"
+              f"{v['write_bytes'] / 1e9:>10.4f}{v['hbm_bytes'] / 1e9:>10.4f}")
+    print(f"wrote {os.path.relpath(path, ROOT)}")
+    return 0
+
+
+def summarize_trace(trace_dir: str, workload: str) -> int:
+    """Per-kernel durations from a rocprofv3 --kernel-trace run of this script (CSV
+    output): calls, average, min, max and share of GPU time, layer kernels by name
+    and torch's own kernels (input generation, cache-flush fills) lumped together."""
+    import csv
+    import statistics
+
+    per = {}
+    for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))):
+        n = r["Kernel_Name"]
+        name = next((st for frag, st in _COUNTER_KERNELS if frag in n), None)
+        if name is None:
+            name = "torch (inputs, flush fills)" if "at::native" in n else n.split("(")[0][-40:]
+        per.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in per.values())
+    print(f"# rocprofv3 kernel trace of bench.py, workload {workload}; durations in microseconds")
+    print(f"{'kernel':<30}{'calls':>7}{'avg_us':>11}{'min_us':>11}{'max_us':>11}{'total_us':>12}{'pct':>8}")
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{k:<30}{len(v):>7}{statistics.mean(v):>11.2f}{min(v):>11.2f}{max(v):>11.2f}"
+              f"{sum(v):>12.1f}{100 * sum(v) / total:>8.2f}")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -59,7 +140,15 @@ def main() -> int:
     ap.add_argument("--cpu-sample", type=int, default=128, help="tokens of the workload the CPU oracle runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timings")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="no GPU: per-kernel durations from a rocprofv3 --kernel-trace run of this script")
     args = ap.parse_args()
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace, args.workload)
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters, args.workload)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -137,19 +226,33 @@ def main() -> int:
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in es) / reps  # ms per launch
 
+    def timed_chain(fns, reps):
+        """Per-launch time of each fn when they run in sequence, as they do in the forward
+        (so each kernel sees the clocks and caches it sees there)."""
+        es = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(reps)]
+        for f in fns:
+            f()
+        for ev in es:
+            ev[0].record(stream)
+            for f, e in zip(fns, ev[1:]):
+                f()
+                e.record(stream)
+        torch.cuda.synchronize()
+        return [sum(ev[i].elapsed_time(ev[i + 1]) for ev in es) / reps for i in range(len(fns))]
+
     R, T, H, I, N, k = w.T * w.k, w.T, w.H, w.I, w.N, w.k
     stages = {}
     gate_up_flops = 4.0 * kept_routes * H * I
-    ms_gate_up = timed(lambda: M.moe_expert_gate_up(cfg, d["h"], tr["sorted_route_ids"], tr["expert_offsets"],
-                                                    d["w13"], d.get("w13_scale"), tr["act"], stream=stream),
-                       max(args.steps, 5), False)
+    down_flops = 2.0 * kept_routes * H * I
+    ms_gate_up, ms_down = timed_chain(
+        [lambda: M.moe_expert_gate_up(cfg, d["h"], tr["sorted_route_ids"], tr["expert_offsets"],
+                                      d["w13"], d.get("w13_scale"), tr["act"], stream=stream),
+         lambda: M.moe_expert_down(cfg, tr["act"], tr["sorted_route_ids"], tr["expert_offsets"],
+                                   d["w2"], d.get("w2_scale"), tr["y_route"], stream=stream)],
+        max(args.steps, 5))
     stages["gate_up_gemm"] = {"us": ms_gate_up * 1e3, "TFLOP/s": gate_up_flops / (ms_gate_up * 1e-3) / 1e12}
+    stages["down_gemm"] = {"us": ms_down * 1e3, "TFLOP/s": down_flops / (ms_down * 1e-3) / 1e12}
     if not args.no_stages:
-        down_flops = 2.0 * kept_routes * H * I
-        ms_down = timed(lambda: M.moe_expert_down(cfg, tr["act"], tr["sorted_route_ids"], tr["expert_offsets"],
-                                                  d["w2"], d.get("w2_scale"), tr["y_route"], stream=stream),
-                        max(args.steps, 5), False)
-        stages["down_gemm"] = {"us": ms_down * 1e3, "TFLOP/s": down_flops / (ms_down * 1e-3) / 1e12}
         route_bytes = T * H * asz + N * H * asz + T * N * 4 + R * 8 + T * 4
         ms_route = timed(lambda: M.moe_route(cfg, d["h"], wts["w_gate"], wts["logit_bias"], tr["logits"],
                                              tr["topk_ids"], tr["topk_gates"], tr["margin"], stream=stream),
