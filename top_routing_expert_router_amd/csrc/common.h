@@ -60,22 +60,66 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Wave-wide max of a 64-bit key with a fixed butterfly.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    uint64_t o = shfl_xor_u64(v, m);
+// Cross-lane moves inside rows of 16 lanes (DPP): swap neighbours (lane ^ 1), swap
+// pairs (lane ^ 2), reverse each 8-lane half row, reverse the 16-lane row.  Applied
+// in that order, each step joins two groups that already agree, so after step s every
+// lane holds the reduction of its aligned group of 2^(s+1) lanes.
+enum : int { kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140 };
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+// Max of a 64-bit key over each aligned group of L lanes (L = 8, 16, 32 or 64); every
+// lane of a group gets the group's max.  Max is exact, so the step order cannot
+// change the result.  A group's lanes must all be active together.
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v, int L) {
+  uint64_t o;
+  o = dpp_u64<kDppXor1>(v);
+  v = o > v ? o : v;
+  o = dpp_u64<kDppXor2>(v);
+  v = o > v ? o : v;
+  o = dpp_u64<kDppHalfMirror>(v);
+  v = o > v ? o : v;
+  if (L > 8) {
+    o = dpp_u64<kDppMirror>(v);
+    v = o > v ? o : v;
+  }
+  if (L > 16) {
+    o = shfl_xor_u64(v, 16);
+    v = o > v ? o : v;
+  }
+  if (L > 32) {
+    o = shfl_xor_u64(v, 32);
     v = o > v ? o : v;
   }
   return v;
 }
 
-// Wave-wide sum with a fixed butterfly (every lane gets the same bits).
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+// Sum over each aligned group of L lanes with a fixed pairing order; the two lanes of
+// a pair add the same two values, so every lane of the group gets the same bits.
+__device__ __forceinline__ float group_sum_f32(float v, int L) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  if (L > 8) v += dpp_f32<kDppMirror>(v);
+  if (L > 16) v += __shfl_xor(v, 16, kWave);
+  if (L > 32) v += __shfl_xor(v, 32, kWave);
   return v;
 }
+
+// Lanes per token for the top-k: the smallest of 8, 16, 32, 64 that holds N experts
+// (N > 64: 64 lanes, up to 4 experts each).
+__host__ __device__ inline int topk_lanes(int N) { return N <= 8 ? 8 : (N <= 16 ? 16 : (N <= 32 ? 32 : 64)); }
 
 __device__ __forceinline__ int wave_sum_i32(int v) {
 #pragma unroll

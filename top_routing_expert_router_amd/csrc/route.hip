@@ -31,20 +31,23 @@ struct RouterUnroll {
 
 typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 
-// Top-k, gates and margin of one token from its N logits (global or LDS), one wave.
-// Each lane holds experts lane + 64 i.  k+1 rounds of a wave-wide max over
+// Top-k, gates and margin of one token from its N logits (global or LDS), by one
+// aligned group of L = topk_lanes(N) lanes; a wave ranks 64 / L tokens at once.
+// Lane g of the group holds experts g + L i.  k+1 rounds of a group max over
 // (value, -index) keys give the ranked ids and the (k+1)-th logit for the margin.
 // Gate weight_j = exp(l_j - l_0) (0 for a NaN logit); divided by the sum over the
 // k chosen in rank order, or by the sum over all N experts without renormalisation.
 template <typename RowPtr>
-__device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int renormalize, int32_t* __restrict__ ids,
-                                         float* __restrict__ gates, float* __restrict__ margin) {
+__device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int renormalize, int L,
+                                         int32_t* __restrict__ ids, float* __restrict__ gates,
+                                         float* __restrict__ margin) {
   const int lane = threadIdx.x & 63;
+  const int g = lane & (L - 1), base = lane - g;
   float lv[4];
   uint64_t key[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
+    const int e = g + L * i;
     lv[i] = e < N ? row[e] : 0.f;
     key[i] = e < N ? rank_key(lv[i], e) : 0ull;
   }
@@ -59,15 +62,15 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
       uint64_t best = key[0];
 #pragma unroll
       for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
-      best = wave_max_u64(best);
+      best = group_max_u64(best, L);
       const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-      const int owner = e & 63, slot = e >> 6;
+      const int owner = e & (L - 1), slot = e / L;
       float mine = lv[0];
 #pragma unroll
       for (int i = 1; i < 4; ++i) mine = slot == i ? lv[i] : mine;
-      sl[j] = __shfl(mine, owner, kWave);
+      sl[j] = __shfl(mine, base + owner, kWave);
       sid[j] = e;
-      if (lane == owner) {
+      if (g == owner) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (i == slot) key[i] = 0ull;
@@ -89,19 +92,19 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
     float z = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
+      const int e = g + L * i;
       if (e < N && lv[i] == lv[i]) z += expf(lv[i] - l0);
     }
-    s = wave_sum_f32(z);
+    s = group_sum_f32(z, L);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    if (j < k && lane == j) {
+    if (j < k && g == j) {
       ids[(size_t)t * k + j] = sid[j];
       gates[(size_t)t * k + j] = w[j] / s;
     }
   }
-  if (margin && lane == 0) {
+  if (margin && g == 0) {
     float m = __builtin_inff();
 #pragma unroll
     for (int j = 1; j < 9; ++j)
@@ -206,12 +209,11 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
     if (t0 + t < T) logits[(size_t)(t0 + t) * N + e] = v;
   }
   __syncthreads();
-  // fused top-k: wave w ranks tokens 2 w, 2 w + 1 of this workgroup
-#pragma unroll
-  for (int j = 0; j < kRouterTokens / kRouterWaves; ++j) {
-    const int t = wave * (kRouterTokens / kRouterWaves) + j;
-    if (t0 + t < T) topk_one(&lg[t][0], t0 + t, N, k, renormalize, ids, gates, margin);
-  }
+  // fused top-k: one group of L lanes per token, 64 / L tokens per wave
+  const int L = topk_lanes(N);
+  const int per_wave = kWave / L;
+  for (int t = wave * per_wave + lane / L; t < kRouterTokens; t += kRouterWaves * per_wave)
+    if (t0 + t < T) topk_one(&lg[t][0], t0 + t, N, k, renormalize, L, ids, gates, margin);
 }
 
 // fp32 projection: one thread per (token, expert), fmaf over H in ascending order.
@@ -229,15 +231,15 @@ __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict
   logits[i] = acc;
 }
 
-// Standalone top-k over stored logits (fp32 path and routing from given logits).
-constexpr int kTopkTokensPerBlock = 4;
-
+// Standalone top-k over stored logits (fp32 path and routing from given logits):
+// 256 threads, one group of L lanes per token, 256 / L tokens per workgroup.
 __global__ __launch_bounds__(256) void topk_gates(const float* __restrict__ logits, int32_t* __restrict__ ids,
                                                    float* __restrict__ gates, float* __restrict__ margin,
                                                    int T, int N, int k, int renormalize) {
-  const int t = blockIdx.x * kTopkTokensPerBlock + (threadIdx.x >> 6);
+  const int L = topk_lanes(N);
+  const int t = blockIdx.x * (256 / L) + threadIdx.x / L;
   if (t >= T) return;
-  topk_one(logits + (size_t)t * N, t, N, k, renormalize, ids, gates, margin);
+  topk_one(logits + (size_t)t * N, t, N, k, renormalize, L, ids, gates, margin);
 }
 
 template <int NSUB>
@@ -275,7 +277,7 @@ hipError_t launch_router(const moe_config& c, const void* h, const void* w_gate,
 
 hipError_t launch_topk(const moe_config& c, const float* logits, int32_t* ids, float* gates, float* margin,
                        hipStream_t s) {
-  dim3 grid(ceil_div(c.T, kTopkTokensPerBlock));
+  dim3 grid(ceil_div(c.T, 256 / topk_lanes(c.N)));
   topk_gates<<<grid, 256, 0, s>>>(logits, ids, gates, margin, c.T, c.N, c.k, c.renormalize);
   return hipGetLastError();
 }
