@@ -105,7 +105,9 @@ enum {
  *   n_shared in {0, 1} (one always-on expert added with gate 1);
  *   renormalize 1 = gates renormalised over the k chosen, 0 = plain softmax values;
  *   dtypes: (act F32, expert F32), (act BF16, expert BF16),
- *           (act BF16, expert FP8_E4M3 with scale_block 128).
+ *           (act BF16, expert FP8_E4M3 with scale_block 128);
+ *   bf16 activations: T*H < 2^31 and 2*I*H < 2^31 (the expert GEMMs address h
+ *           and one expert's weights with 32-bit byte offsets).
  * act_dtype is the type of h, residual, out, W_g, act and y_route.
  */
 typedef struct moe_config {

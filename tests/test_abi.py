@@ -75,7 +75,8 @@ def test_workload_configs_are_valid(w):
 BAD = [
     dict(T=0), dict(T=65537), dict(H=100), dict(H=0), dict(I=64), dict(N=0), dict(N=257), dict(k=0),
     dict(k=9, N=16), dict(k=3, N=2), dict(B=12), dict(B=256), dict(cap_num=5, cap_den=0),
-    dict(cap_num=-1, cap_den=4), dict(n_shared=2), dict(renormalize=2),
+    dict(cap_num=-1, cap_den=4), dict(n_shared=2), dict(renormalize=2), dict(T=65536, H=32768),
+    dict(I=32768, H=32768),
 ]
 
 

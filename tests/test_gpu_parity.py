@@ -224,7 +224,8 @@ def test_expert_ffn(name):
 
 @pytest.mark.parametrize("name", ["toy_fp32", "mixtral_bf16", "deepseekv3_fp8"])
 def test_shared_expert_identity_mode(name):
-    w = SMALL[name].with_(n_shared=1)
+    # at least two 256-row tiles, so a tile that does not start at row 0 is checked
+    w = SMALL[name].with_(n_shared=1, T=max(SMALL[name].T, 300))
     d = W.layer_inputs(w)
     dv = Hn.to_dev(d)
     _say("shared_expert", name)

@@ -33,6 +33,8 @@ moe_status check_config(const moe_config* c) {
                        (c->expert_dtype >= MOE_F32 && c->expert_dtype <= MOE_FP8_E4M3);
     return known ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_CONFIG;
   }
+  // the MFMA GEMMs address h and one expert's weights with 32-bit byte offsets
+  if (!f32 && ((long)c->T * c->H >= (1L << 31) || 2L * c->I * c->H >= (1L << 31))) return MOE_ERR_INVALID_CONFIG;
   return MOE_OK;
 }
 

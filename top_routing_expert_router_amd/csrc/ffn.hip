@@ -37,6 +37,8 @@ namespace {
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 256;
 constexpr int kGroupN = 2;                        // n-tiles per raster group
+// buffer resource word 3 for raw (untyped, stride 0) buffer loads on gfx9-family parts
+constexpr int kBufferFlags = 0x00020000;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -154,23 +156,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // puts there (the swizzle is an involution in the chunk index).
   const int drow = lane >> 3;                    // row within the 8-row group
   auto dchunk = [&](int j) { return swz_chunk(wave * 64 + j * 8 + drow, lane & 7); };
+  // The copies are buffer loads with LDS destination: a buffer resource per operand
+  // (base address + byte size, out-of-range reads return zeros) and a 32-bit byte
+  // offset per lane.  A: the activation rows -- all of h (MODE 0, gathered rows) or
+  // the tile's own act rows (MODE 1, contiguous from p0).  B: this expert's weights.
   const __bf16* X = (const __bf16*)a.x;
-  const __bf16* arow[8];                         // activation row of each of the lane's 8 rows
+  const __amdgpu_buffer_rsrc_t rsrcA =
+      MODE == 0 ? __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)((unsigned)a.T * K * 2u), kBufferFlags)
+                : __builtin_amdgcn_make_buffer_rsrc((void*)(X + (long)p0 * K), (short)0,
+                                                    (int)((unsigned)(p1 - p0) * K * 2u), kBufferFlags);
+  uint32_t aoff[8];                              // byte offset of each of the lane's 8 rows
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int p = p0 + wave * 64 + j * 8 + drow;
-    // rows outside the tile or padding rows read a harmless valid row; their
-    // results are never stored (rows never interact in the product)
-    long row = MODE == 0 ? 0 : p0;
+    // rows outside the tile or padding rows read a harmless valid row (token 0 or
+    // tile row 0); their results are never stored (rows never interact in the product)
+    unsigned row = 0;
     if (p < p1) {
       if (a.sorted == nullptr) {
-        row = p;
+        row = MODE == 0 ? p : p - p0;
       } else {
         const int r = a.sorted[p];
-        if ((unsigned)r < (unsigned)a.sentinel) row = MODE == 0 ? r / a.k : p;
+        if ((unsigned)r < (unsigned)a.sentinel) row = MODE == 0 ? r / a.k : p - p0;
       }
     }
-    arow[j] = X + row * K + dchunk(j) * 8;
+    aoff[j] = (row * (unsigned)K + dchunk(j) * 8) * 2u;
   }
   const int n0 = MODE == 0 ? nt * (BN / 2) : nt * BN;
   // weight rows of the lane's 8 DMA rows (bf16 path) / staging rows (fp8 path)
@@ -180,7 +190,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   };
 
   // ---- bf16 weights: DMA like the activations
-  const __bf16* brow[8];
+  __amdgpu_buffer_rsrc_t rsrcB = rsrcA;  // replaced below on the bf16 path
+  uint32_t boff[8];
   // ---- fp8 weights: register staging with decode + scale (rows rb + 32 i)
   const int chunk = tid & 7, rb = tid >> 3;
   long wrow8[8];
@@ -188,10 +199,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   long srow_lo = 0, srow_hi = 0;
   if constexpr (!FP8) {
     const __bf16* Wb = (const __bf16*)a.w + (long)e * WR * K;
+    rsrcB = __builtin_amdgcn_make_buffer_rsrc((void*)Wb, (short)0, (int)((unsigned)WR * K * 2u), kBufferFlags);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int r = weight_row(wave * 64 + j * 8 + drow);
-      brow[j] = Wb + (long)(r < 0 ? 0 : r) * K + dchunk(j) * 8;
+      boff[j] = ((unsigned)(r < 0 ? 0 : r) * (unsigned)K + dchunk(j) * 8) * 2u;
     }
   } else {
 #pragma unroll
@@ -214,11 +226,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (part == 0) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        __builtin_amdgcn_global_load_lds(arow[j] + k0, LDS_PTR(sA + (wave * 8 + j) * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcA, LDS_PTR(sA + (wave * 8 + j) * 1024), 16, aoff[j], k0 * 2, 0, 0);
     } else if constexpr (!FP8) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        __builtin_amdgcn_global_load_lds(brow[j] + k0, LDS_PTR(sB + (wave * 8 + j) * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcB, LDS_PTR(sB + (wave * 8 + j) * 1024), 16, boff[j], k0 * 2, 0, 0);
     } else {
       const uint8_t* Wq = (const uint8_t*)a.w;
 #pragma unroll
@@ -324,10 +336,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   // Stage s of the K loop lives in buffer s & 1.  The DMA of stage s+2 is issued
   // right after the barrier that ends the reads of stage s, spread over the next
-  // 32 MFMAs.  K is a multiple of 128, so the stage count is even.  The loop body
-  // is one basic block (the DMA is unconditional: past the end it refetches the
-  // last stage into a buffer whose reads are never used) so the scheduling
-  // barriers hold.
+  // 32 MFMAs.  K is a multiple of 128, so the stage count is even.  The loop is
+  // rotated so that its head is a barrier (which waits for all LDS reads anyway),
+  // its body is one basic block (so the scheduling barriers hold), and the last two
+  // stages are peeled off: no copy is ever issued past the end of K.
   const int KT = K / BK;
   issue_loads(sA0, sB0, 0);
   store_fp8(sB0);
@@ -336,25 +348,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   load_frags(sA0, sB0, 0, fw[0], fx[0]);
   load_frags(sA0, sB0, 1, fw[1], fx[1]);
   __builtin_amdgcn_sched_barrier(0);
-  for (int kt = 0; kt < KT; kt += 2) {
-    step(0, sA0, sB0, 2, 2);
-    step(1, sA0, sB0, 3, 3);
+  step(0, sA0, sB0, 2, 2);
+  step(1, sA0, sB0, 3, 3);
+  for (int kt = 0; kt < KT - 2; kt += 2) {
     store_fp8(sB1);  // fp8: stage kt+1 into buffer 1 (codes fetched a stage earlier)
     dma_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const int k2 = min(kt + 2, KT - 1) * BK;
-    step_dma(2, sA1, sB1, 0, 0, sA0, sB0, k2, 0);
-    step_dma(3, sA1, sB1, 1, 1, sA0, sB0, k2, 1);
+    step_dma(2, sA1, sB1, 0, 0, sA0, sB0, (kt + 2) * BK, 0);
+    step_dma(3, sA1, sB1, 1, 1, sA0, sB0, (kt + 2) * BK, 1);
     step(0, sA1, sB1, 2, 2);
     step(1, sA1, sB1, 3, 3);
     store_fp8(sB0);
     dma_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const int k3 = min(kt + 3, KT - 1) * BK;
-    step_dma(2, sA0, sB0, 0, 0, sA1, sB1, k3, 0);
-    step_dma(3, sA0, sB0, 1, 1, sA1, sB1, k3, 1);
+    step_dma(2, sA0, sB0, 0, 0, sA1, sB1, (kt + 3) * BK, 0);
+    step_dma(3, sA0, sB0, 1, 1, sA1, sB1, (kt + 3) * BK, 1);
+    step(0, sA0, sB0, 2, 2);
+    step(1, sA0, sB0, 3, 3);
   }
-  dma_barrier();  // no DMA may outlive the workgroup's LDS
+  // stages KT-2 (fragments 2, 3 in registers) and KT-1 (buffer 1)
+  store_fp8(sB1);
+  dma_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  step(2, sA1, sB1, 0, 0);
+  step(3, sA1, sB1, 1, 1);
+  step(0, sA1, sB1, 2, 2);
+  step(1, sA1, sB1, 3, 3);
+  mfma16(fw[2], fx[2]);
+  mfma16(fw[3], fx[3]);
 
   // ---- epilogue.  Lane holds row (lane & 31) of each 32-row sub-tile and, per
   // register group g, the 4 consecutive columns 8 g + 4 (lane >> 5) + [0, 4).
