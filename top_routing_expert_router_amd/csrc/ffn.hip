@@ -65,50 +65,49 @@ struct FfnArgs {
 __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * (BK * 2) + (swz_chunk(row, chunk) << 4); }
 
-// Resolve M-tile m to (expert, first row, end row) from the expert offsets.
-// Each expert's padded segment is cut into ceil(len / BM) tiles in expert order.
-__device__ bool resolve_tile(const FfnArgs& a, int m, int& e, int& p0, int& p1, int* sh) {
-  if (a.sorted == nullptr) {
-    e = 0;
-    p0 = m * BM;
-    p1 = min(a.T, p0 + BM);
-    return p0 < a.T;
-  }
+// Tile table, built once per workgroup in LDS: beg[e] = first padded row of expert
+// e (beg[N] = end of the last), mt0[e] = number of BM-row m-tiles of the experts
+// before e (mt0[N] = all m-tiles).  Each expert's padded segment is cut into
+// ceil(len / BM) m-tiles in expert order.  Identity rows: one expert, rows [0, T).
+constexpr int kMaxExperts = 256;
+
+__device__ void build_tile_table(const FfnArgs& a, int* beg, int* mt0) {
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
-    int cnt[4], beg[4];
+    int b[4], cnt[4];
     int s = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ee = lane * 4 + i;
-      beg[i] = ee < a.N ? a.offsets[ee] : 0;
-      const int end = ee < a.N ? a.offsets[ee + 1] : 0;
-      cnt[i] = ee < a.N ? ceil_div(end - beg[i], BM) : 0;
+      const bool ok = ee < a.N;
+      b[i] = !ok ? 0 : (a.sorted == nullptr ? 0 : a.offsets[ee]);
+      const int end = !ok ? 0 : (a.sorted == nullptr ? a.T : a.offsets[ee + 1]);
+      cnt[i] = ok ? ceil_div(end - b[i], BM) : 0;
       s += cnt[i];
     }
     const int incl = wave_incl_scan_i32(s);
     int before = incl - s;
-    if (lane == 0) sh[0] = -1;
-    __builtin_amdgcn_wave_barrier();
-    if (m >= before && m < incl) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (m >= before && m < before + cnt[i]) {
-          const int ee = lane * 4 + i;
-          sh[0] = ee;
-          sh[1] = beg[i] + (m - before) * BM;
-          sh[2] = min(min(a.offsets[ee + 1], sh[1] + BM), a.rows);
-        }
-        before += cnt[i];
+    for (int i = 0; i < 4; ++i) {
+      const int ee = lane * 4 + i;
+      if (ee < a.N) {
+        beg[ee] = b[i];
+        mt0[ee] = before;
       }
+      before += cnt[i];
+    }
+    if (lane == kWave - 1) {
+      beg[a.N] = a.sorted == nullptr ? a.T : a.offsets[a.N];
+      mt0[a.N] = incl;
     }
   }
   __syncthreads();
-  e = sh[0];
-  p0 = sh[1];
-  p1 = sh[2];
-  return e >= 0 && p0 >= 0 && p0 < p1;
 }
+
+// One output tile: expert e, padded rows [p0, p1), weight n-tile nt.
+struct Tile {
+  int e, p0, p1, nt;
+};
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -122,6 +121,13 @@ __device__ __forceinline__ void dma_barrier() {
   __syncthreads();
 }
 
+// Barrier after this wave's LDS reads have completed (lgkmcnt(0); vmcnt and expcnt
+// not waited: imm 0xC07F), so no wave's later DMA can overwrite what a read still needs.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __syncthreads();
+}
+
 // MODE 0: W13 + SwiGLU -> act.  MODE 1: W2 -> y rows.
 template <int MODE, bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffn_gemm_bf16(FfnArgs a) {
@@ -131,20 +137,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ __attribute__((aligned(16))) char sB0[BN * BK * 2];
   __shared__ __attribute__((aligned(16))) char sA1[BM * BK * 2];
   __shared__ __attribute__((aligned(16))) char sB1[BN * BK * 2];
-  __shared__ int tile_sh[4];
+  __shared__ int t_beg[kMaxExperts + 1], t_mt0[kMaxExperts + 1];
 
-  // ---- tile selection: XCD-contiguous logical ids, grouped raster over n-tiles
-  const int G = a.mtiles * a.ntiles;
-  const int bid = blockIdx.x;
-  const int lid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
-  if (lid >= G) return;
-  const int group = lid / (kGroupN * a.mtiles);
-  const int gn0 = group * kGroupN;
-  const int gsize = min(kGroupN, a.ntiles - gn0);
-  const int idx = lid - group * kGroupN * a.mtiles;
-  const int mt = idx / gsize, nt = gn0 + idx % gsize;
-  int e, p0, p1;
-  if (!resolve_tile(a, mt, e, p0, p1, tile_sh)) return;
+  // ---- persistent work.  Tiles in logical order: groups of kGroupN n-tiles, all
+  // m-tiles of a group before the next group.  Hardware deals workgroups to the 8
+  // XCDs round-robin; XCD x owns the contiguous run [x, x+1) * ceil(G / 8) of that
+  // order, and its workgroup in slot s takes tiles s, s + slots, ... of the run, so
+  // the ~32 workgroups of an XCD work on neighbouring tiles at any time.
+  build_tile_table(a, t_beg, t_mt0);
+  // values read from the table are the same in every lane; readfirstlane makes them
+  // scalar, so the buffer resources built from them stay in SGPRs
+  const int total_m = __builtin_amdgcn_readfirstlane(t_mt0[a.N]);
+  const int G = total_m * a.ntiles;
+  const int per_xcd = ceil_div(G, 8);
+  const int slots = gridDim.x >> 3;
+  const int lid_end = min(G, ((int)(blockIdx.x & 7) + 1) * per_xcd);
+  int lid = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (lid >= lid_end) return;
+  auto decode = [&](int l, Tile& t) {
+    const int group = l / (kGroupN * total_m);
+    const int gn0 = group * kGroupN;
+    const int gsize = min(kGroupN, a.ntiles - gn0);
+    const int idx = l - group * kGroupN * total_m;
+    const int m = idx / gsize;
+    t.nt = gn0 + idx % gsize;
+    int lo = 0, hi = a.N;  // last expert e with mt0[e] <= m (empty experts have no tiles)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (t_mt0[mid] <= m) lo = mid; else hi = mid;
+    }
+    t.e = __builtin_amdgcn_readfirstlane(lo);
+    t.p0 = __builtin_amdgcn_readfirstlane(t_beg[lo] + (m - t_mt0[lo]) * BM);
+    t.p1 = __builtin_amdgcn_readfirstlane(min(min(t_beg[lo + 1], t.p0 + BM), a.rows));
+  };
+  Tile cur;
+  decode(lid, cur);
 
   const int K = MODE == 0 ? a.H : a.I;
   const int WR = MODE == 0 ? 2 * a.I : a.H;  // weight rows per expert
@@ -161,62 +188,66 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // offset per lane.  A: the activation rows -- all of h (MODE 0, gathered rows) or
   // the tile's own act rows (MODE 1, contiguous from p0).  B: this expert's weights.
   const __bf16* X = (const __bf16*)a.x;
-  const __amdgpu_buffer_rsrc_t rsrcA =
-      MODE == 0 ? __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)((unsigned)a.T * K * 2u), kBufferFlags)
-                : __builtin_amdgcn_make_buffer_rsrc((void*)(X + (long)p0 * K), (short)0,
-                                                    (int)((unsigned)(p1 - p0) * K * 2u), kBufferFlags);
-  uint32_t aoff[8];                              // byte offset of each of the lane's 8 rows
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int p = p0 + wave * 64 + j * 8 + drow;
-    // rows outside the tile or padding rows read a harmless valid row (token 0 or
-    // tile row 0); their results are never stored (rows never interact in the product)
-    unsigned row = 0;
-    if (p < p1) {
-      if (a.sorted == nullptr) {
-        row = MODE == 0 ? p : p - p0;
-      } else {
-        const int r = a.sorted[p];
-        if ((unsigned)r < (unsigned)a.sentinel) row = MODE == 0 ? r / a.k : p - p0;
-      }
-    }
-    aoff[j] = (row * (unsigned)K + dchunk(j) * 8) * 2u;
-  }
-  const int n0 = MODE == 0 ? nt * (BN / 2) : nt * BN;
+  __amdgpu_buffer_rsrc_t rsrcA = __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, 0, kBufferFlags);
+  __amdgpu_buffer_rsrc_t rsrcB = rsrcA;
+  uint32_t aoff[8];                              // byte offset of each of the lane's 8 A rows
+  uint32_t boff[8];                              // byte offset of the lane's 8 weight rows
   // weight rows of the lane's 8 DMA rows (bf16 path) / staging rows (fp8 path)
-  auto weight_row = [&](int j) {  // j = tile row
+  auto weight_row = [&](int n0, int j) {  // j = tile row
     const int r = MODE == 0 ? (j < BN / 2 ? n0 + j : a.I + n0 + (j - BN / 2)) : n0 + j;
     return (MODE == 1 && r >= a.H) ? -1 : r;
   };
-
-  // ---- bf16 weights: DMA like the activations
-  __amdgpu_buffer_rsrc_t rsrcB = rsrcA;  // replaced below on the bf16 path
-  uint32_t boff[8];
-  // ---- fp8 weights: register staging with decode + scale (rows rb + 32 i)
+  // ---- fp8 weights: register staging with decode + scale (rows rb + 32 i); boff[i]
+  // is then the byte offset of row rb + 32 i, chunk (tid & 7), or past the end of the
+  // expert's codes for a row beyond the weights (the load returns zeros)
   const int chunk = tid & 7, rb = tid >> 3;
-  long wrow8[8];
-  bool wok8[8];
   long srow_lo = 0, srow_hi = 0;
-  if constexpr (!FP8) {
-    const __bf16* Wb = (const __bf16*)a.w + (long)e * WR * K;
-    rsrcB = __builtin_amdgcn_make_buffer_rsrc((void*)Wb, (short)0, (int)((unsigned)WR * K * 2u), kBufferFlags);
+  // Buffers, offsets and weight rows of tile t.  A: all of h (MODE 0, gathered
+  // rows) or the tile's own act rows (MODE 1, contiguous from p0).  B: expert e.
+  auto setup = [&](const Tile& t) {
+    rsrcA = MODE == 0
+                ? __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)((unsigned)a.T * K * 2u), kBufferFlags)
+                : __builtin_amdgcn_make_buffer_rsrc((void*)(X + (long)t.p0 * K), (short)0,
+                                                    (int)((unsigned)(t.p1 - t.p0) * K * 2u), kBufferFlags);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int r = weight_row(wave * 64 + j * 8 + drow);
-      boff[j] = ((unsigned)(r < 0 ? 0 : r) * (unsigned)K + dchunk(j) * 8) * 2u;
+      const int p = t.p0 + wave * 64 + j * 8 + drow;
+      // rows outside the tile or padding rows read a harmless valid row (token 0 or
+      // tile row 0); their results are never stored (rows never interact in the product)
+      unsigned row = 0;
+      if (p < t.p1) {
+        if (a.sorted == nullptr) {
+          row = MODE == 0 ? p : p - t.p0;
+        } else {
+          const int r = a.sorted[p];
+          if ((unsigned)r < (unsigned)a.sentinel) row = MODE == 0 ? r / a.k : p - t.p0;
+        }
+      }
+      aoff[j] = (row * (unsigned)K + dchunk(j) * 8) * 2u;
     }
-  } else {
+    const int n0 = MODE == 0 ? t.nt * (BN / 2) : t.nt * BN;
+    if constexpr (!FP8) {
+      const __bf16* Wb = (const __bf16*)a.w + (long)t.e * WR * K;
+      rsrcB = __builtin_amdgcn_make_buffer_rsrc((void*)Wb, (short)0, (int)((unsigned)WR * K * 2u), kBufferFlags);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = weight_row(rb + 32 * i);
-      wok8[i] = r >= 0;
-      wrow8[i] = ((long)e * WR + (r < 0 ? 0 : r)) * K;
+      for (int j = 0; j < 8; ++j) {
+        const int r = weight_row(n0, wave * 64 + j * 8 + drow);
+        boff[j] = ((unsigned)(r < 0 ? 0 : r) * (unsigned)K + dchunk(j) * 8) * 2u;
+      }
+    } else {
+      const uint8_t* Wq = (const uint8_t*)a.w + (long)t.e * WR * K;
+      rsrcB = __builtin_amdgcn_make_buffer_rsrc((void*)Wq, (short)0, (int)((unsigned)WR * K), kBufferFlags);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = weight_row(n0, rb + 32 * i);
+        boff[i] = r < 0 ? 0x80000000u : (unsigned)r * (unsigned)K + chunk * 8;
+      }
+      const int kb = K / 128;
+      const int rhi = MODE == 0 ? a.I + n0 : n0 + 128;
+      srow_lo = ((long)t.e * (WR / 128) + n0 / 128) * kb;
+      srow_hi = ((long)t.e * (WR / 128) + min(rhi, WR - 1) / 128) * kb;
     }
-    const int kb = K / 128;
-    const int rhi = MODE == 0 ? a.I + n0 : n0 + 128;
-    srow_lo = ((long)e * (WR / 128) + n0 / 128) * kb;
-    srow_hi = ((long)e * (WR / 128) + min(rhi, WR - 1) / 128) * kb;
-  }
+  };
   u32x2 bq[8];
   float sc_lo = 1.f, sc_hi = 1.f;
 
@@ -232,10 +263,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int j = 0; j < 8; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcB, LDS_PTR(sB + (wave * 8 + j) * 1024), 16, boff[j], k0 * 2, 0, 0);
     } else {
-      const uint8_t* Wq = (const uint8_t*)a.w;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        bq[i] = wok8[i] ? *reinterpret_cast<const u32x2*>(Wq + wrow8[i] + k0 + chunk * 8) : u32x2{0, 0};
+      for (int i = 0; i < 8; ++i) bq[i] = __builtin_amdgcn_raw_buffer_load_b64(rsrcB, boff[i], k0, 0);
       sc_lo = (float)a.wscale[srow_lo + k0 / 128];
       sc_hi = (float)a.wscale[srow_hi + k0 / 128];
     }
@@ -277,10 +306,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int l32 = lane & 31, khalf = lane >> 5;
 
   f32x16 acc[4][4];
-#pragma unroll
-  for (int ns = 0; ns < 4; ++ns)
-#pragma unroll
-    for (int ms = 0; ms < 4; ++ms) acc[ns][ms] = f32x16{};
 
   // Fragments of one 16-wide K step: 4 weight sub-tiles and 4 activation sub-tiles.
   auto load_frags = [&](const char* sA, const char* sB, int kk, bf16x8* wf, bf16x8* xf) {
@@ -290,12 +315,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms) xf[ms] = *reinterpret_cast<const bf16x8*>(sA + swz(wm * 128 + ms * 32 + l32, ch));
   };
-  auto mfma16 = [&](const bf16x8* wf, const bf16x8* xf) {
+  // first: the tile's first K step, which starts every accumulator from zero
+  auto mfma16 = [&](const bf16x8* wf, const bf16x8* xf, bool first) {
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
       for (int ms = 0; ms < 4; ++ms)
-        acc[ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ns], xf[ms], acc[ns][ms], 0, 0, 0);
+        acc[ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ns], xf[ms], first ? f32x16{} : acc[ns][ms], 0, 0, 0);
   };
   // Software pipeline over fragments.  Four register sets hold the fragments of
   // the four 16-wide steps of a 64-deep stage.  Every block of 16 MFMAs runs with
@@ -306,9 +332,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // The reads of stage s+1 can start before its half-way barrier because that
   // barrier of stage s already waited for stage s+1's DMA.
   bf16x8 fw[4][4], fx[4][4];
-  auto step = [&](int mset, const char* sA, const char* sB, int kk, int lset) {
+  auto step = [&](int mset, const char* sA, const char* sB, int kk, int lset, bool first = false) {
     load_frags(sA, sB, kk, fw[lset], fx[lset]);
-    mfma16(fw[mset], fx[mset]);
+    mfma16(fw[mset], fx[mset], first);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -323,7 +349,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                       int part) {
     load_frags(sA, sB, kk, fw[lset], fx[lset]);
     issue_part(dA, dB, k0, part);
-    mfma16(fw[mset], fx[mset]);
+    mfma16(fw[mset], fx[mset], false);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -334,99 +360,127 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Stage s of the K loop lives in buffer s & 1.  The DMA of stage s+2 is issued
-  // right after the barrier that ends the reads of stage s, spread over the next
-  // 32 MFMAs.  K is a multiple of 128, so the stage count is even.  The loop is
+  // ---- epilogue of tile t.  Lane holds row (lane & 31) of each 32-row sub-tile and,
+  // per register group g, the 4 consecutive columns 8 g + 4 (lane >> 5) + [0, 4).
+  auto epilogue = [&](const Tile& t) {
+    const int n0 = MODE == 0 ? t.nt * (BN / 2) : t.nt * BN;
+    const int p0 = t.p0, p1 = t.p1;
+    if (MODE == 0) {
+      __bf16* act = (__bf16*)a.out;
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) {
+        const int p = p0 + wm * 128 + ms * 32 + l32;
+        bool ok = p < p1;
+        if (ok && a.sorted != nullptr) ok = (unsigned)a.sorted[p] < (unsigned)a.sentinel;
+        if (!ok) continue;
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = n0 + wn * 64 + ns * 32 + g * 8 + khalf * 4;
+            bf16x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float gt = acc[ns][ms][g * 4 + q], up = acc[ns + 2][ms][g * 4 + q];
+              o[q] = (__bf16)(silu_fast(gt) * up);
+            }
+            *reinterpret_cast<bf16x4*>(act + (long)p * a.I + col) = o;
+          }
+        }
+      }
+    } else {
+      __bf16* y = (__bf16*)a.out;
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) {
+        const int p = p0 + wm * 128 + ms * 32 + l32;
+        if (p >= p1) continue;
+        int dest = p;
+        if (a.sorted != nullptr) {
+          dest = a.sorted[p];
+          if ((unsigned)dest >= (unsigned)a.sentinel) continue;
+        }
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) {
+          const int cbase = n0 + wn * 128 + ns * 32;
+          if (cbase >= a.H) continue;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = cbase + g * 8 + khalf * 4;
+            bf16x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = (__bf16)acc[ns][ms][g * 4 + q];
+            *reinterpret_cast<bf16x4*>(y + (long)dest * a.H + col) = o;
+          }
+        }
+      }
+    }
+  };
+
+  // Stage s of a tile's K loop lives in buffer s & 1.  The DMA of stage s+2 is
+  // issued right after the barrier that ends the reads of stage s, spread over the
+  // next 32 MFMAs.  K is a multiple of 128, so the stage count is even.  The loop is
   // rotated so that its head is a barrier (which waits for all LDS reads anyway),
   // its body is one basic block (so the scheduling barriers hold), and the last two
-  // stages are peeled off: no copy is ever issued past the end of K.
+  // stages are peeled off: no copy is issued past the end of K.  The next tile's
+  // first two stages are copied during this tile's tail and epilogue.
   const int KT = K / BK;
+  setup(cur);
   issue_loads(sA0, sB0, 0);
   store_fp8(sB0);
   issue_loads(sA1, sB1, BK);
-  dma_barrier();
-  load_frags(sA0, sB0, 0, fw[0], fx[0]);
-  load_frags(sA0, sB0, 1, fw[1], fx[1]);
-  __builtin_amdgcn_sched_barrier(0);
-  step(0, sA0, sB0, 2, 2);
-  step(1, sA0, sB0, 3, 3);
-  for (int kt = 0; kt < KT - 2; kt += 2) {
-    store_fp8(sB1);  // fp8: stage kt+1 into buffer 1 (codes fetched a stage earlier)
+  while (true) {
     dma_barrier();
+    load_frags(sA0, sB0, 0, fw[0], fx[0]);
+    load_frags(sA0, sB0, 1, fw[1], fx[1]);
     __builtin_amdgcn_sched_barrier(0);
-    step_dma(2, sA1, sB1, 0, 0, sA0, sB0, (kt + 2) * BK, 0);
-    step_dma(3, sA1, sB1, 1, 1, sA0, sB0, (kt + 2) * BK, 1);
+    step(0, sA0, sB0, 2, 2, true);
+    step(1, sA0, sB0, 3, 3);
+    for (int kt = 0; kt < KT - 2; kt += 2) {
+      store_fp8(sB1);  // fp8: stage kt+1 into buffer 1 (codes fetched a stage earlier)
+      dma_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      step_dma(2, sA1, sB1, 0, 0, sA0, sB0, (kt + 2) * BK, 0);
+      step_dma(3, sA1, sB1, 1, 1, sA0, sB0, (kt + 2) * BK, 1);
+      step(0, sA1, sB1, 2, 2);
+      step(1, sA1, sB1, 3, 3);
+      store_fp8(sB0);
+      dma_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      step_dma(2, sA0, sB0, 0, 0, sA1, sB1, (kt + 3) * BK, 0);
+      step_dma(3, sA0, sB0, 1, 1, sA1, sB1, (kt + 3) * BK, 1);
+      step(0, sA0, sB0, 2, 2);
+      step(1, sA0, sB0, 3, 3);
+    }
+    // stages KT-2 (fragments 2, 3 in registers) and KT-1 (buffer 1)
+    store_fp8(sB1);
+    dma_barrier();
+    // buffer 0 is free: the next tile's stage 0 goes there now
+    const int nlid = lid + slots;
+    const bool more = nlid < lid_end;
+    Tile nxt = cur;
+    if (more) {
+      decode(nlid, nxt);
+      setup(nxt);
+      issue_loads(sA0, sB0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    step(2, sA1, sB1, 0, 0);
+    step(3, sA1, sB1, 1, 1);
     step(0, sA1, sB1, 2, 2);
     step(1, sA1, sB1, 3, 3);
-    store_fp8(sB0);
-    dma_barrier();
+    // every wave has read buffer 1: the next tile's stage 1 goes there
+    if (more) {
+      lds_barrier();
+      store_fp8(sB0);
+      issue_loads(sA1, sB1, BK);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    step_dma(2, sA0, sB0, 0, 0, sA1, sB1, (kt + 3) * BK, 0);
-    step_dma(3, sA0, sB0, 1, 1, sA1, sB1, (kt + 3) * BK, 1);
-    step(0, sA0, sB0, 2, 2);
-    step(1, sA0, sB0, 3, 3);
-  }
-  // stages KT-2 (fragments 2, 3 in registers) and KT-1 (buffer 1)
-  store_fp8(sB1);
-  dma_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  step(2, sA1, sB1, 0, 0);
-  step(3, sA1, sB1, 1, 1);
-  step(0, sA1, sB1, 2, 2);
-  step(1, sA1, sB1, 3, 3);
-  mfma16(fw[2], fx[2]);
-  mfma16(fw[3], fx[3]);
-
-  // ---- epilogue.  Lane holds row (lane & 31) of each 32-row sub-tile and, per
-  // register group g, the 4 consecutive columns 8 g + 4 (lane >> 5) + [0, 4).
-  if (MODE == 0) {
-    __bf16* act = (__bf16*)a.out;
-#pragma unroll
-    for (int ms = 0; ms < 4; ++ms) {
-      const int p = p0 + wm * 128 + ms * 32 + l32;
-      bool ok = p < p1;
-      if (ok && a.sorted != nullptr) ok = (unsigned)a.sorted[p] < (unsigned)a.sentinel;
-      if (!ok) continue;
-#pragma unroll
-      for (int ns = 0; ns < 2; ++ns) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = n0 + wn * 64 + ns * 32 + g * 8 + khalf * 4;
-          bf16x4 o;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float gt = acc[ns][ms][g * 4 + q], up = acc[ns + 2][ms][g * 4 + q];
-            o[q] = (__bf16)(silu_fast(gt) * up);
-          }
-          *reinterpret_cast<bf16x4*>(act + (long)p * a.I + col) = o;
-        }
-      }
-    }
-  } else {
-    __bf16* y = (__bf16*)a.out;
-#pragma unroll
-    for (int ms = 0; ms < 4; ++ms) {
-      const int p = p0 + wm * 128 + ms * 32 + l32;
-      if (p >= p1) continue;
-      int dest = p;
-      if (a.sorted != nullptr) {
-        dest = a.sorted[p];
-        if ((unsigned)dest >= (unsigned)a.sentinel) continue;
-      }
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns) {
-        const int cbase = n0 + wn * 128 + ns * 32;
-        if (cbase >= a.H) continue;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = cbase + g * 8 + khalf * 4;
-          bf16x4 o;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) o[q] = (__bf16)acc[ns][ms][g * 4 + q];
-          *reinterpret_cast<bf16x4*>(y + (long)dest * a.H + col) = o;
-        }
-      }
-    }
+    mfma16(fw[2], fx[2], false);
+    mfma16(fw[3], fx[3], false);
+    epilogue(cur);
+    if (!more) break;
+    cur = nxt;
+    lid = nlid;
   }
 }
 
@@ -491,10 +545,16 @@ int mtile_bound(const moe_config& c, bool identity) {
   return (int)((p_max + (long)c.N * (BM - 1)) / BM);
 }
 
+// Persistent launch: one workgroup per CU (the kernel's LDS allows no more), at most
+// as many as there can be tiles, a multiple of the 8 XCDs.
 template <int MODE, bool FP8>
 hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
+  int dev = 0, cus = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
   const int G = a.mtiles * a.ntiles;
-  const int grid = ceil_div(G, 8) * 8;
+  const int grid = ceil_div(min(G, max(cus, 8)), 8) * 8;
   ffn_gemm_bf16<MODE, FP8><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
