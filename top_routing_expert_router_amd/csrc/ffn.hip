@@ -34,7 +34,7 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 64;  // BN: the W13 tile (128 gate + 128 up rows)
 constexpr int kThreads = 256;
 constexpr int kGroupN = 2;                        // n-tiles per raster group
 // buffer resource word 3 for raw (untyped, stride 0) buffer loads on gfx9-family parts
@@ -128,15 +128,22 @@ __device__ __forceinline__ void lds_barrier() {
   __syncthreads();
 }
 
-// MODE 0: W13 + SwiGLU -> act.  MODE 1: W2 -> y rows.
-template <int MODE, bool FP8>
+// MODE 0: W13 + SwiGLU -> act.  MODE 1: W2 -> y rows.  WNS: 32-wide weight sub-tiles
+// per wave; the workgroup's weight tile has TBN = 64 WNS rows (4: 256 rows, for W13
+// 128 gate and 128 up).  An output element's K order does not depend on WNS.  (W2
+// with WNS = 2 -- twice the tiles -- measured slower than the last-round idle time it
+// saves on the Mixtral shape, so only 4 is instantiated.)
+template <int MODE, bool FP8, int WNS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffn_gemm_bf16(FfnArgs a) {
+  static_assert(MODE == 1 || WNS == 4, "W13 tiles pair 64 gate and 64 up columns per wave");
+  constexpr int TBN = 64 * WNS;     // weight rows per tile
+  constexpr int BJ = TBN / 32;      // weight-row DMA instructions (8 rows each) per wave and stage
   // Two stages, each its own array so the compiler can see that the tile being
   // filled by DMA never aliases the tile being read.
   __shared__ __attribute__((aligned(16))) char sA0[BM * BK * 2];
-  __shared__ __attribute__((aligned(16))) char sB0[BN * BK * 2];
+  __shared__ __attribute__((aligned(16))) char sB0[TBN * BK * 2];
   __shared__ __attribute__((aligned(16))) char sA1[BM * BK * 2];
-  __shared__ __attribute__((aligned(16))) char sB1[BN * BK * 2];
+  __shared__ __attribute__((aligned(16))) char sB1[TBN * BK * 2];
   __shared__ int t_beg[kMaxExperts + 1], t_mt0[kMaxExperts + 1];
 
   // ---- persistent work.  Tiles in logical order: groups of kGroupN n-tiles, all
@@ -183,6 +190,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // puts there (the swizzle is an involution in the chunk index).
   const int drow = lane >> 3;                    // row within the 8-row group
   auto dchunk = [&](int j) { return swz_chunk(wave * 64 + j * 8 + drow, lane & 7); };
+  // weight tile: wave w fills rows [w TBN/4, (w+1) TBN/4), BJ instructions of 8 rows
+  auto brow_of = [&](int j) { return wave * (TBN / 4) + j * 8 + drow; };
   // The copies are buffer loads with LDS destination: a buffer resource per operand
   // (base address + byte size, out-of-range reads return zeros) and a 32-bit byte
   // offset per lane.  A: the activation rows -- all of h (MODE 0, gathered rows) or
@@ -194,7 +203,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   uint32_t boff[8];                              // byte offset of the lane's 8 weight rows
   // weight rows of the lane's 8 DMA rows (bf16 path) / staging rows (fp8 path)
   auto weight_row = [&](int n0, int j) {  // j = tile row
-    const int r = MODE == 0 ? (j < BN / 2 ? n0 + j : a.I + n0 + (j - BN / 2)) : n0 + j;
+    const int r = MODE == 0 ? (j < TBN / 2 ? n0 + j : a.I + n0 + (j - TBN / 2)) : n0 + j;
     return (MODE == 1 && r >= a.H) ? -1 : r;
   };
   // ---- fp8 weights: register staging with decode + scale (rows rb + 32 i); boff[i]
@@ -225,20 +234,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
       aoff[j] = (row * (unsigned)K + dchunk(j) * 8) * 2u;
     }
-    const int n0 = MODE == 0 ? t.nt * (BN / 2) : t.nt * BN;
+    const int n0 = MODE == 0 ? t.nt * (TBN / 2) : t.nt * TBN;
     if constexpr (!FP8) {
       const __bf16* Wb = (const __bf16*)a.w + (long)t.e * WR * K;
       rsrcB = __builtin_amdgcn_make_buffer_rsrc((void*)Wb, (short)0, (int)((unsigned)WR * K * 2u), kBufferFlags);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = weight_row(n0, wave * 64 + j * 8 + drow);
-        boff[j] = ((unsigned)(r < 0 ? 0 : r) * (unsigned)K + dchunk(j) * 8) * 2u;
+      for (int j = 0; j < BJ; ++j) {
+        const int r = weight_row(n0, brow_of(j));
+        boff[j] = ((unsigned)(r < 0 ? 0 : r) * (unsigned)K + swz_chunk(brow_of(j), lane & 7) * 8) * 2u;
       }
     } else {
       const uint8_t* Wq = (const uint8_t*)a.w + (long)t.e * WR * K;
       rsrcB = __builtin_amdgcn_make_buffer_rsrc((void*)Wq, (short)0, (int)((unsigned)WR * K), kBufferFlags);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < BJ; ++i) {
         const int r = weight_row(n0, rb + 32 * i);
         boff[i] = r < 0 ? 0x80000000u : (unsigned)r * (unsigned)K + chunk * 8;
       }
@@ -260,11 +269,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcA, LDS_PTR(sA + (wave * 8 + j) * 1024), 16, aoff[j], k0 * 2, 0, 0);
     } else if constexpr (!FP8) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcB, LDS_PTR(sB + (wave * 8 + j) * 1024), 16, boff[j], k0 * 2, 0, 0);
+      for (int j = 0; j < BJ; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcB, LDS_PTR(sB + (wave * BJ + j) * 1024), 16, boff[j], k0 * 2, 0, 0);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) bq[i] = __builtin_amdgcn_raw_buffer_load_b64(rsrcB, boff[i], k0, 0);
+      for (int i = 0; i < BJ; ++i) bq[i] = __builtin_amdgcn_raw_buffer_load_b64(rsrcB, boff[i], k0, 0);
       sc_lo = (float)a.wscale[srow_lo + k0 / 128];
       sc_hi = (float)a.wscale[srow_hi + k0 / 128];
     }
@@ -277,7 +286,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   auto store_fp8 = [&](char* sB) {
     if constexpr (FP8) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < BJ; ++i) {
         const u32x2 q = bq[i];
         const float s = i < 4 ? sc_lo : sc_hi;
         const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[0], false);
@@ -295,30 +304,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   // ---- wave sub-tile: rows [wm*128, +128); weight rows per MODE
   const int wm = wave & 1, wn = wave >> 1;
-  int brw[4];
+  int brw[WNS];
 #pragma unroll
-  for (int ns = 0; ns < 4; ++ns) {
+  for (int ns = 0; ns < WNS; ++ns) {
     if (MODE == 0)
-      brw[ns] = ns < 2 ? wn * 64 + ns * 32 : BN / 2 + wn * 64 + (ns - 2) * 32;
+      brw[ns] = ns < 2 ? wn * 64 + ns * 32 : TBN / 2 + wn * 64 + (ns - 2) * 32;
     else
-      brw[ns] = wn * 128 + ns * 32;
+      brw[ns] = wn * (WNS * 32) + ns * 32;
   }
   const int l32 = lane & 31, khalf = lane >> 5;
 
-  f32x16 acc[4][4];
+  f32x16 acc[WNS][4];
 
   // Fragments of one 16-wide K step: 4 weight sub-tiles and 4 activation sub-tiles.
   auto load_frags = [&](const char* sA, const char* sB, int kk, bf16x8* wf, bf16x8* xf) {
     const int ch = kk * 2 + khalf;
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) wf[ns] = *reinterpret_cast<const bf16x8*>(sB + swz(brw[ns] + l32, ch));
+    for (int ns = 0; ns < WNS; ++ns) wf[ns] = *reinterpret_cast<const bf16x8*>(sB + swz(brw[ns] + l32, ch));
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms) xf[ms] = *reinterpret_cast<const bf16x8*>(sA + swz(wm * 128 + ms * 32 + l32, ch));
   };
   // first: the tile's first K step, which starts every accumulator from zero
   auto mfma16 = [&](const bf16x8* wf, const bf16x8* xf, bool first) {
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns)
+    for (int ns = 0; ns < WNS; ++ns)
 #pragma unroll
       for (int ms = 0; ms < 4; ++ms)
         acc[ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ns], xf[ms], first ? f32x16{} : acc[ns][ms], 0, 0, 0);
@@ -331,15 +340,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   //   [MFMA s.2 | read (s+1).0] [MFMA s.3 | read (s+1).1]
   // The reads of stage s+1 can start before its half-way barrier because that
   // barrier of stage s already waited for stage s+1's DMA.
-  bf16x8 fw[4][4], fx[4][4];
+  bf16x8 fw[4][WNS], fx[4][4];
+  // a step issues MF MFMAs and RD fragment reads; reads (and the copies of step_dma)
+  // are spread evenly between the MFMAs
+  constexpr int MF = 4 * WNS, RD = WNS + 4;
   auto step = [&](int mset, const char* sA, const char* sB, int kk, int lset, bool first = false) {
     load_frags(sA, sB, kk, fw[lset], fx[lset]);
     mfma16(fw[mset], fx[mset], first);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    for (int i = 0; i < MF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           // MFMA
+      if ((i * RD) / MF != ((i + 1) * RD) / MF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -350,12 +361,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     load_frags(sA, sB, kk, fw[lset], fx[lset]);
     issue_part(dA, dB, k0, part);
     mfma16(fw[mset], fx[mset], false);
+    const int VM = part == 0 ? 8 : BJ;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // global load
+    for (int i = 0; i < MF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           // MFMA
+      if ((i * RD) / MF != ((i + 1) * RD) / MF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      if ((i * VM) / MF != ((i + 1) * VM) / MF) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // global load
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -363,7 +374,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // ---- epilogue of tile t.  Lane holds row (lane & 31) of each 32-row sub-tile and,
   // per register group g, the 4 consecutive columns 8 g + 4 (lane >> 5) + [0, 4).
   auto epilogue = [&](const Tile& t) {
-    const int n0 = MODE == 0 ? t.nt * (BN / 2) : t.nt * BN;
+    const int n0 = MODE == 0 ? t.nt * (TBN / 2) : t.nt * TBN;
     const int p0 = t.p0, p1 = t.p1;
     if (MODE == 0) {
       __bf16* act = (__bf16*)a.out;
@@ -400,8 +411,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
           if ((unsigned)dest >= (unsigned)a.sentinel) continue;
         }
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) {
-          const int cbase = n0 + wn * 128 + ns * 32;
+        for (int ns = 0; ns < WNS; ++ns) {
+          const int cbase = n0 + wn * (WNS * 32) + ns * 32;
           if (cbase >= a.H) continue;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
@@ -547,7 +558,7 @@ int mtile_bound(const moe_config& c, bool identity) {
 
 // Persistent launch: one workgroup per CU (the kernel's LDS allows no more), at most
 // as many as there can be tiles, a multiple of the 8 XCDs.
-template <int MODE, bool FP8>
+template <int MODE, bool FP8, int WNS>
 hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
   int dev = 0, cus = 0;
   hipError_t err = hipGetDevice(&dev);
@@ -555,7 +566,7 @@ hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
   if (err != hipSuccess) return err;
   const int G = a.mtiles * a.ntiles;
   const int grid = ceil_div(min(G, max(cus, 8)), 8) * 8;
-  ffn_gemm_bf16<MODE, FP8><<<grid, kThreads, 0, s>>>(a);
+  ffn_gemm_bf16<MODE, FP8, WNS><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -593,7 +604,7 @@ hipError_t launch_gate_up(const moe_config& c, const void* h, const int32_t* sor
     return hipGetLastError();
   }
   a.ntiles = c.I / (BN / 2);
-  return c.expert_dtype == MOE_FP8_E4M3 ? launch_gemm<0, true>(a, s) : launch_gemm<0, false>(a, s);
+  return c.expert_dtype == MOE_FP8_E4M3 ? launch_gemm<0, true, 4>(a, s) : launch_gemm<0, false, 4>(a, s);
 }
 
 hipError_t launch_down(const moe_config& c, const void* act, const int32_t* sorted_ids, const int32_t* offsets,
@@ -608,8 +619,8 @@ hipError_t launch_down(const moe_config& c, const void* act, const int32_t* sort
     ffn_w2_f32<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(a, a.rows);
     return hipGetLastError();
   }
-  a.ntiles = ceil_div(c.H, BN);
-  return c.expert_dtype == MOE_FP8_E4M3 ? launch_gemm<1, true>(a, s) : launch_gemm<1, false>(a, s);
+  a.ntiles = ceil_div(c.H, 256);
+  return c.expert_dtype == MOE_FP8_E4M3 ? launch_gemm<1, true, 4>(a, s) : launch_gemm<1, false, 4>(a, s);
 }
 
 hipError_t launch_expert_ffn(const moe_config& c, const void* h, const int32_t* sorted_ids, const int32_t* offsets,
