@@ -33,9 +33,15 @@ FLAGS = [
 ]
 
 
+# per-source flags.  ffn.hip: the tile claims of the expert GEMMs are single-lane
+# atomics whose result is needed only a whole tile later; the atomic optimizer would
+# turn each into a wave-aggregated form that waits for the result at once.
+SOURCE_FLAGS = {"ffn.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l)

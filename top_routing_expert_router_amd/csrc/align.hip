@@ -50,7 +50,9 @@ __global__ __launch_bounds__(kThreads) void align_scan(int32_t* __restrict__ cou
                                                        int cap, int n_blocks,
                                                        int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ num_padded,
-                                                       int32_t* __restrict__ stats, int sentinel) {
+                                                       int32_t* __restrict__ stats, int sentinel,
+                                                       int32_t* __restrict__ zero, int nzero) {
+  if ((int)threadIdx.x < nzero) zero[threadIdx.x] = 0;
   __shared__ int wave_tot[4];
   __shared__ int red[4][4];
   const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
@@ -197,7 +199,7 @@ size_t align_workspace_bytes(const moe_config& c) {
 
 hipError_t launch_align(const moe_config& c, const int32_t* ids, uint8_t* kept, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* offsets, int32_t* num_padded, int32_t* stats, void* ws,
-                        hipStream_t s) {
+                        hipStream_t s, int32_t* zero, int nzero) {
   const int R = c.T * c.k;
   const int nchunks = ceil_div(R, kChunk);
   const int p_max = R + c.N * (c.B - 1);
@@ -212,7 +214,7 @@ hipError_t launch_align(const moe_config& c, const int32_t* ids, uint8_t* kept, 
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   align_scan<<<1, kThreads, 0, s>>>(counts, nchunks, c.N, c.B, cap, n_blocks, sorted_ids, block_expert, offsets,
-                                    num_padded, stats, R);
+                                    num_padded, stats, R, zero, zero ? nzero : 0);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   align_scatter<<<nchunks, kThreads, 0, s>>>(ids, R, c.N, cap, counts, offsets, num_padded, p_max, kept, sorted_ids, R);

@@ -46,7 +46,8 @@ size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Regions of the moe_forward workspace, in order, each 256-byte aligned.
 struct FwdLayout {
-  size_t logits, ids, gates, margin, kept, sorted, blocks, offsets, npad, stats, align_ws, act, y, sact, sout, total;
+  size_t logits, ids, gates, margin, kept, sorted, blocks, offsets, npad, stats, align_ws, work, act, y, sact, sout,
+      total;
 };
 
 FwdLayout forward_layout(const moe_config& c) {
@@ -69,6 +70,7 @@ FwdLayout forward_layout(const moe_config& c) {
   L.npad = take(4);
   L.stats = take((N + MOE_STATS_EXTRA) * 4);
   L.align_ws = take(align_workspace_bytes(c));
+  L.work = take(4 * kGemmWorkWords * 4);  // tile counters of the 4 expert GEMM launches
   L.act = take(P * (size_t)c.I * a);
   L.y = take(R * (size_t)c.H * a);
   L.sact = c.n_shared ? take(T * (size_t)c.I * a) : o;
@@ -276,6 +278,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   int32_t* stats = (int32_t*)pick(tr.stats, L.stats);
   void* act = pick(tr.act, L.act);
   void* y = pick(tr.y_route, L.y);
+  int32_t* work = (int32_t*)(base + L.work);  // zeroed by the alignment scan, used by the GEMMs
   if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4) || !aligned(margin, 4) || !aligned(sorted, 4) ||
       !aligned(blocks, 4) || !aligned(offsets, 4) || !aligned(npad, 4) || !aligned(stats, 4) || !aligned(act, 16) ||
       !aligned(y, 16))
@@ -284,13 +287,15 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_router(c, h, wt->w_gate, wt->logit_bias, logits, ids, gates, margin, s);
   if (e == hipSuccess)
-    e = launch_align(c, ids, kept, sorted, blocks, offsets, npad, stats, base + L.align_ws, s);
+    e = launch_align(c, ids, kept, sorted, blocks, offsets, npad, stats, base + L.align_ws, s, work,
+                     4 * kGemmWorkWords);
   if (e == hipSuccess)
-    e = launch_expert_ffn(c, h, sorted, offsets, wt->w13, wt->w2, wt->w13_scale, wt->w2_scale, act, y, false, s);
+    e = launch_expert_ffn(c, h, sorted, offsets, wt->w13, wt->w2, wt->w13_scale, wt->w2_scale, act, y, false, s,
+                          work);
   const void* shared_out = nullptr;
   if (e == hipSuccess && c.n_shared) {
     e = launch_expert_ffn(c, h, nullptr, nullptr, wt->shared_w13, wt->shared_w2, wt->shared_w13_scale,
-                          wt->shared_w2_scale, base + L.sact, base + L.sout, true, s);
+                          wt->shared_w2_scale, base + L.sact, base + L.sout, true, s, work + 2 * kGemmWorkWords);
     shared_out = base + L.sout;
   }
   if (e == hipSuccess) e = launch_combine(c, y, gates, kept, shared_out, residual, out, s);

@@ -28,6 +28,8 @@
 //   run of (n-tile group, m-tile) pairs and shares weight tiles in its L2.
 // fp8 weights: E4M3FN codes are decoded with the hardware converter, multiplied
 // by their 128x128 block's bf16 scale in fp32, and rounded to bf16 on the way into LDS.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -55,6 +57,7 @@ struct FfnArgs {
   int rows;               // rows of the act buffer (P_max routed, T identity): no row index reaches it
   int mtiles;             // M-tile bound used for the grid
   int ntiles;
+  int32_t* work;          // nullable: 8 zeroed per-XCD tile counters (dynamic schedule)
 };
 
 // LDS tile layout: row-major 128-byte rows of 8 16-byte chunks, chunk index XORed
@@ -128,15 +131,19 @@ __device__ __forceinline__ void lds_barrier() {
   __syncthreads();
 }
 
-// MODE 0: W13 + SwiGLU -> act.  MODE 1: W2 -> y rows.  WNS: 32-wide weight sub-tiles
-// per wave; the workgroup's weight tile has TBN = 64 WNS rows (4: 256 rows, for W13
-// 128 gate and 128 up).  An output element's K order does not depend on WNS.  (W2
-// with WNS = 2 -- twice the tiles -- measured slower than the last-round idle time it
-// saves on the Mixtral shape, so only 4 is instantiated.)
-template <int MODE, bool FP8, int WNS>
+// MODE 0: W13 + SwiGLU -> act.  MODE 1: W2 -> y rows.
+//
+// Two tile modes over the same 256-row weight tile (W13: 128 gate and the matching
+// 128 up rows):
+//  - full (up to 256 activation rows): waves 2 x 2, each 128 rows x 128 weight rows;
+//  - half (an m-tile with at most 128 valid rows, as the last tile of an expert often
+//    is): all 4 waves on the same 128 rows, each with 64 weight rows -- half the MFMAs
+//    of a full tile instead of the same number on empty rows.
+// An output element's K order is the same in both modes (one MFMA chain over K in
+// ascending 16-wide steps), so the mode changes no output bit.
+template <int MODE, bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffn_gemm_bf16(FfnArgs a) {
-  static_assert(MODE == 1 || WNS == 4, "W13 tiles pair 64 gate and 64 up columns per wave");
-  constexpr int TBN = 64 * WNS;     // weight rows per tile
+  constexpr int TBN = BN;           // weight rows per tile
   constexpr int BJ = TBN / 32;      // weight-row DMA instructions (8 rows each) per wave and stage
   // Two stages, each its own array so the compiler can see that the tile being
   // filled by DMA never aliases the tile being read.
@@ -149,8 +156,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // ---- persistent work.  Tiles in logical order: groups of kGroupN n-tiles, all
   // m-tiles of a group before the next group.  Hardware deals workgroups to the 8
   // XCDs round-robin; XCD x owns the contiguous run [x, x+1) * ceil(G / 8) of that
-  // order, and its workgroup in slot s takes tiles s, s + slots, ... of the run, so
-  // the ~32 workgroups of an XCD work on neighbouring tiles at any time.
+  // order, so the ~32 workgroups of an XCD work on neighbouring tiles at any time.
+  // Static schedule: the workgroup in slot s takes tiles s, s + slots, ... of the run.
+  // Dynamic schedule (a.work): workgroups claim the run's tiles in order from the
+  // XCD's counter -- a workgroup claims its next tile when it starts the current
+  // one, so tiles of unequal cost (full and half) balance across the XCD.
   build_tile_table(a, t_beg, t_mt0);
   // values read from the table are the same in every lane; readfirstlane makes them
   // scalar, so the buffer resources built from them stay in SGPRs
@@ -158,8 +168,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int G = total_m * a.ntiles;
   const int per_xcd = ceil_div(G, 8);
   const int slots = gridDim.x >> 3;
-  const int lid_end = min(G, ((int)(blockIdx.x & 7) + 1) * per_xcd);
-  int lid = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int xcd = blockIdx.x & 7;
+  const int run0 = xcd * per_xcd;
+  const int lid_end = min(G, run0 + per_xcd);
+  const bool dyn = a.work != nullptr;
+  __shared__ int sh_claim;
+  int lid = run0 + (blockIdx.x >> 3);
+  if (dyn) {
+    if (threadIdx.x == 0) sh_claim = atomicAdd(a.work + xcd, 1);
+    __syncthreads();
+    lid = run0 + __builtin_amdgcn_readfirstlane(sh_claim);
+  }
   if (lid >= lid_end) return;
   auto decode = [&](int l, Tile& t) {
     const int group = l / (kGroupN * total_m);
@@ -177,6 +196,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     t.p0 = __builtin_amdgcn_readfirstlane(t_beg[lo] + (m - t_mt0[lo]) * BM);
     t.p1 = __builtin_amdgcn_readfirstlane(min(min(t_beg[lo + 1], t.p0 + BM), a.rows));
   };
+  auto is_half = [&](const Tile& t) { return t.p1 - t.p0 <= BM / 2; };
   Tile cur;
   decode(lid, cur);
 
@@ -184,24 +204,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int WR = MODE == 0 ? 2 * a.I : a.H;  // weight rows per expert
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // ---- global -> LDS copy plan.  Wave w fills rows [64 w, 64 w + 64) of each tile,
-  // 8 rows (1 KB) per DMA instruction; lane L lands in physical 16-byte chunk L % 8
-  // of tile row 64 w + 8 j + L / 8, so it fetches the logical chunk that the swizzle
-  // puts there (the swizzle is an involution in the chunk index).
+  // ---- global -> LDS copy plan.  8 rows (1 KB) per DMA instruction; lane L lands
+  // in physical 16-byte chunk L % 8 of its row, so it fetches the logical chunk that
+  // the swizzle puts there (the swizzle is an involution in the chunk index).
+  // Activation rows: wave w fills rows [64 w, 64 w + 64) of a full tile (8
+  // instructions), [32 w, 32 w + 32) of a half tile (4).  Weight rows: wave w fills
+  // rows [64 w, 64 w + 64) in both modes.
   const int drow = lane >> 3;                    // row within the 8-row group
-  auto dchunk = [&](int j) { return swz_chunk(wave * 64 + j * 8 + drow, lane & 7); };
-  // weight tile: wave w fills rows [w TBN/4, (w+1) TBN/4), BJ instructions of 8 rows
+  auto arow_of = [&](bool half, int j) { return wave * (half ? 32 : 64) + j * 8 + drow; };
   auto brow_of = [&](int j) { return wave * (TBN / 4) + j * 8 + drow; };
   // The copies are buffer loads with LDS destination: a buffer resource per operand
   // (base address + byte size, out-of-range reads return zeros) and a 32-bit byte
-  // offset per lane.  A: the activation rows -- all of h (MODE 0, gathered rows) or
-  // the tile's own act rows (MODE 1, contiguous from p0).  B: this expert's weights.
+  // offset per lane.
   const __bf16* X = (const __bf16*)a.x;
   __amdgpu_buffer_rsrc_t rsrcA = __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, 0, kBufferFlags);
   __amdgpu_buffer_rsrc_t rsrcB = rsrcA;
-  uint32_t aoff[8];                              // byte offset of each of the lane's 8 A rows
-  uint32_t boff[8];                              // byte offset of the lane's 8 weight rows
-  // weight rows of the lane's 8 DMA rows (bf16 path) / staging rows (fp8 path)
+  uint32_t aoff[8];                              // byte offset of each of the lane's A rows
+  uint32_t boff[8];                              // byte offset of each of the lane's weight rows
   auto weight_row = [&](int n0, int j) {  // j = tile row
     const int r = MODE == 0 ? (j < TBN / 2 ? n0 + j : a.I + n0 + (j - TBN / 2)) : n0 + j;
     return (MODE == 1 && r >= a.H) ? -1 : r;
@@ -214,13 +233,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // Buffers, offsets and weight rows of tile t.  A: all of h (MODE 0, gathered
   // rows) or the tile's own act rows (MODE 1, contiguous from p0).  B: expert e.
   auto setup = [&](const Tile& t) {
+    const bool half = is_half(t);
     rsrcA = MODE == 0
                 ? __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)((unsigned)a.T * K * 2u), kBufferFlags)
                 : __builtin_amdgcn_make_buffer_rsrc((void*)(X + (long)t.p0 * K), (short)0,
                                                     (int)((unsigned)(t.p1 - t.p0) * K * 2u), kBufferFlags);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int p = t.p0 + wave * 64 + j * 8 + drow;
+      const int ar = arow_of(half, j);
+      const int p = t.p0 + ar;
       // rows outside the tile or padding rows read a harmless valid row (token 0 or
       // tile row 0); their results are never stored (rows never interact in the product)
       unsigned row = 0;
@@ -232,7 +253,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
           if ((unsigned)r < (unsigned)a.sentinel) row = MODE == 0 ? r / a.k : p - t.p0;
         }
       }
-      aoff[j] = (row * (unsigned)K + dchunk(j) * 8) * 2u;
+      aoff[j] = (row * (unsigned)K + swz_chunk(ar, lane & 7) * 8) * 2u;
     }
     const int n0 = MODE == 0 ? t.nt * (TBN / 2) : t.nt * TBN;
     if constexpr (!FP8) {
@@ -257,16 +278,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       srow_hi = ((long)t.e * (WR / 128) + min(rhi, WR - 1) / 128) * kb;
     }
   };
-  u32x2 bq[8];
+  u32x2 bq[BJ];
   float sc_lo = 1.f, sc_hi = 1.f;
 
-  // part 0: the 8 activation-row DMAs; part 1: the 8 weight-row DMAs (bf16) or
-  // the 8 weight-code loads into registers (fp8).
-  auto issue_part = [&](char* sA, char* sB, int k0, int part) {
+  // part 0: the activation-row DMAs (AJ of them); part 1: the weight-row DMAs
+  // (bf16) or the weight-code loads into registers (fp8).
+  auto issue_part = [&](auto half_tag, char* sA, char* sB, int k0, int part) {
+    constexpr int AJ = decltype(half_tag)::value ? 4 : 8;
     if (part == 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcA, LDS_PTR(sA + (wave * 8 + j) * 1024), 16, aoff[j], k0 * 2, 0, 0);
+      for (int j = 0; j < AJ; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcA, LDS_PTR(sA + (wave * AJ + j) * 1024), 16, aoff[j], k0 * 2, 0, 0);
     } else if constexpr (!FP8) {
 #pragma unroll
       for (int j = 0; j < BJ; ++j)
@@ -278,9 +300,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       sc_hi = (float)a.wscale[srow_hi + k0 / 128];
     }
   };
-  auto issue_loads = [&](char* sA, char* sB, int k0) {
-    issue_part(sA, sB, k0, 0);
-    issue_part(sA, sB, k0, 1);
+  auto issue_loads = [&](auto half_tag, char* sA, char* sB, int k0) {
+    issue_part(half_tag, sA, sB, k0, 0);
+    issue_part(half_tag, sA, sB, k0, 1);
+  };
+  // the next tile's first copies, in its own mode (outside any scheduled region)
+  auto issue_loads_for = [&](const Tile& t, char* sA, char* sB, int k0) {
+    if (is_half(t))
+      issue_loads(std::true_type{}, sA, sB, k0);
+    else
+      issue_loads(std::false_type{}, sA, sB, k0);
   };
   // fp8 only: decode the staged codes, scale, round to bf16 and write the B tile
   auto store_fp8 = [&](char* sB) {
@@ -302,145 +331,98 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
   };
 
-  // ---- wave sub-tile: rows [wm*128, +128); weight rows per MODE
+  // ---- wave sub-tiles.  Full: rows [wm*128, +128), weight sub-tiles brf[0..3]
+  // (W13: gate 0, 1 and up 2, 3).  Half: rows [0, 128), weight sub-tiles brh[0..1]
+  // (W13: gate 0, up 1).
   const int wm = wave & 1, wn = wave >> 1;
-  int brw[WNS];
+  int brf[4], brh[2];
 #pragma unroll
-  for (int ns = 0; ns < WNS; ++ns) {
-    if (MODE == 0)
-      brw[ns] = ns < 2 ? wn * 64 + ns * 32 : TBN / 2 + wn * 64 + (ns - 2) * 32;
-    else
-      brw[ns] = wn * (WNS * 32) + ns * 32;
-  }
-  const int l32 = lane & 31, khalf = lane >> 5;
+  for (int ns = 0; ns < 4; ++ns)
+    brf[ns] = MODE == 0 ? (ns < 2 ? wn * 64 + ns * 32 : TBN / 2 + wn * 64 + (ns - 2) * 32) : wn * 128 + ns * 32;
+#pragma unroll
+  for (int ns = 0; ns < 2; ++ns) brh[ns] = MODE == 0 ? ns * (TBN / 2) + wave * 32 : wave * 64 + ns * 32;
+  const int khalf = lane >> 5;
 
-  f32x16 acc[WNS][4];
+  f32x16 acc[4][4];
+  bf16x8 fw[4][4], fx[4][4];
+  int next_lid = 0;
 
-  // Fragments of one 16-wide K step: 4 weight sub-tiles and 4 activation sub-tiles.
-  auto load_frags = [&](const char* sA, const char* sB, int kk, bf16x8* wf, bf16x8* xf) {
-    const int ch = kk * 2 + khalf;
-#pragma unroll
-    for (int ns = 0; ns < WNS; ++ns) wf[ns] = *reinterpret_cast<const bf16x8*>(sB + swz(brw[ns] + l32, ch));
-#pragma unroll
-    for (int ms = 0; ms < 4; ++ms) xf[ms] = *reinterpret_cast<const bf16x8*>(sA + swz(wm * 128 + ms * 32 + l32, ch));
-  };
-  // first: the tile's first K step, which starts every accumulator from zero
-  auto mfma16 = [&](const bf16x8* wf, const bf16x8* xf, bool first) {
-#pragma unroll
-    for (int ns = 0; ns < WNS; ++ns)
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
-        acc[ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ns], xf[ms], first ? f32x16{} : acc[ns][ms], 0, 0, 0);
-  };
-  // Software pipeline over fragments.  Four register sets hold the fragments of
-  // the four 16-wide steps of a 64-deep stage.  Every block of 16 MFMAs runs with
-  // the reads of a later step interleaved (one read per two MFMAs), so LDS latency
-  // hides behind the matrix core:
-  //   [MFMA s.0 | read s.2] [MFMA s.1 | read s.3] barrier, DMA(stage s+2)
-  //   [MFMA s.2 | read (s+1).0] [MFMA s.3 | read (s+1).1]
-  // The reads of stage s+1 can start before its half-way barrier because that
-  // barrier of stage s already waited for stage s+1's DMA.
-  bf16x8 fw[4][WNS], fx[4][4];
-  // a step issues MF MFMAs and RD fragment reads; reads (and the copies of step_dma)
-  // are spread evenly between the MFMAs
-  constexpr int MF = 4 * WNS, RD = WNS + 4;
-  auto step = [&](int mset, const char* sA, const char* sB, int kk, int lset, bool first = false) {
-    load_frags(sA, sB, kk, fw[lset], fx[lset]);
-    mfma16(fw[mset], fx[mset], first);
-#pragma unroll
-    for (int i = 0; i < MF; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           // MFMA
-      if ((i * RD) / MF != ((i + 1) * RD) / MF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // The same, with 8 global loads of a later stage spread through the 16 MFMAs
-  // (a burst of them would stall the wave at issue while the matrix core idles).
-  auto step_dma = [&](int mset, const char* sA, const char* sB, int kk, int lset, char* dA, char* dB, int k0,
-                      int part) {
-    load_frags(sA, sB, kk, fw[lset], fx[lset]);
-    issue_part(dA, dB, k0, part);
-    mfma16(fw[mset], fx[mset], false);
-    const int VM = part == 0 ? 8 : BJ;
-#pragma unroll
-    for (int i = 0; i < MF; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           // MFMA
-      if ((i * RD) / MF != ((i + 1) * RD) / MF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      if ((i * VM) / MF != ((i + 1) * VM) / MF) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // global load
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
+  // ---- one tile, in mode HALF, from its first stage's barrier to its epilogue.
+  // The next tile's first two stages are copied during this tile's tail and epilogue.
+  auto run_tile = [&](auto half_tag, const Tile& t, bool& more, Tile& nxt) {
+    constexpr bool HALF = decltype(half_tag)::value;
+    constexpr int NS = HALF ? 2 : 4;           // weight sub-tiles per wave
+    constexpr int AJ = HALF ? 4 : 8;           // activation DMAs per wave and stage
+    const int* br = HALF ? brh : brf;
+    const int arow0 = HALF ? 0 : wm * 128;
+    // fragment addresses are computed per tile from an opaque copy of the lane
+    // index: hoisted out of the tile loop, both modes' addresses would stay live
+    // together and spill
+    int l32 = lane & 31;
+    asm volatile("" : "+v"(l32));
 
-  // ---- epilogue of tile t.  Lane holds row (lane & 31) of each 32-row sub-tile and,
-  // per register group g, the 4 consecutive columns 8 g + 4 (lane >> 5) + [0, 4).
-  auto epilogue = [&](const Tile& t) {
-    const int n0 = MODE == 0 ? t.nt * (TBN / 2) : t.nt * TBN;
-    const int p0 = t.p0, p1 = t.p1;
-    if (MODE == 0) {
-      __bf16* act = (__bf16*)a.out;
+    // Fragments of one 16-wide K step: NS weight sub-tiles and 4 activation sub-tiles.
+    auto load_frags = [&](const char* sA, const char* sB, int kk, bf16x8* wf, bf16x8* xf) {
+      const int ch = kk * 2 + khalf;
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
-        const int p = p0 + wm * 128 + ms * 32 + l32;
-        bool ok = p < p1;
-        if (ok && a.sorted != nullptr) ok = (unsigned)a.sorted[p] < (unsigned)a.sentinel;
-        if (!ok) continue;
+      for (int ns = 0; ns < NS; ++ns) wf[ns] = *reinterpret_cast<const bf16x8*>(sB + swz(br[ns] + l32, ch));
 #pragma unroll
-        for (int ns = 0; ns < 2; ++ns) {
+      for (int ms = 0; ms < 4; ++ms) xf[ms] = *reinterpret_cast<const bf16x8*>(sA + swz(arow0 + ms * 32 + l32, ch));
+    };
+    // first: the tile's first K step, which starts every accumulator from zero
+    auto mfma_step = [&](const bf16x8* wf, const bf16x8* xf, bool first) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = n0 + wn * 64 + ns * 32 + g * 8 + khalf * 4;
-            bf16x4 o;
+      for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float gt = acc[ns][ms][g * 4 + q], up = acc[ns + 2][ms][g * 4 + q];
-              o[q] = (__bf16)(silu_fast(gt) * up);
-            }
-            *reinterpret_cast<bf16x4*>(act + (long)p * a.I + col) = o;
-          }
-        }
+        for (int ms = 0; ms < 4; ++ms)
+          acc[ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ns], xf[ms], first ? f32x16{} : acc[ns][ms], 0, 0, 0);
+    };
+    // Software pipeline over fragments.  Four register sets hold the fragments of
+    // the four 16-wide steps of a 64-deep stage.  Every block of MF MFMAs runs with
+    // the RD reads of a later step spread between them, so LDS latency hides behind
+    // the matrix core:
+    //   [MFMA s.0 | read s.2] [MFMA s.1 | read s.3] barrier, DMA(stage s+2)
+    //   [MFMA s.2 | read (s+1).0] [MFMA s.3 | read (s+1).1]
+    // The reads of stage s+1 can start before its half-way barrier because that
+    // barrier of stage s already waited for stage s+1's DMA.
+    constexpr int MF = 4 * NS, RD = NS + 4;
+    auto step = [&](int mset, const char* sA, const char* sB, int kk, int lset, bool first = false) {
+      load_frags(sA, sB, kk, fw[lset], fx[lset]);
+      mfma_step(fw[mset], fx[mset], first);
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           // MFMA
+        if ((i * RD) / MF != ((i + 1) * RD) / MF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       }
-    } else {
-      __bf16* y = (__bf16*)a.out;
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // The same, with the global loads of a later stage spread between the MFMAs
+    // (a burst of them would stall the wave at issue while the matrix core idles).
+    auto step_dma = [&](int mset, const char* sA, const char* sB, int kk, int lset, char* dA, char* dB, int k0,
+                        int part) {
+      load_frags(sA, sB, kk, fw[lset], fx[lset]);
+      issue_part(half_tag, dA, dB, k0, part);
+      mfma_step(fw[mset], fx[mset], false);
+      const int VM = part == 0 ? AJ : BJ;
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
-        const int p = p0 + wm * 128 + ms * 32 + l32;
-        if (p >= p1) continue;
-        int dest = p;
-        if (a.sorted != nullptr) {
-          dest = a.sorted[p];
-          if ((unsigned)dest >= (unsigned)a.sentinel) continue;
-        }
-#pragma unroll
-        for (int ns = 0; ns < WNS; ++ns) {
-          const int cbase = n0 + wn * (WNS * 32) + ns * 32;
-          if (cbase >= a.H) continue;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = cbase + g * 8 + khalf * 4;
-            bf16x4 o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = (__bf16)acc[ns][ms][g * 4 + q];
-            *reinterpret_cast<bf16x4*>(y + (long)dest * a.H + col) = o;
-          }
-        }
+      for (int i = 0; i < MF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           // MFMA
+        if ((i * RD) / MF != ((i + 1) * RD) / MF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        if ((i * VM) / MF != ((i + 1) * VM) / MF) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // global load
       }
-    }
-  };
+      __builtin_amdgcn_sched_barrier(0);
+    };
 
-  // Stage s of a tile's K loop lives in buffer s & 1.  The DMA of stage s+2 is
-  // issued right after the barrier that ends the reads of stage s, spread over the
-  // next 32 MFMAs.  K is a multiple of 128, so the stage count is even.  The loop is
-  // rotated so that its head is a barrier (which waits for all LDS reads anyway),
-  // its body is one basic block (so the scheduling barriers hold), and the last two
-  // stages are peeled off: no copy is issued past the end of K.  The next tile's
-  // first two stages are copied during this tile's tail and epilogue.
-  const int KT = K / BK;
-  setup(cur);
-  issue_loads(sA0, sB0, 0);
-  store_fp8(sB0);
-  issue_loads(sA1, sB1, BK);
-  while (true) {
+    // Stage s of the K loop lives in buffer s & 1.  The DMA of stage s+2 is issued
+    // right after the barrier that ends the reads of stage s, spread over the next
+    // two steps.  K is a multiple of 128, so the stage count is even.  The loop is
+    // rotated so that its head is a barrier (which waits for all LDS reads anyway),
+    // its body is one basic block (so the scheduling barriers hold), and the last
+    // two stages are peeled off: no copy is issued past the end of K.
+    const int KT = K / BK;
     dma_barrier();
+    int claim = 0;  // dynamic schedule: this workgroup's next tile, claimed now
+    if (dyn && threadIdx.x == 0) claim = atomicAdd(a.work + xcd, 1);
     load_frags(sA0, sB0, 0, fw[0], fx[0]);
     load_frags(sA0, sB0, 1, fw[1], fx[1]);
     __builtin_amdgcn_sched_barrier(0);
@@ -463,16 +445,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       step(1, sA0, sB0, 3, 3);
     }
     // stages KT-2 (fragments 2, 3 in registers) and KT-1 (buffer 1)
+    if (dyn && threadIdx.x == 0) sh_claim = claim;
     store_fp8(sB1);
     dma_barrier();
     // buffer 0 is free: the next tile's stage 0 goes there now
-    const int nlid = lid + slots;
-    const bool more = nlid < lid_end;
-    Tile nxt = cur;
+    const int nlid = dyn ? run0 + __builtin_amdgcn_readfirstlane(sh_claim) : lid + slots;
+    next_lid = nlid;
+    more = nlid < lid_end;
     if (more) {
       decode(nlid, nxt);
       setup(nxt);
-      issue_loads(sA0, sB0, 0);
+      issue_loads_for(nxt, sA0, sB0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     step(2, sA1, sB1, 0, 0);
@@ -483,15 +466,82 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (more) {
       lds_barrier();
       store_fp8(sB0);
-      issue_loads(sA1, sB1, BK);
+      issue_loads_for(nxt, sA1, sB1, BK);
     }
     __builtin_amdgcn_sched_barrier(0);
-    mfma16(fw[2], fx[2], false);
-    mfma16(fw[3], fx[3], false);
-    epilogue(cur);
+    mfma_step(fw[2], fx[2], false);
+    mfma_step(fw[3], fx[3], false);
+
+    // ---- epilogue.  Lane holds row (lane & 31) of each 32-row sub-tile and, per
+    // register group g, the 4 consecutive columns 8 g + 4 (lane >> 5) + [0, 4) of a
+    // weight sub-tile (W2: output columns; W13: act columns of a gate sub-tile, its
+    // up partner NS/2 sub-tiles later).
+    const int n0 = MODE == 0 ? t.nt * (TBN / 2) : t.nt * TBN;
+    if (MODE == 0) {
+      __bf16* act = (__bf16*)a.out;
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) {
+        const int p = t.p0 + arow0 + ms * 32 + l32;
+        bool ok = p < t.p1;
+        if (ok && a.sorted != nullptr) ok = (unsigned)a.sorted[p] < (unsigned)a.sentinel;
+        if (!ok) continue;
+#pragma unroll
+        for (int ns = 0; ns < NS / 2; ++ns) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = n0 + br[ns] + g * 8 + khalf * 4;
+            bf16x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float gt = acc[ns][ms][g * 4 + q], up = acc[ns + NS / 2][ms][g * 4 + q];
+              o[q] = (__bf16)(silu_fast(gt) * up);
+            }
+            *reinterpret_cast<bf16x4*>(act + (long)p * a.I + col) = o;
+          }
+        }
+      }
+    } else {
+      __bf16* y = (__bf16*)a.out;
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) {
+        const int p = t.p0 + arow0 + ms * 32 + l32;
+        if (p >= t.p1) continue;
+        int dest = p;
+        if (a.sorted != nullptr) {
+          dest = a.sorted[p];
+          if ((unsigned)dest >= (unsigned)a.sentinel) continue;
+        }
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+          const int cbase = n0 + br[ns];
+          if (cbase >= a.H) continue;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = cbase + g * 8 + khalf * 4;
+            bf16x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = (__bf16)acc[ns][ms][g * 4 + q];
+            *reinterpret_cast<bf16x4*>(y + (long)dest * a.H + col) = o;
+          }
+        }
+      }
+    }
+  };
+
+  setup(cur);
+  issue_loads_for(cur, sA0, sB0, 0);
+  store_fp8(sB0);
+  issue_loads_for(cur, sA1, sB1, BK);
+  while (true) {
+    bool more = false;
+    Tile nxt = cur;
+    if (is_half(cur))
+      run_tile(std::true_type{}, cur, more, nxt);
+    else
+      run_tile(std::false_type{}, cur, more, nxt);
     if (!more) break;
     cur = nxt;
-    lid = nlid;
+    lid = next_lid;
   }
 }
 
@@ -558,7 +608,7 @@ int mtile_bound(const moe_config& c, bool identity) {
 
 // Persistent launch: one workgroup per CU (the kernel's LDS allows no more), at most
 // as many as there can be tiles, a multiple of the 8 XCDs.
-template <int MODE, bool FP8, int WNS>
+template <int MODE, bool FP8>
 hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
   int dev = 0, cus = 0;
   hipError_t err = hipGetDevice(&dev);
@@ -566,7 +616,7 @@ hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
   if (err != hipSuccess) return err;
   const int G = a.mtiles * a.ntiles;
   const int grid = ceil_div(min(G, max(cus, 8)), 8) * 8;
-  ffn_gemm_bf16<MODE, FP8, WNS><<<grid, kThreads, 0, s>>>(a);
+  ffn_gemm_bf16<MODE, FP8><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -592,8 +642,10 @@ FfnArgs base_args(const moe_config& c, const int32_t* sorted_ids, const int32_t*
 }  // namespace
 
 hipError_t launch_gate_up(const moe_config& c, const void* h, const int32_t* sorted_ids, const int32_t* offsets,
-                          const void* w13, const void* w13_scale, void* act, bool identity, hipStream_t s) {
+                          const void* w13, const void* w13_scale, void* act, bool identity, hipStream_t s,
+                          int32_t* work) {
   FfnArgs a = base_args(c, sorted_ids, offsets, identity);
+  a.work = work;
   a.x = h;
   a.w = w13;
   a.wscale = (const __bf16*)w13_scale;
@@ -604,12 +656,14 @@ hipError_t launch_gate_up(const moe_config& c, const void* h, const int32_t* sor
     return hipGetLastError();
   }
   a.ntiles = c.I / (BN / 2);
-  return c.expert_dtype == MOE_FP8_E4M3 ? launch_gemm<0, true, 4>(a, s) : launch_gemm<0, false, 4>(a, s);
+  return c.expert_dtype == MOE_FP8_E4M3 ? launch_gemm<0, true>(a, s) : launch_gemm<0, false>(a, s);
 }
 
 hipError_t launch_down(const moe_config& c, const void* act, const int32_t* sorted_ids, const int32_t* offsets,
-                       const void* w2, const void* w2_scale, void* y, bool identity, hipStream_t s) {
+                       const void* w2, const void* w2_scale, void* y, bool identity, hipStream_t s,
+                       int32_t* work) {
   FfnArgs a = base_args(c, sorted_ids, offsets, identity);
+  a.work = work;
   a.x = act;
   a.w = w2;
   a.wscale = (const __bf16*)w2_scale;
@@ -620,15 +674,16 @@ hipError_t launch_down(const moe_config& c, const void* act, const int32_t* sort
     return hipGetLastError();
   }
   a.ntiles = ceil_div(c.H, 256);
-  return c.expert_dtype == MOE_FP8_E4M3 ? launch_gemm<1, true, 4>(a, s) : launch_gemm<1, false, 4>(a, s);
+  return c.expert_dtype == MOE_FP8_E4M3 ? launch_gemm<1, true>(a, s) : launch_gemm<1, false>(a, s);
 }
 
 hipError_t launch_expert_ffn(const moe_config& c, const void* h, const int32_t* sorted_ids, const int32_t* offsets,
                              const void* w13, const void* w2, const void* w13_scale, const void* w2_scale, void* act,
-                             void* y, bool identity, hipStream_t s) {
-  hipError_t err = launch_gate_up(c, h, sorted_ids, offsets, w13, w13_scale, act, identity, s);
+                             void* y, bool identity, hipStream_t s, int32_t* work) {
+  hipError_t err = launch_gate_up(c, h, sorted_ids, offsets, w13, w13_scale, act, identity, s, work);
   if (err != hipSuccess) return err;
-  return launch_down(c, act, sorted_ids, offsets, w2, w2_scale, y, identity, s);
+  return launch_down(c, act, sorted_ids, offsets, w2, w2_scale, y, identity, s,
+                     work ? work + kGemmWorkWords : nullptr);
 }
 
 }  // namespace moe

@@ -20,19 +20,29 @@ hipError_t launch_topk(const moe_config& c, const float* logits, int32_t* ids, f
 // ---- alignment (align.hip)
 int align_chunk_routes();                       // routes per alignment chunk
 size_t align_workspace_bytes(const moe_config& c);
+// zero / nzero (nullable): words the scan kernel also sets to 0 (the GEMMs' work
+// counters in the forward workspace), so no separate fill launch is needed
 hipError_t launch_align(const moe_config& c, const int32_t* ids, uint8_t* kept, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* offsets, int32_t* num_padded, int32_t* stats,
-                        void* ws, hipStream_t s);
+                        void* ws, hipStream_t s, int32_t* zero = nullptr, int nzero = 0);
 
 // ---- expert FFN (ffn.hip)
 // identity == true: one expert over T token rows (shared expert), offsets ignored.
+// work (nullable): kGemmWorkWords zeroed ints per GEMM launch; with them the
+// persistent workgroups claim tiles from per-XCD counters, without them each takes a
+// fixed share.  The schedule changes no output bit.
+constexpr int kGemmWorkWords = 8;
 hipError_t launch_gate_up(const moe_config& c, const void* h, const int32_t* sorted_ids, const int32_t* offsets,
-                          const void* w13, const void* w13_scale, void* act, bool identity, hipStream_t s);
+                          const void* w13, const void* w13_scale, void* act, bool identity, hipStream_t s,
+                          int32_t* work = nullptr);
 hipError_t launch_down(const moe_config& c, const void* act, const int32_t* sorted_ids, const int32_t* offsets,
-                       const void* w2, const void* w2_scale, void* y, bool identity, hipStream_t s);
+                       const void* w2, const void* w2_scale, void* y, bool identity, hipStream_t s,
+                       int32_t* work = nullptr);
+// work: 2 * kGemmWorkWords ints (W13, then W2), or null
 hipError_t launch_expert_ffn(const moe_config& c, const void* h, const int32_t* sorted_ids,
                              const int32_t* offsets, const void* w13, const void* w2, const void* w13_scale,
-                             const void* w2_scale, void* act, void* y, bool identity, hipStream_t s);
+                             const void* w2_scale, void* act, void* y, bool identity, hipStream_t s,
+                             int32_t* work = nullptr);
 
 // ---- combine (combine.hip)
 hipError_t launch_combine(const moe_config& c, const void* y_route, const float* gates, const uint8_t* kept,
