@@ -29,7 +29,7 @@ import numpy as np
 
 __all__ = [
     "decode_bf16", "decode_e4m3", "round_bf16", "dequantize_blocks", "router_logits", "rank_experts",
-    "topk_route", "capacity", "capacity_keep", "align", "silu", "swiglu_expert",
+    "topk_route", "replay_route", "capacity", "capacity_keep", "align", "silu", "swiglu_expert",
     "expert_ffn", "combine", "routing_stats", "moe_forward",
 ]
 
@@ -141,6 +141,35 @@ def topk_route(logits: np.ndarray, k: int, renormalize: bool = True):
     else:
         margin = np.full(T, np.inf)
     return ids.astype(np.int64), gates, margin
+
+
+def replay_route(logits: np.ndarray, ids: np.ndarray, renormalize: bool = True):
+    """Gates for recorded expert ids, and this run's router margin.
+
+    [R&R] paragraph on router replay: the top-k expert indices of an earlier run are
+    stored and used again, so the expert path of a later run is the same; it fixes the
+    path only.  READING: only the indices are replayed; the gate weights come from
+    this run's scores by the usual gate rule ([MIR] "How sparse routing works":
+    softmax over all N, take the recorded experts, divide by their sum when
+    renormalising).  An id outside [0, N) carries zero weight.  The margin is that of
+    this run's own ranking ([R&R] margin paragraph), as topk_route gives it.
+
+    Returns (gates [T, k] float64 in the recorded order, margin [T] float64).
+    """
+    l = np.asarray(logits, np.float64)
+    ids = np.asarray(ids, np.int64)
+    T, N = l.shape
+    lw = np.where(np.isnan(l), -np.inf, l)
+    lmax = np.max(lw, axis=1, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = np.exp(lw - lmax)
+        p = p / p.sum(axis=1, keepdims=True)        # softmax over all N experts
+    valid = (ids >= 0) & (ids < N)
+    sel = np.where(valid, np.take_along_axis(p, np.clip(ids, 0, N - 1), axis=1), 0.0)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        gates = sel / sel.sum(axis=1, keepdims=True) if renormalize else sel
+    _, _, margin = topk_route(l, ids.shape[1], renormalize)
+    return gates, margin
 
 
 # ---------------------------------------------------------------- capacity and alignment
@@ -323,19 +352,25 @@ def routing_stats(ids: np.ndarray, kept: np.ndarray, N: int, cap: Optional[int])
 
 def moe_forward(h, w_gate, w13_of, w2_of, *, k: int, B: int, cap_num: int = 0, cap_den: int = 0,
                 renormalize: bool = True, bias=None, residual=None, shared_w13=None, shared_w2=None,
-                logits=None, tokens=None) -> dict:
+                logits=None, tokens=None, replay_ids=None) -> dict:
     """The whole layer, step after step in the pages' order, all in float64.
 
     route ([MIR] "How sparse routing works") -> capacity and drops ([R&R], [MIR]
     "The hard part") -> alignment ([RB]) -> expert FFN on kept routes -> combine.
     ``logits`` (if given) replaces the projection, for routing from stored logits.
     ``tokens`` restricts the expert FFN and combine to a sample of token rows.
+    ``replay_ids`` (if given) are recorded expert ids used instead of this run's top-k
+    ([R&R] router replay; gates from replay_route).
     """
     h = np.asarray(h, np.float64)
     T, H = h.shape
     N = (np.asarray(logits).shape[1] if logits is not None else np.asarray(w_gate).shape[0])
     l = router_logits(h, w_gate, bias) if logits is None else np.asarray(logits, np.float64)
-    ids, gates, margin = topk_route(l, k, renormalize)
+    if replay_ids is None:
+        ids, gates, margin = topk_route(l, k, renormalize)
+    else:
+        ids = np.asarray(replay_ids, np.int64).reshape(T, k)
+        gates, margin = replay_route(l, ids, renormalize)
     cap = capacity(T, k, N, cap_num, cap_den)
     kept = capacity_keep(ids, N, cap)
     al = align(ids, kept, N, B)

@@ -476,3 +476,68 @@ def test_sampled_tokens_equal_full_pass():
     part = O.moe_forward(*args, k=wl.k, B=wl.B, residual=d["h"].double().numpy(), tokens=sub)
     # BLAS may block a smaller product differently: equal up to fp64 rounding
     assert np.allclose(part["out"], full["out"][sub], rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------------ router replay
+
+def test_golden_replay_k2():
+    d, _ = _read_fixture("replay_k2.txt")
+    l = _floats(d["logits"])[None, :]
+    ids = _ints(d["replay_ids"])[None, :]
+    gates, margin = O.replay_route(l, ids, renormalize=True)
+    assert np.allclose(gates[0], _floats(d["gates"]), rtol=1e-14, atol=0)
+    gates_sm, _ = O.replay_route(l, ids, renormalize=False)
+    assert np.allclose(gates_sm[0], _floats(d["gates_softmax"]), rtol=1e-14, atol=0)
+    assert margin[0] == float(d["margin"])
+
+
+def test_replay_of_own_route_reproduces_it():
+    rng = np.random.default_rng(5)
+    for N, k in ((8, 2), (16, 1), (64, 8), (6, 6)):
+        l = rng.standard_normal((40, N))
+        l[3, :] = 0.25          # all tied
+        l[4, 1] = np.nan
+        for renorm in (True, False):
+            ids, gates, margin = O.topk_route(l, k, renorm)
+            g2, m2 = O.replay_route(l, ids, renorm)
+            assert np.allclose(g2, gates, rtol=1e-15, atol=0)
+            assert np.array_equal(m2, margin)
+
+
+def test_replay_gates_follow_the_recorded_order_and_ignore_invalid_ids():
+    rng = np.random.default_rng(6)
+    N, k = 12, 4
+    l = rng.standard_normal((30, N))
+    ids = np.stack([rng.permutation(N)[:k] for _ in range(30)])
+    g, _ = O.replay_route(l, ids)
+    perm = np.array([2, 0, 3, 1])
+    gp, _ = O.replay_route(l, ids[:, perm])
+    assert np.allclose(gp, g[:, perm], rtol=1e-15, atol=0)
+    assert np.allclose(g.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    # ids outside [0, N) carry no weight; the rest renormalise among themselves
+    bad = ids.copy()
+    bad[:, 1] = N
+    bad[:, 3] = -1
+    gb, _ = O.replay_route(l, bad)
+    assert np.all(gb[:, [1, 3]] == 0)
+    ref, _ = O.replay_route(l, ids[:, [0, 2]])
+    assert np.allclose(gb[:, [0, 2]], ref, rtol=1e-15, atol=0)
+    # one recorded expert: gate exactly 1
+    g1, _ = O.replay_route(l, ids[:, :1])
+    assert np.all(g1 == 1.0)
+
+
+def test_forward_replay_of_own_ids_matches_forward():
+    w = W.TOY_FP32
+    d = W.layer_inputs(w, device="cpu")
+    f64 = lambda t: t.double().numpy()
+    w13 = f64(d["w13"]); w2 = f64(d["w2"])
+    kw = dict(k=w.k, B=w.B, residual=f64(d["residual"]))
+    a = O.moe_forward(f64(d["h"]), f64(d["w_gate"]), lambda e: w13[e], lambda e: w2[e], **kw)
+    b = O.moe_forward(f64(d["h"]), f64(d["w_gate"]), lambda e: w13[e], lambda e: w2[e], replay_ids=a["ids"], **kw)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["gates"], b["gates"])
+    # a different recorded route changes the experts that run, not the projection
+    other = np.roll(a["ids"], 1, axis=1)
+    c = O.moe_forward(f64(d["h"]), f64(d["w_gate"]), lambda e: w13[e], lambda e: w2[e], replay_ids=other, **kw)
+    assert np.array_equal(c["ids"], other) and np.array_equal(c["logits"], a["logits"])
+    assert np.allclose(c["gates"], np.roll(a["gates"], 1, axis=1), rtol=1e-15, atol=0)
