@@ -267,6 +267,10 @@ def main() -> int:
         ms_comb = timed(lambda: M.moe_combine(cfg, tr["y_route"], tr["topk_gates"], tr["route_kept"], None,
                                               d["residual"], out, stream=stream), max(args.steps, 5), True)
         stages["combine"] = {"us": ms_comb * 1e3, "GB/s": comb_bytes / (ms_comb * 1e-3) / 1e9}
+        # router replay: the whole layer on the recorded ids of the forward above
+        ms_replay = timed(lambda: M.moe_forward_replay(cfg, wts, d["h"], d["residual"], tr["topk_ids"], out, None, ws,
+                                                       stream=stream), max(args.steps, 5), False)
+        stages["forward_replay"] = {"us": ms_replay * 1e3, "tokens/s": T / (ms_replay * 1e-3)}
         for kname, v in stages.items():
             log(f"[bench] stage {kname}: " + ", ".join(f"{a} {b:,.2f}" for a, b in v.items()))
 

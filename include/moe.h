@@ -75,9 +75,10 @@ enum {
 /* Element types.  fp8 is OCP E4M3FN (bias 7, max 448, no infinities). */
 enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 };
 
-/* moe_route flags */
+/* moe_route flags (may be combined) */
 enum {
-  MOE_ROUTE_LOGITS_IN = 1u /* skip the projection: `logits` is an input (stored or replayed logits) */
+  MOE_ROUTE_LOGITS_IN = 1u, /* skip the projection: `logits` is an input (stored or replayed logits) */
+  MOE_ROUTE_IDS_IN = 2u     /* router replay: `topk_ids` is an input (recorded expert ids) */
 };
 
 /* moe_workspace_size operations */
@@ -189,6 +190,16 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes);
  *   margin     [T] float32, nullable: l_(k-1) - l_(k) in rank order, +inf when k = N
  * Logits are accumulated in fp32 over fixed 32-wide K steps in ascending K.
  * A NaN logit ranks below every number and carries zero gate weight; -0 == +0.
+ *
+ * MOE_ROUTE_IDS_IN, router replay ("Mixture-of-experts routing & LLM repeatability",
+ * router replay paragraph: the top-k indices of an earlier run are stored and used
+ * again, fixing the expert path): topk_ids holds recorded expert ids and is only
+ * read.  topk_gates are then this run's gates over those experts in their recorded
+ * order: exp(l_id - m) / sum over the recorded ids (m their largest logit), or the
+ * plain softmax values with renormalize = 0; an id outside [0, N) weighs 0 (a token
+ * with no valid id gets NaN gates, 0/0, and moe_align never keeps its routes).  The
+ * margin is this run's own (how close its scores are to a different route).
+ * Replaying a run's own ids reproduces its gates bit for bit.
  */
 moe_status moe_route(const moe_config* cfg, const void* h, const void* w_gate, const float* logit_bias,
                      float* logits, int32_t* topk_ids, float* topk_gates, float* margin, uint32_t flags,
@@ -265,6 +276,21 @@ moe_status moe_combine(const moe_config* cfg, const void* y_route, const float* 
 moe_status moe_forward(const moe_config* cfg, const moe_weights* weights, const void* h,
                        const void* residual, void* out, const moe_trace* trace, void* ws,
                        size_t ws_bytes, void* stream);
+
+/*
+ * The whole layer with router replay ("Mixture-of-experts routing & LLM
+ * repeatability", router replay paragraph): as moe_forward, but the experts are the
+ * recorded ids instead of this run's top-k (moe_route with MOE_ROUTE_IDS_IN);
+ * capacity, alignment, expert FFN and combine run on them.
+ *   replay_ids [T, k] int32, recorded expert ids (e.g. trace->topk_ids of an earlier
+ *              moe_forward); only read.  trace->topk_ids is not used.
+ * Everything else as moe_forward, same workspace size.  Replaying a run's own ids
+ * reproduces its output bit for bit.  Returns MOE_ERR_NULL_POINTER for a NULL
+ * replay_ids and MOE_ERR_MISALIGNED if it is not 4-byte aligned.
+ */
+moe_status moe_forward_replay(const moe_config* cfg, const moe_weights* weights, const void* h,
+                              const void* residual, const int32_t* replay_ids, void* out,
+                              const moe_trace* trace, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -137,6 +137,14 @@ def test_host_validation_of_pointers_and_workspace():
     _expect("MOE_ERR_NULL_POINTER", M.moe_forward, cfg8, full, A, None, A, None, A, 1 << 40, s)
     bad = config(W.MIXTRAL_BF16, k=0)
     _expect("MOE_ERR_INVALID_CONFIG", M.moe_forward, bad, full, A, None, A, None, A, 1 << 40, s)
+    # forward replay: the recorded ids are required and 4-byte aligned; the rest as moe_forward
+    _expect("MOE_ERR_NULL_POINTER", M.moe_forward_replay, cfg, full, A, None, None, A, None, A, 1 << 40, s)
+    _expect("MOE_ERR_MISALIGNED", M.moe_forward_replay, cfg, full, A, None, A + 2, A, None, A, 1 << 40, s)
+    _expect("MOE_ERR_WORKSPACE_TOO_SMALL", M.moe_forward_replay, cfg, full, A, None, A, A, None, A, 1024, s)
+    _expect("MOE_ERR_INVALID_CONFIG", M.moe_forward_replay, bad, full, A, None, A, A, None, A, 1 << 40, s)
+    # route with recorded ids: the flag is known; unknown bits are not
+    _expect("MOE_ERR_NULL_POINTER", M.moe_route, cfg, A, A, None, A, None, A, None, M.MOE_ROUTE_IDS_IN, s)
+    _expect("MOE_ERR_UNSUPPORTED", M.moe_route, cfg, A, A, None, A, A, A, None, 0x4 | M.MOE_ROUTE_IDS_IN, s)
 
 
 def test_workspace_op_codes():

@@ -19,13 +19,14 @@ __all__ = [
     "moe_abi_version", "moe_status_str", "moe_validate_config", "moe_align_sizes",
     "moe_workspace_size", "moe_route", "moe_align", "moe_expert_ffn", "moe_expert_gate_up",
     "moe_expert_down", "moe_combine",
-    "moe_forward", "MOE_ROUTE_LOGITS_IN", "MOE_OP_ALIGN", "MOE_OP_FORWARD", "STATUS",
+    "moe_forward", "moe_forward_replay", "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_IDS_IN", "MOE_OP_ALIGN", "MOE_OP_FORWARD", "STATUS",
     "DTYPES", "STATS_EXTRA", "STAT",
 ]
 
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3}
 MOE_ROUTE_LOGITS_IN = 1
+MOE_ROUTE_IDS_IN = 2
 MOE_OP_ALIGN, MOE_OP_FORWARD = 1, 2
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL_POINTER", 2: "MOE_ERR_INVALID_CONFIG", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_MISALIGNED", 5: "MOE_ERR_WORKSPACE_TOO_SMALL", 6: "MOE_ERR_HIP"}
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
             "moe_expert_down": ([cfgp, P, P, P, P, P, P, P], I32),
             "moe_combine": ([cfgp, P, P, P, P, P, P, P], I32),
             "moe_forward": ([cfgp, ctypes.POINTER(moe_weights), P, P, P, ctypes.POINTER(moe_trace), P, SZ, P], I32),
+            "moe_forward_replay": ([cfgp, ctypes.POINTER(moe_weights), P, P, P, P, ctypes.POINTER(moe_trace), P, SZ,
+                                    P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -192,3 +195,15 @@ def moe_forward(cfg, weights: dict, h, residual, out, trace: Optional[dict], ws,
     _check("moe_forward", lib().moe_forward(ctypes.byref(cfg), ctypes.byref(w), _ptr(h), _ptr(residual), _ptr(out),
                                             ctypes.byref(tr) if tr is not None else None, _ptr(ws), nb,
                                             _stream(stream)))
+
+
+def moe_forward_replay(cfg, weights: dict, h, residual, replay_ids, out, trace: Optional[dict], ws,
+                       ws_bytes: Optional[int] = None, stream=None):
+    """moe_forward with recorded expert ids ([T, k] int32) instead of this run's top-k."""
+    w = moe_weights(**{k: _ptr(weights.get(k)) for k, _ in moe_weights._fields_})
+    tr = moe_trace(**{k: _ptr(trace.get(k)) for k, _ in moe_trace._fields_}) if trace else None
+    nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
+    _check("moe_forward_replay",
+           lib().moe_forward_replay(ctypes.byref(cfg), ctypes.byref(w), _ptr(h), _ptr(residual), _ptr(replay_ids),
+                                    _ptr(out), ctypes.byref(tr) if tr is not None else None, _ptr(ws), nb,
+                                    _stream(stream)))

@@ -84,7 +84,7 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 moe_status check_route_args(const moe_config& c, const void* h, const void* w_gate, const float* bias,
                             const float* logits, const int32_t* ids, const float* gates, const float* margin,
                             uint32_t flags) {
-  if (flags & ~(uint32_t)MOE_ROUTE_LOGITS_IN) return MOE_ERR_UNSUPPORTED;
+  if (flags & ~(uint32_t)(MOE_ROUTE_LOGITS_IN | MOE_ROUTE_IDS_IN)) return MOE_ERR_UNSUPPORTED;
   const bool in = flags & MOE_ROUTE_LOGITS_IN;
   if (!logits || !ids || !gates) return MOE_ERR_NULL_POINTER;
   if (!in && (!h || !w_gate)) return MOE_ERR_NULL_POINTER;
@@ -179,8 +179,12 @@ moe_status moe_route(const moe_config* cfg, const void* h, const void* w_gate, c
   st = check_route_args(*cfg, h, w_gate, logit_bias, logits, topk_ids, topk_gates, margin, flags);
   if (st != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (flags & MOE_ROUTE_LOGITS_IN) return hip_status(launch_topk(*cfg, logits, topk_ids, topk_gates, margin, s));
-  return hip_status(launch_router(*cfg, h, w_gate, logit_bias, logits, topk_ids, topk_gates, margin, s));
+  // replay: the recorded ids are read, never written
+  const int32_t* replay = (flags & MOE_ROUTE_IDS_IN) ? topk_ids : nullptr;
+  int32_t* ids_out = replay ? nullptr : topk_ids;
+  if (flags & MOE_ROUTE_LOGITS_IN)
+    return hip_status(launch_topk(*cfg, logits, ids_out, topk_gates, margin, s, replay));
+  return hip_status(launch_router(*cfg, h, w_gate, logit_bias, logits, ids_out, topk_gates, margin, s, replay));
 }
 
 moe_status moe_align(const moe_config* cfg, const int32_t* topk_ids, uint8_t* route_kept, int32_t* sorted_route_ids,
@@ -244,8 +248,12 @@ moe_status moe_combine(const moe_config* cfg, const void* y_route, const float* 
                                    (hipStream_t)stream));
 }
 
-moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void* h, const void* residual, void* out,
-                       const moe_trace* trace, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// moe_forward and moe_forward_replay (replay: recorded expert ids, or null)
+moe_status forward_impl(const moe_config* cfg, const moe_weights* wt, const void* h, const void* residual,
+                        const int32_t* replay, void* out, const moe_trace* trace, void* ws, size_t ws_bytes,
+                        void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   const moe_config& c = *cfg;
@@ -267,7 +275,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   if (trace) tr = *trace;
   auto pick = [&](void* user, size_t off) -> void* { return user ? user : (void*)(base + off); };
   float* logits = (float*)pick(tr.logits, L.logits);
-  int32_t* ids = (int32_t*)pick(tr.topk_ids, L.ids);
+  int32_t* ids = replay ? const_cast<int32_t*>(replay) : (int32_t*)pick(tr.topk_ids, L.ids);
   float* gates = (float*)pick(tr.topk_gates, L.gates);
   float* margin = (float*)pick(tr.margin, L.margin);
   uint8_t* kept = (uint8_t*)pick(tr.route_kept, L.kept);
@@ -285,7 +293,8 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
     return MOE_ERR_MISALIGNED;
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_router(c, h, wt->w_gate, wt->logit_bias, logits, ids, gates, margin, s);
+  hipError_t e = launch_router(c, h, wt->w_gate, wt->logit_bias, logits, replay ? nullptr : ids, gates, margin, s,
+                               replay);
   if (e == hipSuccess)
     e = launch_align(c, ids, kept, sorted, blocks, offsets, npad, stats, base + L.align_ws, s, work,
                      4 * kGemmWorkWords);
@@ -300,6 +309,23 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   }
   if (e == hipSuccess) e = launch_combine(c, y, gates, kept, shared_out, residual, out, s);
   return hip_status(e);
+}
+
+}  // namespace
+
+moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void* h, const void* residual, void* out,
+                       const moe_trace* trace, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(cfg, wt, h, residual, nullptr, out, trace, ws, ws_bytes, stream);
+}
+
+moe_status moe_forward_replay(const moe_config* cfg, const moe_weights* wt, const void* h, const void* residual,
+                              const int32_t* replay_ids, void* out, const moe_trace* trace, void* ws,
+                              size_t ws_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!replay_ids) return MOE_ERR_NULL_POINTER;
+  if (!aligned(replay_ids, 4)) return MOE_ERR_MISALIGNED;
+  return forward_impl(cfg, wt, h, residual, replay_ids, out, trace, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

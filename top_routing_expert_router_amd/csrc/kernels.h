@@ -11,11 +11,12 @@
 namespace moe {
 
 // ---- routing (route.hip)
-// projection + top-k + gates + margin (fused for bf16)
+// projection + top-k + gates + margin (fused for bf16).  replay (nullable): recorded
+// expert ids [T, k]; gates are then taken over them and ids is not written.
 hipError_t launch_router(const moe_config& c, const void* h, const void* w_gate, const float* bias, float* logits,
-                         int32_t* ids, float* gates, float* margin, hipStream_t s);
+                         int32_t* ids, float* gates, float* margin, hipStream_t s, const int32_t* replay = nullptr);
 hipError_t launch_topk(const moe_config& c, const float* logits, int32_t* ids, float* gates, float* margin,
-                       hipStream_t s);
+                       hipStream_t s, const int32_t* replay = nullptr);
 
 // ---- alignment (align.hip)
 int align_chunk_routes();                       // routes per alignment chunk

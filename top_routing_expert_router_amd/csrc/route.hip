@@ -37,10 +37,15 @@ typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 // (value, -index) keys give the ranked ids and the (k+1)-th logit for the margin.
 // Gate weight_j = exp(l_j - l_0) (0 for a NaN logit); divided by the sum over the
 // k chosen in rank order, or by the sum over all N experts without renormalisation.
+// Replay ("Mixture-of-experts routing & LLM repeatability", router replay paragraph):
+// with recorded ids the experts are those ids in their recorded order, ids are not
+// written, and weight_j = exp(l_{id_j} - m), m the largest recorded logit (an id
+// outside [0, N) weighs 0); the margin is still this run's.  Replaying a run's own
+// ids gives its gates bit for bit (same values, same order, m = l_0).
 template <typename RowPtr>
 __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int renormalize, int L,
                                          int32_t* __restrict__ ids, float* __restrict__ gates,
-                                         float* __restrict__ margin) {
+                                         float* __restrict__ margin, const int32_t* __restrict__ replay) {
   const int lane = threadIdx.x & 63;
   const int g = lane & (L - 1), base = lane - g;
   float lv[4];
@@ -80,12 +85,35 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
   const float l0 = sl[0];
   float w[8];
   float s = 0.f;
+  if (replay == nullptr) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    w[j] = 0.f;
-    if (j < k) {
-      w[j] = (sl[j] != sl[j]) ? 0.f : expf(sl[j] - l0);
-      s += w[j];
+    for (int j = 0; j < 8; ++j) {
+      w[j] = 0.f;
+      if (j < k) {
+        w[j] = (sl[j] != sl[j]) ? 0.f : expf(sl[j] - l0);
+        s += w[j];
+      }
+    }
+  } else {
+    float rl[8];
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      rl[j] = __builtin_nanf("");
+      if (j < k) {
+        const int id = replay[(size_t)t * k + j];
+        if ((unsigned)id < (unsigned)N) rl[j] = row[id];
+        m = rl[j] > m ? rl[j] : m;  // NaN never wins
+      }
+    }
+    const float ref = renormalize ? m : l0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      w[j] = 0.f;
+      if (j < k) {
+        w[j] = (rl[j] != rl[j]) ? 0.f : expf(rl[j] - ref);
+        s += w[j];
+      }
     }
   }
   if (!renormalize) {
@@ -100,7 +128,7 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (j < k && g == j) {
-      ids[(size_t)t * k + j] = sid[j];
+      if (replay == nullptr) ids[(size_t)t * k + j] = sid[j];
       gates[(size_t)t * k + j] = w[j] / s;
     }
   }
@@ -124,7 +152,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
                                                    const float* __restrict__ bias, float* __restrict__ logits,
                                                    int32_t* __restrict__ ids, float* __restrict__ gates,
                                                    float* __restrict__ margin, int T, int H, int N, int k,
-                                                   int renormalize) {
+                                                   int renormalize, const int32_t* __restrict__ replay) {
   constexpr int NP = NSUB * 16;
   __shared__ float part[kRouterWaves][NP][kRouterTokens];
   __shared__ float lg[kRouterTokens][NP + 1];
@@ -213,7 +241,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
   const int L = topk_lanes(N);
   const int per_wave = kWave / L;
   for (int t = wave * per_wave + lane / L; t < kRouterTokens; t += kRouterWaves * per_wave)
-    if (t0 + t < T) topk_one(&lg[t][0], t0 + t, N, k, renormalize, L, ids, gates, margin);
+    if (t0 + t < T) topk_one(&lg[t][0], t0 + t, N, k, renormalize, L, ids, gates, margin, replay);
 }
 
 // fp32 projection: one thread per (token, expert), fmaf over H in ascending order.
@@ -235,50 +263,51 @@ __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict
 // 256 threads, one group of L lanes per token, 256 / L tokens per workgroup.
 __global__ __launch_bounds__(256) void topk_gates(const float* __restrict__ logits, int32_t* __restrict__ ids,
                                                    float* __restrict__ gates, float* __restrict__ margin,
-                                                   int T, int N, int k, int renormalize) {
+                                                   int T, int N, int k, int renormalize,
+                                                   const int32_t* __restrict__ replay) {
   const int L = topk_lanes(N);
   const int t = blockIdx.x * (256 / L) + threadIdx.x / L;
   if (t >= T) return;
-  topk_one(logits + (size_t)t * N, t, N, k, renormalize, L, ids, gates, margin);
+  topk_one(logits + (size_t)t * N, t, N, k, renormalize, L, ids, gates, margin, replay);
 }
 
 template <int NSUB>
 hipError_t launch_router_bf16(const moe_config& c, const void* h, const void* wg, const float* bias, float* logits,
-                              int32_t* ids, float* gates, float* margin, hipStream_t s) {
+                              int32_t* ids, float* gates, float* margin, hipStream_t s, const int32_t* replay) {
   dim3 grid(ceil_div(c.T, kRouterTokens));
   router_bf16<NSUB><<<grid, kRouterThreads, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits, ids, gates, margin, c.T,
-                                         c.H, c.N, c.k, c.renormalize);
+                                         c.H, c.N, c.k, c.renormalize, replay);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_router(const moe_config& c, const void* h, const void* w_gate, const float* bias, float* logits,
-                         int32_t* ids, float* gates, float* margin, hipStream_t s) {
+                         int32_t* ids, float* gates, float* margin, hipStream_t s, const int32_t* replay) {
   if (c.act_dtype == MOE_F32) {
     const long n = (long)c.T * c.N;
     router_logits_f32<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>((const float*)h, (const float*)w_gate, bias,
                                                                         logits, c.T, c.H, c.N);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch_topk(c, logits, ids, gates, margin, s);
+    return launch_topk(c, logits, ids, gates, margin, s, replay);
   }
 #define MOE_ROUTER_CASE(n) \
   case n:                  \
-    return launch_router_bf16<n>(c, h, w_gate, bias, logits, ids, gates, margin, s);
+    return launch_router_bf16<n>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay);
   switch (ceil_div(c.N, 16)) {
     MOE_ROUTER_CASE(1) MOE_ROUTER_CASE(2) MOE_ROUTER_CASE(3) MOE_ROUTER_CASE(4) MOE_ROUTER_CASE(5)
     MOE_ROUTER_CASE(6) MOE_ROUTER_CASE(7) MOE_ROUTER_CASE(8) MOE_ROUTER_CASE(9) MOE_ROUTER_CASE(10)
     MOE_ROUTER_CASE(11) MOE_ROUTER_CASE(12) MOE_ROUTER_CASE(13) MOE_ROUTER_CASE(14) MOE_ROUTER_CASE(15)
-    default: return launch_router_bf16<16>(c, h, w_gate, bias, logits, ids, gates, margin, s);
+    default: return launch_router_bf16<16>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay);
   }
 #undef MOE_ROUTER_CASE
 }
 
 hipError_t launch_topk(const moe_config& c, const float* logits, int32_t* ids, float* gates, float* margin,
-                       hipStream_t s) {
+                       hipStream_t s, const int32_t* replay) {
   dim3 grid(ceil_div(c.T, 256 / topk_lanes(c.N)));
-  topk_gates<<<grid, 256, 0, s>>>(logits, ids, gates, margin, c.T, c.N, c.k, c.renormalize);
+  topk_gates<<<grid, 256, 0, s>>>(logits, ids, gates, margin, c.T, c.N, c.k, c.renormalize, replay);
   return hipGetLastError();
 }
 
