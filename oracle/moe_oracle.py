@@ -29,7 +29,7 @@ import numpy as np
 
 __all__ = [
     "decode_bf16", "decode_e4m3", "round_bf16", "dequantize_blocks", "router_logits", "rank_experts",
-    "topk_route", "replay_route", "capacity", "capacity_keep", "align", "silu", "swiglu_expert",
+    "topk_route", "replay_route", "capacity", "capacity_keep", "capacity_reroute", "align", "silu", "swiglu_expert",
     "expert_ffn", "combine", "routing_stats", "moe_forward",
 ]
 
@@ -208,6 +208,53 @@ def capacity_keep(ids: np.ndarray, N: int, cap: Optional[int]) -> np.ndarray:
     return kept
 
 
+def capacity_reroute(ids: np.ndarray, logits: np.ndarray, N: int, cap: Optional[int], depth: int):
+    """Capacity with the reroute overflow policy.
+
+    [MIR] "The hard part", Figure 2 (an expert at capacity: drop, or reroute -- send
+    the token to its 2nd-choice expert) and the mitigation paragraph after the
+    routing-stats probe (change the overflow policy from drop to reroute, sending
+    overflow tokens to their second-choice expert).
+    READING (rounds): first the drop policy fills capacity (capacity_keep).  Then up
+    to ``depth`` rounds: in each, every token with an overflowed route offers its
+    lowest such route one new candidate -- the next expert in the token's ranking of
+    this run's logits (rank_experts) that is not among its recorded ids and was not
+    offered before -- and requests are admitted in token order while the candidate
+    has room left.  An admitted route runs the candidate with its original gate.
+    depth 1 is the literal "second choice"; depth N - k walks the whole ranking.
+    Routes with ids outside [0, N) never take part.
+
+    Returns (expert [T*k] int64: the expert each route runs, -1 if none;
+             kept [T*k] bool; rerouted [T*k] bool).
+    """
+    ids = np.asarray(ids, np.int64)
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    kept = capacity_keep(ids, N, cap)
+    expert = np.where(kept, flat, -1)
+    rerouted = np.zeros(T * k, dtype=bool)
+    if cap is None or depth <= 0:
+        return expert, kept, rerouted
+    room = [cap - int(np.count_nonzero(expert == e)) for e in range(N)]
+    order = rank_experts(logits)
+    cand = [[int(e) for e in order[t] if int(e) not in set(ids[t].tolist())] for t in range(T)]
+    nxt = [0] * T
+    for _ in range(depth):
+        for t in range(T):
+            pending = [j for j in range(k) if not kept[t * k + j] and 0 <= ids[t, j] < N]
+            if not pending or nxt[t] >= len(cand[t]):
+                continue
+            c = cand[t][nxt[t]]
+            nxt[t] += 1
+            if room[c] > 0:
+                r = t * k + pending[0]
+                room[c] -= 1
+                kept[r] = True
+                expert[r] = c
+                rerouted[r] = True
+    return expert, kept, rerouted
+
+
 def align(ids: np.ndarray, kept: np.ndarray, N: int, B: int):
     """Group kept routes by expert and pad each group to whole B-row blocks.
 
@@ -352,7 +399,7 @@ def routing_stats(ids: np.ndarray, kept: np.ndarray, N: int, cap: Optional[int])
 
 def moe_forward(h, w_gate, w13_of, w2_of, *, k: int, B: int, cap_num: int = 0, cap_den: int = 0,
                 renormalize: bool = True, bias=None, residual=None, shared_w13=None, shared_w2=None,
-                logits=None, tokens=None, replay_ids=None) -> dict:
+                logits=None, tokens=None, replay_ids=None, reroute_depth: int = 0) -> dict:
     """The whole layer, step after step in the pages' order, all in float64.
 
     route ([MIR] "How sparse routing works") -> capacity and drops ([R&R], [MIR]
@@ -360,7 +407,8 @@ def moe_forward(h, w_gate, w13_of, w2_of, *, k: int, B: int, cap_num: int = 0, c
     ``logits`` (if given) replaces the projection, for routing from stored logits.
     ``tokens`` restricts the expert FFN and combine to a sample of token rows.
     ``replay_ids`` (if given) are recorded expert ids used instead of this run's top-k
-    ([R&R] router replay; gates from replay_route).
+    ([R&R] router replay; gates from replay_route).  ``reroute_depth`` > 0 selects the
+    reroute overflow policy (capacity_reroute) instead of dropping.
     """
     h = np.asarray(h, np.float64)
     T, H = h.shape
@@ -372,15 +420,19 @@ def moe_forward(h, w_gate, w13_of, w2_of, *, k: int, B: int, cap_num: int = 0, c
         ids = np.asarray(replay_ids, np.int64).reshape(T, k)
         gates, margin = replay_route(l, ids, renormalize)
     cap = capacity(T, k, N, cap_num, cap_den)
-    kept = capacity_keep(ids, N, cap)
-    al = align(ids, kept, N, B)
+    expert, kept, rerouted = capacity_reroute(ids, l, N, cap, reroute_depth)
+    run_ids = np.where(kept.reshape(T, k), expert.reshape(T, k), ids)  # the expert each kept route runs
+    al = align(run_ids, kept, N, B)
     rows = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
     routes = (rows[:, None] * k + np.arange(k)[None, :]).reshape(-1)
-    y = expert_ffn(h, ids, kept, w13_of, w2_of, N, routes=routes)
+    y = expert_ffn(h, run_ids, kept, w13_of, w2_of, N, routes=routes)
     shared = None
     if shared_w13 is not None:
         shared = swiglu_expert(h[rows], shared_w13, shared_w2)
     out = combine(y, gates, kept, T, H, shared=shared, residual=residual, tokens=rows)
+    stats = routing_stats(ids, kept, N, cap)
+    stats["rerouted"] = int(np.count_nonzero(rerouted))
+    stats["dropped_after_reroute"] = int(np.count_nonzero(~kept & (ids.reshape(-1) >= 0) & (ids.reshape(-1) < N)))
     return {"logits": l, "ids": ids, "gates": gates, "margin": margin, "cap": cap, "kept": kept,
-            "align": al, "y_route": y, "shared": shared, "out": out, "tokens": rows,
-            "stats": routing_stats(ids, kept, N, cap)}
+            "run_ids": run_ids, "rerouted": rerouted, "align": al, "y_route": y, "shared": shared, "out": out,
+            "tokens": rows, "stats": stats}

@@ -541,3 +541,107 @@ def test_forward_replay_of_own_ids_matches_forward():
     c = O.moe_forward(f64(d["h"]), f64(d["w_gate"]), lambda e: w13[e], lambda e: w2[e], replay_ids=other, **kw)
     assert np.array_equal(c["ids"], other) and np.array_equal(c["logits"], a["logits"])
     assert np.allclose(c["gates"], np.roll(a["gates"], 1, axis=1), rtol=1e-15, atol=0)
+
+
+# ------------------------------------------------------------------ reroute overflow policy
+
+def test_golden_reroute():
+    d, _ = _read_fixture("reroute_T6_N3_k1.txt")
+    T, N, k, cap = int(d["T"]), int(d["N"]), int(d["k"]), int(d["cap"])
+    l = _floats(d["logits"]).reshape(T, N)
+    assert O.capacity(T, k, N, 1, 1) == cap
+    ids, _, _ = O.topk_route(l, k)
+    for depth in (0, 1, 2, 5):
+        expert, kept, rerouted = O.capacity_reroute(ids, l, N, cap, depth)
+        want = _ints(d[f"expert_depth{min(depth, 2)}"])
+        assert expert.tolist() == want.tolist(), depth
+        assert kept.tolist() == (want >= 0).tolist()
+        assert rerouted.tolist() == ((want >= 0) & (want != ids.reshape(-1))).tolist()
+
+
+def _reroute_by_rounds(ids, logits, N, cap, depth):
+    """The same policy written round-parallel: per round, gather every token's request,
+    then per expert admit the first `room` requests in token order."""
+    T, k = ids.shape
+    kept = O.capacity_keep(ids, N, cap)
+    expert = np.where(kept, ids.reshape(-1), -1)
+    room = np.array([cap - np.count_nonzero(expert == e) for e in range(N)])
+    order = O.rank_experts(logits)
+    offered = np.zeros((T, N), dtype=bool)
+    for t in range(T):
+        offered[t, [e for e in ids[t] if 0 <= e < N]] = True
+    for _ in range(depth):
+        req = []
+        for t in range(T):
+            pend = [j for j in range(k) if not kept[t * k + j] and 0 <= ids[t, j] < N]
+            free = [e for e in order[t] if not offered[t, e]]
+            if pend and free:
+                offered[t, free[0]] = True
+                req.append((t, pend[0], free[0]))
+        for e in range(N):
+            mine = [(t, j) for t, j, c in req if c == e]
+            for t, j in mine[: max(room[e], 0)]:
+                kept[t * k + j] = True
+                expert[t * k + j] = e
+            room[e] -= min(len(mine), max(room[e], 0))
+    return expert, kept
+
+
+def test_reroute_invariants_and_round_parallel_form():
+    rng = np.random.default_rng(9)
+    for trial in range(60):
+        N = int(rng.integers(2, 9))
+        k = int(rng.integers(1, min(N, 3) + 1))
+        T = int(rng.integers(1, 30))
+        l = rng.standard_normal((T, N))
+        l[rng.random((T, N)) < 0.1] = 0.5                # ties
+        ids, _, _ = O.topk_route(l, k)
+        if trial % 3 == 0:                                # replayed, non-top-k ids (some invalid)
+            ids = np.stack([rng.permutation(N)[:k] for _ in range(T)])
+            ids[rng.random((T, k)) < 0.1] = N
+        cap = int(rng.integers(0, 4))
+        base = O.capacity_keep(ids, N, cap)
+        prev = base
+        for depth in range(0, N - k + 2):
+            expert, kept, rerouted = O.capacity_reroute(ids, l, N, cap, depth)
+            ex2, kept2 = _reroute_by_rounds(ids, l, N, cap, depth)
+            assert np.array_equal(expert, ex2) and np.array_equal(kept, kept2)
+            assert np.all(kept[base]) and np.array_equal(expert[base], ids.reshape(-1)[base])  # phase 1 stays
+            assert np.all(kept[prev])                                                         # monotone in depth
+            assert np.array_equal(rerouted, kept & ~base)
+            load = np.bincount(expert[kept], minlength=N)
+            assert np.all(load <= cap)
+            for t in range(T):
+                mine = expert[t * k:(t + 1) * k][kept[t * k:(t + 1) * k]]
+                assert len(set(mine.tolist())) == len(mine)               # no expert twice per token
+                rr = expert[t * k:(t + 1) * k][rerouted[t * k:(t + 1) * k]]
+                assert not set(rr.tolist()) & set(ids[t].tolist())         # reroutes leave the recorded set
+            if depth == 0:
+                assert np.array_equal(kept, base)
+            prev = kept
+    # no capacity: nothing overflows, nothing reroutes
+    l = rng.standard_normal((10, 4))
+    ids, _, _ = O.topk_route(l, 2)
+    e, kp, rr = O.capacity_reroute(ids, l, 4, None, 3)
+    assert kp.all() and not rr.any()
+
+
+def test_forward_reroute_runs_the_new_expert_with_the_old_gate():
+    # Switch-like: top-1, tight capacity; a rerouted token's output is h + 1 * E_c(h)
+    rng = np.random.default_rng(3)
+    T, H, I, N, k = 12, 8, 16, 3, 1
+    h = rng.standard_normal((T, H))
+    wg = rng.standard_normal((N, H))
+    w13 = rng.standard_normal((N, 2 * I, H)) / math.sqrt(H)
+    w2 = rng.standard_normal((N, H, I)) / math.sqrt(I)
+    kw = dict(k=k, B=2, cap_num=1, cap_den=1, residual=h)
+    drop = O.moe_forward(h, wg, lambda e: w13[e], lambda e: w2[e], **kw)
+    rr = O.moe_forward(h, wg, lambda e: w13[e], lambda e: w2[e], reroute_depth=N - k, **kw)
+    assert rr["stats"]["rerouted"] > 0
+    for t in range(T):
+        if rr["rerouted"][t]:
+            c = rr["run_ids"][t, 0]
+            assert c != drop["ids"][t, 0] and not drop["kept"][t]
+            assert np.allclose(rr["out"][t], h[t] + O.swiglu_expert(h[t:t + 1], w13[c], w2[c])[0], rtol=1e-13)
+        elif drop["kept"][t]:
+            assert np.array_equal(rr["out"][t], drop["out"][t])
