@@ -169,7 +169,7 @@ def main() -> int:
     d = W.layer_inputs(w, device=dev)
     cfg = M.make_config(w.T, w.H, w.N, w.k, w.I, w.B, cap_num=w.cap_num, cap_den=w.cap_den, n_shared=w.n_shared,
                         renormalize=w.renormalize, act_dtype=w.act_dtype, expert_dtype=w.expert_dtype,
-                        scale_block=w.scale_block)
+                        scale_block=w.scale_block, reroute_depth=w.reroute_depth)
     p_max, n_blocks = M.moe_align_sizes(cfg)
     act_t = torch.float32 if w.act_dtype == W.F32 else torch.bfloat16
     asz = 4 if w.act_dtype == W.F32 else 2
@@ -259,10 +259,19 @@ def main() -> int:
                          max(args.steps, 5), True)
         stages["route"] = {"us": ms_route * 1e3, "GB/s": route_bytes / (ms_route * 1e-3) / 1e9}
         align_bytes = R * 4 + R + p_max * 4 + n_blocks * 4
-        ms_align = timed(lambda: M.moe_align(cfg, tr["topk_ids"], tr["route_kept"], tr["sorted_route_ids"],
-                                             tr["block_expert"], tr["expert_offsets"], tr["num_padded"], tr["stats"],
-                                             aws, stream=stream), max(args.steps, 5), True)
-        stages["align"] = {"us": ms_align * 1e3, "GB/s": align_bytes / (ms_align * 1e-3) / 1e9}
+        if w.reroute_depth and w.cap_den:  # the reroute policy also reads each token's logits
+            rexp = torch.empty(R, dtype=torch.int32, device=dev)
+            ms_align = timed(lambda: M.moe_align_reroute(cfg, tr["topk_ids"], tr["logits"], rexp, tr["route_kept"],
+                                                         tr["sorted_route_ids"], tr["block_expert"],
+                                                         tr["expert_offsets"], tr["num_padded"], tr["stats"], aws,
+                                                         stream=stream), max(args.steps, 5), True)
+            stages["align_reroute"] = {"us": ms_align * 1e3, "rerouted": int(tr["stats"][N + M.STAT["rerouted"]]),
+                                       "dropped": int(tr["stats"][N + M.STAT["dropped"]])}
+        else:
+            ms_align = timed(lambda: M.moe_align(cfg, tr["topk_ids"], tr["route_kept"], tr["sorted_route_ids"],
+                                                 tr["block_expert"], tr["expert_offsets"], tr["num_padded"],
+                                                 tr["stats"], aws, stream=stream), max(args.steps, 5), True)
+            stages["align"] = {"us": ms_align * 1e3, "GB/s": align_bytes / (ms_align * 1e-3) / 1e9}
         comb_bytes = kept_routes * H * asz + T * H * asz * 2 + R * 5
         ms_comb = timed(lambda: M.moe_combine(cfg, tr["y_route"], tr["topk_gates"], tr["route_kept"], None,
                                               d["residual"], out, stream=stream), max(args.steps, 5), True)
@@ -365,14 +374,33 @@ def cpu_baseline(w, d, sample: int):
     h_b, wg_b = bits(d["h"]), bits(d["w_gate"])
     w13_b = d["w13"].to("cpu")
     w2_b = d["w2"].to("cpu")
+    fp8 = w.expert_dtype == W.FP8
+    if fp8:
+        s13 = d["w13_scale"].float().cpu().double().numpy()
+        s2 = d["w2_scale"].float().cpu().double().numpy()
+    bias = None if d.get("bias") is None else d["bias"].double().cpu().numpy()
     g = torch.Generator().manual_seed(1234)
     tokens = torch.randperm(w.T, generator=g)[:sample].sort().values.numpy()
     t0 = time.perf_counter()
     h64 = O.decode_bf16(h_b)
-    res = O.moe_forward(h64, O.decode_bf16(wg_b),
-                        lambda e: O.decode_bf16(w13_b[e].view(torch.int16).numpy().view(np.uint16)),
-                        lambda e: O.decode_bf16(w2_b[e].view(torch.int16).numpy().view(np.uint16)),
-                        k=w.k, B=w.B, cap_num=w.cap_num, cap_den=w.cap_den, residual=h64, tokens=tokens)
+
+    def expert(t, sc):
+        if fp8:
+            return lambda e: O.dequantize_blocks(t[e].numpy(), sc[e], w.scale_block)
+        return lambda e: O.decode_bf16(t[e].view(torch.int16).numpy().view(np.uint16))
+
+    shared = {}
+    if w.n_shared:
+        for which in ("w13", "w2"):
+            t = d["shared_" + which].to("cpu")
+            if fp8:
+                sc = d[f"shared_{which}_scale"].float().cpu().double().numpy()
+                shared["shared_" + which] = O.dequantize_blocks(t.numpy(), sc, w.scale_block)
+            else:
+                shared["shared_" + which] = O.decode_bf16(t.view(torch.int16).numpy().view(np.uint16))
+    res = O.moe_forward(h64, O.decode_bf16(wg_b), expert(w13_b, s13 if fp8 else None), expert(w2_b, s2 if fp8 else None),
+                        k=w.k, B=w.B, cap_num=w.cap_num, cap_den=w.cap_den, residual=h64, tokens=tokens,
+                        bias=bias, reroute_depth=w.reroute_depth, **shared)
     dt = time.perf_counter() - t0
     assert res["out"].shape[0] == sample
     log(f"[bench] cpu baseline: {sample} tokens in {dt:.2f} s")

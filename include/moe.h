@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef int32_t moe_status;
 enum {
@@ -93,7 +93,7 @@ enum {
   MOE_STAT_MAX_LOAD = 4,  /* max over experts of routed load (before capacity) */
   MOE_STAT_MIN_LOAD = 5,  /* min over experts of routed load */
   MOE_STAT_NUM_PADDED = 6,/* padded rows used (same as *num_padded) */
-  MOE_STAT_RESERVED = 7,
+  MOE_STAT_REROUTED = 7,  /* routes kept by rerouting to another expert (reroute policy) */
   MOE_STATS_EXTRA = 8
 };
 
@@ -108,7 +108,15 @@ enum {
  *   dtypes: (act F32, expert F32), (act BF16, expert BF16),
  *           (act BF16, expert FP8_E4M3 with scale_block 128);
  *   bf16 activations: T*H < 2^31 and 2*I*H < 2^31 (the expert GEMMs address h
- *           and one expert's weights with 32-bit byte offsets).
+ *           and one expert's weights with 32-bit byte offsets);
+ *   0 <= reroute_depth <= N - k: overflow policy under capacity.  0 = drop ("Mixture-
+ *           of-Experts Routing at Inference Time", "The hard part", Figure 2, drop
+ *           branch); d > 0 = reroute (Figure 2's reroute branch, and the mitigation
+ *           paragraph after the routing-stats probe): after the drop-policy fill, up to
+ *           d rounds in which each token with an overflowed route offers its lowest such
+ *           route the next expert of its own ranking not among its ids and not offered
+ *           before; requests are admitted in token order while the expert has room.  The
+ *           route keeps its gate.  d = 1 is the "second choice"; see moe_align_reroute.
  * act_dtype is the type of h, residual, out, W_g, act and y_route.
  */
 typedef struct moe_config {
@@ -120,6 +128,7 @@ typedef struct moe_config {
   int32_t act_dtype;
   int32_t expert_dtype;
   int32_t scale_block;  /* 128 for fp8 experts, else 0 */
+  int32_t reroute_depth; /* 0 = drop overflow; > 0 = reroute rounds (see above) */
 } moe_config;
 
 /*
@@ -163,6 +172,7 @@ typedef struct moe_trace {
   int32_t* stats;            /* [N + MOE_STATS_EXTRA] */
   void* act;                 /* [P_max, I] act dtype */
   void* y_route;             /* [T*k, H] act dtype */
+  int32_t* route_expert;     /* [T*k]: expert each route runs, -1 none (reroute policy only) */
 } moe_trace;
 
 /* ABI version (MOE_ABI_VERSION) of the loaded library. */
@@ -206,7 +216,8 @@ moe_status moe_route(const moe_config* cfg, const void* h, const void* w_gate, c
                      void* stream);
 
 /*
- * Capacity and alignment (deterministic: no atomic decides any order).
+ * Capacity with the drop policy (whatever reroute_depth says; moe_align_reroute
+ * applies the config's policy) and alignment (deterministic: no atomic decides any order).
  *   topk_ids         [T*k] int32 (from moe_route, or replayed by the caller)
  *   route_kept       [T*k] uint8 out: 1 = the route runs its expert, 0 = dropped or invalid id
  *   sorted_route_ids [P_max] int32 out: per expert (ascending), its kept route ids ascending,
@@ -221,6 +232,25 @@ moe_status moe_route(const moe_config* cfg, const void* h, const void* w_gate, c
 moe_status moe_align(const moe_config* cfg, const int32_t* topk_ids, uint8_t* route_kept,
                      int32_t* sorted_route_ids, int32_t* block_expert, int32_t* expert_offsets,
                      int32_t* num_padded, int32_t* stats, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Capacity with the config's overflow policy (reroute when reroute_depth > 0), then
+ * the alignment of the routes as they run.  Arguments as moe_align, plus:
+ *   logits       [T, N] float32: this run's scores; each token's candidates are its
+ *                experts in ranking order (value descending, lower index first, NaN
+ *                last, -0 == +0) without its topk_ids
+ *   route_expert [T*k] int32 out: the expert each route runs (its own id, the expert
+ *                it was rerouted to, or -1 when dropped or invalid)
+ * sorted_route_ids, block_expert and expert_offsets group the routes by route_expert;
+ * stats[N + MOE_STAT_REROUTED] counts routes kept by rerouting, DROPPED those left
+ * without an expert; per-expert loads are before capacity.  The decisions are made by
+ * one workgroup in token order (no atomic decides an order).  With reroute_depth 0
+ * the result equals moe_align's (plus route_expert).
+ */
+moe_status moe_align_reroute(const moe_config* cfg, const int32_t* topk_ids, const float* logits,
+                             int32_t* route_expert, uint8_t* route_kept, int32_t* sorted_route_ids,
+                             int32_t* block_expert, int32_t* expert_offsets, int32_t* num_padded, int32_t* stats,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Grouped SwiGLU expert FFN over aligned rows.

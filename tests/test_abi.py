@@ -53,7 +53,7 @@ def test_ceiling_library_exports_and_rejects_bad_arguments():
 
 
 def test_abi_version_and_status_strings():
-    assert M.moe_abi_version() == 1
+    assert M.moe_abi_version() == 2
     for code, name in M.STATUS.items():
         assert M.moe_status_str(code).startswith(name)
     assert "unknown" in M.moe_status_str(99)
@@ -76,7 +76,7 @@ BAD = [
     dict(T=0), dict(T=65537), dict(H=100), dict(H=0), dict(I=64), dict(N=0), dict(N=257), dict(k=0),
     dict(k=9, N=16), dict(k=3, N=2), dict(B=12), dict(B=256), dict(cap_num=5, cap_den=0),
     dict(cap_num=-1, cap_den=4), dict(n_shared=2), dict(renormalize=2), dict(T=65536, H=32768),
-    dict(I=32768, H=32768),
+    dict(I=32768, H=32768), dict(reroute_depth=-1), dict(reroute_depth=7, N=8, k=2),
 ]
 
 
@@ -142,6 +142,12 @@ def test_host_validation_of_pointers_and_workspace():
     _expect("MOE_ERR_MISALIGNED", M.moe_forward_replay, cfg, full, A, None, A + 2, A, None, A, 1 << 40, s)
     _expect("MOE_ERR_WORKSPACE_TOO_SMALL", M.moe_forward_replay, cfg, full, A, None, A, A, None, A, 1024, s)
     _expect("MOE_ERR_INVALID_CONFIG", M.moe_forward_replay, bad, full, A, None, A, A, None, A, 1 << 40, s)
+    # reroute alignment: logits and route_expert are required
+    cs = config(W.SWITCH_BF16, reroute_depth=2)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_align_reroute, cs, A, None, A, A, A, A, A, A, None, A, 1 << 20, s)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_align_reroute, cs, A, A, None, A, A, A, A, A, None, A, 1 << 20, s)
+    _expect("MOE_ERR_MISALIGNED", M.moe_align_reroute, cs, A, A + 2, A, A, A, A, A, A, None, A, 1 << 20, s)
+    _expect("MOE_ERR_WORKSPACE_TOO_SMALL", M.moe_align_reroute, cs, A, A, A, A, A, A, A, A, None, A, 64, s)
     # route with recorded ids: the flag is known; unknown bits are not
     _expect("MOE_ERR_NULL_POINTER", M.moe_route, cfg, A, A, None, A, None, A, None, M.MOE_ROUTE_IDS_IN, s)
     _expect("MOE_ERR_UNSUPPORTED", M.moe_route, cfg, A, A, None, A, A, A, None, 0x4 | M.MOE_ROUTE_IDS_IN, s)

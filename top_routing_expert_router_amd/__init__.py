@@ -17,7 +17,7 @@ from .build import LIB_PATH
 __all__ = [
     "MoeError", "moe_config", "moe_weights", "moe_trace", "make_config", "lib",
     "moe_abi_version", "moe_status_str", "moe_validate_config", "moe_align_sizes",
-    "moe_workspace_size", "moe_route", "moe_align", "moe_expert_ffn", "moe_expert_gate_up",
+    "moe_workspace_size", "moe_route", "moe_align", "moe_align_reroute", "moe_expert_ffn", "moe_expert_gate_up",
     "moe_expert_down", "moe_combine",
     "moe_forward", "moe_forward_replay", "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_IDS_IN", "MOE_OP_ALIGN", "MOE_OP_FORWARD", "STATUS",
     "DTYPES", "STATS_EXTRA", "STAT",
@@ -31,7 +31,8 @@ MOE_OP_ALIGN, MOE_OP_FORWARD = 1, 2
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL_POINTER", 2: "MOE_ERR_INVALID_CONFIG", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_MISALIGNED", 5: "MOE_ERR_WORKSPACE_TOO_SMALL", 6: "MOE_ERR_HIP"}
 STATS_EXTRA = 8
-STAT = {"kept": 0, "dropped": 1, "invalid": 2, "capacity": 3, "max_load": 4, "min_load": 5, "num_padded": 6}
+STAT = {"kept": 0, "dropped": 1, "invalid": 2, "capacity": 3, "max_load": 4, "min_load": 5, "num_padded": 6,
+        "rerouted": 7}
 
 
 class MoeError(RuntimeError):
@@ -44,7 +45,7 @@ class MoeError(RuntimeError):
 class moe_config(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32)] + [
         (n, ctypes.c_int32) for n in ("T", "H", "N", "k", "I", "B", "cap_num", "cap_den", "n_shared",
-                                      "renormalize", "act_dtype", "expert_dtype", "scale_block")]
+                                      "renormalize", "act_dtype", "expert_dtype", "scale_block", "reroute_depth")]
 
 
 class moe_weights(ctypes.Structure):
@@ -56,7 +57,7 @@ class moe_weights(ctypes.Structure):
 class moe_trace(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "topk_ids", "topk_gates", "margin", "route_kept", "sorted_route_ids", "block_expert",
-        "expert_offsets", "num_padded", "stats", "act", "y_route")]
+        "expert_offsets", "num_padded", "stats", "act", "y_route", "route_expert")]
 
 
 _lib = None
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "moe_workspace_size": ([cfgp, I32, ctypes.POINTER(SZ)], I32),
             "moe_route": ([cfgp, P, P, P, P, P, P, P, U32, P], I32),
             "moe_align": ([cfgp, P, P, P, P, P, P, P, P, SZ, P], I32),
+            "moe_align_reroute": ([cfgp, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_expert_ffn": ([cfgp, P, P, P, P, P, P, P, P, P, P], I32),
             "moe_expert_gate_up": ([cfgp, P, P, P, P, P, P, P], I32),
             "moe_expert_down": ([cfgp, P, P, P, P, P, P, P], I32),
@@ -121,9 +123,9 @@ def _check(fn: str, st: int) -> None:
 
 def make_config(T: int, H: int, N: int, k: int, I: int, B: int, *, cap_num: int = 0, cap_den: int = 0,
                 n_shared: int = 0, renormalize: int = 1, act_dtype: str = "bf16", expert_dtype: str = "bf16",
-                scale_block: int = 0) -> moe_config:
+                scale_block: int = 0, reroute_depth: int = 0) -> moe_config:
     return moe_config(ctypes.sizeof(moe_config), T, H, N, k, I, B, cap_num, cap_den, n_shared, renormalize,
-                      DTYPES[act_dtype], DTYPES[expert_dtype], scale_block)
+                      DTYPES[act_dtype], DTYPES[expert_dtype], scale_block, reroute_depth)
 
 
 def moe_abi_version() -> int:
@@ -207,3 +209,13 @@ def moe_forward_replay(cfg, weights: dict, h, residual, replay_ids, out, trace: 
            lib().moe_forward_replay(ctypes.byref(cfg), ctypes.byref(w), _ptr(h), _ptr(residual), _ptr(replay_ids),
                                     _ptr(out), ctypes.byref(tr) if tr is not None else None, _ptr(ws), nb,
                                     _stream(stream)))
+
+
+def moe_align_reroute(cfg, topk_ids, logits, route_expert, route_kept, sorted_route_ids, block_expert, expert_offsets,
+                      num_padded, stats, ws, ws_bytes: Optional[int] = None, stream=None):
+    """Capacity with the config's overflow policy (reroute_depth) and the alignment of the routes as they run."""
+    nb = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check("moe_align_reroute",
+           lib().moe_align_reroute(ctypes.byref(cfg), _ptr(topk_ids), _ptr(logits), _ptr(route_expert),
+                                   _ptr(route_kept), _ptr(sorted_route_ids), _ptr(block_expert), _ptr(expert_offsets),
+                                   _ptr(num_padded), _ptr(stats), _ptr(ws), nb, _stream(stream)))

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void align_scan(int32_t* __restrict__ cou
                                                        int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ num_padded,
                                                        int32_t* __restrict__ stats, int sentinel,
-                                                       int32_t* __restrict__ zero, int nzero) {
+                                                       int32_t* __restrict__ zero, int nzero, int stats_ready) {
   if ((int)threadIdx.x < nzero) zero[threadIdx.x] = 0;
   __shared__ int wave_tot[4];
   __shared__ int red[4][4];
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void align_scan(int32_t* __restrict__ cou
     offsets[e] = off;
     for (int i = off + kept; i < off + padded; ++i) sorted_ids[i] = sentinel;
     for (int b = off / B; b < (off + padded) / B; ++b) block_expert[b] = e;
-    if (stats) stats[e] = load;
+    if (stats && !stats_ready) stats[e] = load;
   }
   if (e == 0) {
     offsets[N] = total;
@@ -109,28 +109,19 @@ __global__ __launch_bounds__(kThreads) void align_scan(int32_t* __restrict__ cou
       mxx = max(mxx, red[w][1]);
       mnn = min(mnn, red[w][2]);
     }
-    stats[N + MOE_STAT_KEPT] = ks;
-    stats[N + MOE_STAT_DROPPED] = (sentinel - invalid) - ks;  // valid routes not kept
-    stats[N + MOE_STAT_INVALID] = invalid;
-    stats[N + MOE_STAT_CAPACITY] = cap;
-    stats[N + MOE_STAT_MAX_LOAD] = mxx;
-    stats[N + MOE_STAT_MIN_LOAD] = mnn;
     stats[N + MOE_STAT_NUM_PADDED] = total;
-    stats[N + MOE_STAT_RESERVED] = 0;
+    if (!stats_ready) {  // else the reroute pass wrote the rest (its loads are before capacity)
+      stats[N + MOE_STAT_KEPT] = ks;
+      stats[N + MOE_STAT_DROPPED] = (sentinel - invalid) - ks;  // valid routes not kept
+      stats[N + MOE_STAT_INVALID] = invalid;
+      stats[N + MOE_STAT_CAPACITY] = cap;
+      stats[N + MOE_STAT_MAX_LOAD] = mxx;
+      stats[N + MOE_STAT_MIN_LOAD] = mnn;
+      stats[N + MOE_STAT_REROUTED] = 0;
+    }
   }
 }
 
-// Lanes whose keys are equal (keys in [0, 512)).
-__device__ __forceinline__ uint64_t peer_mask(int key) {
-  uint64_t peers = __ballot(1);
-#pragma unroll
-  for (int b = 0; b < 9; ++b) {
-    const bool bit = (key >> b) & 1;
-    const uint64_t bal = __ballot(bit);
-    peers &= bit ? bal : ~bal;
-  }
-  return peers;
-}
 
 __global__ __launch_bounds__(kThreads) void align_scatter(const int32_t* __restrict__ ids, int R, int N, int cap,
                                                           const int32_t* __restrict__ chunk_base,
@@ -199,7 +190,7 @@ size_t align_workspace_bytes(const moe_config& c) {
 
 hipError_t launch_align(const moe_config& c, const int32_t* ids, uint8_t* kept, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* offsets, int32_t* num_padded, int32_t* stats, void* ws,
-                        hipStream_t s, int32_t* zero, int nzero) {
+                        hipStream_t s, int32_t* zero, int nzero, bool stats_ready) {
   const int R = c.T * c.k;
   const int nchunks = ceil_div(R, kChunk);
   const int p_max = R + c.N * (c.B - 1);
@@ -214,7 +205,7 @@ hipError_t launch_align(const moe_config& c, const int32_t* ids, uint8_t* kept, 
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   align_scan<<<1, kThreads, 0, s>>>(counts, nchunks, c.N, c.B, cap, n_blocks, sorted_ids, block_expert, offsets,
-                                    num_padded, stats, R, zero, zero ? nzero : 0);
+                                    num_padded, stats, R, zero, zero ? nzero : 0, stats_ready ? 1 : 0);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   align_scatter<<<nchunks, kThreads, 0, s>>>(ids, R, c.N, cap, counts, offsets, num_padded, p_max, kept, sorted_ids, R);

@@ -25,6 +25,7 @@ moe_status check_config(const moe_config* c) {
   if (!dropless && (c->cap_num <= 0 || c->cap_den <= 0)) return MOE_ERR_INVALID_CONFIG;
   if (c->n_shared != 0 && c->n_shared != 1) return MOE_ERR_INVALID_CONFIG;
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_CONFIG;
+  if (c->reroute_depth < 0 || c->reroute_depth > c->N - c->k) return MOE_ERR_INVALID_CONFIG;
   const bool f32 = c->act_dtype == MOE_F32 && c->expert_dtype == MOE_F32 && c->scale_block == 0;
   const bool bf16 = c->act_dtype == MOE_BF16 && c->expert_dtype == MOE_BF16 && c->scale_block == 0;
   const bool fp8 = c->act_dtype == MOE_BF16 && c->expert_dtype == MOE_FP8_E4M3 && c->scale_block == 128;
@@ -46,8 +47,8 @@ size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Regions of the moe_forward workspace, in order, each 256-byte aligned.
 struct FwdLayout {
-  size_t logits, ids, gates, margin, kept, sorted, blocks, offsets, npad, stats, align_ws, work, act, y, sact, sout,
-      total;
+  size_t logits, ids, gates, margin, kept, rexp, sorted, blocks, offsets, npad, stats, align_ws, work, act, y, sact,
+      sout, total;
 };
 
 FwdLayout forward_layout(const moe_config& c) {
@@ -64,12 +65,13 @@ FwdLayout forward_layout(const moe_config& c) {
   L.gates = take(R * 4);
   L.margin = take(T * 4);
   L.kept = take(R);
+  L.rexp = take(R * 4);
   L.sorted = take(P * 4);
   L.blocks = take(n_blocks_of(c) * 4);
   L.offsets = take((N + 1) * 4);
   L.npad = take(4);
   L.stats = take((N + MOE_STATS_EXTRA) * 4);
-  L.align_ws = take(align_workspace_bytes(c));
+  L.align_ws = take(reroute_workspace_bytes(c) + round_up(align_workspace_bytes(c)));
   L.work = take(4 * kGemmWorkWords * 4);  // tile counters of the 4 expert GEMM launches
   L.act = take(P * (size_t)c.I * a);
   L.y = take(R * (size_t)c.H * a);
@@ -161,8 +163,8 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes) 
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (!bytes) return MOE_ERR_NULL_POINTER;
-  if (op == MOE_OP_ALIGN) {
-    *bytes = round_up(align_workspace_bytes(*cfg));
+  if (op == MOE_OP_ALIGN) {  // moe_align and moe_align_reroute
+    *bytes = reroute_workspace_bytes(*cfg) + round_up(align_workspace_bytes(*cfg));
     return MOE_OK;
   }
   if (op == MOE_OP_FORWARD) {
@@ -197,6 +199,22 @@ moe_status moe_align(const moe_config* cfg, const int32_t* topk_ids, uint8_t* ro
   if (ws_bytes < align_workspace_bytes(*cfg)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   return hip_status(launch_align(*cfg, topk_ids, route_kept, sorted_route_ids, block_expert, expert_offsets,
                                  num_padded, stats, ws, (hipStream_t)stream));
+}
+
+moe_status moe_align_reroute(const moe_config* cfg, const int32_t* topk_ids, const float* logits,
+                             int32_t* route_expert, uint8_t* route_kept, int32_t* sorted_route_ids,
+                             int32_t* block_expert, int32_t* expert_offsets, int32_t* num_padded, int32_t* stats,
+                             void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  st = check_align_args(topk_ids, route_kept, sorted_route_ids, block_expert, expert_offsets, num_padded, stats, ws);
+  if (st != MOE_OK) return st;
+  if (!logits || !route_expert) return MOE_ERR_NULL_POINTER;
+  if (!aligned(logits, 4) || !aligned(route_expert, 4) || !aligned(ws, 256)) return MOE_ERR_MISALIGNED;
+  if (ws_bytes < reroute_workspace_bytes(*cfg) + round_up(align_workspace_bytes(*cfg)))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(launch_align_reroute(*cfg, topk_ids, logits, route_expert, route_kept, sorted_route_ids,
+                                         block_expert, expert_offsets, num_padded, stats, ws, (hipStream_t)stream));
 }
 
 moe_status moe_expert_ffn(const moe_config* cfg, const void* h, const int32_t* sorted_route_ids,
@@ -287,6 +305,9 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* wt, const void
   void* act = pick(tr.act, L.act);
   void* y = pick(tr.y_route, L.y);
   int32_t* work = (int32_t*)(base + L.work);  // zeroed by the alignment scan, used by the GEMMs
+  int32_t* rexp = (int32_t*)pick(tr.route_expert, L.rexp);
+  const bool reroute = c.reroute_depth > 0 && !(c.cap_num == 0 && c.cap_den == 0);
+  if (!aligned(rexp, 4)) return MOE_ERR_MISALIGNED;
   if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4) || !aligned(margin, 4) || !aligned(sorted, 4) ||
       !aligned(blocks, 4) || !aligned(offsets, 4) || !aligned(npad, 4) || !aligned(stats, 4) || !aligned(act, 16) ||
       !aligned(y, 16))
@@ -296,8 +317,10 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* wt, const void
   hipError_t e = launch_router(c, h, wt->w_gate, wt->logit_bias, logits, replay ? nullptr : ids, gates, margin, s,
                                replay);
   if (e == hipSuccess)
-    e = launch_align(c, ids, kept, sorted, blocks, offsets, npad, stats, base + L.align_ws, s, work,
-                     4 * kGemmWorkWords);
+    e = reroute ? launch_align_reroute(c, ids, logits, rexp, kept, sorted, blocks, offsets, npad, stats,
+                                       base + L.align_ws, s, work, 4 * kGemmWorkWords)
+                : launch_align(c, ids, kept, sorted, blocks, offsets, npad, stats,
+                               base + L.align_ws + reroute_workspace_bytes(c), s, work, 4 * kGemmWorkWords);
   if (e == hipSuccess)
     e = launch_expert_ffn(c, h, sorted, offsets, wt->w13, wt->w2, wt->w13_scale, wt->w2_scale, act, y, false, s,
                           work);

@@ -47,6 +47,18 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Lanes of this wave holding the same key (0..511) as this lane, from 9 ballots.
+__device__ __forceinline__ uint64_t peer_mask(int key) {
+  uint64_t peers = __ballot(1);
+#pragma unroll
+  for (int b = 0; b < 9; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    peers &= bit ? bal : ~bal;
+  }
+  return peers;
+}
+
 // Ranking key of (logit, expert): larger = ranked higher; ties go to the lower
 // expert index.  0 is reserved for "already taken / no expert".
 __device__ __forceinline__ uint64_t rank_key(float logit, int e) {

@@ -23,9 +23,23 @@ int align_chunk_routes();                       // routes per alignment chunk
 size_t align_workspace_bytes(const moe_config& c);
 // zero / nzero (nullable): words the scan kernel also sets to 0 (the GEMMs' work
 // counters in the forward workspace), so no separate fill launch is needed
+// stats_ready: the stats other than the padded row count were written already
+// (by the reroute pass) and are left alone.
 hipError_t launch_align(const moe_config& c, const int32_t* ids, uint8_t* kept, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* offsets, int32_t* num_padded, int32_t* stats,
-                        void* ws, hipStream_t s, int32_t* zero = nullptr, int nzero = 0);
+                        void* ws, hipStream_t s, int32_t* zero = nullptr, int nzero = 0, bool stats_ready = false);
+
+// ---- reroute overflow policy (reroute.hip)
+// Workspace bytes of the reroute pass (besides the alignment's own).
+size_t reroute_workspace_bytes(const moe_config& c);
+// Capacity with rerouting, then the alignment of the routes as rerouted:
+// route_expert [T*k] out = the expert each route runs (-1: none); logits [T, N]
+// give each token's ranking for its candidates.  cap from the config (dropless:
+// every valid route runs its own expert).
+hipError_t launch_align_reroute(const moe_config& c, const int32_t* ids, const float* logits, int32_t* route_expert,
+                                uint8_t* kept, int32_t* sorted_ids, int32_t* block_expert, int32_t* offsets,
+                                int32_t* num_padded, int32_t* stats, void* ws, hipStream_t s,
+                                int32_t* zero = nullptr, int nzero = 0);
 
 // ---- expert FFN (ffn.hip)
 // identity == true: one expert over T token rows (shared expert), offsets ignored.

@@ -1,0 +1,195 @@
+// Capacity with the reroute overflow policy.
+//
+// "Mixture-of-Experts Routing at Inference Time", "The hard part", Figure 2: a
+// token routed to an expert that is at capacity is either dropped or rerouted --
+// sent to its second-choice expert -- and the mitigation paragraph after the
+// routing-stats probe: change the overflow policy from drop to reroute.
+//
+// Policy (rounds; the config's reroute_depth is the number of rounds):
+//  1. the drop policy fills capacity in ascending route id (a route runs its expert
+//     iff fewer than cap earlier routes chose that expert);
+//  2. per round, every token with an overflowed route offers its lowest such route
+//     one new candidate: the next expert in the token's ranking of its logits
+//     (value descending, lower index first, NaN last, -0 == +0) that is not among
+//     its recorded ids and was not offered before.  Requests to an expert are
+//     admitted in token order while it has room left.  An admitted route runs the
+//     candidate with its original gate.
+// Depth 1 is the literal "second choice"; depth N - k walks the whole ranking.
+//
+// One workgroup does it all: the decisions chain through the remaining capacity,
+// round after round.  Every position in token or route order is a prefix count --
+// ballot peer masks inside a wave, waves added in order -- so no atomic decides an
+// order; LDS atomics only add up totals.  The alignment proper then runs on the
+// experts the routes ended up with (dropless: every route with an expert runs it).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRThreads = 1024;
+constexpr int kRWaves = kRThreads / kWave;
+
+// Position of this lane's key (0..N-1; -1 = none) among the keys of this chunk of
+// kRThreads entries that come before it in chunk order, plus base[key]; afterwards
+// base[key] has grown by the chunk's count of that key.  Called by every thread.
+__device__ int chunk_position(int key, int N, int* base, int (*cnt)[256]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int i = tid; i < kRWaves * 256; i += kRThreads) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  const bool valid = key >= 0;
+  const uint64_t peers = peer_mask(valid ? key : 256);
+  if (valid && (peers & lt) == 0) cnt[wave][key] = __popcll(peers);  // one writer per (wave, key)
+  __syncthreads();
+  for (int e = tid; e < N; e += kRThreads) {
+    int acc = base[e];
+    for (int w = 0; w < kRWaves; ++w) {
+      const int c = cnt[w][e];
+      cnt[w][e] = acc;
+      acc += c;
+    }
+    base[e] = acc;
+  }
+  __syncthreads();
+  const int pos = valid ? cnt[wave][key] + __popcll(peers & lt) : -1;
+  __syncthreads();
+  return pos;
+}
+
+__global__ __launch_bounds__(kRThreads) void reroute_capacity(const int32_t* __restrict__ ids,
+                                                              const float* __restrict__ logits, int T, int N,
+                                                              int k, int cap, int depth,
+                                                              int32_t* __restrict__ route_expert,
+                                                              uint64_t* __restrict__ offered,
+                                                              int32_t* __restrict__ stats) {
+  __shared__ int base[256], room[256];
+  __shared__ int cnt[kRWaves][256];
+  __shared__ int sh_any, sh_kept, sh_rer, sh_invalid, sh_max, sh_min;
+  const int tid = threadIdx.x;
+  const int R = T * k;
+  for (int e = tid; e < N; e += kRThreads) base[e] = 0;
+  if (tid == 0) {
+    sh_kept = 0;
+    sh_rer = 0;
+    sh_invalid = 0;
+    sh_max = 0;
+    sh_min = 0x7fffffff;
+  }
+  __syncthreads();
+
+  // 1. drop-policy fill in route-id order
+  for (int r0 = 0; r0 < R; r0 += kRThreads) {
+    const int r = r0 + tid;
+    const int e = r < R ? ids[r] : -1;
+    const bool valid = e >= 0 && e < N;
+    const int pos = chunk_position(valid ? e : -1, N, base, cnt);
+    if (r < R) route_expert[r] = (valid && (cap < 0 || pos < cap)) ? e : -1;
+  }
+  // base[e] is now expert e's routed load (before capacity)
+  for (int e = tid; e < N; e += kRThreads) {
+    room[e] = cap < 0 ? 0 : cap - min(base[e], cap);
+    atomicMax(&sh_max, base[e]);
+    atomicMin(&sh_min, base[e]);
+    if (stats) stats[e] = base[e];
+  }
+  for (int t = tid; t < T; t += kRThreads) offered[t] = ~0ull;  // nothing offered yet
+  __syncthreads();
+
+  // 2. rounds
+  for (int round = 0; cap >= 0 && round < depth; ++round) {
+    for (int e = tid; e < N; e += kRThreads) base[e] = 0;
+    if (tid == 0) sh_any = 0;
+    __syncthreads();
+    for (int t0 = 0; t0 < T; t0 += kRThreads) {
+      const int t = t0 + tid;
+      int want = -1, route = -1;
+      if (t < T) {
+        const int32_t* tid_ids = ids + (size_t)t * k;
+        for (int j = 0; j < k; ++j) {
+          const int e = tid_ids[j];
+          if (e >= 0 && e < N && route_expert[t * k + j] < 0) {
+            route = t * k + j;
+            break;
+          }
+        }
+        if (route >= 0) {
+          const uint64_t last = offered[t];
+          uint64_t best = 0;
+          const float* lt = logits + (size_t)t * N;
+          for (int e = 0; e < N; ++e) {
+            bool mine = false;
+            for (int j = 0; j < k; ++j) mine |= tid_ids[j] == e;
+            const uint64_t key = rank_key(lt[e], e);
+            if (!mine && key < last && key > best) {
+              best = key;
+              want = e;
+            }
+          }
+          if (want >= 0) offered[t] = best;
+        }
+      }
+      const int pos = chunk_position(want, N, base, cnt);
+      if (want >= 0) {
+        sh_any = 1;
+        if (pos < room[want]) route_expert[route] = want;
+      }
+    }
+    __syncthreads();
+    // base[e] = requests to e this round; the first room[e] of them were admitted
+    for (int e = tid; e < N; e += kRThreads) room[e] -= min(base[e], room[e]);
+    const int any = sh_any;
+    __syncthreads();
+    if (!any) break;
+  }
+
+  // 3. totals
+  int kept = 0, rer = 0, invalid = 0;
+  for (int r = tid; r < R; r += kRThreads) {
+    const int e = ids[r], x = route_expert[r];
+    invalid += (e < 0 || e >= N) ? 1 : 0;
+    kept += x >= 0 ? 1 : 0;
+    rer += (x >= 0 && x != e) ? 1 : 0;
+  }
+  atomicAdd(&sh_kept, kept);
+  atomicAdd(&sh_rer, rer);
+  atomicAdd(&sh_invalid, invalid);
+  __syncthreads();
+  if (stats && tid == 0) {
+    stats[N + MOE_STAT_KEPT] = sh_kept;
+    stats[N + MOE_STAT_DROPPED] = (R - sh_invalid) - sh_kept;
+    stats[N + MOE_STAT_INVALID] = sh_invalid;
+    stats[N + MOE_STAT_CAPACITY] = cap;
+    stats[N + MOE_STAT_MAX_LOAD] = sh_max;
+    stats[N + MOE_STAT_MIN_LOAD] = sh_min;
+    stats[N + MOE_STAT_REROUTED] = sh_rer;
+  }
+}
+
+}  // namespace
+
+size_t reroute_workspace_bytes(const moe_config& c) { return ((size_t)c.T * 8 + 255) & ~(size_t)255; }
+
+hipError_t launch_align_reroute(const moe_config& c, const int32_t* ids, const float* logits, int32_t* route_expert,
+                                uint8_t* kept, int32_t* sorted_ids, int32_t* block_expert, int32_t* offsets,
+                                int32_t* num_padded, int32_t* stats, void* ws, hipStream_t s, int32_t* zero,
+                                int nzero) {
+  int cap = -1;
+  if (!(c.cap_num == 0 && c.cap_den == 0)) {
+    const long long cl = ((long long)c.T * c.k * c.cap_num) / ((long long)c.N * c.cap_den);
+    cap = cl > 0x7fffffffLL ? 0x7fffffff : (int)cl;
+  }
+  uint64_t* offered = (uint64_t*)ws;
+  reroute_capacity<<<1, kRThreads, 0, s>>>(ids, logits, c.T, c.N, c.k, cap, c.reroute_depth, route_expert, offered,
+                                           stats);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // the alignment of the routes as they run: dropless on route_expert
+  moe_config d = c;
+  d.cap_num = 0;
+  d.cap_den = 0;
+  return launch_align(d, route_expert, kept, sorted_ids, block_expert, offsets, num_padded, stats,
+                      (char*)ws + reroute_workspace_bytes(c), s, zero, nzero, true);
+}
+
+}  // namespace moe

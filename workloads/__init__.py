@@ -44,6 +44,7 @@ class Workload:
     n_shared: int = 0
     renormalize: int = 1
     scale_block: int = 0       # fp8 block scale size (128) or 0
+    reroute_depth: int = 0     # overflow policy under capacity: 0 drop, d > 0 reroute rounds
     zipf_s: float = 0.0        # additive per-expert logit bias -s*ln(e+1)
     near_tie_frac: float = 0.0 # fraction of tokens given a k-th/(k+1)-th margin < 1e-3
     seed: int = 0
@@ -73,7 +74,9 @@ QWEN3MOE_BF16 = Workload("qwen3moe_bf16", T=8192, H=2048, N=128, k=8, I=768, B=1
 DEEPSEEKV3_FP8 = Workload("deepseekv3_fp8", T=16384, H=7168, N=256, k=8, I=2048, B=64,
                           act_dtype=BF16, expert_dtype=FP8, n_shared=1, scale_block=128)
 
-ALL = {w.name: w for w in (TOY_FP32, SWITCH_BF16, MIXTRAL_BF16, QWEN3MOE_BF16, DEEPSEEKV3_FP8)}
+# the capacity workload with the reroute overflow policy walking each token's whole ranking
+SWITCH_REROUTE_BF16 = SWITCH_BF16.with_(name="switch_reroute_bf16", reroute_depth=15)
+ALL = {w.name: w for w in (TOY_FP32, SWITCH_BF16, SWITCH_REROUTE_BF16, MIXTRAL_BF16, QWEN3MOE_BF16, DEEPSEEKV3_FP8)}
 
 
 def _stream_seed(seed: int, name: str, index: int = 0) -> int:
