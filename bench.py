@@ -374,6 +374,8 @@ def cpu_baseline(w, d, sample: int):
     h_b, wg_b = bits(d["h"]), bits(d["w_gate"])
     w13_b = d["w13"].to("cpu")
     w2_b = d["w2"].to("cpu")
+    import workloads as W
+
     fp8 = w.expert_dtype == W.FP8
     if fp8:
         s13 = d["w13_scale"].float().cpu().double().numpy()
