@@ -36,7 +36,7 @@ constexpr int kRWaves = kRThreads / kWave;
 __device__ int chunk_position(int key, int N, int* base, int (*cnt)[256]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t lt = (1ull << lane) - 1ull;
-  for (int i = tid; i < kRWaves * 256; i += kRThreads) (&cnt[0][0])[i] = 0;
+  for (int i = tid; i < kRWaves * N; i += kRThreads) cnt[i / N][i % N] = 0;
   __syncthreads();
   const bool valid = key >= 0;
   const uint64_t peers = peer_mask(valid ? key : 256);
@@ -117,14 +117,31 @@ __global__ __launch_bounds__(kRThreads) void reroute_capacity(const int32_t* __r
           const uint64_t last = offered[t];
           uint64_t best = 0;
           const float* lt = logits + (size_t)t * N;
-          for (int e = 0; e < N; ++e) {
+          int own[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) own[j] = j < k ? tid_ids[j] : -1;
+          // the next candidate: the largest key below the last one offered, among the
+          // experts that are not the token's own (4 logits per load when N allows)
+          auto consider = [&](float v, int e) {
             bool mine = false;
-            for (int j = 0; j < k; ++j) mine |= tid_ids[j] == e;
-            const uint64_t key = rank_key(lt[e], e);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mine |= own[j] == e;
+            const uint64_t key = rank_key(v, e);
             if (!mine && key < last && key > best) {
               best = key;
               want = e;
             }
+          };
+          if ((N & 3) == 0 && ((uintptr_t)logits & 15) == 0) {
+            for (int e = 0; e < N; e += 4) {
+              const float4 v = *reinterpret_cast<const float4*>(lt + e);
+              consider(v.x, e);
+              consider(v.y, e + 1);
+              consider(v.z, e + 2);
+              consider(v.w, e + 3);
+            }
+          } else {
+            for (int e = 0; e < N; ++e) consider(lt[e], e);
           }
           if (want >= 0) offered[t] = best;
         }
