@@ -1,4 +1,8 @@
-"""CPU oracle for the token-choice MoE layer forward pass -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the MoE layer forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Token-choice routing (each token picks its top-k experts) with the drop and reroute
+overflow policies and router replay, and expert-choice routing (each expert picks its
+top-C tokens).
 
 Only the tests, the smoke entry point and the CPU-baseline leg of the benchmark
 may import this module.  The product path (the HIP library and its Python
@@ -30,7 +34,8 @@ import numpy as np
 __all__ = [
     "decode_bf16", "decode_e4m3", "round_bf16", "dequantize_blocks", "router_logits", "rank_experts",
     "topk_route", "replay_route", "capacity", "capacity_keep", "capacity_reroute", "align", "silu", "swiglu_expert",
-    "expert_ffn", "combine", "routing_stats", "moe_forward",
+    "expert_ffn", "combine", "routing_stats", "moe_forward", "expert_scores", "expert_choice_capacity",
+    "expert_choice_select", "expert_choice_align", "expert_choice_combine", "expert_choice_forward",
 ]
 
 
@@ -436,3 +441,144 @@ def moe_forward(h, w_gate, w13_of, w2_of, *, k: int, B: int, cap_num: int = 0, c
     return {"logits": l, "ids": ids, "gates": gates, "margin": margin, "cap": cap, "kept": kept,
             "run_ids": run_ids, "rerouted": rerouted, "align": al, "y_route": y, "shared": shared, "out": out,
             "tokens": rows, "stats": stats}
+
+
+# ---------------------------------------------------------------- expert-choice routing
+#
+# [R&R] paragraph on expert-choice routing: the assignment is turned around, and each
+# expert takes its highest-scoring tokens out of the whole batch.  [MIR] "Integration:
+# where routing lives in a serving stack", paragraph on expert-choice routing (among the
+# routing variants): each expert picks its tokens up to its capacity, so no expert
+# overflows, and a token may be picked by no expert at all.
+
+def expert_scores(logits: np.ndarray) -> np.ndarray:
+    """Token-to-expert scores [T, N]: per token, the softmax over its N logits.
+
+    READING: the score an expert ranks tokens by is the router's softmax probability
+    ([MIR] "How sparse routing works" and the worked router: logits, then softmax over
+    the experts).  A NaN logit weighs zero, as in topk_route.
+    """
+    l = np.asarray(logits, np.float64)
+    lw = np.where(np.isnan(l), -np.inf, l)
+    lmax = np.max(lw, axis=1, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = np.exp(lw - lmax)
+        return p / p.sum(axis=1, keepdims=True)
+
+
+def expert_choice_capacity(T: int, k: int, N: int, cap_num: int, cap_den: int) -> int:
+    """Tokens each expert takes: C = min(floor(T*k*cf / N), T), cf = cap_num / cap_den.
+
+    READING: the capacity formula of the token-choice layer ([R&R] capacity paragraph,
+    [MIR] worked example), with k read as the average number of experts per token; an
+    unset factor (0/0) means cf = 1, where expert choice runs as many expert rows as
+    token-choice top-k.  An expert cannot take a token twice, so C <= T.
+    """
+    if cap_num == 0 and cap_den == 0:
+        cap_num, cap_den = 1, 1
+    return min((T * k * cap_num) // (N * cap_den), T)
+
+
+def expert_choice_select(scores: np.ndarray, C: int):
+    """Each expert's C highest-scoring tokens.
+
+    Returns (tokens [N, C] int64: expert e's picks in ascending token order;
+    slot [T, N] int64: position of token t in expert e's list, -1 if not picked;
+    margin [N] float64: C-th highest score minus the (C+1)-th, +inf when C = 0 or C = T).
+    READING: tokens are ranked by score descending, equal scores to the lower token
+    index, a NaN score below every number (the token-choice tie rule applied to tokens).
+    """
+    S = np.asarray(scores, np.float64) + 0.0
+    T, N = S.shape
+    tokens = np.zeros((N, C), np.int64)
+    slot = np.full((T, N), -1, np.int64)
+    margin = np.full(N, np.inf)
+    for e in range(N):
+        # stable ascending sort of -score: highest first, equal scores in token order, NaN last
+        order = np.argsort(-S[:, e], kind="stable")
+        picked = np.sort(order[:C])
+        tokens[e] = picked
+        slot[picked, e] = np.arange(C)
+        if 0 < C < T:
+            margin[e] = S[order[C - 1], e] - S[order[C], e]
+    return tokens, slot, margin
+
+
+def expert_choice_align(tokens: np.ndarray, T: int, B: int) -> dict:
+    """Expert e's picks as one segment of whole B-row blocks, experts in ascending order.
+
+    Every expert has C picks, so segment e starts at e * Cp, Cp = ceil(C / B) * B, and
+    holds the picked token ids ascending, then the sentinel T ([RB] "The bookkeeping
+    before the matrix multiplication": expert-homogeneous padded blocks).
+    """
+    tokens = np.asarray(tokens, np.int64)
+    N, C = tokens.shape
+    Cp = -(-C // B) * B
+    sorted_tokens = np.full(N * Cp, T, np.int64)
+    for e in range(N):
+        sorted_tokens[e * Cp:e * Cp + C] = tokens[e]
+    return {"sorted_tokens": sorted_tokens, "block_expert": np.repeat(np.arange(N), Cp // B),
+            "expert_offsets": np.arange(N + 1) * Cp, "num_padded": N * Cp, "segment": Cp}
+
+
+def expert_choice_combine(y: dict, scores: np.ndarray, slot: np.ndarray, H: int,
+                          shared: Optional[np.ndarray] = None, residual: Optional[np.ndarray] = None,
+                          tokens: Optional[np.ndarray] = None) -> np.ndarray:
+    """out[t] = residual[t] + shared[t] + sum over the experts e that picked t of score[t, e] * y_(t,e).
+
+    READING: the gate of a pick is the token's score for that expert, not renormalised
+    (a token's set of experts has no fixed size); a token no expert picked outputs its
+    residual alone, like a fully dropped token ([MIR] "The hard part", drop branch).
+    ``y`` maps (t, e) -> expert e's output row for token t.
+    """
+    S = np.asarray(scores, np.float64)
+    T, N = S.shape
+    rows = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    out = np.zeros((rows.shape[0], H), np.float64)
+    for i, t in enumerate(rows.tolist()):
+        acc = np.zeros(H, np.float64)
+        for e in range(N):
+            if slot[t, e] >= 0:
+                acc = acc + S[t, e] * y[(t, e)]
+        if shared is not None:
+            acc = acc + shared[i]
+        if residual is not None:
+            acc = acc + np.asarray(residual[t], np.float64)
+        out[i] = acc
+    return out
+
+
+def expert_choice_forward(h, w_gate, w13_of, w2_of, *, k: int, B: int, cap_num: int = 0, cap_den: int = 0,
+                          bias=None, residual=None, shared_w13=None, shared_w2=None, logits=None, scores=None,
+                          tokens=None) -> dict:
+    """The layer with expert-choice routing, all in float64.
+
+    logits ([MIR] "How sparse routing works") -> scores -> each expert's top-C tokens
+    -> padded segments -> SwiGLU expert FFN per pick -> score-weighted combine.
+    ``logits`` / ``scores`` (if given) replace the projection / the softmax, for
+    routing from stored values.  ``tokens`` restricts the FFN and combine to a sample.
+    """
+    h = np.asarray(h, np.float64)
+    T, H = h.shape
+    l = router_logits(h, w_gate, bias) if logits is None and scores is None else (
+        None if logits is None else np.asarray(logits, np.float64))
+    S = expert_scores(l) if scores is None else np.asarray(scores, np.float64)
+    N = S.shape[1]
+    C = expert_choice_capacity(T, k, N, cap_num, cap_den)
+    picks, slot, margin = expert_choice_select(S, C)
+    al = expert_choice_align(picks, T, B)
+    rows = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    y = {}
+    for e in range(N):
+        ts = [t for t in rows.tolist() if slot[t, e] >= 0]
+        if ts:
+            ye = swiglu_expert(h[ts], w13_of(e), w2_of(e))
+            for t, row in zip(ts, ye):
+                y[(t, e)] = row
+    shared = swiglu_expert(h[rows], shared_w13, shared_w2) if shared_w13 is not None else None
+    out = expert_choice_combine(y, S, slot, H, shared=shared, residual=residual, tokens=rows)
+    picks_per_token = np.count_nonzero(slot >= 0, axis=1)
+    stats = {"capacity": C, "picks": N * C, "unpicked_tokens": int(np.count_nonzero(picks_per_token == 0)),
+             "max_picks": int(picks_per_token.max()) if T else 0}
+    return {"logits": l, "scores": S, "cap": C, "tokens": picks, "slot": slot, "margin": margin, "align": al,
+            "y": y, "shared": shared, "out": out, "rows": rows, "stats": stats}

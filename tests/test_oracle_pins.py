@@ -645,3 +645,159 @@ def test_forward_reroute_runs_the_new_expert_with_the_old_gate():
             assert np.allclose(rr["out"][t], h[t] + O.swiglu_expert(h[t:t + 1], w13[c], w2[c])[0], rtol=1e-13)
         elif drop["kept"][t]:
             assert np.array_equal(rr["out"][t], drop["out"][t])
+
+
+# ------------------------------------------------------------------ expert-choice routing
+
+def test_golden_expert_choice():
+    d, _ = _read_fixture("expert_choice_T6_N3.txt")
+    T, N, k = int(d["T"]), int(d["N"]), int(d["k"])
+    S = _floats(d["scores"]).reshape(T, N)
+    assert O.expert_choice_capacity(T, k, N, 1, 1) == int(d["C_cf1"])
+    assert O.expert_choice_capacity(T, k, N, 0, 0) == int(d["C_cf1"])  # unset factor = 1
+    assert O.expert_choice_capacity(T, k, N, 3, 2) == int(d["C_cf3_2"])
+    for C in (2, 3):
+        tokens, slot, margin = O.expert_choice_select(S, C)
+        assert tokens.reshape(-1).tolist() == _ints(d[f"picks_C{C}"]).tolist()
+        assert margin.tolist() == _floats(d[f"margin_C{C}"]).tolist()
+        assert np.count_nonzero(slot >= 0, axis=1).tolist() == _ints(d[f"picks_per_token_C{C}"]).tolist()
+        for e in range(N):
+            assert [slot[t, e] for t in tokens[e]] == list(range(C))
+
+
+def _beats(sa, a, sb, b):
+    """(score sa, token a) ranks above (score sb, token b): larger score, then lower index; NaN last."""
+    na, nb = math.isnan(sa), math.isnan(sb)
+    if na or nb:
+        return (a < b) if (na and nb) else nb
+    return sa > sb or (sa == sb and a < b)
+
+
+def test_expert_choice_select_brute_force():
+    # every C-subset of tokens: exactly one dominates all the others under the order
+    # (score desc, lower token first, NaN last), and it is the oracle's pick
+    rng = np.random.default_rng(21)
+    for trial in range(150):
+        T, N = int(rng.integers(1, 7)), int(rng.integers(1, 4))
+        S = rng.choice(np.array([0.0, 0.25, 0.5, -0.0, np.nan]) if trial % 5 == 0 else np.array([0.1, 0.2, 0.7]),
+                       size=(T, N))
+        for C in range(0, T + 1):
+            tokens, slot, margin = O.expert_choice_select(S, C)
+            for e in range(N):
+                good = [set(P) for P in itertools.combinations(range(T), C)
+                        if all(_beats(S[p, e], p, S[q, e], q) for p in P for q in range(T) if q not in P)]
+                assert len(good) == 1 and set(tokens[e].tolist()) == good[0]
+                assert tokens[e].tolist() == sorted(tokens[e].tolist())
+                assert [t for t in range(T) if slot[t, e] >= 0] == tokens[e].tolist()
+                if 0 < C < T:
+                    vals = sorted(S[:, e], key=lambda v: (not math.isnan(v), v), reverse=True)
+                    assert (np.isnan(margin[e]) and (math.isnan(vals[C - 1]) or math.isnan(vals[C]))) or \
+                        margin[e] == vals[C - 1] - vals[C]
+                else:
+                    assert margin[e] == np.inf
+
+
+def test_expert_choice_select_matches_torch_topk_on_distinct_scores():
+    g = torch.Generator().manual_seed(4)
+    for T, N, C in ((50, 4, 7), (300, 16, 60), (1000, 8, 250)):
+        S = torch.rand(T, N, generator=g, dtype=torch.float64)
+        tokens, _, margin = O.expert_choice_select(S.numpy(), C)
+        vals, idx = torch.topk(S, C + 1, dim=0)
+        for e in range(N):
+            assert sorted(idx[:C, e].tolist()) == tokens[e].tolist()
+            assert margin[e] == (vals[C - 1, e] - vals[C, e]).item()
+
+
+def test_expert_scores_closed_forms_and_softmax():
+    # logits ln(w) -> scores w / sum(w); NaN weighs zero; rows sum to one; torch's softmax
+    w = np.array([[1.0, 1.0, 2.0], [6.0, 1.0, 1.0], [1.0, 3.0, 4.0]])
+    S = O.expert_scores(np.log(w))
+    assert np.allclose(S, w / w.sum(axis=1, keepdims=True), rtol=1e-15, atol=0)
+    l = np.array([[0.0, np.nan, np.log(3.0)]])
+    assert np.allclose(O.expert_scores(l), [[0.25, 0.0, 0.75]], rtol=1e-15, atol=0)
+    rng = np.random.default_rng(2)
+    l = rng.standard_normal((200, 37)) * 3
+    S = O.expert_scores(l)
+    assert np.allclose(S.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    assert np.allclose(S, torch.softmax(torch.from_numpy(l), dim=1).numpy(), rtol=1e-14, atol=0)
+    # the scores of a token's top-k experts are its token-choice gates without renormalisation
+    ids, gates, _ = O.topk_route(l, 5, renormalize=False)
+    assert np.array_equal(np.take_along_axis(S, ids, axis=1), gates)
+
+
+def test_expert_choice_capacity_formula():
+    assert O.expert_choice_capacity(4096, 2, 8, 0, 0) == 1024      # Mixtral-shaped, factor 1
+    assert O.expert_choice_capacity(2048, 1, 16, 5, 4) == 160      # the Switch capacity, factor 1.25
+    assert O.expert_choice_capacity(5, 1, 8, 1, 1) == 0            # fewer tokens than experts
+    assert O.expert_choice_capacity(10, 2, 4, 4, 2) == 10          # factor N/k: every expert takes every token
+    assert O.expert_choice_capacity(10, 2, 4, 9, 1) == 10          # never more than T
+
+
+def test_expert_choice_align_invariants():
+    rng = np.random.default_rng(5)
+    for T, N, C, B in ((9, 3, 4, 2), (40, 5, 13, 8), (7, 2, 7, 16), (6, 4, 0, 8)):
+        S = rng.random((T, N))
+        tokens, _, _ = O.expert_choice_select(S, C)
+        al = O.expert_choice_align(tokens, T, B)
+        Cp = -(-C // B) * B
+        assert al["segment"] == Cp and al["num_padded"] == N * Cp
+        assert al["expert_offsets"].tolist() == [e * Cp for e in range(N + 1)]
+        assert al["block_expert"].tolist() == [b // (Cp // B) for b in range(N * Cp // B)] if Cp else \
+            al["block_expert"].size == 0
+        for e in range(N):
+            seg = al["sorted_tokens"][e * Cp:(e + 1) * Cp]
+            assert seg[:C].tolist() == tokens[e].tolist() and np.all(seg[C:] == T)
+
+
+def _ec_layer(seed, T, H, I, N):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((T, H))
+    wg = rng.standard_normal((N, H)) * 0.3
+    w13 = rng.standard_normal((N, 2 * I, H)) / math.sqrt(H)
+    w2 = rng.standard_normal((N, H, I)) / math.sqrt(I)
+    return h, wg, w13, w2
+
+
+def test_expert_choice_with_every_token_is_the_dense_soft_mixture():
+    # C = T (factor N/k): every expert takes every token with weight softmax_e -- the same
+    # layer as token choice with k = N and no renormalisation (a different, pinned path)
+    T, H, I, N, k = 9, 8, 12, 4, 2
+    h, wg, w13, w2 = _ec_layer(1, T, H, I, N)
+    ec = O.expert_choice_forward(h, wg, lambda e: w13[e], lambda e: w2[e], k=k, B=4, cap_num=N, cap_den=k,
+                                 residual=h)
+    assert ec["cap"] == T and ec["stats"]["unpicked_tokens"] == 0 and ec["stats"]["max_picks"] == N
+    tc = O.moe_forward(h, wg, lambda e: w13[e], lambda e: w2[e], k=N, B=4, renormalize=False, residual=h)
+    assert np.allclose(ec["out"], tc["out"], rtol=1e-12, atol=1e-12)
+
+
+def test_expert_choice_single_expert_is_a_plain_swiglu_ffn():
+    T, H, I = 7, 8, 12
+    h, wg, w13, w2 = _ec_layer(2, T, H, I, 1)
+    ec = O.expert_choice_forward(h, wg, lambda e: w13[e], lambda e: w2[e], k=1, B=4, residual=h)
+    assert ec["cap"] == T and np.all(ec["scores"] == 1.0)
+    x = torch.from_numpy(h)
+    ref = x + F.linear(F.silu(F.linear(x, torch.from_numpy(w13[0, :I]))) * F.linear(x, torch.from_numpy(w13[0, I:])),
+                       torch.from_numpy(w2[0]))
+    assert np.allclose(ec["out"], ref.numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_expert_choice_forward_picks_and_unpicked_tokens():
+    T, H, I, N, k = 16, 8, 12, 4, 1
+    h, wg, w13, w2 = _ec_layer(3, T, H, I, N)
+    ec = O.expert_choice_forward(h, wg, lambda e: w13[e], lambda e: w2[e], k=k, B=2, residual=h)
+    C = ec["cap"]
+    assert C == 4
+    picks = np.count_nonzero(ec["slot"] >= 0, axis=1)
+    assert ec["stats"]["unpicked_tokens"] == np.count_nonzero(picks == 0) > 0
+    assert picks.sum() == N * C
+    for t in range(T):
+        want = h[t].copy()
+        for e in range(N):
+            if ec["slot"][t, e] >= 0:
+                want = want + ec["scores"][t, e] * O.swiglu_expert(h[t:t + 1], w13[e], w2[e])[0]
+        if picks[t] == 0:
+            assert np.array_equal(ec["out"][t], h[t])       # the dual failure: h alone
+        assert np.allclose(ec["out"][t], want, rtol=1e-13, atol=1e-13)
+    # a sample of rows gives the same rows (up to the matrix product's blocking)
+    sub = O.expert_choice_forward(h, wg, lambda e: w13[e], lambda e: w2[e], k=k, B=2, residual=h, tokens=[3, 0, 11])
+    assert np.allclose(sub["out"], ec["out"][[3, 0, 11]], rtol=1e-14, atol=1e-14)
