@@ -1,6 +1,7 @@
 /*
- * moe.h -- C ABI of libmoe_mi355x.so: the token-choice Mixture-of-Experts layer
- * forward pass on AMD Instinct MI355X (gfx950).
+ * moe.h -- C ABI of libmoe_mi355x.so: the Mixture-of-Experts layer forward pass on
+ * AMD Instinct MI355X (gfx950), with token-choice routing (below) or expert-choice
+ * routing (moe_route_expert_choice and its companions, further down).
  *
  * Per token the layer computes (pages cited by title and section):
  *   1. router logits  l = h . W_g^T (+ optional per-expert bias)
@@ -59,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef int32_t moe_status;
 enum {
@@ -81,6 +82,12 @@ enum {
   MOE_ROUTE_IDS_IN = 2u     /* router replay: `topk_ids` is an input (recorded expert ids) */
 };
 
+/* moe_config.routing */
+enum {
+  MOE_ROUTING_TOKEN_CHOICE = 0, /* each token picks its top-k experts */
+  MOE_ROUTING_EXPERT_CHOICE = 1 /* each expert picks its top-C tokens */
+};
+
 /* moe_workspace_size operations */
 enum { MOE_OP_ALIGN = 1, MOE_OP_FORWARD = 2 };
 
@@ -94,7 +101,9 @@ enum {
   MOE_STAT_MIN_LOAD = 5,  /* min over experts of routed load */
   MOE_STAT_NUM_PADDED = 6,/* padded rows used (same as *num_padded) */
   MOE_STAT_REROUTED = 7,  /* routes kept by rerouting to another expert (reroute policy) */
-  MOE_STATS_EXTRA = 8
+  MOE_STAT_UNPICKED = 8,  /* expert choice: tokens that no expert picked (0 for token choice) */
+  MOE_STAT_MAX_PICKS = 9, /* expert choice: most experts that picked one token (0 for token choice) */
+  MOE_STATS_EXTRA = 10
 };
 
 /*
@@ -117,6 +126,9 @@ enum {
  *           route the next expert of its own ranking not among its ids and not offered
  *           before; requests are admitted in token order while the expert has room.  The
  *           route keeps its gate.  d = 1 is the "second choice"; see moe_align_reroute.
+ *   routing: MOE_ROUTING_TOKEN_CHOICE, or MOE_ROUTING_EXPERT_CHOICE (needs
+ *           reroute_depth 0; see moe_route_expert_choice for what k and the capacity
+ *           factor mean there, and which entry points apply).
  * act_dtype is the type of h, residual, out, W_g, act and y_route.
  */
 typedef struct moe_config {
@@ -129,6 +141,7 @@ typedef struct moe_config {
   int32_t expert_dtype;
   int32_t scale_block;  /* 128 for fp8 experts, else 0 */
   int32_t reroute_depth; /* 0 = drop overflow; > 0 = reroute rounds (see above) */
+  int32_t routing;       /* MOE_ROUTING_TOKEN_CHOICE or MOE_ROUTING_EXPERT_CHOICE */
 } moe_config;
 
 /*
@@ -161,6 +174,7 @@ typedef struct moe_weights {
  */
 typedef struct moe_trace {
   float* logits;             /* [T, N] */
+  /* token choice */
   int32_t* topk_ids;         /* [T, k] */
   float* topk_gates;         /* [T, k] */
   float* margin;             /* [T] */
@@ -173,6 +187,11 @@ typedef struct moe_trace {
   void* act;                 /* [P_max, I] act dtype */
   void* y_route;             /* [T*k, H] act dtype */
   int32_t* route_expert;     /* [T*k]: expert each route runs, -1 none (reroute policy only) */
+  /* expert choice (sorted_route_ids then holds token ids, y_route is [P, H] by padded row) */
+  float* scores;             /* [T, N] */
+  int32_t* choice_tokens;    /* [N, C] */
+  int32_t* choice_slot;      /* [T, N] */
+  float* choice_margin;      /* [N] */
 } moe_trace;
 
 /* ABI version (MOE_ABI_VERSION) of the loaded library. */
@@ -184,7 +203,8 @@ const char* moe_status_str(moe_status s);
 /* Host-only check of a config against the supported envelope. */
 moe_status moe_validate_config(const moe_config* cfg);
 
-/* Host-only: P_max = T*k + N*(B-1) and ceil(P_max / B) for a valid config. */
+/* Host-only: the padded row bound P and ceil(P / B) for a valid config: token choice
+ * P = P_max = T*k + N*(B-1); expert choice P = N * ceil(C / B) * B (exact). */
 moe_status moe_align_sizes(const moe_config* cfg, int32_t* p_max, int32_t* n_blocks);
 
 /* Host-only: workspace bytes needed by moe_align (MOE_OP_ALIGN) or moe_forward (MOE_OP_FORWARD). */
@@ -321,6 +341,84 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* weights, const 
 moe_status moe_forward_replay(const moe_config* cfg, const moe_weights* weights, const void* h,
                               const void* residual, const int32_t* replay_ids, void* out,
                               const moe_trace* trace, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- expert-choice routing
+ *
+ * "Mixture-of-experts routing & LLM repeatability", paragraph on expert-choice routing:
+ * the assignment is turned around, and each expert takes its highest-scoring tokens from
+ * the whole batch.  "Mixture-of-Experts Routing at Inference Time", "Integration: where
+ * routing lives in a serving stack", paragraph on expert-choice routing: each expert picks
+ * up to its capacity, so no expert overflows, and a token may be picked by no expert.
+ *
+ * For a config with routing = MOE_ROUTING_EXPERT_CHOICE:
+ *   score[t, e]  = softmax over the N logits of token t (the router's probabilities; a
+ *                  NaN logit weighs 0).  For a token's top-k experts these are bitwise the
+ *                  token-choice gates with renormalize = 0.
+ *   C            = min(floor(T*k*cap_num / (N*cap_den)), T) tokens per expert, the factor
+ *                  being 1 when cap_num = cap_den = 0 (k reads as the mean number of
+ *                  experts per token; factor 1 runs as many expert rows as top-k).
+ *   picks        expert e takes the C tokens ranked first by (score descending, lower token
+ *                index first, NaN last).
+ *   gate         a pick's gate is its score, not renormalised.  out[t] = round(((sum over
+ *                the experts that picked t, ascending e, of score[t,e] * y) + shared[t])
+ *                + residual[t]); a token no expert picked outputs its residual bitwise.
+ *   rows         P = N * Cp padded rows, Cp = ceil(C / B) * B: expert e's picks at rows
+ *                [e*Cp, e*Cp + C) in ascending token order, sentinel T after them.
+ * Entry points: moe_route_expert_choice, moe_align_expert_choice, moe_expert_ffn /
+ * moe_expert_gate_up / moe_expert_down (sorted_route_ids then holds token ids with the
+ * sentinel T, and y_out is [P, H], written at each real padded row), moe_combine_expert_choice
+ * and moe_forward (trace: logits, scores, choice_*, sorted_route_ids, block_expert,
+ * expert_offsets, num_padded, stats, act, y_route).  moe_route, moe_align,
+ * moe_align_reroute, moe_combine and moe_forward_replay return MOE_ERR_UNSUPPORTED for such
+ * a config, and the expert-choice entry points do for a token-choice config.  The picks
+ * depend on the whole batch by construction: no batch invariance is claimed, only that the
+ * same inputs give the same bits.
+ */
+
+/* Host-only, expert-choice config: C (tokens per expert) and Cp = ceil(C / B) * B. */
+moe_status moe_expert_choice_sizes(const moe_config* cfg, int32_t* capacity, int32_t* segment);
+
+/*
+ * Scores and each expert's picks.
+ *   h, w_gate, logit_bias, logits: as moe_route (MOE_ROUTE_LOGITS_IN: logits are read)
+ *   scores        [T, N] float32 out
+ *   choice_tokens [N, C] int32 out: expert e's picks, ascending token ids (nothing if C = 0)
+ *   choice_slot   [T, N] int32 out: position of t in expert e's list, -1 if not picked
+ *   choice_margin [N] float32 out, nullable: C-th minus (C+1)-th highest score of expert e
+ *                 (0 on a tie at the cut), +inf when C = 0 or C = T
+ * One workgroup per expert selects with a radix select over the 32-bit score keys (counts
+ * only, no atomic decides an order) and lists its picks with prefix counts in token order.
+ * Flags other than MOE_ROUTE_LOGITS_IN return MOE_ERR_UNSUPPORTED.
+ */
+moe_status moe_route_expert_choice(const moe_config* cfg, const void* h, const void* w_gate,
+                                   const float* logit_bias, float* logits, float* scores,
+                                   int32_t* choice_tokens, int32_t* choice_slot, float* choice_margin,
+                                   uint32_t flags, void* stream);
+
+/*
+ * Padded rows of the picks (no workspace).
+ *   choice_tokens, choice_slot   from moe_route_expert_choice
+ *   sorted_route_ids [P] int32 out: token ids per expert segment, sentinel T as padding
+ *   block_expert     [P / B] int32 out;  expert_offsets [N+1] int32 out (e * Cp);
+ *   num_padded       [1] int32 out (P)
+ *   stats            [N + MOE_STATS_EXTRA] int32 out, nullable: C per expert, KEPT = N*C,
+ *                    CAPACITY = C, MAX_LOAD = MIN_LOAD = C, NUM_PADDED = P, UNPICKED and
+ *                    MAX_PICKS from choice_slot, the others 0
+ */
+moe_status moe_align_expert_choice(const moe_config* cfg, const int32_t* choice_tokens,
+                                   const int32_t* choice_slot, int32_t* sorted_route_ids,
+                                   int32_t* block_expert, int32_t* expert_offsets, int32_t* num_padded,
+                                   int32_t* stats, void* stream);
+
+/*
+ * Combine of the picks: out[t] = round(((sum over e ascending with choice_slot[t,e] >= 0 of
+ * scores[t,e] * y_rows[e*Cp + choice_slot[t,e]]) + shared_out[t]) + residual[t]), fp32,
+ * one rounding.  y_rows [P, H], scores and choice_slot [T, N], shared_out / residual
+ * nullable [T, H], out [T, H]; act dtype but scores and slots.
+ */
+moe_status moe_combine_expert_choice(const moe_config* cfg, const void* y_rows, const float* scores,
+                                     const int32_t* choice_slot, const void* shared_out, const void* residual,
+                                     void* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,8 @@ def config(w: W.Workload, **kw) -> M.moe_config:
     w = w.with_(**kw) if kw else w
     return M.make_config(w.T, w.H, w.N, w.k, w.I, w.B, cap_num=w.cap_num, cap_den=w.cap_den,
                          n_shared=w.n_shared, renormalize=w.renormalize, act_dtype=w.act_dtype,
-                         expert_dtype=w.expert_dtype, scale_block=w.scale_block, reroute_depth=w.reroute_depth)
+                         expert_dtype=w.expert_dtype, scale_block=w.scale_block, reroute_depth=w.reroute_depth,
+                         routing=w.routing)
 
 
 def f64(t: torch.Tensor) -> np.ndarray:

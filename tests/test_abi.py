@@ -53,7 +53,7 @@ def test_ceiling_library_exports_and_rejects_bad_arguments():
 
 
 def test_abi_version_and_status_strings():
-    assert M.moe_abi_version() == 2
+    assert M.moe_abi_version() == 3
     for code, name in M.STATUS.items():
         assert M.moe_status_str(code).startswith(name)
     assert "unknown" in M.moe_status_str(99)
@@ -64,11 +64,18 @@ def test_workload_configs_are_valid(w):
     cfg = config(w)
     M.moe_validate_config(cfg)
     p_max, n_blocks = M.moe_align_sizes(cfg)
+    act = 4 if w.act_dtype == W.F32 else 2
+    fwd = M.moe_workspace_size(cfg, M.MOE_OP_FORWARD)
+    if w.routing == "expert_choice":
+        C, seg = M.moe_expert_choice_sizes(cfg)
+        assert C == min(w.T * w.k * (w.cap_num or 1) // (w.N * (w.cap_den or 1)), w.T)
+        assert seg == -(-C // w.B) * w.B and p_max == w.N * seg and n_blocks == p_max // w.B
+        assert M.moe_workspace_size(cfg, M.MOE_OP_ALIGN) == 0
+        assert fwd >= p_max * (w.I + w.H) * act + 3 * w.T * w.N * 4
+        return
     assert p_max == w.T * w.k + w.N * (w.B - 1)
     assert n_blocks == -(-p_max // w.B)
     assert M.moe_workspace_size(cfg, M.MOE_OP_ALIGN) > 0
-    fwd = M.moe_workspace_size(cfg, M.MOE_OP_FORWARD)
-    act = 4 if w.act_dtype == W.F32 else 2
     assert fwd >= p_max * w.I * act + w.T * w.k * w.H * act
 
 
@@ -77,12 +84,15 @@ BAD = [
     dict(k=9, N=16), dict(k=3, N=2), dict(B=12), dict(B=256), dict(cap_num=5, cap_den=0),
     dict(cap_num=-1, cap_den=4), dict(n_shared=2), dict(renormalize=2), dict(T=65536, H=32768),
     dict(I=32768, H=32768), dict(reroute_depth=-1), dict(reroute_depth=7, N=8, k=2),
+    dict(routing=2), dict(routing=-1), dict(routing=1, reroute_depth=1, cap_num=1, cap_den=1),
 ]
 
 
 @pytest.mark.parametrize("bad", BAD, ids=[str(b) for b in BAD])
 def test_invalid_configs_rejected(bad):
+    routing = bad.pop("routing", 0)
     cfg = config(W.MIXTRAL_BF16, **bad)
+    cfg.routing = routing
     with pytest.raises(M.MoeError) as ei:
         M.moe_validate_config(cfg)
     assert ei.value.name == "MOE_ERR_INVALID_CONFIG"
@@ -156,3 +166,44 @@ def test_host_validation_of_pointers_and_workspace():
 def test_workspace_op_codes():
     cfg = config(W.TOY_FP32)
     _expect("MOE_ERR_INVALID_CONFIG", M.moe_workspace_size, cfg, 7)
+
+
+def test_routing_mode_mismatch_is_unsupported():
+    tc, ec = config(W.MIXTRAL_BF16), config(W.MIXTRAL_EC_BF16)
+    A = 4096  # stand-in address: every call below fails validation, nothing is enqueued
+    s = 0
+    full = {"w_gate": A, "w13": A, "w2": A}
+    # token-choice entry points refuse an expert-choice config
+    _expect("MOE_ERR_UNSUPPORTED", M.moe_route, ec, A, A, None, A, A, A, None, 0, s)
+    _expect("MOE_ERR_UNSUPPORTED", M.moe_align, ec, A, A, A, A, A, A, None, A, 1 << 20, s)
+    _expect("MOE_ERR_UNSUPPORTED", M.moe_align_reroute, ec, A, A, A, A, A, A, A, A, None, A, 1 << 20, s)
+    _expect("MOE_ERR_UNSUPPORTED", M.moe_combine, ec, A, A, A, None, None, A, s)
+    _expect("MOE_ERR_UNSUPPORTED", M.moe_forward_replay, ec, full, A, None, A, A, None, A, 1 << 40, s)
+    # and the expert-choice ones a token-choice config
+    _expect("MOE_ERR_UNSUPPORTED", M.moe_expert_choice_sizes, tc)
+    _expect("MOE_ERR_UNSUPPORTED", M.moe_route_expert_choice, tc, A, A, None, A, A, A, A, None, 0, s)
+    _expect("MOE_ERR_UNSUPPORTED", M.moe_align_expert_choice, tc, A, A, A, A, A, A, None, s)
+    _expect("MOE_ERR_UNSUPPORTED", M.moe_combine_expert_choice, tc, A, A, A, None, None, A, s)
+
+
+def test_expert_choice_host_validation():
+    ec = config(W.MIXTRAL_EC_BF16)
+    A, s = 4096, 0
+    _expect("MOE_ERR_NULL_POINTER", M.moe_route_expert_choice, ec, A, A, None, None, A, A, A, None, 0, s)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_route_expert_choice, ec, A, A, None, A, None, A, A, None, 0, s)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_route_expert_choice, ec, A, A, None, A, A, None, A, None, 0, s)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_route_expert_choice, ec, None, A, None, A, A, A, A, None, 0, s)
+    _expect("MOE_ERR_MISALIGNED", M.moe_route_expert_choice, ec, A, A, None, A, A + 2, A, A, None, 0, s)
+    _expect("MOE_ERR_MISALIGNED", M.moe_route_expert_choice, ec, A + 8, A, None, A, A, A, A, None, 0, s)
+    _expect("MOE_ERR_UNSUPPORTED", M.moe_route_expert_choice, ec, A, A, None, A, A, A, A, None,
+            M.MOE_ROUTE_IDS_IN, s)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_align_expert_choice, ec, None, A, A, A, A, A, None, s)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_align_expert_choice, ec, A, None, A, A, A, A, A, s)
+    _expect("MOE_ERR_MISALIGNED", M.moe_align_expert_choice, ec, A, A, A + 1, A, A, A, None, s)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_combine_expert_choice, ec, A, A, None, None, None, A, s)
+    _expect("MOE_ERR_MISALIGNED", M.moe_combine_expert_choice, ec, A + 4, A, A, None, None, A, s)
+    full = {"w_gate": A, "w13": A, "w2": A}
+    _expect("MOE_ERR_WORKSPACE_TOO_SMALL", M.moe_forward, ec, full, A, None, A, None, A, 1024, s)
+    assert M.moe_expert_choice_sizes(ec) == (1024, 1024)
+    assert M.moe_expert_choice_sizes(config(W.MIXTRAL_EC_BF16, T=5, cap_num=1, cap_den=1)) == (1, 64)
+    assert M.moe_expert_choice_sizes(config(W.MIXTRAL_EC_BF16, T=3, k=1)) == (0, 0)

@@ -178,6 +178,7 @@ def test_align_bit_exact(case):
     assert gs[N + X["max_load"]] == st["max_expert_load"]
     assert gs[N + X["min_load"]] == st["min_expert_load"]
     assert gs[N + X["num_padded"]] == al["num_padded"]
+    assert gs[N + X["rerouted"]] == 0 and gs[N + X["unpicked"]] == 0 and gs[N + X["max_picks"]] == 0
 
 
 # ------------------------------------------------------------------ expert FFN

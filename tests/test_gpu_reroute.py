@@ -63,6 +63,7 @@ def _check_against_oracle(w, ids, logits, depth):
     assert st[N + M.STAT["invalid"]] == (~valid).sum()
     assert st[N + M.STAT["capacity"]] == (-1 if cap is None else cap)
     assert st[N + M.STAT["num_padded"]] == al["num_padded"]
+    assert st[N + M.STAT["unpicked"]] == 0 and st[N + M.STAT["max_picks"]] == 0
     return kept.sum(), rerouted.sum()
 
 

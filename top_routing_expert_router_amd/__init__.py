@@ -18,9 +18,10 @@ __all__ = [
     "MoeError", "moe_config", "moe_weights", "moe_trace", "make_config", "lib",
     "moe_abi_version", "moe_status_str", "moe_validate_config", "moe_align_sizes",
     "moe_workspace_size", "moe_route", "moe_align", "moe_align_reroute", "moe_expert_ffn", "moe_expert_gate_up",
-    "moe_expert_down", "moe_combine",
-    "moe_forward", "moe_forward_replay", "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_IDS_IN", "MOE_OP_ALIGN", "MOE_OP_FORWARD", "STATUS",
-    "DTYPES", "STATS_EXTRA", "STAT",
+    "moe_expert_down", "moe_combine", "moe_forward", "moe_forward_replay", "moe_route_expert_choice",
+    "moe_align_expert_choice", "moe_combine_expert_choice", "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_IDS_IN", "MOE_OP_ALIGN",
+    "MOE_OP_FORWARD", "STATUS", "DTYPES", "ROUTING", "STATS_EXTRA", "STAT", "moe_expert_choice_sizes", "ec_capacity",
+    "ec_segment",
 ]
 
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
@@ -28,11 +29,12 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3}
 MOE_ROUTE_LOGITS_IN = 1
 MOE_ROUTE_IDS_IN = 2
 MOE_OP_ALIGN, MOE_OP_FORWARD = 1, 2
+ROUTING = {"token_choice": 0, "expert_choice": 1}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL_POINTER", 2: "MOE_ERR_INVALID_CONFIG", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_MISALIGNED", 5: "MOE_ERR_WORKSPACE_TOO_SMALL", 6: "MOE_ERR_HIP"}
-STATS_EXTRA = 8
+STATS_EXTRA = 10
 STAT = {"kept": 0, "dropped": 1, "invalid": 2, "capacity": 3, "max_load": 4, "min_load": 5, "num_padded": 6,
-        "rerouted": 7}
+        "rerouted": 7, "unpicked": 8, "max_picks": 9}
 
 
 class MoeError(RuntimeError):
@@ -45,7 +47,8 @@ class MoeError(RuntimeError):
 class moe_config(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32)] + [
         (n, ctypes.c_int32) for n in ("T", "H", "N", "k", "I", "B", "cap_num", "cap_den", "n_shared",
-                                      "renormalize", "act_dtype", "expert_dtype", "scale_block", "reroute_depth")]
+                                      "renormalize", "act_dtype", "expert_dtype", "scale_block", "reroute_depth",
+                                      "routing")]
 
 
 class moe_weights(ctypes.Structure):
@@ -57,7 +60,8 @@ class moe_weights(ctypes.Structure):
 class moe_trace(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "topk_ids", "topk_gates", "margin", "route_kept", "sorted_route_ids", "block_expert",
-        "expert_offsets", "num_padded", "stats", "act", "y_route", "route_expert")]
+        "expert_offsets", "num_padded", "stats", "act", "y_route", "route_expert", "scores", "choice_tokens",
+        "choice_slot", "choice_margin")]
 
 
 _lib = None
@@ -89,6 +93,10 @@ def lib() -> ctypes.CDLL:
             "moe_forward": ([cfgp, ctypes.POINTER(moe_weights), P, P, P, ctypes.POINTER(moe_trace), P, SZ, P], I32),
             "moe_forward_replay": ([cfgp, ctypes.POINTER(moe_weights), P, P, P, P, ctypes.POINTER(moe_trace), P, SZ,
                                     P], I32),
+            "moe_expert_choice_sizes": ([cfgp, ctypes.POINTER(I32), ctypes.POINTER(I32)], I32),
+            "moe_route_expert_choice": ([cfgp, P, P, P, P, P, P, P, P, U32, P], I32),
+            "moe_align_expert_choice": ([cfgp, P, P, P, P, P, P, P, P], I32),
+            "moe_combine_expert_choice": ([cfgp, P, P, P, P, P, P, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -123,9 +131,25 @@ def _check(fn: str, st: int) -> None:
 
 def make_config(T: int, H: int, N: int, k: int, I: int, B: int, *, cap_num: int = 0, cap_den: int = 0,
                 n_shared: int = 0, renormalize: int = 1, act_dtype: str = "bf16", expert_dtype: str = "bf16",
-                scale_block: int = 0, reroute_depth: int = 0) -> moe_config:
+                scale_block: int = 0, reroute_depth: int = 0, routing: str = "token_choice") -> moe_config:
     return moe_config(ctypes.sizeof(moe_config), T, H, N, k, I, B, cap_num, cap_den, n_shared, renormalize,
-                      DTYPES[act_dtype], DTYPES[expert_dtype], scale_block, reroute_depth)
+                      DTYPES[act_dtype], DTYPES[expert_dtype], scale_block, reroute_depth, ROUTING[routing])
+
+
+def moe_expert_choice_sizes(cfg: moe_config):
+    """Expert choice: (C tokens per expert, padded rows per expert segment)."""
+    c, seg = ctypes.c_int32(), ctypes.c_int32()
+    _check("moe_expert_choice_sizes",
+           lib().moe_expert_choice_sizes(ctypes.byref(cfg), ctypes.byref(c), ctypes.byref(seg)))
+    return c.value, seg.value
+
+
+def ec_capacity(cfg: moe_config) -> int:
+    return moe_expert_choice_sizes(cfg)[0]
+
+
+def ec_segment(cfg: moe_config) -> int:
+    return moe_expert_choice_sizes(cfg)[1]
 
 
 def moe_abi_version() -> int:
@@ -219,3 +243,28 @@ def moe_align_reroute(cfg, topk_ids, logits, route_expert, route_kept, sorted_ro
            lib().moe_align_reroute(ctypes.byref(cfg), _ptr(topk_ids), _ptr(logits), _ptr(route_expert),
                                    _ptr(route_kept), _ptr(sorted_route_ids), _ptr(block_expert), _ptr(expert_offsets),
                                    _ptr(num_padded), _ptr(stats), _ptr(ws), nb, _stream(stream)))
+
+
+def moe_route_expert_choice(cfg, h, w_gate, logit_bias, logits, scores, choice_tokens, choice_slot,
+                            choice_margin=None, flags: int = 0, stream=None):
+    """Expert choice: scores [T, N] and each expert's picks (tokens [N, C], slot [T, N], margin [N])."""
+    _check("moe_route_expert_choice",
+           lib().moe_route_expert_choice(ctypes.byref(cfg), _ptr(h), _ptr(w_gate), _ptr(logit_bias), _ptr(logits),
+                                         _ptr(scores), _ptr(choice_tokens), _ptr(choice_slot), _ptr(choice_margin),
+                                         flags, _stream(stream)))
+
+
+def moe_align_expert_choice(cfg, choice_tokens, choice_slot, sorted_route_ids, block_expert, expert_offsets,
+                            num_padded, stats=None, stream=None):
+    """Expert choice: the picks as padded rows (token ids, sentinel T) and the routing stats."""
+    _check("moe_align_expert_choice",
+           lib().moe_align_expert_choice(ctypes.byref(cfg), _ptr(choice_tokens), _ptr(choice_slot),
+                                         _ptr(sorted_route_ids), _ptr(block_expert), _ptr(expert_offsets),
+                                         _ptr(num_padded), _ptr(stats), _stream(stream)))
+
+
+def moe_combine_expert_choice(cfg, y_rows, scores, choice_slot, shared_out, residual, out, stream=None):
+    """Expert choice: out = residual + shared + score-weighted sum of each token's picks."""
+    _check("moe_combine_expert_choice",
+           lib().moe_combine_expert_choice(ctypes.byref(cfg), _ptr(y_rows), _ptr(scores), _ptr(choice_slot),
+                                           _ptr(shared_out), _ptr(residual), _ptr(out), _stream(stream)))

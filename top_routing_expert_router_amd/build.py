@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "route.hip", "align.hip", "reroute.hip", "ffn.hip", "combine.hip"]
+SOURCES = ["api.hip", "route.hip", "align.hip", "reroute.hip", "expert_choice.hip", "ffn.hip", "combine.hip"]
 # measured hardware ceilings (copy / read streams, MFMA issue); not part of the layer
 CEILING_LIB_PATH = os.path.join(HERE, "libmoe_ceiling.so")
 CEILING_SOURCES = ["ceiling.hip"]

@@ -118,6 +118,8 @@ __global__ __launch_bounds__(kThreads) void align_scan(int32_t* __restrict__ cou
       stats[N + MOE_STAT_MAX_LOAD] = mxx;
       stats[N + MOE_STAT_MIN_LOAD] = mnn;
       stats[N + MOE_STAT_REROUTED] = 0;
+      stats[N + MOE_STAT_UNPICKED] = 0;  // expert-choice counters
+      stats[N + MOE_STAT_MAX_PICKS] = 0;
     }
   }
 }

@@ -26,6 +26,8 @@ moe_status check_config(const moe_config* c) {
   if (c->n_shared != 0 && c->n_shared != 1) return MOE_ERR_INVALID_CONFIG;
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_CONFIG;
   if (c->reroute_depth < 0 || c->reroute_depth > c->N - c->k) return MOE_ERR_INVALID_CONFIG;
+  if (c->routing != MOE_ROUTING_TOKEN_CHOICE && c->routing != MOE_ROUTING_EXPERT_CHOICE) return MOE_ERR_INVALID_CONFIG;
+  if (c->routing == MOE_ROUTING_EXPERT_CHOICE && c->reroute_depth != 0) return MOE_ERR_INVALID_CONFIG;
   const bool f32 = c->act_dtype == MOE_F32 && c->expert_dtype == MOE_F32 && c->scale_block == 0;
   const bool bf16 = c->act_dtype == MOE_BF16 && c->expert_dtype == MOE_BF16 && c->scale_block == 0;
   const bool fp8 = c->act_dtype == MOE_BF16 && c->expert_dtype == MOE_FP8_E4M3 && c->scale_block == 128;
@@ -40,20 +42,25 @@ moe_status check_config(const moe_config* c) {
 }
 
 size_t act_size(const moe_config& c) { return c.act_dtype == MOE_F32 ? 4 : 2; }
-long p_max_of(const moe_config& c) { return (long)c.T * c.k + (long)c.N * (c.B - 1); }
+// padded row bound: token choice T*k + N*(B-1); expert choice exactly N segments
+long p_max_of(const moe_config& c) {
+  return expert_choice(c) ? (long)c.N * ec_segment(c) : (long)c.T * c.k + (long)c.N * (c.B - 1);
+}
 long n_blocks_of(const moe_config& c) { return (p_max_of(c) + c.B - 1) / c.B; }
 
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Regions of the moe_forward workspace, in order, each 256-byte aligned.
 struct FwdLayout {
-  size_t logits, ids, gates, margin, kept, rexp, sorted, blocks, offsets, npad, stats, align_ws, work, act, y, sact,
-      sout, total;
+  size_t logits, ids, gates, margin, kept, rexp, scores, ctok, cslot, cmargin, sorted, blocks, offsets, npad, stats,
+      align_ws, work, act, y, sact, sout, total;
 };
 
 FwdLayout forward_layout(const moe_config& c) {
   FwdLayout L{};
-  const size_t T = c.T, N = c.N, R = (size_t)c.T * c.k, P = p_max_of(c), a = act_size(c);
+  const bool ec = expert_choice(c);
+  const size_t T = c.T, N = c.N, R = ec ? 0 : (size_t)c.T * c.k, P = p_max_of(c), a = act_size(c);
+  const size_t TN = ec ? T * N : 0, C = ec ? ec_capacity(c) : 0;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -66,15 +73,19 @@ FwdLayout forward_layout(const moe_config& c) {
   L.margin = take(T * 4);
   L.kept = take(R);
   L.rexp = take(R * 4);
+  L.scores = take(TN * 4);
+  L.ctok = take(N * C * 4);
+  L.cslot = take(TN * 4);
+  L.cmargin = take(ec ? N * 4 : 0);
   L.sorted = take(P * 4);
   L.blocks = take(n_blocks_of(c) * 4);
   L.offsets = take((N + 1) * 4);
   L.npad = take(4);
   L.stats = take((N + MOE_STATS_EXTRA) * 4);
-  L.align_ws = take(reroute_workspace_bytes(c) + round_up(align_workspace_bytes(c)));
+  L.align_ws = take(ec ? 0 : reroute_workspace_bytes(c) + round_up(align_workspace_bytes(c)));
   L.work = take(4 * kGemmWorkWords * 4);  // tile counters of the 4 expert GEMM launches
   L.act = take(P * (size_t)c.I * a);
-  L.y = take(R * (size_t)c.H * a);
+  L.y = take((ec ? P : R) * (size_t)c.H * a);
   L.sact = c.n_shared ? take(T * (size_t)c.I * a) : o;
   L.sout = c.n_shared ? take(T * (size_t)c.H * a) : o;
   L.total = o;
@@ -82,6 +93,13 @@ FwdLayout forward_layout(const moe_config& c) {
 }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// A valid config with the given routing, else the error to return.
+moe_status check_routing(const moe_config* c, bool want_expert_choice) {
+  moe_status st = check_config(c);
+  if (st != MOE_OK) return st;
+  return expert_choice(*c) == want_expert_choice ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
 
 moe_status check_route_args(const moe_config& c, const void* h, const void* w_gate, const float* bias,
                             const float* logits, const int32_t* ids, const float* gates, const float* margin,
@@ -163,8 +181,8 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes) 
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (!bytes) return MOE_ERR_NULL_POINTER;
-  if (op == MOE_OP_ALIGN) {  // moe_align and moe_align_reroute
-    *bytes = reroute_workspace_bytes(*cfg) + round_up(align_workspace_bytes(*cfg));
+  if (op == MOE_OP_ALIGN) {  // moe_align and moe_align_reroute (moe_align_expert_choice needs none)
+    *bytes = expert_choice(*cfg) ? 0 : reroute_workspace_bytes(*cfg) + round_up(align_workspace_bytes(*cfg));
     return MOE_OK;
   }
   if (op == MOE_OP_FORWARD) {
@@ -176,7 +194,7 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes) 
 
 moe_status moe_route(const moe_config* cfg, const void* h, const void* w_gate, const float* logit_bias, float* logits,
                      int32_t* topk_ids, float* topk_gates, float* margin, uint32_t flags, void* stream) {
-  moe_status st = check_config(cfg);
+  moe_status st = check_routing(cfg, false);
   if (st != MOE_OK) return st;
   st = check_route_args(*cfg, h, w_gate, logit_bias, logits, topk_ids, topk_gates, margin, flags);
   if (st != MOE_OK) return st;
@@ -192,7 +210,7 @@ moe_status moe_route(const moe_config* cfg, const void* h, const void* w_gate, c
 moe_status moe_align(const moe_config* cfg, const int32_t* topk_ids, uint8_t* route_kept, int32_t* sorted_route_ids,
                      int32_t* block_expert, int32_t* expert_offsets, int32_t* num_padded, int32_t* stats, void* ws,
                      size_t ws_bytes, void* stream) {
-  moe_status st = check_config(cfg);
+  moe_status st = check_routing(cfg, false);
   if (st != MOE_OK) return st;
   st = check_align_args(topk_ids, route_kept, sorted_route_ids, block_expert, expert_offsets, num_padded, stats, ws);
   if (st != MOE_OK) return st;
@@ -205,7 +223,7 @@ moe_status moe_align_reroute(const moe_config* cfg, const int32_t* topk_ids, con
                              int32_t* route_expert, uint8_t* route_kept, int32_t* sorted_route_ids,
                              int32_t* block_expert, int32_t* expert_offsets, int32_t* num_padded, int32_t* stats,
                              void* ws, size_t ws_bytes, void* stream) {
-  moe_status st = check_config(cfg);
+  moe_status st = check_routing(cfg, false);
   if (st != MOE_OK) return st;
   st = check_align_args(topk_ids, route_kept, sorted_route_ids, block_expert, expert_offsets, num_padded, stats, ws);
   if (st != MOE_OK) return st;
@@ -258,12 +276,71 @@ moe_status moe_expert_down(const moe_config* cfg, const void* act, const int32_t
 
 moe_status moe_combine(const moe_config* cfg, const void* y_route, const float* topk_gates, const uint8_t* route_kept,
                        const void* shared_out, const void* residual, void* out, void* stream) {
-  moe_status st = check_config(cfg);
+  moe_status st = check_routing(cfg, false);
   if (st != MOE_OK) return st;
   st = check_combine_args(y_route, topk_gates, route_kept, shared_out, residual, out);
   if (st != MOE_OK) return st;
   return hip_status(launch_combine(*cfg, y_route, topk_gates, route_kept, shared_out, residual, out,
                                    (hipStream_t)stream));
+}
+
+moe_status moe_expert_choice_sizes(const moe_config* cfg, int32_t* capacity, int32_t* segment) {
+  moe_status st = check_routing(cfg, true);
+  if (st != MOE_OK) return st;
+  if (!capacity || !segment) return MOE_ERR_NULL_POINTER;
+  *capacity = ec_capacity(*cfg);
+  *segment = ec_segment(*cfg);
+  return MOE_OK;
+}
+
+moe_status moe_route_expert_choice(const moe_config* cfg, const void* h, const void* w_gate, const float* logit_bias,
+                                   float* logits, float* scores, int32_t* choice_tokens, int32_t* choice_slot,
+                                   float* choice_margin, uint32_t flags, void* stream) {
+  moe_status st = check_routing(cfg, true);
+  if (st != MOE_OK) return st;
+  if (flags & ~(uint32_t)MOE_ROUTE_LOGITS_IN) return MOE_ERR_UNSUPPORTED;
+  const bool in = flags & MOE_ROUTE_LOGITS_IN;
+  if (!logits || !scores || !choice_slot || (!choice_tokens && ec_capacity(*cfg) > 0)) return MOE_ERR_NULL_POINTER;
+  if (!in && (!h || !w_gate)) return MOE_ERR_NULL_POINTER;
+  if (!aligned(logits, 4) || !aligned(scores, 4) || !aligned(choice_tokens, 4) || !aligned(choice_slot, 4) ||
+      !aligned(choice_margin, 4))
+    return MOE_ERR_MISALIGNED;
+  if (!in && (!aligned(h, 16) || !aligned(w_gate, 16) || (logit_bias && !aligned(logit_bias, 4))))
+    return MOE_ERR_MISALIGNED;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = in ? launch_topk(*cfg, logits, nullptr, nullptr, nullptr, s, nullptr, scores)
+                    : launch_router(*cfg, h, w_gate, logit_bias, logits, nullptr, nullptr, nullptr, s, nullptr, scores);
+  if (e == hipSuccess) e = launch_ec_select(*cfg, scores, choice_tokens, choice_slot, choice_margin, s);
+  return hip_status(e);
+}
+
+moe_status moe_align_expert_choice(const moe_config* cfg, const int32_t* choice_tokens, const int32_t* choice_slot,
+                                   int32_t* sorted_route_ids, int32_t* block_expert, int32_t* expert_offsets,
+                                   int32_t* num_padded, int32_t* stats, void* stream) {
+  moe_status st = check_routing(cfg, true);
+  if (st != MOE_OK) return st;
+  const bool rows = ec_capacity(*cfg) > 0;
+  if ((rows && (!choice_tokens || !sorted_route_ids || !block_expert)) || !expert_offsets || !num_padded ||
+      (stats && !choice_slot))
+    return MOE_ERR_NULL_POINTER;
+  if (!aligned(choice_tokens, 4) || !aligned(choice_slot, 4) || !aligned(sorted_route_ids, 4) ||
+      !aligned(block_expert, 4) || !aligned(expert_offsets, 4) || !aligned(num_padded, 4) || !aligned(stats, 4))
+    return MOE_ERR_MISALIGNED;
+  return hip_status(launch_ec_align(*cfg, choice_tokens, choice_slot, sorted_route_ids, block_expert, expert_offsets,
+                                    num_padded, stats, (hipStream_t)stream));
+}
+
+moe_status moe_combine_expert_choice(const moe_config* cfg, const void* y_rows, const float* scores,
+                                     const int32_t* choice_slot, const void* shared_out, const void* residual,
+                                     void* out, void* stream) {
+  moe_status st = check_routing(cfg, true);
+  if (st != MOE_OK) return st;
+  if ((!y_rows && ec_capacity(*cfg) > 0) || !scores || !choice_slot || !out) return MOE_ERR_NULL_POINTER;
+  if (!aligned(y_rows, 16) || !aligned(scores, 4) || !aligned(choice_slot, 4) || !aligned(out, 16) ||
+      !aligned(shared_out, 16) || !aligned(residual, 16))
+    return MOE_ERR_MISALIGNED;
+  return hip_status(launch_combine_ec(*cfg, y_rows, scores, choice_slot, shared_out, residual, out,
+                                     (hipStream_t)stream));
 }
 
 namespace {
@@ -314,6 +391,30 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* wt, const void
     return MOE_ERR_MISALIGNED;
 
   hipStream_t s = (hipStream_t)stream;
+  if (expert_choice(c)) {
+    float* scores = (float*)pick(tr.scores, L.scores);
+    int32_t* ctok = (int32_t*)pick(tr.choice_tokens, L.ctok);
+    int32_t* cslot = (int32_t*)pick(tr.choice_slot, L.cslot);
+    float* cmargin = (float*)pick(tr.choice_margin, L.cmargin);
+    if (!aligned(scores, 4) || !aligned(ctok, 4) || !aligned(cslot, 4) || !aligned(cmargin, 4))
+      return MOE_ERR_MISALIGNED;
+    hipError_t e = launch_router(c, h, wt->w_gate, wt->logit_bias, logits, nullptr, nullptr, nullptr, s, nullptr,
+                                 scores);
+    if (e == hipSuccess) e = launch_ec_select(c, scores, ctok, cslot, cmargin, s);
+    if (e == hipSuccess)
+      e = launch_ec_align(c, ctok, cslot, sorted, blocks, offsets, npad, stats, s, work, 4 * kGemmWorkWords);
+    if (e == hipSuccess)
+      e = launch_expert_ffn(c, h, sorted, offsets, wt->w13, wt->w2, wt->w13_scale, wt->w2_scale, act, y, false, s,
+                            work);
+    const void* shared_out = nullptr;
+    if (e == hipSuccess && c.n_shared) {
+      e = launch_expert_ffn(c, h, nullptr, nullptr, wt->shared_w13, wt->shared_w2, wt->shared_w13_scale,
+                            wt->shared_w2_scale, base + L.sact, base + L.sout, true, s, work + 2 * kGemmWorkWords);
+      shared_out = base + L.sout;
+    }
+    if (e == hipSuccess) e = launch_combine_ec(c, y, scores, cslot, shared_out, residual, out, s);
+    return hip_status(e);
+  }
   hipError_t e = launch_router(c, h, wt->w_gate, wt->logit_bias, logits, replay ? nullptr : ids, gates, margin, s,
                                replay);
   if (e == hipSuccess)
@@ -344,7 +445,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
 moe_status moe_forward_replay(const moe_config* cfg, const moe_weights* wt, const void* h, const void* residual,
                               const int32_t* replay_ids, void* out, const moe_trace* trace, void* ws,
                               size_t ws_bytes, void* stream) {
-  moe_status st = check_config(cfg);
+  moe_status st = check_routing(cfg, false);
   if (st != MOE_OK) return st;
   if (!replay_ids) return MOE_ERR_NULL_POINTER;
   if (!aligned(replay_ids, 4)) return MOE_ERR_MISALIGNED;

@@ -83,6 +83,61 @@ __global__ __launch_bounds__(kThreads) void combine_rows(const T* __restrict__ y
   *reinterpret_cast<V*>(out + (long)t * H + col) = o;
 }
 
+// Expert choice: out[t] = round(((sum over the experts e that picked t, ascending, of
+// score[t, e] * y[e * Cp + slot[t, e]]) + shared[t]) + residual[t]), fmaf per term in
+// that order, one rounding ("Mixture-of-experts routing & LLM repeatability", paragraph
+// on expert-choice routing: the gate of a pick is the token's score for that expert).
+// A workgroup's token is uniform, so its slots and scores are scalar loads; experts are
+// taken eight at a time, and the rows of a group's picks are loaded together.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void combine_ec_rows(const T* __restrict__ y, const float* __restrict__ scores,
+                                                             const int32_t* __restrict__ slot,
+                                                             const T* __restrict__ shared,
+                                                             const T* __restrict__ residual, T* __restrict__ out,
+                                                             int H, int N, int C, int Cp, int slices) {
+  typedef typename Vec8<T>::type V;
+  const int t = blockIdx.x / slices;
+  const long col = (long)(blockIdx.x % slices) * kColsPerBlock + threadIdx.x * kColsPerThread;
+  if (col >= H) return;
+  const int32_t* sl = slot + (long)t * N;
+  const float* sc = scores + (long)t * N;
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = -0.0f;
+  for (int e0 = 0; e0 < N; e0 += 8) {
+    int pos[8];
+    V yv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pos[j] = e0 + j < N ? sl[e0 + j] : -1;
+      if (pos[j] >= C) pos[j] = -1;  // slots are < C; anything else is not a pick
+      if (pos[j] >= 0) yv[j] = *reinterpret_cast<const V*>(y + ((long)(e0 + j) * Cp + pos[j]) * H + col);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (pos[j] >= 0) {
+        const float g = sc[e0 + j];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, (float)yv[j][q], acc[q]);
+      }
+    }
+  }
+  if (shared) {
+    const V sv = *reinterpret_cast<const V*>(shared + (long)t * H + col);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += (float)sv[q];
+  }
+  if (residual) {
+    const V rv = *reinterpret_cast<const V*>(residual + (long)t * H + col);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += (float)rv[q];
+  }
+  V o;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) o[q] = cvt_act<T>(acc[q]);
+  *reinterpret_cast<V*>(out + (long)t * H + col) = o;
+}
+
 }  // namespace
 
 hipError_t launch_combine(const moe_config& c, const void* y_route, const float* gates, const uint8_t* kept,
@@ -95,6 +150,27 @@ hipError_t launch_combine(const moe_config& c, const void* y_route, const float*
   } else {
     combine_rows<__bf16><<<grid, kThreads, 0, s>>>((const __bf16*)y_route, gates, kept, (const __bf16*)shared_out,
                                                    (const __bf16*)residual, (__bf16*)out, c.H, c.k, slices);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+hipError_t launch_combine_ec(const moe_config& c, const void* y_rows, const float* scores, const int32_t* slot,
+                             const void* shared_out, const void* residual, void* out, hipStream_t s) {
+  const int slices = ceil_div(c.H, kColsPerBlock);
+  const dim3 grid((unsigned)c.T * slices);
+  const int Cp = ec_segment(c);
+  if (c.act_dtype == MOE_F32) {
+    combine_ec_rows<float><<<grid, kThreads, 0, s>>>((const float*)y_rows, scores, slot, (const float*)shared_out,
+                                                     (const float*)residual, (float*)out, c.H, c.N, ec_capacity(c), Cp,
+                                                     slices);
+  } else {
+    combine_ec_rows<__bf16><<<grid, kThreads, 0, s>>>((const __bf16*)y_rows, scores, slot,
+                                                      (const __bf16*)shared_out, (const __bf16*)residual,
+                                                      (__bf16*)out, c.H, c.N, ec_capacity(c), Cp, slices);
   }
   return hipGetLastError();
 }

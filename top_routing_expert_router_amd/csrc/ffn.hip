@@ -58,6 +58,7 @@ struct FfnArgs {
   int mtiles;             // M-tile bound used for the grid
   int ntiles;
   int32_t* work;          // nullable: 8 zeroed per-XCD tile counters (dynamic schedule)
+  int dest_is_row;        // W2: 1 = y row p (expert choice: sorted holds token ids), 0 = y row sorted[p]
 };
 
 // LDS tile layout: row-major 128-byte rows of 8 16-byte chunks, chunk index XORed
@@ -508,8 +509,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         if (p >= t.p1) continue;
         int dest = p;
         if (a.sorted != nullptr) {
-          dest = a.sorted[p];
-          if ((unsigned)dest >= (unsigned)a.sentinel) continue;
+          const int r = a.sorted[p];
+          if ((unsigned)r >= (unsigned)a.sentinel) continue;
+          if (!a.dest_is_row) dest = r;
         }
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
@@ -589,8 +591,9 @@ __global__ __launch_bounds__(256) void ffn_w2_f32(FfnArgs a, int rows) {
   int e = 0, dest = p;
   if (a.sorted != nullptr) {
     if (p >= a.offsets[a.N]) return;
-    dest = a.sorted[p];
-    if ((unsigned)dest >= (unsigned)a.sentinel) return;
+    const int r = a.sorted[p];
+    if ((unsigned)r >= (unsigned)a.sentinel) return;
+    if (!a.dest_is_row) dest = r;
     e = expert_of_row(a.offsets, a.N, p);
   }
   const float* x = (const float*)a.x + (long)p * a.I;
@@ -602,6 +605,7 @@ __global__ __launch_bounds__(256) void ffn_w2_f32(FfnArgs a, int rows) {
 
 int mtile_bound(const moe_config& c, bool identity) {
   if (identity) return ceil_div(c.T, BM);
+  if (expert_choice(c)) return c.N * ceil_div(ec_segment(c), BM);
   const long p_max = (long)c.T * c.k + (long)c.N * (c.B - 1);
   return (int)((p_max + (long)c.N * (BM - 1)) / BM);
 }
@@ -615,6 +619,7 @@ hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
   if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (err != hipSuccess) return err;
   const int G = a.mtiles * a.ntiles;
+  if (G == 0) return hipSuccess;  // no rows (an expert-choice capacity of 0)
   const int grid = ceil_div(min(G, max(cus, 8)), 8) * 8;
   ffn_gemm_bf16<MODE, FP8><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
@@ -636,6 +641,12 @@ FfnArgs base_args(const moe_config& c, const int32_t* sorted_ids, const int32_t*
   a.sentinel = c.T * c.k;
   a.mtiles = mtile_bound(c, identity);
   a.rows = identity ? c.T : c.T * c.k + c.N * (c.B - 1);
+  if (!identity && expert_choice(c)) {  // rows hold token ids; y is written by padded row
+    a.k = 1;
+    a.sentinel = c.T;
+    a.rows = c.N * ec_segment(c);
+    a.dest_is_row = 1;
+  }
   return a;
 }
 
@@ -652,6 +663,7 @@ hipError_t launch_gate_up(const moe_config& c, const void* h, const int32_t* sor
   a.out = act;
   if (c.expert_dtype == MOE_F32) {
     const long n = (long)a.rows * c.I;
+    if (n == 0) return hipSuccess;
     ffn_w13_f32<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(a, a.rows);
     return hipGetLastError();
   }
@@ -670,6 +682,7 @@ hipError_t launch_down(const moe_config& c, const void* act, const int32_t* sort
   a.out = y;
   if (c.expert_dtype == MOE_F32) {
     const long n = (long)a.rows * c.H;
+    if (n == 0) return hipSuccess;
     ffn_w2_f32<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(a, a.rows);
     return hipGetLastError();
   }

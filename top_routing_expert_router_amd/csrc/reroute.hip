@@ -180,6 +180,8 @@ __global__ __launch_bounds__(kRThreads) void reroute_capacity(const int32_t* __r
     stats[N + MOE_STAT_MAX_LOAD] = sh_max;
     stats[N + MOE_STAT_MIN_LOAD] = sh_min;
     stats[N + MOE_STAT_REROUTED] = sh_rer;
+    stats[N + MOE_STAT_UNPICKED] = 0;  // expert-choice counters
+    stats[N + MOE_STAT_MAX_PICKS] = 0;
   }
 }
 

@@ -42,10 +42,15 @@ typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 // written, and weight_j = exp(l_{id_j} - m), m the largest recorded logit (an id
 // outside [0, N) weighs 0); the margin is still this run's.  Replaying a run's own
 // ids gives its gates bit for bit (same values, same order, m = l_0).
+// Expert-choice scores (scores != null; "Mixture-of-experts routing & LLM repeatability",
+// paragraph on expert-choice routing): every expert's softmax value exp(l_e - l_0) / sum
+// over all N, written to scores[t, :] instead of ids, gates and margin -- the same
+// operations, so a token's top-k scores equal its gates with renormalize = 0 bit for bit.
 template <typename RowPtr>
 __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int renormalize, int L,
                                          int32_t* __restrict__ ids, float* __restrict__ gates,
-                                         float* __restrict__ margin, const int32_t* __restrict__ replay) {
+                                         float* __restrict__ margin, const int32_t* __restrict__ replay,
+                                         float* __restrict__ scores) {
   const int lane = threadIdx.x & 63;
   const int g = lane & (L - 1), base = lane - g;
   float lv[4];
@@ -55,6 +60,31 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
     const int e = g + L * i;
     lv[i] = e < N ? row[e] : 0.f;
     key[i] = e < N ? rank_key(lv[i], e) : 0ull;
+  }
+  if (scores != nullptr) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+    best = group_max_u64(best, L);
+    const int e0 = (int)(0xFFFFFFFFu - (uint32_t)best);
+    const int owner = e0 & (L - 1), slot = e0 / L;
+    float mine = lv[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) mine = slot == i ? lv[i] : mine;
+    const float l0 = __shfl(mine, base + owner, kWave);
+    float z = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = g + L * i;
+      if (e < N && lv[i] == lv[i]) z += expf(lv[i] - l0);
+    }
+    const float sum = group_sum_f32(z, L);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = g + L * i;
+      if (e < N) scores[(size_t)t * N + e] = (lv[i] == lv[i] ? expf(lv[i] - l0) : 0.f) / sum;
+    }
+    return;
   }
   const int rounds = k < N ? k + 1 : k;
   float sl[9];
@@ -152,7 +182,8 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
                                                    const float* __restrict__ bias, float* __restrict__ logits,
                                                    int32_t* __restrict__ ids, float* __restrict__ gates,
                                                    float* __restrict__ margin, int T, int H, int N, int k,
-                                                   int renormalize, const int32_t* __restrict__ replay) {
+                                                   int renormalize, const int32_t* __restrict__ replay,
+                                                   float* __restrict__ scores) {
   constexpr int NP = NSUB * 16;
   __shared__ float part[kRouterWaves][NP][kRouterTokens];
   __shared__ float lg[kRouterTokens][NP + 1];
@@ -241,7 +272,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
   const int L = topk_lanes(N);
   const int per_wave = kWave / L;
   for (int t = wave * per_wave + lane / L; t < kRouterTokens; t += kRouterWaves * per_wave)
-    if (t0 + t < T) topk_one(&lg[t][0], t0 + t, N, k, renormalize, L, ids, gates, margin, replay);
+    if (t0 + t < T) topk_one(&lg[t][0], t0 + t, N, k, renormalize, L, ids, gates, margin, replay, scores);
 }
 
 // fp32 projection: one thread per (token, expert), fmaf over H in ascending order.
@@ -264,50 +295,52 @@ __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict
 __global__ __launch_bounds__(256) void topk_gates(const float* __restrict__ logits, int32_t* __restrict__ ids,
                                                    float* __restrict__ gates, float* __restrict__ margin,
                                                    int T, int N, int k, int renormalize,
-                                                   const int32_t* __restrict__ replay) {
+                                                   const int32_t* __restrict__ replay, float* __restrict__ scores) {
   const int L = topk_lanes(N);
   const int t = blockIdx.x * (256 / L) + threadIdx.x / L;
   if (t >= T) return;
-  topk_one(logits + (size_t)t * N, t, N, k, renormalize, L, ids, gates, margin, replay);
+  topk_one(logits + (size_t)t * N, t, N, k, renormalize, L, ids, gates, margin, replay, scores);
 }
 
 template <int NSUB>
 hipError_t launch_router_bf16(const moe_config& c, const void* h, const void* wg, const float* bias, float* logits,
-                              int32_t* ids, float* gates, float* margin, hipStream_t s, const int32_t* replay) {
+                              int32_t* ids, float* gates, float* margin, hipStream_t s, const int32_t* replay,
+                              float* scores) {
   dim3 grid(ceil_div(c.T, kRouterTokens));
   router_bf16<NSUB><<<grid, kRouterThreads, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits, ids, gates, margin, c.T,
-                                         c.H, c.N, c.k, c.renormalize, replay);
+                                         c.H, c.N, c.k, c.renormalize, replay, scores);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_router(const moe_config& c, const void* h, const void* w_gate, const float* bias, float* logits,
-                         int32_t* ids, float* gates, float* margin, hipStream_t s, const int32_t* replay) {
+                         int32_t* ids, float* gates, float* margin, hipStream_t s, const int32_t* replay,
+                         float* scores) {
   if (c.act_dtype == MOE_F32) {
     const long n = (long)c.T * c.N;
     router_logits_f32<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>((const float*)h, (const float*)w_gate, bias,
                                                                         logits, c.T, c.H, c.N);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch_topk(c, logits, ids, gates, margin, s, replay);
+    return launch_topk(c, logits, ids, gates, margin, s, replay, scores);
   }
 #define MOE_ROUTER_CASE(n) \
   case n:                  \
-    return launch_router_bf16<n>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay);
+    return launch_router_bf16<n>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
   switch (ceil_div(c.N, 16)) {
     MOE_ROUTER_CASE(1) MOE_ROUTER_CASE(2) MOE_ROUTER_CASE(3) MOE_ROUTER_CASE(4) MOE_ROUTER_CASE(5)
     MOE_ROUTER_CASE(6) MOE_ROUTER_CASE(7) MOE_ROUTER_CASE(8) MOE_ROUTER_CASE(9) MOE_ROUTER_CASE(10)
     MOE_ROUTER_CASE(11) MOE_ROUTER_CASE(12) MOE_ROUTER_CASE(13) MOE_ROUTER_CASE(14) MOE_ROUTER_CASE(15)
-    default: return launch_router_bf16<16>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay);
+    default: return launch_router_bf16<16>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
   }
 #undef MOE_ROUTER_CASE
 }
 
 hipError_t launch_topk(const moe_config& c, const float* logits, int32_t* ids, float* gates, float* margin,
-                       hipStream_t s, const int32_t* replay) {
+                       hipStream_t s, const int32_t* replay, float* scores) {
   dim3 grid(ceil_div(c.T, 256 / topk_lanes(c.N)));
-  topk_gates<<<grid, 256, 0, s>>>(logits, ids, gates, margin, c.T, c.N, c.k, c.renormalize, replay);
+  topk_gates<<<grid, 256, 0, s>>>(logits, ids, gates, margin, c.T, c.N, c.k, c.renormalize, replay, scores);
   return hipGetLastError();
 }
 

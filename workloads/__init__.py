@@ -47,18 +47,11 @@ class Workload:
     reroute_depth: int = 0     # overflow policy under capacity: 0 drop, d > 0 reroute rounds
     zipf_s: float = 0.0        # additive per-expert logit bias -s*ln(e+1)
     near_tie_frac: float = 0.0 # fraction of tokens given a k-th/(k+1)-th margin < 1e-3
+    routing: str = "token_choice"  # or "expert_choice" (each expert picks its tokens)
     seed: int = 0
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
-
-    @property
-    def routes(self) -> int:
-        return self.T * self.k
-
-    @property
-    def p_max(self) -> int:
-        return self.T * self.k + self.N * (self.B - 1)
 
 
 # The five layer shapes.  c0 is small enough for pure-Python checks, c2 is the
@@ -76,7 +69,15 @@ DEEPSEEKV3_FP8 = Workload("deepseekv3_fp8", T=16384, H=7168, N=256, k=8, I=2048,
 
 # the capacity workload with the reroute overflow policy walking each token's whole ranking
 SWITCH_REROUTE_BF16 = SWITCH_BF16.with_(name="switch_reroute_bf16", reroute_depth=15)
-ALL = {w.name: w for w in (TOY_FP32, SWITCH_BF16, SWITCH_REROUTE_BF16, MIXTRAL_BF16, QWEN3MOE_BF16, DEEPSEEKV3_FP8)}
+# Expert-choice routing on the same inputs ("Mixture-of-experts routing & LLM repeatability",
+# paragraph on expert-choice routing): k is the mean number of experts per token, so each
+# expert takes T*k/N tokens (capacity factor 1) -- as many expert rows as token choice.
+TOY_EC_FP32 = TOY_FP32.with_(name="toy_ec_fp32", routing="expert_choice")
+MIXTRAL_EC_BF16 = MIXTRAL_BF16.with_(name="mixtral_ec_bf16", routing="expert_choice")
+QWEN3MOE_EC_BF16 = QWEN3MOE_BF16.with_(name="qwen3moe_ec_bf16", routing="expert_choice", near_tie_frac=0.0)
+DEEPSEEKV3_EC_FP8 = DEEPSEEKV3_FP8.with_(name="deepseekv3_ec_fp8", routing="expert_choice")
+ALL = {w.name: w for w in (TOY_FP32, SWITCH_BF16, SWITCH_REROUTE_BF16, MIXTRAL_BF16, QWEN3MOE_BF16, DEEPSEEKV3_FP8,
+                           TOY_EC_FP32, MIXTRAL_EC_BF16, QWEN3MOE_EC_BF16, DEEPSEEKV3_EC_FP8)}
 
 
 def _stream_seed(seed: int, name: str, index: int = 0) -> int:
