@@ -169,8 +169,10 @@ def main() -> int:
     d = W.layer_inputs(w, device=dev)
     cfg = M.make_config(w.T, w.H, w.N, w.k, w.I, w.B, cap_num=w.cap_num, cap_den=w.cap_den, n_shared=w.n_shared,
                         renormalize=w.renormalize, act_dtype=w.act_dtype, expert_dtype=w.expert_dtype,
-                        scale_block=w.scale_block, reroute_depth=w.reroute_depth)
+                        scale_block=w.scale_block, reroute_depth=w.reroute_depth, routing=w.routing)
     p_max, n_blocks = M.moe_align_sizes(cfg)
+    ec = w.routing == "expert_choice"
+    C = M.moe_expert_choice_sizes(cfg)[0] if ec else 0
     act_t = torch.float32 if w.act_dtype == W.F32 else torch.bfloat16
     asz = 4 if w.act_dtype == W.F32 else 2
     ws = torch.empty(M.moe_workspace_size(cfg, M.MOE_OP_FORWARD), dtype=torch.uint8, device=dev)
@@ -198,19 +200,27 @@ def main() -> int:
     log(f"[bench] forward: {ms:.4f} ms/step, {value:,.0f} tokens/s")
 
     # ---- per-stage timings through the individual entry points (same buffers)
-    tr = dict(logits=torch.empty(w.T, w.N, device=dev), topk_ids=torch.empty(w.T, w.k, dtype=torch.int32, device=dev),
-              topk_gates=torch.empty(w.T, w.k, device=dev), margin=torch.empty(w.T, device=dev),
-              route_kept=torch.empty(w.T * w.k, dtype=torch.uint8, device=dev),
-              sorted_route_ids=torch.empty(p_max, dtype=torch.int32, device=dev),
-              block_expert=torch.empty(n_blocks, dtype=torch.int32, device=dev),
+    tr = dict(logits=torch.empty(w.T, w.N, device=dev),
+              sorted_route_ids=torch.empty(max(p_max, 1), dtype=torch.int32, device=dev),
+              block_expert=torch.empty(max(n_blocks, 1), dtype=torch.int32, device=dev),
               expert_offsets=torch.empty(w.N + 1, dtype=torch.int32, device=dev),
               num_padded=torch.empty(1, dtype=torch.int32, device=dev),
               stats=torch.empty(w.N + M.STATS_EXTRA, dtype=torch.int32, device=dev),
-              act=torch.empty(p_max, w.I, dtype=act_t, device=dev),
-              y_route=torch.empty(w.T * w.k, w.H, dtype=act_t, device=dev))
+              act=torch.empty(max(p_max, 1), w.I, dtype=act_t, device=dev))
+    if ec:
+        tr.update(scores=torch.empty(w.T, w.N, device=dev),
+                  choice_tokens=torch.empty(max(w.N * C, 1), dtype=torch.int32, device=dev),
+                  choice_slot=torch.empty(w.T, w.N, dtype=torch.int32, device=dev),
+                  choice_margin=torch.empty(w.N, device=dev),
+                  y_route=torch.empty(max(p_max, 1), w.H, dtype=act_t, device=dev))
+    else:
+        tr.update(topk_ids=torch.empty(w.T, w.k, dtype=torch.int32, device=dev),
+                  topk_gates=torch.empty(w.T, w.k, device=dev), margin=torch.empty(w.T, device=dev),
+                  route_kept=torch.empty(w.T * w.k, dtype=torch.uint8, device=dev),
+                  y_route=torch.empty(w.T * w.k, w.H, dtype=act_t, device=dev))
     M.moe_forward(cfg, wts, d["h"], d["residual"], out, tr, ws, stream=stream)
     torch.cuda.synchronize()
-    kept_routes = int(tr["route_kept"].sum().item())
+    kept_routes = w.N * C if ec else int(tr["route_kept"].sum().item())
     aws = torch.empty(M.moe_workspace_size(cfg, M.MOE_OP_ALIGN), dtype=torch.uint8, device=dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)  # larger than L2 + MALL
 
@@ -252,7 +262,11 @@ def main() -> int:
         max(args.steps, 5))
     stages["gate_up_gemm"] = {"us": ms_gate_up * 1e3, "TFLOP/s": gate_up_flops / (ms_gate_up * 1e-3) / 1e12}
     stages["down_gemm"] = {"us": ms_down * 1e3, "TFLOP/s": down_flops / (ms_down * 1e-3) / 1e12}
-    if not args.no_stages:
+    if not args.no_stages and ec:
+        ec_stages(stages, w, cfg, d, wts, tr, out, ws, C, p_max, n_blocks, asz, timed, max(args.steps, 5), stream)
+        for kname, v in stages.items():
+            log(f"[bench] stage {kname}: " + ", ".join(f"{a} {b:,.2f}" for a, b in v.items()))
+    elif not args.no_stages:
         route_bytes = T * H * asz + N * H * asz + T * N * 4 + R * 8 + T * 4
         ms_route = timed(lambda: M.moe_route(cfg, d["h"], wts["w_gate"], wts["logit_bias"], tr["logits"],
                                              tr["topk_ids"], tr["topk_gates"], tr["margin"], stream=stream),
@@ -304,7 +318,8 @@ def main() -> int:
         "data": "synthetic (seeded; Gaussian inits; see DESIGN.md)",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "N": w.N, "k": w.k, "I": w.I, "B": w.B,
                    "expert_dtype": w.expert_dtype, "capacity": None if w.cap_den == 0 else f"{w.cap_num}/{w.cap_den}",
-                   "n_shared": w.n_shared, "kept_routes": kept_routes, "parallelism": "none (1 GPU)"},
+                   "routing": w.routing, "n_shared": w.n_shared, "kept_routes": kept_routes,
+                   "parallelism": "none (1 GPU)"},
         "roofline": roofline, "stages": {k: {a: round(b, 3) for a, b in v.items()} for k, v in stages.items()},
         "measured_ceilings": ceil,
         "cpu_baseline": cpu,
@@ -357,6 +372,35 @@ def ceilings(stream):
     return {k: round(v, 1) for k, v in out.items()}
 
 
+def ec_stages(stages, w, cfg, d, wts, tr, out, ws, C, p_max, n_blocks, asz, timed, reps, stream):
+    """Per-stage timings of an expert-choice layer (scores + picks, picks alone, alignment, combine)."""
+    import top_routing_expert_router_amd as M
+
+    T, H, N = w.T, w.H, w.N
+    tn = T * N * 4
+    # projection reads h and W_g; writes logits, scores, slots; picks and margins are small
+    route_bytes = T * H * asz + N * H * asz + 3 * tn + N * C * 4
+    f = lambda flags: M.moe_route_expert_choice(cfg, d["h"], wts["w_gate"], wts["logit_bias"], tr["logits"],
+                                               tr["scores"], tr["choice_tokens"], tr["choice_slot"],
+                                               tr["choice_margin"], flags=flags, stream=stream)
+    ms = timed(lambda: f(0), reps, True)
+    stages["route_expert_choice"] = {"us": ms * 1e3, "GB/s": route_bytes / (ms * 1e-3) / 1e9}
+    # from given logits: the softmax pass (logits in, scores out) and the per-expert select
+    # (each expert's score column in, its slot column out)
+    ms = timed(lambda: f(M.MOE_ROUTE_LOGITS_IN), reps, True)
+    stages["scores_and_picks"] = {"us": ms * 1e3, "GB/s": (4 * tn + N * C * 4) / (ms * 1e-3) / 1e9}
+    ms = timed(lambda: M.moe_align_expert_choice(cfg, tr["choice_tokens"], tr["choice_slot"], tr["sorted_route_ids"],
+                                                 tr["block_expert"], tr["expert_offsets"], tr["num_padded"],
+                                                 tr["stats"], stream=stream), reps, True)
+    stages["align_expert_choice"] = {"us": ms * 1e3, "GB/s": (N * C * 4 + tn + p_max * 4 + n_blocks * 4) / (ms * 1e-3) / 1e9,
+                                     "unpicked": int(tr["stats"][N + M.STAT["unpicked"]]),
+                                     "max_picks": int(tr["stats"][N + M.STAT["max_picks"]])}
+    comb_bytes = N * C * H * asz + 2 * T * H * asz + 2 * tn
+    ms = timed(lambda: M.moe_combine_expert_choice(cfg, tr["y_route"], tr["scores"], tr["choice_slot"], None,
+                                                   d["residual"], out, stream=stream), reps, True)
+    stages["combine"] = {"us": ms * 1e3, "GB/s": comb_bytes / (ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(w, d, sample: int):
     """The oracle (fp64 numpy) on this workload, restricted to a seeded token sample."""
     import numpy as np
@@ -400,9 +444,14 @@ def cpu_baseline(w, d, sample: int):
                 shared["shared_" + which] = O.dequantize_blocks(t.numpy(), sc, w.scale_block)
             else:
                 shared["shared_" + which] = O.decode_bf16(t.view(torch.int16).numpy().view(np.uint16))
-    res = O.moe_forward(h64, O.decode_bf16(wg_b), expert(w13_b, s13 if fp8 else None), expert(w2_b, s2 if fp8 else None),
-                        k=w.k, B=w.B, cap_num=w.cap_num, cap_den=w.cap_den, residual=h64, tokens=tokens,
-                        bias=bias, reroute_depth=w.reroute_depth, **shared)
+    if w.routing == "expert_choice":
+        res = O.expert_choice_forward(h64, O.decode_bf16(wg_b), expert(w13_b, s13 if fp8 else None),
+                                      expert(w2_b, s2 if fp8 else None), k=w.k, B=w.B, cap_num=w.cap_num,
+                                      cap_den=w.cap_den, residual=h64, tokens=tokens, bias=bias, **shared)
+    else:
+        res = O.moe_forward(h64, O.decode_bf16(wg_b), expert(w13_b, s13 if fp8 else None),
+                            expert(w2_b, s2 if fp8 else None), k=w.k, B=w.B, cap_num=w.cap_num, cap_den=w.cap_den,
+                            residual=h64, tokens=tokens, bias=bias, reroute_depth=w.reroute_depth, **shared)
     dt = time.perf_counter() - t0
     assert res["out"].shape[0] == sample
     log(f"[bench] cpu baseline: {sample} tokens in {dt:.2f} s")

@@ -10,7 +10,8 @@ import workloads as W
 
 def test_cpu_baseline_runs_on_every_weight_format():
     for w in (W.TOY_FP32.with_(expert_dtype=W.F32), W.SWITCH_REROUTE_BF16.with_(T=64, H=128, I=256),
-              W.DEEPSEEKV3_FP8.with_(T=64, H=256, I=256, N=8, k=2)):
+              W.DEEPSEEKV3_FP8.with_(T=64, H=256, I=256, N=8, k=2),
+              W.DEEPSEEKV3_EC_FP8.with_(T=64, H=256, I=256, N=8, k=2), W.MIXTRAL_EC_BF16.with_(T=64, H=128, I=256)):
         if w.act_dtype == W.F32:
             continue  # the baseline decodes bf16 activations (the bench workloads' format)
         d = W.layer_inputs(w, device="cpu")

@@ -87,8 +87,9 @@ __global__ __launch_bounds__(kThreads) void combine_rows(const T* __restrict__ y
 // score[t, e] * y[e * Cp + slot[t, e]]) + shared[t]) + residual[t]), fmaf per term in
 // that order, one rounding ("Mixture-of-experts routing & LLM repeatability", paragraph
 // on expert-choice routing: the gate of a pick is the token's score for that expert).
-// A workgroup's token is uniform, so its slots and scores are scalar loads; experts are
-// taken eight at a time, and the rows of a group's picks are loaded together.
+// The workgroup first lists its token's picks in LDS (thread e looks at expert e; ballot
+// prefix counts keep ascending expert order), then loads the picked rows eight at a
+// time, so a token's few picks among many experts are in flight together.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void combine_ec_rows(const T* __restrict__ y, const float* __restrict__ scores,
                                                              const int32_t* __restrict__ slot,
@@ -96,27 +97,43 @@ __global__ __launch_bounds__(kThreads) void combine_ec_rows(const T* __restrict_
                                                              const T* __restrict__ residual, T* __restrict__ out,
                                                              int H, int N, int C, int Cp, int slices) {
   typedef typename Vec8<T>::type V;
+  __shared__ int s_row[kThreads];
+  __shared__ float s_gate[kThreads];
+  __shared__ int s_cnt[kThreads / kWave];
   const int t = blockIdx.x / slices;
   const long col = (long)(blockIdx.x % slices) * kColsPerBlock + threadIdx.x * kColsPerThread;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  int pos = tid < N ? slot[(long)t * N + tid] : -1;  // N <= kThreads
+  if (pos >= C) pos = -1;                            // slots are < C; anything else is not a pick
+  const bool picked = pos >= 0;
+  const uint64_t bal = __ballot(picked);
+  if (lane == 0) s_cnt[wave] = __popcll(bal);
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) {
+    before += w < wave ? s_cnt[w] : 0;
+    total += s_cnt[w];
+  }
+  if (picked) {
+    const int i = before + __popcll(bal & ((1ull << lane) - 1ull));
+    s_row[i] = tid * Cp + pos;
+    s_gate[i] = scores[(long)t * N + tid];
+  }
+  __syncthreads();
   if (col >= H) return;
-  const int32_t* sl = slot + (long)t * N;
-  const float* sc = scores + (long)t * N;
   float acc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = -0.0f;
-  for (int e0 = 0; e0 < N; e0 += 8) {
-    int pos[8];
+  for (int i0 = 0; i0 < total; i0 += 8) {
     V yv[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pos[j] = e0 + j < N ? sl[e0 + j] : -1;
-      if (pos[j] >= C) pos[j] = -1;  // slots are < C; anything else is not a pick
-      if (pos[j] >= 0) yv[j] = *reinterpret_cast<const V*>(y + ((long)(e0 + j) * Cp + pos[j]) * H + col);
-    }
+    for (int j = 0; j < 8; ++j)
+      if (i0 + j < total) yv[j] = *reinterpret_cast<const V*>(y + (long)s_row[i0 + j] * H + col);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (pos[j] >= 0) {
-        const float g = sc[e0 + j];
+      if (i0 + j < total) {
+        const float g = s_gate[i0 + j];
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, (float)yv[j][q], acc[q]);
       }
