@@ -108,6 +108,40 @@ __device__ void build_tile_table(const FfnArgs& a, int* beg, int* mt0) {
   __syncthreads();
 }
 
+// A pointer that is the same in every lane, made scalar: a 64-bit product may be
+// computed on the vector unit, and a buffer resource built from it must be scalar.
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (void*)(((uint64_t)hi << 32) | lo);
+}
+
+// Buffer resources of a tile's operands, built from scalar values where they are used
+// (a resource carried from tile to tile can end up in VGPRs, and every copy then
+// becomes a waterfall loop).  A: all of h (W13, gathered rows) or the tile's own act
+// rows (W2, contiguous from p0).  B: expert e's weights.
+template <int MODE>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t act_rsrc(const __bf16* X, int T, int K, int p0, int p1) {
+  p0 = __builtin_amdgcn_readfirstlane(p0);
+  p1 = __builtin_amdgcn_readfirstlane(p1);
+  if constexpr (MODE == 0)
+    return __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)((unsigned)T * K * 2u), kBufferFlags);
+  else
+    return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(X + (long)p0 * K), (short)0,
+                                             (int)((unsigned)(p1 - p0) * K * 2u), kBufferFlags);
+}
+template <bool FP8>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const void* w, int e, int WR, int K) {
+  const long ex = __builtin_amdgcn_readfirstlane(e);
+  if constexpr (!FP8)
+    return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr((const __bf16*)w + ex * WR * K), (short)0,
+                                             (int)((unsigned)WR * K * 2u), kBufferFlags);
+  else
+    return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr((const uint8_t*)w + ex * WR * K), (short)0,
+                                             (int)((unsigned)WR * K), kBufferFlags);
+}
+
 // One output tile: expert e, padded rows [p0, p1), weight n-tile nt.
 struct Tile {
   int e, p0, p1, nt;
@@ -134,13 +168,13 @@ __device__ __forceinline__ void lds_barrier() {
 
 // MODE 0: W13 + SwiGLU -> act.  MODE 1: W2 -> y rows.
 //
-// Two tile modes over the same 256-row weight tile (W13: 128 gate and the matching
-// 128 up rows):
-//  - full (up to 256 activation rows): waves 2 x 2, each 128 rows x 128 weight rows;
-//  - half (an m-tile with at most 128 valid rows, as the last tile of an expert often
-//    is): all 4 waves on the same 128 rows, each with 64 weight rows -- half the MFMAs
-//    of a full tile instead of the same number on empty rows.
-// An output element's K order is the same in both modes (one MFMA chain over K in
+// Three tile modes over the same 256-row weight tile (W13: 128 gate and the matching
+// 128 up rows), by the m-tile's valid rows R:
+//  - full (R > 128): waves 2 x 2, each 128 rows x 128 weight rows;
+//  - half (64 < R <= 128, as the last tile of an expert often is): all 4 waves on the
+//    same 128 rows, each with 64 weight rows -- half the MFMAs of a full tile;
+//  - quarter (R <= 64): all 4 waves on the same 64 rows, each with 64 weight rows.
+// An output element's K order is the same in every mode (one MFMA chain over K in
 // ascending 16-wide steps), so the mode changes no output bit.
 template <int MODE, bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffn_gemm_bf16(FfnArgs a) {
@@ -197,7 +231,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     t.p0 = __builtin_amdgcn_readfirstlane(t_beg[lo] + (m - t_mt0[lo]) * BM);
     t.p1 = __builtin_amdgcn_readfirstlane(min(min(t_beg[lo + 1], t.p0 + BM), a.rows));
   };
-  auto is_half = [&](const Tile& t) { return t.p1 - t.p0 <= BM / 2; };
+  // activation rows a tile mode covers: 256 (full), 128 (half) or 64 (quarter)
+  auto tile_rows = [&](const Tile& t) {
+    const int r = __builtin_amdgcn_readfirstlane(t.p1 - t.p0);
+    return r <= BM / 4 ? BM / 4 : (r <= BM / 2 ? BM / 2 : BM);
+  };
   Tile cur;
   decode(lid, cur);
 
@@ -209,17 +247,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // in physical 16-byte chunk L % 8 of its row, so it fetches the logical chunk that
   // the swizzle puts there (the swizzle is an involution in the chunk index).
   // Activation rows: wave w fills rows [64 w, 64 w + 64) of a full tile (8
-  // instructions), [32 w, 32 w + 32) of a half tile (4).  Weight rows: wave w fills
-  // rows [64 w, 64 w + 64) in both modes.
+  // instructions), [32 w, 32 w + 32) of a half tile (4), [16 w, 16 w + 16) of a quarter
+  // tile (2).  Weight rows: wave w fills rows [64 w, 64 w + 64) in every mode.
   const int drow = lane >> 3;                    // row within the 8-row group
-  auto arow_of = [&](bool half, int j) { return wave * (half ? 32 : 64) + j * 8 + drow; };
+  auto arow_of = [&](int rows, int j) { return wave * (rows / 4) + j * 8 + drow; };
   auto brow_of = [&](int j) { return wave * (TBN / 4) + j * 8 + drow; };
   // The copies are buffer loads with LDS destination: a buffer resource per operand
   // (base address + byte size, out-of-range reads return zeros) and a 32-bit byte
-  // offset per lane.
+  // offset per lane.  The resources are rebuilt from the tile's (scalar) fields where
+  // they are used rather than carried from tile to tile, so they stay in SGPRs (a
+  // carried resource can end up in VGPRs, and every copy then becomes a waterfall loop).
   const __bf16* X = (const __bf16*)a.x;
-  __amdgpu_buffer_rsrc_t rsrcA = __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, 0, kBufferFlags);
-  __amdgpu_buffer_rsrc_t rsrcB = rsrcA;
   uint32_t aoff[8];                              // byte offset of each of the lane's A rows
   uint32_t boff[8];                              // byte offset of each of the lane's weight rows
   auto weight_row = [&](int n0, int j) {  // j = tile row
@@ -234,40 +272,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // Buffers, offsets and weight rows of tile t.  A: all of h (MODE 0, gathered
   // rows) or the tile's own act rows (MODE 1, contiguous from p0).  B: expert e.
   auto setup = [&](const Tile& t) {
-    const bool half = is_half(t);
-    rsrcA = MODE == 0
-                ? __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)((unsigned)a.T * K * 2u), kBufferFlags)
-                : __builtin_amdgcn_make_buffer_rsrc((void*)(X + (long)t.p0 * K), (short)0,
-                                                    (int)((unsigned)(t.p1 - t.p0) * K * 2u), kBufferFlags);
+    const int rows = tile_rows(t);
+    // Rows outside the tile or padding rows read a harmless valid row (token 0, or a
+    // row of the tile's own act block); their results are never stored (rows never
+    // interact in the product).  W13 gathers token rows: the eight route ids are loaded
+    // unconditionally (index clamped into the tile), so the loads are in flight together.
+    // W2 reads the tile's act rows in order and needs no route id.
+    int rid[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      rid[j] = (MODE == 0 && a.sorted != nullptr) ? a.sorted[min(t.p0 + arow_of(rows, j), t.p1 - 1)] : 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int ar = arow_of(half, j);
+      const int ar = arow_of(rows, j);
       const int p = t.p0 + ar;
-      // rows outside the tile or padding rows read a harmless valid row (token 0 or
-      // tile row 0); their results are never stored (rows never interact in the product)
       unsigned row = 0;
       if (p < t.p1) {
-        if (a.sorted == nullptr) {
-          row = MODE == 0 ? p : p - t.p0;
-        } else {
-          const int r = a.sorted[p];
-          if ((unsigned)r < (unsigned)a.sentinel) row = MODE == 0 ? r / a.k : p - t.p0;
-        }
+        if (MODE == 1) row = p - t.p0;
+        else if (a.sorted == nullptr) row = p;
+        else if ((unsigned)rid[j] < (unsigned)a.sentinel) row = rid[j] / a.k;
       }
       aoff[j] = (row * (unsigned)K + swz_chunk(ar, lane & 7) * 8) * 2u;
     }
     const int n0 = MODE == 0 ? t.nt * (TBN / 2) : t.nt * TBN;
     if constexpr (!FP8) {
-      const __bf16* Wb = (const __bf16*)a.w + (long)t.e * WR * K;
-      rsrcB = __builtin_amdgcn_make_buffer_rsrc((void*)Wb, (short)0, (int)((unsigned)WR * K * 2u), kBufferFlags);
 #pragma unroll
       for (int j = 0; j < BJ; ++j) {
         const int r = weight_row(n0, brow_of(j));
         boff[j] = ((unsigned)(r < 0 ? 0 : r) * (unsigned)K + swz_chunk(brow_of(j), lane & 7) * 8) * 2u;
       }
     } else {
-      const uint8_t* Wq = (const uint8_t*)a.w + (long)t.e * WR * K;
-      rsrcB = __builtin_amdgcn_make_buffer_rsrc((void*)Wq, (short)0, (int)((unsigned)WR * K), kBufferFlags);
 #pragma unroll
       for (int i = 0; i < BJ; ++i) {
         const int r = weight_row(n0, rb + 32 * i);
@@ -284,8 +318,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   // part 0: the activation-row DMAs (AJ of them); part 1: the weight-row DMAs
   // (bf16) or the weight-code loads into registers (fp8).
-  auto issue_part = [&](auto half_tag, char* sA, char* sB, int k0, int part) {
-    constexpr int AJ = decltype(half_tag)::value ? 4 : 8;
+  auto issue_part = [&](auto rows_tag, const Tile& t, char* sA, char* sB, int k0, int part) {
+    constexpr int AJ = decltype(rows_tag)::value / 32;
+    const __amdgpu_buffer_rsrc_t rsrcA = act_rsrc<MODE>(X, a.T, K, t.p0, t.p1);
+    const __amdgpu_buffer_rsrc_t rsrcB = weight_rsrc<FP8>(a.w, t.e, WR, K);
     if (part == 0) {
 #pragma unroll
       for (int j = 0; j < AJ; ++j)
@@ -301,16 +337,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       sc_hi = (float)a.wscale[srow_hi + k0 / 128];
     }
   };
-  auto issue_loads = [&](auto half_tag, char* sA, char* sB, int k0) {
-    issue_part(half_tag, sA, sB, k0, 0);
-    issue_part(half_tag, sA, sB, k0, 1);
+  auto issue_loads = [&](auto rows_tag, const Tile& t, char* sA, char* sB, int k0) {
+    issue_part(rows_tag, t, sA, sB, k0, 0);
+    issue_part(rows_tag, t, sA, sB, k0, 1);
   };
   // the next tile's first copies, in its own mode (outside any scheduled region)
   auto issue_loads_for = [&](const Tile& t, char* sA, char* sB, int k0) {
-    if (is_half(t))
-      issue_loads(std::true_type{}, sA, sB, k0);
+    const int rows = tile_rows(t);
+    if (rows == BM / 4)
+      issue_loads(std::integral_constant<int, BM / 4>{}, t, sA, sB, k0);
+    else if (rows == BM / 2)
+      issue_loads(std::integral_constant<int, BM / 2>{}, t, sA, sB, k0);
     else
-      issue_loads(std::false_type{}, sA, sB, k0);
+      issue_loads(std::integral_constant<int, BM>{}, t, sA, sB, k0);
   };
   // fp8 only: decode the staged codes, scale, round to bf16 and write the B tile
   auto store_fp8 = [&](char* sB) {
@@ -333,8 +372,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   };
 
   // ---- wave sub-tiles.  Full: rows [wm*128, +128), weight sub-tiles brf[0..3]
-  // (W13: gate 0, 1 and up 2, 3).  Half: rows [0, 128), weight sub-tiles brh[0..1]
-  // (W13: gate 0, up 1).
+  // (W13: gate 0, 1 and up 2, 3).  Half: rows [0, 128), quarter: rows [0, 64); weight
+  // sub-tiles brh[0..1] (W13: gate 0, up 1).
   const int wm = wave & 1, wn = wave >> 1;
   int brf[4], brh[2];
 #pragma unroll
@@ -348,14 +387,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   bf16x8 fw[4][4], fx[4][4];
   int next_lid = 0;
 
-  // ---- one tile, in mode HALF, from its first stage's barrier to its epilogue.
-  // The next tile's first two stages are copied during this tile's tail and epilogue.
-  auto run_tile = [&](auto half_tag, const Tile& t, bool& more, Tile& nxt) {
-    constexpr bool HALF = decltype(half_tag)::value;
-    constexpr int NS = HALF ? 2 : 4;           // weight sub-tiles per wave
-    constexpr int AJ = HALF ? 4 : 8;           // activation DMAs per wave and stage
-    const int* br = HALF ? brh : brf;
-    const int arow0 = HALF ? 0 : wm * 128;
+  // ---- one tile, in the mode of its rows R, from its first stage's barrier to its
+  // epilogue.  The next tile's first two stages are copied during this tile's tail and
+  // epilogue.
+  auto run_tile = [&](auto rows_tag, const Tile& t, bool& more, Tile& nxt) {
+    constexpr int R = decltype(rows_tag)::value;
+    constexpr int NS = R == BM ? 4 : 2;        // weight sub-tiles per wave
+    constexpr int MSUB = R == BM / 4 ? 2 : 4;  // 32-row activation sub-tiles per wave
+    constexpr int AJ = R / 32;                 // activation DMAs per wave and stage
+    const int* br = R == BM ? brf : brh;
+    const int arow0 = R == BM ? wm * 128 : 0;
     // fragment addresses are computed per tile from an opaque copy of the lane
     // index: hoisted out of the tile loop, both modes' addresses would stay live
     // together and spill
@@ -368,14 +409,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) wf[ns] = *reinterpret_cast<const bf16x8*>(sB + swz(br[ns] + l32, ch));
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms) xf[ms] = *reinterpret_cast<const bf16x8*>(sA + swz(arow0 + ms * 32 + l32, ch));
+      for (int ms = 0; ms < MSUB; ++ms) xf[ms] = *reinterpret_cast<const bf16x8*>(sA + swz(arow0 + ms * 32 + l32, ch));
     };
     // first: the tile's first K step, which starts every accumulator from zero
     auto mfma_step = [&](const bf16x8* wf, const bf16x8* xf, bool first) {
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
+        for (int ms = 0; ms < MSUB; ++ms)
           acc[ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ns], xf[ms], first ? f32x16{} : acc[ns][ms], 0, 0, 0);
     };
     // Software pipeline over fragments.  Four register sets hold the fragments of
@@ -386,7 +427,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     //   [MFMA s.2 | read (s+1).0] [MFMA s.3 | read (s+1).1]
     // The reads of stage s+1 can start before its half-way barrier because that
     // barrier of stage s already waited for stage s+1's DMA.
-    constexpr int MF = 4 * NS, RD = NS + 4;
+    constexpr int MF = MSUB * NS, RD = NS + MSUB;
     auto step = [&](int mset, const char* sA, const char* sB, int kk, int lset, bool first = false) {
       load_frags(sA, sB, kk, fw[lset], fx[lset]);
       mfma_step(fw[mset], fx[mset], first);
@@ -402,7 +443,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     auto step_dma = [&](int mset, const char* sA, const char* sB, int kk, int lset, char* dA, char* dB, int k0,
                         int part) {
       load_frags(sA, sB, kk, fw[lset], fx[lset]);
-      issue_part(half_tag, dA, dB, k0, part);
+      issue_part(rows_tag, t, dA, dB, k0, part);
       mfma_step(fw[mset], fx[mset], false);
       const int VM = part == 0 ? AJ : BJ;
 #pragma unroll
@@ -472,6 +513,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     __builtin_amdgcn_sched_barrier(0);
     mfma_step(fw[2], fx[2], false);
     mfma_step(fw[3], fx[3], false);
+    // route ids of this lane's four output rows, all in flight together
+    int erid[4];
+#pragma unroll
+    for (int ms = 0; ms < MSUB; ++ms)
+      erid[ms] = (!FP8 && a.sorted != nullptr) ? a.sorted[min(t.p0 + arow0 + ms * 32 + l32, t.p1 - 1)] : 0;
 
     // ---- epilogue.  Lane holds row (lane & 31) of each 32-row sub-tile and, per
     // register group g, the 4 consecutive columns 8 g + 4 (lane >> 5) + [0, 4) of a
@@ -481,10 +527,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (MODE == 0) {
       __bf16* act = (__bf16*)a.out;
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
+      for (int ms = 0; ms < MSUB; ++ms) {
         const int p = t.p0 + arow0 + ms * 32 + l32;
         bool ok = p < t.p1;
-        if (ok && a.sorted != nullptr) ok = (unsigned)a.sorted[p] < (unsigned)a.sentinel;
+        if (ok && a.sorted != nullptr) ok = (unsigned)(FP8 ? a.sorted[p] : erid[ms]) < (unsigned)a.sentinel;
         if (!ok) continue;
 #pragma unroll
         for (int ns = 0; ns < NS / 2; ++ns) {
@@ -504,12 +550,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     } else {
       __bf16* y = (__bf16*)a.out;
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
+      for (int ms = 0; ms < MSUB; ++ms) {
         const int p = t.p0 + arow0 + ms * 32 + l32;
         if (p >= t.p1) continue;
         int dest = p;
         if (a.sorted != nullptr) {
-          const int r = a.sorted[p];
+          const int r = FP8 ? a.sorted[p] : erid[ms];
           if ((unsigned)r >= (unsigned)a.sentinel) continue;
           if (!a.dest_is_row) dest = r;
         }
@@ -537,10 +583,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   while (true) {
     bool more = false;
     Tile nxt = cur;
-    if (is_half(cur))
-      run_tile(std::true_type{}, cur, more, nxt);
+    const int rows = tile_rows(cur);
+    if (rows == BM / 4)
+      run_tile(std::integral_constant<int, BM / 4>{}, cur, more, nxt);
+    else if (rows == BM / 2)
+      run_tile(std::integral_constant<int, BM / 2>{}, cur, more, nxt);
     else
-      run_tile(std::false_type{}, cur, more, nxt);
+      run_tile(std::integral_constant<int, BM>{}, cur, more, nxt);
     if (!more) break;
     cur = nxt;
     lid = next_lid;
