@@ -342,3 +342,37 @@ def test_forward_end_to_end(name):
     if gone.size and not w.n_shared:
         idx = torch.from_numpy(gone).to(DEV)
         assert torch.equal(out[idx], dv["residual"][idx])
+
+
+@pytest.mark.parametrize("T,N,H", [(300, 256, 1024), (777, 200, 2048), (16384, 256, 7168)])
+def test_route_projection_many_experts(T, N, H):
+    """More than 128 experts take the kernel that stages W_g once per 32 or 64 tokens:
+    logits within 1e-5 x max|l| of the oracle, routes exact away from near ties, and the
+    bits of a token's logits the same whether it runs in a 64-token or a 32-token tile."""
+    w = W.DEEPSEEKV3_FP8.with_(T=T, N=N, H=H)
+    _say("route_projection many experts", T, N, H)
+    h = W.hidden_states(w, device=DEV)
+    wg = W.router_weight(w, device=DEV)
+    cfg = Hn.config(w)
+    b = Hn.route_buffers(w)
+    M.moe_route(cfg, h, wg, None, b["logits"], b["ids"], b["gates"], b["margin"])
+    torch.cuda.synchronize()
+    rows = np.arange(T) if T <= 1024 else np.sort(np.random.default_rng(3).choice(T, 512, replace=False))
+    l_ref = O.router_logits(Hn.f64(h[torch.from_numpy(rows).to(DEV)]), Hn.f64(wg))
+    l_gpu = b["logits"].cpu().double().numpy()[rows]
+    scale = np.max(np.abs(l_ref), axis=1)
+    err = np.max(np.abs(l_gpu - l_ref), axis=1) / scale
+    assert err.max() <= 1e-5, err.max()
+    ids_ref, _, margin_ref = O.topk_route(l_ref, w.k)
+    ids = b["ids"].cpu().numpy()[rows]
+    diff = np.any(ids != ids_ref, axis=1)
+    assert not np.any(diff & ~(margin_ref <= 2e-5 * scale))
+    assert Hn.topk_valid(b["logits"].cpu().double().numpy()[rows], ids).all()
+    # the same tokens alone (a smaller grid, 32-token tiles): the same logit bits
+    sub = torch.from_numpy(rows[:100]).to(DEV)
+    w2 = w.with_(T=100)
+    b2 = Hn.route_buffers(w2)
+    M.moe_route(Hn.config(w2), h[sub].contiguous(), wg, None, b2["logits"], b2["ids"], b2["gates"], b2["margin"])
+    torch.cuda.synchronize()
+    assert torch.equal(b2["logits"].view(torch.int32), b["logits"][sub].view(torch.int32))
+    assert torch.equal(b2["ids"], b["ids"][sub])

@@ -30,6 +30,7 @@ struct RouterUnroll {
 };
 
 typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 // Top-k, gates and margin of one token from its N logits (global or LDS), by one
 // aligned group of L = topk_lanes(N) lanes; a wave ranks 64 / L tokens at once.
@@ -275,6 +276,123 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
     if (t0 + t < T) topk_one(&lg[t][0], t0 + t, N, k, renormalize, L, ids, gates, margin, replay, scores);
 }
 
+// bf16 router for many experts (more than 128), top-k fused.  With one 16-token
+// workgroup per CU, every workgroup would read all of W_g (3.7 MB for 256 experts of
+// 7168), 16 tokens at a time -- the weights, not h, would set the time.  Here a
+// workgroup of NW waves takes TW = 32 or 64 tokens, and each 64-wide K chunk of W_g (all
+// NP padded experts) and of the tokens' rows is staged once in LDS for all waves (loads
+// for chunk c + 2 in flight while chunk c is multiplied).  Wave w computes experts
+// [w NP/NW, (w+1) NP/NW) for all TW tokens with 32x32x16 MFMAs (W_g rows as the A
+// operand, token rows as B), so each logit is one MFMA chain over K in ascending
+// 16-wide steps, then the bias is added: the order depends only on H, not on T or TW.
+// LDS rows are 128 B (8 chunks of 16 B), chunk c of row r stored at c ^ ((r >> 1) & 7):
+// the 32-row fragment reads then hit all 64 banks.
+template <int NP, int TW, int NW>
+__global__ __launch_bounds__(NW * 64) void router_bf16_wide(const __bf16* __restrict__ h, const __bf16* __restrict__ wg,
+                                                        const float* __restrict__ bias, float* __restrict__ logits,
+                                                        int32_t* __restrict__ ids, float* __restrict__ gates,
+                                                        float* __restrict__ margin, int T, int H, int N, int k,
+                                                        int renormalize, const int32_t* __restrict__ replay,
+                                                        float* __restrict__ scores) {
+  constexpr int ROWS = NP + TW;                 // staged rows per chunk: experts, then tokens
+  constexpr int STAGE = ROWS * 128;             // bytes per stage
+  constexpr int RPL = NW * 8;                   // staged rows per load instruction of the workgroup
+  constexpr int LOADS = (ROWS + RPL - 1) / RPL; // 16-byte loads per thread per chunk (the last may be partial)
+  constexpr int ES = NP / NW / 32;              // 32-expert sub-tiles per wave
+  constexpr int TS = TW / 32;                   // 32-token sub-tiles
+  static_assert(ES >= 1, "tile shape");
+  static_assert(2 * STAGE >= TW * (NP + 1) * 4, "the logit rows reuse the staging buffers");
+  __shared__ __attribute__((aligned(16))) char stage[2][STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * TW;
+  auto swz = [](int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); };
+  // copy plan: load i of thread tid moves chunk (tid & 7) of staged row RPL i + (tid >> 3);
+  // expert rows past N and token rows past T read row 0 (their results are never used)
+  const int crow = tid >> 3, cchunk = tid & 7;
+  const __bf16* src[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int r = RPL * i + crow;
+    src[i] = r < NP ? wg + (size_t)(r < N ? r : 0) * H : h + (size_t)(t0 + r - NP < T ? t0 + r - NP : 0) * H;
+    src[i] += cchunk * 8;
+  }
+  // two register buffers: chunk c + 2 is loaded while chunk c is multiplied, so each
+  // load has two chunks' time to arrive before it is stored to LDS
+  u32x4_t bufA[LOADS], bufB[LOADS];
+  auto load = [&](u32x4_t* buf, int c) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      if (ROWS % RPL == 0 || RPL * i + crow < ROWS) buf[i] = *reinterpret_cast<const u32x4_t*>(src[i] + c * 64);
+  };
+  auto store = [&](const u32x4_t* buf, char* st) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      if (ROWS % RPL == 0 || RPL * i + crow < ROWS) *reinterpret_cast<u32x4_t*>(st + swz(RPL * i + crow, cchunk)) = buf[i];
+  };
+  f32x16 acc[ES][TS];
+#pragma unroll
+  for (int es = 0; es < ES; ++es)
+#pragma unroll
+    for (int ts = 0; ts < TS; ++ts) acc[es][ts] = f32x16{};
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int e0 = wave * (NP / NW);
+  const int nchunks = H / 64;
+  auto chunk_mfma = [&](const char* st) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 wf[ES], hf[TS];
+#pragma unroll
+      for (int es = 0; es < ES; ++es)
+        wf[es] = *reinterpret_cast<const bf16x8*>(st + swz(e0 + es * 32 + l32, kk * 2 + kh));
+#pragma unroll
+      for (int ts = 0; ts < TS; ++ts)
+        hf[ts] = *reinterpret_cast<const bf16x8*>(st + swz(NP + ts * 32 + l32, kk * 2 + kh));
+#pragma unroll
+      for (int es = 0; es < ES; ++es)
+#pragma unroll
+        for (int ts = 0; ts < TS; ++ts) acc[es][ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[es], hf[ts], acc[es][ts], 0, 0, 0);
+    }
+  };
+  load(bufA, 0);
+  if (nchunks > 1) load(bufB, 1);
+  store(bufA, stage[0]);
+  __syncthreads();
+  for (int c = 0; c < nchunks; c += 2) {  // chunk c in stage 0, chunk c + 1 in stage 1
+    if (c + 2 < nchunks) load(bufA, c + 2);
+    chunk_mfma(stage[0]);
+    if (c + 1 < nchunks) store(bufB, stage[1]);
+    __syncthreads();
+    if (c + 1 >= nchunks) break;
+    if (c + 3 < nchunks) load(bufB, c + 3);
+    chunk_mfma(stage[1]);
+    if (c + 2 < nchunks) store(bufA, stage[0]);
+    __syncthreads();
+  }
+  // logits of the TW tokens, [TW][NP + 1] floats over the staging buffers: lane holds
+  // token (lane & 31) of each token sub-tile and experts 8 g + 4 (lane >> 5) + q
+  float* lg = reinterpret_cast<float*>(&stage[0][0]);
+#pragma unroll
+  for (int es = 0; es < ES; ++es)
+#pragma unroll
+    for (int ts = 0; ts < TS; ++ts)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = e0 + es * 32 + 8 * (i / 4) + 4 * kh + (i % 4);
+        const int t = ts * 32 + l32;
+        float v = acc[es][ts][i];
+        if (bias && e < N) v += bias[e];
+        lg[t * (NP + 1) + e] = v;
+      }
+  __syncthreads();
+  for (int i = tid; i < TW * N; i += NW * 64) {
+    const int t = i / N, e = i - t * N;
+    if (t0 + t < T) logits[(size_t)(t0 + t) * N + e] = lg[t * (NP + 1) + e];
+  }
+  const int L = topk_lanes(N);  // 64: one token per wave at a time
+  for (int t = wave; t < TW; t += NW)
+    if (t0 + t < T) topk_one(lg + t * (NP + 1), t0 + t, N, k, renormalize, L, ids, gates, margin, replay, scores);
+}
+
 // fp32 projection: one thread per (token, expert), fmaf over H in ascending order.
 __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict__ h, const float* __restrict__ wg,
                                                           const float* __restrict__ bias,
@@ -312,6 +430,27 @@ hipError_t launch_router_bf16(const moe_config& c, const void* h, const void* wg
   return hipGetLastError();
 }
 
+template <int NP>
+hipError_t launch_router_wide(const moe_config& c, const void* h, const void* wg, const float* bias, float* logits,
+                              int32_t* ids, float* gates, float* margin, hipStream_t s, const int32_t* replay,
+                              float* scores) {
+  int dev = 0, cus = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  // 64 tokens per workgroup when that still gives every CU a workgroup, else 32
+  constexpr int NW = 8;
+  if (ceil_div(c.T, 64) >= cus)
+    router_bf16_wide<NP, 64, NW><<<ceil_div(c.T, 64), NW * 64, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits,
+                                                                        ids, gates, margin, c.T, c.H, c.N, c.k,
+                                                                        c.renormalize, replay, scores);
+  else
+    router_bf16_wide<NP, 32, NW><<<ceil_div(c.T, 32), NW * 64, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits,
+                                                                        ids, gates, margin, c.T, c.H, c.N, c.k,
+                                                                        c.renormalize, replay, scores);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_router(const moe_config& c, const void* h, const void* w_gate, const float* bias, float* logits,
@@ -325,6 +464,9 @@ hipError_t launch_router(const moe_config& c, const void* h, const void* w_gate,
     if (err != hipSuccess) return err;
     return launch_topk(c, logits, ids, gates, margin, s, replay, scores);
   }
+  // more than 128 experts: W_g staged once per 64 tokens (for up to 128 the 16-token
+  // kernel below measured faster)
+  if (c.N > 128) return launch_router_wide<256>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
 #define MOE_ROUTER_CASE(n) \
   case n:                  \
     return launch_router_bf16<n>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
