@@ -52,8 +52,11 @@ def _traffic(workload: str, launches_per_unit: float):
 
 # rocprofv3 kernel-name fragments -> stage names used in the counter summary
 _COUNTER_KERNELS = [("ffn_gemm_bf16<0", "gate_up_gemm"), ("ffn_gemm_bf16<1", "down_gemm"),
-                    ("router_bf16", "route"), ("topk_gates", "route_topk"), ("align_hist", "align_hist"),
-                    ("align_scan", "align_scan"), ("align_scatter", "align_scatter"),
+                    ("router_bf16_wide", "route_wide"), ("router_bf16", "route"), ("topk_gates", "route_topk"),
+                    ("align_hist", "align_hist"), ("align_scan", "align_scan"), ("align_scatter", "align_scatter"),
+                    ("align_fused", "align_one_workgroup"), ("ec_select", "expert_choice_select"),
+                    ("ec_align", "align_expert_choice"), ("combine_ec_rows", "combine_expert_choice"),
+                    ("reroute_capacity", "reroute"),
                     ("combine_rows", "combine"), ("copy16", "ceiling_copy_1GiB"), ("read16", "ceiling_read_1GiB"),
                     ("mfma_loop<1>", "ceiling_mfma_1wave"), ("mfma_loop<2>", "ceiling_mfma_2wave")]
 

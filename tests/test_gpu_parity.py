@@ -142,6 +142,11 @@ ALIGN_CASES = [
     ("skewed_cap", 3000, 32, 4, 32, 1, 1, 1.5),
     ("ragged", 1, 3, 2, 128, 0, 0, 0.0),
     ("max_t", 65536, 64, 8, 128, 3, 2, 0.5),
+    # one-workgroup alignment up to 8192 routes, three kernels above: both sides of the
+    # switch, 256 experts, invalid ids (one of them the last route)
+    ("one_wg_max", 8192, 256, 1, 64, 3, 2, 0.8),
+    ("three_kernel_min", 8193, 256, 1, 64, 3, 2, 0.8),
+    ("one_wg_k8", 1000, 256, 8, 32, 0, 0, 0.3),
 ]
 
 
@@ -156,6 +161,11 @@ def test_align_bit_exact(case):
         ids[5, 0] = -1
         ids[77, 3] = N
         ids[100, 7] = 1 << 20
+    if name in ("one_wg_max", "three_kernel_min", "one_wg_k8"):
+        flat = ids.view(-1)
+        flat[5] = -1
+        flat[77] = N
+        flat[-1] = 1 << 20
     cfg = Hn.config(w)
     b = Hn.run_align(cfg, w, ids.to(DEV))
     torch.cuda.synchronize()

@@ -30,33 +30,6 @@ namespace {
 constexpr int kRThreads = 1024;
 constexpr int kRWaves = kRThreads / kWave;
 
-// Position of this lane's key (0..N-1; -1 = none) among the keys of this chunk of
-// kRThreads entries that come before it in chunk order, plus base[key]; afterwards
-// base[key] has grown by the chunk's count of that key.  Called by every thread.
-__device__ int chunk_position(int key, int N, int* base, int (*cnt)[256]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  for (int i = tid; i < kRWaves * N; i += kRThreads) cnt[i / N][i % N] = 0;
-  __syncthreads();
-  const bool valid = key >= 0;
-  const uint64_t peers = peer_mask(valid ? key : 256);
-  if (valid && (peers & lt) == 0) cnt[wave][key] = __popcll(peers);  // one writer per (wave, key)
-  __syncthreads();
-  for (int e = tid; e < N; e += kRThreads) {
-    int acc = base[e];
-    for (int w = 0; w < kRWaves; ++w) {
-      const int c = cnt[w][e];
-      cnt[w][e] = acc;
-      acc += c;
-    }
-    base[e] = acc;
-  }
-  __syncthreads();
-  const int pos = valid ? cnt[wave][key] + __popcll(peers & lt) : -1;
-  __syncthreads();
-  return pos;
-}
-
 __global__ __launch_bounds__(kRThreads) void reroute_capacity(const int32_t* __restrict__ ids,
                                                               const float* __restrict__ logits, int T, int N,
                                                               int k, int cap, int depth,
@@ -83,7 +56,7 @@ __global__ __launch_bounds__(kRThreads) void reroute_capacity(const int32_t* __r
     const int r = r0 + tid;
     const int e = r < R ? ids[r] : -1;
     const bool valid = e >= 0 && e < N;
-    const int pos = chunk_position(valid ? e : -1, N, base, cnt);
+    const int pos = chunk_position<kRThreads>(valid ? e : -1, N, base, cnt);
     if (r < R) route_expert[r] = (valid && (cap < 0 || pos < cap)) ? e : -1;
   }
   // base[e] is now expert e's routed load (before capacity)
@@ -146,7 +119,7 @@ __global__ __launch_bounds__(kRThreads) void reroute_capacity(const int32_t* __r
           if (want >= 0) offered[t] = best;
         }
       }
-      const int pos = chunk_position(want, N, base, cnt);
+      const int pos = chunk_position<kRThreads>(want, N, base, cnt);
       if (want >= 0) {
         sh_any = 1;
         if (pos < room[want]) route_expert[route] = want;
