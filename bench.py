@@ -293,6 +293,26 @@ def main() -> int:
         ms_comb = timed(lambda: M.moe_combine(cfg, tr["y_route"], tr["topk_gates"], tr["route_kept"], None,
                                               d["residual"], out, stream=stream), max(args.steps, 5), True)
         stages["combine"] = {"us": ms_comb * 1e3, "GB/s": comb_bytes / (ms_comb * 1e-3) / 1e9}
+        if "align" in stages:
+            # the same kernels back to back in forward order (no flush between them): what
+            # each stage costs inside the layer, with the caches and clocks it sees there
+            chain = timed_chain(
+                [lambda: M.moe_route(cfg, d["h"], wts["w_gate"], wts["logit_bias"], tr["logits"], tr["topk_ids"],
+                                     tr["topk_gates"], tr["margin"], stream=stream),
+                 lambda: M.moe_align(cfg, tr["topk_ids"], tr["route_kept"], tr["sorted_route_ids"],
+                                     tr["block_expert"], tr["expert_offsets"], tr["num_padded"], tr["stats"], aws,
+                                     stream=stream),
+                 lambda: M.moe_expert_gate_up(cfg, d["h"], tr["sorted_route_ids"], tr["expert_offsets"], d["w13"],
+                                              d.get("w13_scale"), tr["act"], stream=stream),
+                 lambda: M.moe_expert_down(cfg, tr["act"], tr["sorted_route_ids"], tr["expert_offsets"], d["w2"],
+                                           d.get("w2_scale"), tr["y_route"], stream=stream),
+                 lambda: M.moe_combine(cfg, tr["y_route"], tr["topk_gates"], tr["route_kept"], None, d["residual"],
+                                       out, stream=stream)],
+                max(args.steps, 5))
+            for name, ms, nbytes in (("route", chain[0], route_bytes), ("align", chain[1], align_bytes),
+                                     ("combine", chain[4], comb_bytes)):
+                stages[name]["in_forward_us"] = ms * 1e3
+                stages[name]["in_forward_GB/s"] = nbytes / (ms * 1e-3) / 1e9
         # router replay: the whole layer on the recorded ids of the forward above
         ms_replay = timed(lambda: M.moe_forward_replay(cfg, wts, d["h"], d["residual"], tr["topk_ids"], out, None, ws,
                                                        stream=stream), max(args.steps, 5), False)
