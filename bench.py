@@ -239,34 +239,35 @@ def main() -> int:
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in es) / reps  # ms per launch
 
-    def timed_chain(fns, reps):
-        """Per-launch time of each fn when they run in sequence, as they do in the forward
-        (so each kernel sees the clocks and caches it sees there)."""
-        es = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(reps)]
-        for f in fns:
-            f()
-        for ev in es:
-            ev[0].record(stream)
-            for f, e in zip(fns, ev[1:]):
-                f()
-                e.record(stream)
+    def in_forward(reps):
+        """Stage times inside the layer: moe_forward with the trace's stage events (the
+        kernels exactly as the forward launches them, each seeing the clocks and caches it
+        sees there).  ms per stage: route, align, W13, W2, shared expert, combine."""
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(M.TRACE_EVENTS)] for _ in range(reps)]
+        M.moe_forward(cfg, wts, d["h"], d["residual"], out, {"stage_events": evs[0]}, ws, stream=stream)
         torch.cuda.synchronize()
-        return [sum(ev[i].elapsed_time(ev[i + 1]) for ev in es) / reps for i in range(len(fns))]
+        for ev in evs:
+            M.moe_forward(cfg, wts, d["h"], d["residual"], out, {"stage_events": ev}, ws, stream=stream)
+        torch.cuda.synchronize()
+        return [sum(ev[i].elapsed_time(ev[i + 1]) for ev in evs) / reps for i in range(M.TRACE_EVENTS - 1)]
 
     R, T, H, I, N, k = w.T * w.k, w.T, w.H, w.I, w.N, w.k
     stages = {}
     gate_up_flops = 4.0 * kept_routes * H * I
     down_flops = 2.0 * kept_routes * H * I
-    ms_gate_up, ms_down = timed_chain(
-        [lambda: M.moe_expert_gate_up(cfg, d["h"], tr["sorted_route_ids"], tr["expert_offsets"],
-                                      d["w13"], d.get("w13_scale"), tr["act"], stream=stream),
-         lambda: M.moe_expert_down(cfg, tr["act"], tr["sorted_route_ids"], tr["expert_offsets"],
-                                   d["w2"], d.get("w2_scale"), tr["y_route"], stream=stream)],
-        max(args.steps, 5))
+    fwd_stage_ms = in_forward(max(args.steps, 5))
+    ms_gate_up, ms_down = fwd_stage_ms[2], fwd_stage_ms[3]
     stages["gate_up_gemm"] = {"us": ms_gate_up * 1e3, "TFLOP/s": gate_up_flops / (ms_gate_up * 1e-3) / 1e12}
     stages["down_gemm"] = {"us": ms_down * 1e3, "TFLOP/s": down_flops / (ms_down * 1e-3) / 1e12}
+    if w.n_shared:
+        sh_flops = 6.0 * T * H * I * w.n_shared
+        stages["shared_expert"] = {"us": fwd_stage_ms[4] * 1e3,
+                                   "TFLOP/s": sh_flops / (fwd_stage_ms[4] * 1e-3) / 1e12}
     if not args.no_stages and ec:
         ec_stages(stages, w, cfg, d, wts, tr, out, ws, C, p_max, n_blocks, asz, timed, max(args.steps, 5), stream)
+        for name, ms_stage in (("route_expert_choice", fwd_stage_ms[0]), ("align_expert_choice", fwd_stage_ms[1]),
+                               ("combine", fwd_stage_ms[5])):
+            stages[name]["in_forward_us"] = ms_stage * 1e3
         for kname, v in stages.items():
             log(f"[bench] stage {kname}: " + ", ".join(f"{a} {b:,.2f}" for a, b in v.items()))
     elif not args.no_stages:
@@ -293,26 +294,12 @@ def main() -> int:
         ms_comb = timed(lambda: M.moe_combine(cfg, tr["y_route"], tr["topk_gates"], tr["route_kept"], None,
                                               d["residual"], out, stream=stream), max(args.steps, 5), True)
         stages["combine"] = {"us": ms_comb * 1e3, "GB/s": comb_bytes / (ms_comb * 1e-3) / 1e9}
-        if "align" in stages:
-            # the same kernels back to back in forward order (no flush between them): what
-            # each stage costs inside the layer, with the caches and clocks it sees there
-            chain = timed_chain(
-                [lambda: M.moe_route(cfg, d["h"], wts["w_gate"], wts["logit_bias"], tr["logits"], tr["topk_ids"],
-                                     tr["topk_gates"], tr["margin"], stream=stream),
-                 lambda: M.moe_align(cfg, tr["topk_ids"], tr["route_kept"], tr["sorted_route_ids"],
-                                     tr["block_expert"], tr["expert_offsets"], tr["num_padded"], tr["stats"], aws,
-                                     stream=stream),
-                 lambda: M.moe_expert_gate_up(cfg, d["h"], tr["sorted_route_ids"], tr["expert_offsets"], d["w13"],
-                                              d.get("w13_scale"), tr["act"], stream=stream),
-                 lambda: M.moe_expert_down(cfg, tr["act"], tr["sorted_route_ids"], tr["expert_offsets"], d["w2"],
-                                           d.get("w2_scale"), tr["y_route"], stream=stream),
-                 lambda: M.moe_combine(cfg, tr["y_route"], tr["topk_gates"], tr["route_kept"], None, d["residual"],
-                                       out, stream=stream)],
-                max(args.steps, 5))
-            for name, ms, nbytes in (("route", chain[0], route_bytes), ("align", chain[1], align_bytes),
-                                     ("combine", chain[4], comb_bytes)):
-                stages[name]["in_forward_us"] = ms * 1e3
-                stages[name]["in_forward_GB/s"] = nbytes / (ms * 1e-3) / 1e9
+        for name, ms_stage, nbytes in (("route", fwd_stage_ms[0], route_bytes),
+                                       ("align" if "align" in stages else "align_reroute", fwd_stage_ms[1],
+                                        align_bytes),
+                                       ("combine", fwd_stage_ms[5], comb_bytes)):
+            stages[name]["in_forward_us"] = ms_stage * 1e3
+            stages[name]["in_forward_GB/s"] = nbytes / (ms_stage * 1e-3) / 1e9
         # router replay: the whole layer on the recorded ids of the forward above
         ms_replay = timed(lambda: M.moe_forward_replay(cfg, wts, d["h"], d["residual"], tr["topk_ids"], out, None, ws,
                                                        stream=stream), max(args.steps, 5), False)

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef int32_t moe_status;
 enum {
@@ -192,7 +192,17 @@ typedef struct moe_trace {
   int32_t* choice_tokens;    /* [N, C] */
   int32_t* choice_slot;      /* [T, N] */
   float* choice_margin;      /* [N] */
+  /* Nullable: MOE_TRACE_EVENTS HIP events (hipEvent_t, created by the caller, with timing
+   * enabled), recorded on the forward's stream around its stages: [0] before the router,
+   * [1] after routing (expert choice: scores and picks), [2] after the alignment, [3]
+   * after the W13 + SwiGLU GEMM, [4] after the W2 GEMM, [5] after the shared expert (the
+   * same point as [4] without one), [6] after the combine.  The time between two
+   * consecutive events is that stage as it runs inside the layer.  A failed record is
+   * returned as MOE_ERR_HIP. */
+  void* const* stage_events;
 } moe_trace;
+
+#define MOE_TRACE_EVENTS 7
 
 /* ABI version (MOE_ABI_VERSION) of the loaded library. */
 int32_t moe_abi_version(void);

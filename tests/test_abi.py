@@ -53,7 +53,7 @@ def test_ceiling_library_exports_and_rejects_bad_arguments():
 
 
 def test_abi_version_and_status_strings():
-    assert M.moe_abi_version() == 3
+    assert M.moe_abi_version() == 4
     for code, name in M.STATUS.items():
         assert M.moe_status_str(code).startswith(name)
     assert "unknown" in M.moe_status_str(99)
@@ -207,3 +207,27 @@ def test_expert_choice_host_validation():
     assert M.moe_expert_choice_sizes(ec) == (1024, 1024)
     assert M.moe_expert_choice_sizes(config(W.MIXTRAL_EC_BF16, T=5, cap_num=1, cap_den=1)) == (1, 64)
     assert M.moe_expert_choice_sizes(config(W.MIXTRAL_EC_BF16, T=3, k=1)) == (0, 0)
+
+
+def _header_fields(struct: str):
+    """Member names of a struct in include/moe.h, in declaration order."""
+    import os
+    import re
+    text = open(os.path.join(os.path.dirname(__file__), "..", "include", "moe.h")).read()
+    body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (struct, struct), text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    return [re.search(r"(\w+)\s*(\[[^\]]*\])?\s*$", d.strip()).group(1) for d in body.split(";") if d.strip()]
+
+
+def test_binding_structs_match_the_header():
+    # the ctypes mirrors must list the C members in the same order (all pointer-sized here)
+    assert [n for n, _ in M.moe_trace._fields_] == _header_fields("moe_trace")
+    assert [n for n, _ in M.moe_weights._fields_] == _header_fields("moe_weights")
+    assert M.TRACE_EVENTS == 7
+
+
+def test_stage_events_argument_checked_by_the_binding():
+    with pytest.raises(ValueError):
+        M._trace_struct({"stage_events": [0, 0, 0]})
+    tr, arr = M._trace_struct({"stage_events": [0] * M.TRACE_EVENTS})
+    assert arr is not None and len(arr) == M.TRACE_EVENTS

@@ -1,0 +1,114 @@
+"""Tile modes of the grouped down-projection GEMM give the same bits.
+
+On the Mixtral-shaped layer the down projection makes one to four rounds of 256x256
+tiles over the CUs, so an expert's last m-tile of at most 128 rows runs as two narrow
+tiles (128 weight rows each, 128-deep stages), scheduled after the full-height tiles.
+Every output element is still one MFMA chain over K in ascending 16-wide steps, so each
+y row must equal, bit for bit, the same row computed in a problem small enough that no
+narrow tile is used (one expert's rows in identity mode: full, half or quarter tiles).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import top_routing_expert_router_amd as M
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    M.lib()
+
+
+def test_w2_narrow_tiles_match_standard_tiles():
+    T, H, N, k, I, B = 4096, 4096, 8, 2, 14336, 64
+    # expert loads: last m-tiles of 64 (expert 1) and 128 rows (expert 2) become narrow
+    # tiles; 1000 and 952 leave padded, partly empty last tiles of 256 and 192 rows
+    loads = [1024, 1088, 1152, 1024, 1000, 1000, 952, 952]
+    assert sum(loads) == T * k
+    _say("w2 narrow tiles vs standard tiles, loads", loads)
+    g = torch.Generator().manual_seed(5)
+    perm = torch.randperm(T * k, generator=g).numpy()
+    cfg = M.make_config(T, H, N, k, I, B)
+    p_max, _ = M.moe_align_sizes(cfg)
+    sorted_ids = np.full(p_max, T * k, dtype=np.int32)
+    offsets = np.zeros(N + 1, dtype=np.int32)
+    pos = 0
+    for e, n in enumerate(loads):
+        offsets[e] = sum(-(-x // B) * B for x in loads[:e])
+        sorted_ids[offsets[e]:offsets[e] + n] = np.sort(perm[pos:pos + n])
+        pos += n
+    offsets[N] = sum(-(-x // B) * B for x in loads)
+    gd = torch.Generator(device=DEV).manual_seed(6)
+    act = (torch.randn(p_max, I, device=DEV, generator=gd) * 0.05).to(torch.bfloat16)
+    w2 = (torch.randn(N, H, I, device=DEV, generator=gd) / I ** 0.5).to(torch.bfloat16)
+    y = torch.full((T * k, H), 7.0, dtype=torch.bfloat16, device=DEV)
+    sd = torch.from_numpy(sorted_ids).to(DEV)
+    od = torch.from_numpy(offsets).to(DEV)
+    M.moe_expert_down(cfg, act, sd, od, w2, None, y)
+    torch.cuda.synchronize()
+    checked = 0
+    for e, n in enumerate(loads):
+        seg = -(-n // B) * B
+        # one expert's padded rows alone, identity rows: at most 5 x 16 tiles, no narrow tiles
+        ce = M.make_config(seg, H, 1, 1, I, B)
+        ye = torch.empty(seg, H, dtype=torch.bfloat16, device=DEV)
+        M.moe_expert_down(ce, act[offsets[e]:offsets[e] + seg].contiguous(), None, None, w2[e:e + 1].contiguous(),
+                          None, ye)
+        torch.cuda.synchronize()
+        routes = torch.from_numpy(sorted_ids[offsets[e]:offsets[e] + n].astype(np.int64)).to(DEV)
+        got = y[routes].view(torch.int16)
+        want = ye[:n].view(torch.int16)
+        bad = (got != want).any(dim=1).nonzero().flatten()
+        assert bad.numel() == 0, (e, bad[:8].tolist())
+        checked += n
+    assert checked == T * k  # every y row (all filled with 7.0 before) was compared
+    _say(f"  {checked} y rows bitwise equal to the standard-tile results")
+
+
+@pytest.mark.parametrize("name", ["toy_fp32", "mixtral_bf16", "mixtral_ec_bf16", "deepseekv3_fp8"])
+def test_forward_stage_events(name):
+    """Trace stage events: recorded in order on the forward's stream, the stage times add
+    up to the whole, and recording them changes no output bit."""
+    import workloads as W
+    import harness as Hn
+    w = {"toy_fp32": W.TOY_FP32, "mixtral_bf16": W.MIXTRAL_BF16.with_(T=512),
+         "mixtral_ec_bf16": W.MIXTRAL_EC_BF16.with_(T=512),
+         "deepseekv3_fp8": W.DEEPSEEKV3_FP8.with_(T=200, N=24, H=1024, I=512)}[name]
+    _say("stage events", name)
+    d = W.layer_inputs(w)
+    dv = Hn.to_dev(d)
+    out0, _ = Hn.run_forward(w, dv, trace=False)
+    cfg = Hn.config(w)
+    ws = torch.empty(M.moe_workspace_size(cfg, M.MOE_OP_FORWARD), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(out0)
+    wts = {k: dv.get(k) for k in Hn.WEIGHT_KEYS}
+    wts["logit_bias"] = None if dv.get("bias") is None else dv["bias"].to(DEV)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(M.TRACE_EVENTS)]
+    before, after = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for rep in range(2):
+        before.record()
+        M.moe_forward(cfg, wts, dv["h"], dv["h"], out, {"stage_events": evs}, ws)
+        after.record()
+        torch.cuda.synchronize()
+        stages = [evs[i].elapsed_time(evs[i + 1]) for i in range(M.TRACE_EVENTS - 1)]
+        assert all(t >= 0 for t in stages), stages
+        total = evs[0].elapsed_time(evs[-1])
+        assert abs(sum(stages) - total) <= 1e-3 + 1e-6 * total
+        assert before.elapsed_time(evs[0]) >= 0 and evs[-1].elapsed_time(after) >= 0
+        if w.n_shared == 0:
+            assert stages[4] < 0.05  # no shared expert: an empty stage
+        assert torch.equal(out.view(torch.int16 if out.element_size() == 2 else torch.int32),
+                           out0.view(torch.int16 if out0.element_size() == 2 else torch.int32))
+    _say("  stage ms", [round(t, 4) for t in stages])

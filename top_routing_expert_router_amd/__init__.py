@@ -20,7 +20,7 @@ __all__ = [
     "moe_workspace_size", "moe_route", "moe_align", "moe_align_reroute", "moe_expert_ffn", "moe_expert_gate_up",
     "moe_expert_down", "moe_combine", "moe_forward", "moe_forward_replay", "moe_route_expert_choice",
     "moe_align_expert_choice", "moe_combine_expert_choice", "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_IDS_IN", "MOE_OP_ALIGN",
-    "MOE_OP_FORWARD", "STATUS", "DTYPES", "ROUTING", "STATS_EXTRA", "STAT", "moe_expert_choice_sizes", "ec_capacity",
+    "MOE_OP_FORWARD", "TRACE_EVENTS", "STATUS", "DTYPES", "ROUTING", "STATS_EXTRA", "STAT", "moe_expert_choice_sizes", "ec_capacity",
     "ec_segment",
 ]
 
@@ -61,7 +61,35 @@ class moe_trace(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "topk_ids", "topk_gates", "margin", "route_kept", "sorted_route_ids", "block_expert",
         "expert_offsets", "num_padded", "stats", "act", "y_route", "route_expert", "scores", "choice_tokens",
-        "choice_slot", "choice_margin")]
+        "choice_slot", "choice_margin")] + [("stage_events", ctypes.POINTER(ctypes.c_void_p))]
+
+
+TRACE_EVENTS = 7  # router, alignment, W13, W2, shared expert, combine: 7 boundaries
+
+
+def _event_handle(e) -> int:
+    """Raw hipEvent_t of a torch.cuda.Event (created by one record on the current stream)."""
+    if isinstance(e, int):
+        return e
+    if e.cuda_event == 0:
+        e.record()
+    return e.cuda_event
+
+
+def _trace_struct(trace: Optional[dict]):
+    """moe_trace for a dict of buffers; stage_events (optional) = TRACE_EVENTS timing events.
+    Returns (struct or None, the event array, which must outlive the call)."""
+    if not trace:
+        return None, None
+    tr = moe_trace(**{k: _ptr(trace.get(k)) for k, _ in moe_trace._fields_ if k != "stage_events"})
+    evs = trace.get("stage_events")
+    arr = None
+    if evs is not None:
+        if len(evs) != TRACE_EVENTS:
+            raise ValueError(f"stage_events: {TRACE_EVENTS} events expected, got {len(evs)}")
+        arr = (ctypes.c_void_p * TRACE_EVENTS)(*[_event_handle(e) for e in evs])
+        tr.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    return tr, arr
 
 
 _lib = None
@@ -216,7 +244,7 @@ def moe_forward(cfg, weights: dict, h, residual, out, trace: Optional[dict], ws,
                 stream=None):
     """weights: dict with the moe_weights member names (tensors or None); trace likewise."""
     w = moe_weights(**{k: _ptr(weights.get(k)) for k, _ in moe_weights._fields_})
-    tr = moe_trace(**{k: _ptr(trace.get(k)) for k, _ in moe_trace._fields_}) if trace else None
+    tr, _events = _trace_struct(trace)
     nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
     _check("moe_forward", lib().moe_forward(ctypes.byref(cfg), ctypes.byref(w), _ptr(h), _ptr(residual), _ptr(out),
                                             ctypes.byref(tr) if tr is not None else None, _ptr(ws), nb,
@@ -227,7 +255,7 @@ def moe_forward_replay(cfg, weights: dict, h, residual, replay_ids, out, trace: 
                        ws_bytes: Optional[int] = None, stream=None):
     """moe_forward with recorded expert ids ([T, k] int32) instead of this run's top-k."""
     w = moe_weights(**{k: _ptr(weights.get(k)) for k, _ in moe_weights._fields_})
-    tr = moe_trace(**{k: _ptr(trace.get(k)) for k, _ in moe_trace._fields_}) if trace else None
+    tr, _events = _trace_struct(trace)
     nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
     _check("moe_forward_replay",
            lib().moe_forward_replay(ctypes.byref(cfg), ctypes.byref(w), _ptr(h), _ptr(residual), _ptr(replay_ids),

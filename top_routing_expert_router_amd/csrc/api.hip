@@ -391,6 +391,27 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* wt, const void
     return MOE_ERR_MISALIGNED;
 
   hipStream_t s = (hipStream_t)stream;
+  // stage events of the trace (nullable): recorded between the stages on this stream
+  auto mark = [&](int i) -> hipError_t {
+    return tr.stage_events && tr.stage_events[i] ? hipEventRecord((hipEvent_t)tr.stage_events[i], s) : hipSuccess;
+  };
+  // W13 then W2 of the routed experts, the shared expert, each followed by its event
+  auto expert_stages = [&](hipError_t e, const void* shared_out_buf, const void** shared_out) -> hipError_t {
+    if (e == hipSuccess)
+      e = launch_gate_up(c, h, sorted, offsets, wt->w13, wt->w13_scale, act, false, s, work);
+    if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess)
+      e = launch_down(c, act, sorted, offsets, wt->w2, wt->w2_scale, y, false, s, work + kGemmWorkWords);
+    if (e == hipSuccess) e = mark(4);
+    if (e == hipSuccess && c.n_shared) {
+      e = launch_expert_ffn(c, h, nullptr, nullptr, wt->shared_w13, wt->shared_w2, wt->shared_w13_scale,
+                            wt->shared_w2_scale, base + L.sact, (void*)shared_out_buf, true, s,
+                            work + 2 * kGemmWorkWords);
+      *shared_out = shared_out_buf;
+    }
+    if (e == hipSuccess) e = mark(5);
+    return e;
+  };
   if (expert_choice(c)) {
     float* scores = (float*)pick(tr.scores, L.scores);
     int32_t* ctok = (int32_t*)pick(tr.choice_tokens, L.ctok);
@@ -398,40 +419,34 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* wt, const void
     float* cmargin = (float*)pick(tr.choice_margin, L.cmargin);
     if (!aligned(scores, 4) || !aligned(ctok, 4) || !aligned(cslot, 4) || !aligned(cmargin, 4))
       return MOE_ERR_MISALIGNED;
-    hipError_t e = launch_router(c, h, wt->w_gate, wt->logit_bias, logits, nullptr, nullptr, nullptr, s, nullptr,
-                                 scores);
+    hipError_t e = mark(0);
+    if (e == hipSuccess)
+      e = launch_router(c, h, wt->w_gate, wt->logit_bias, logits, nullptr, nullptr, nullptr, s, nullptr, scores);
     if (e == hipSuccess) e = launch_ec_select(c, scores, ctok, cslot, cmargin, s);
+    if (e == hipSuccess) e = mark(1);
     if (e == hipSuccess)
       e = launch_ec_align(c, ctok, cslot, sorted, blocks, offsets, npad, stats, s, work, 4 * kGemmWorkWords);
-    if (e == hipSuccess)
-      e = launch_expert_ffn(c, h, sorted, offsets, wt->w13, wt->w2, wt->w13_scale, wt->w2_scale, act, y, false, s,
-                            work);
+    if (e == hipSuccess) e = mark(2);
     const void* shared_out = nullptr;
-    if (e == hipSuccess && c.n_shared) {
-      e = launch_expert_ffn(c, h, nullptr, nullptr, wt->shared_w13, wt->shared_w2, wt->shared_w13_scale,
-                            wt->shared_w2_scale, base + L.sact, base + L.sout, true, s, work + 2 * kGemmWorkWords);
-      shared_out = base + L.sout;
-    }
+    e = expert_stages(e, base + L.sout, &shared_out);
     if (e == hipSuccess) e = launch_combine_ec(c, y, scores, cslot, shared_out, residual, out, s);
+    if (e == hipSuccess) e = mark(6);
     return hip_status(e);
   }
-  hipError_t e = launch_router(c, h, wt->w_gate, wt->logit_bias, logits, replay ? nullptr : ids, gates, margin, s,
-                               replay);
+  hipError_t e = mark(0);
+  if (e == hipSuccess)
+    e = launch_router(c, h, wt->w_gate, wt->logit_bias, logits, replay ? nullptr : ids, gates, margin, s, replay);
+  if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess)
     e = reroute ? launch_align_reroute(c, ids, logits, rexp, kept, sorted, blocks, offsets, npad, stats,
                                        base + L.align_ws, s, work, 4 * kGemmWorkWords)
                 : launch_align(c, ids, kept, sorted, blocks, offsets, npad, stats,
                                base + L.align_ws + reroute_workspace_bytes(c), s, work, 4 * kGemmWorkWords);
-  if (e == hipSuccess)
-    e = launch_expert_ffn(c, h, sorted, offsets, wt->w13, wt->w2, wt->w13_scale, wt->w2_scale, act, y, false, s,
-                          work);
+  if (e == hipSuccess) e = mark(2);
   const void* shared_out = nullptr;
-  if (e == hipSuccess && c.n_shared) {
-    e = launch_expert_ffn(c, h, nullptr, nullptr, wt->shared_w13, wt->shared_w2, wt->shared_w13_scale,
-                          wt->shared_w2_scale, base + L.sact, base + L.sout, true, s, work + 2 * kGemmWorkWords);
-    shared_out = base + L.sout;
-  }
+  e = expert_stages(e, base + L.sout, &shared_out);
   if (e == hipSuccess) e = launch_combine(c, y, gates, kept, shared_out, residual, out, s);
+  if (e == hipSuccess) e = mark(6);
   return hip_status(e);
 }
 

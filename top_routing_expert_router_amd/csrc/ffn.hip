@@ -59,6 +59,8 @@ struct FfnArgs {
   int ntiles;
   int32_t* work;          // nullable: 8 zeroed per-XCD tile counters (dynamic schedule)
   int dest_is_row;        // W2: 1 = y row p (expert choice: sorted holds token ids), 0 = y row sorted[p]
+  int narrow;             // W2, bf16 weights, K % 256 == 0, one to four rounds of tiles: small last
+                          // m-tiles run as two narrow tiles, after all full-height tiles
 };
 
 // LDS tile layout: row-major 128-byte rows of 8 16-byte chunks, chunk index XORed
@@ -68,41 +70,61 @@ struct FfnArgs {
 // the bank half, rows 2m.. in the chunk).
 __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * (BK * 2) + (swz_chunk(row, chunk) << 4); }
+// Narrow tiles: 128-deep stages, rows of 256 B (16 chunks); chunk index XORed with
+// row & 15, so the 16 consecutive rows a 16-lane group reads at one logical chunk
+// land in 16 different chunks, i.e. all 64 banks.
+__device__ __forceinline__ int swzn_chunk(int row, int chunk) { return chunk ^ (row & 15); }
+__device__ __forceinline__ int swzn(int row, int chunk) { return row * (BK * 4) + (swzn_chunk(row, chunk) << 4); }
 
 // Tile table, built once per workgroup in LDS: beg[e] = first padded row of expert
-// e (beg[N] = end of the last), mt0[e] = number of BM-row m-tiles of the experts
-// before e (mt0[N] = all m-tiles).  Each expert's padded segment is cut into
-// ceil(len / BM) m-tiles in expert order.  Identity rows: one expert, rows [0, T).
+// e (beg[N] = end of the last).  Each expert's padded segment is cut into
+// ceil(len / BM) m-tiles; m-slots are numbered in expert order, big0[e] = m-slots of
+// the experts before e (big0[N] = all of them), so an expert's m-tiles stay together
+// and share its weight tiles in L2.  Narrow kernels: a last m-tile of at most BM / 2
+// rows is "small": it takes two m-slots (one per half of the weight n-tile), numbered
+// after all other m-tiles (sm0[e] = small m-slots before e), so within each raster
+// group the short tiles come last and fill the end of the schedule instead of pushing
+// full tiles into an extra round.  Identity rows: one expert, rows [0, T).
 constexpr int kMaxExperts = 256;
 
-__device__ void build_tile_table(const FfnArgs& a, int* beg, int* mt0) {
+template <bool NARROW>
+__device__ void build_tile_table(const FfnArgs& a, int* beg, int* big0, int* sm0) {
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
-    int b[4], cnt[4];
-    int s = 0;
+    int b[4], nb[4], ns[4];
+    int sb = 0, ss = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ee = lane * 4 + i;
       const bool ok = ee < a.N;
       b[i] = !ok ? 0 : (a.sorted == nullptr ? 0 : a.offsets[ee]);
       const int end = !ok ? 0 : (a.sorted == nullptr ? a.T : a.offsets[ee + 1]);
-      cnt[i] = ok ? ceil_div(end - b[i], BM) : 0;
-      s += cnt[i];
+      const int len = end - b[i];
+      const int nf = ok ? ceil_div(len, BM) : 0;
+      const bool small = NARROW && nf > 0 && len - (nf - 1) * BM <= BM / 2;
+      nb[i] = small ? nf - 1 : nf;
+      ns[i] = small ? 2 : 0;
+      sb += nb[i];
+      ss += ns[i];
     }
-    const int incl = wave_incl_scan_i32(s);
-    int before = incl - s;
+    const int ib = wave_incl_scan_i32(sb);
+    const int is = NARROW ? wave_incl_scan_i32(ss) : 0;
+    int pb = ib - sb, ps = is - ss;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ee = lane * 4 + i;
       if (ee < a.N) {
         beg[ee] = b[i];
-        mt0[ee] = before;
+        big0[ee] = pb;
+        if (NARROW) sm0[ee] = ps;
       }
-      before += cnt[i];
+      pb += nb[i];
+      ps += ns[i];
     }
     if (lane == kWave - 1) {
       beg[a.N] = a.sorted == nullptr ? a.T : a.offsets[a.N];
-      mt0[a.N] = incl;
+      big0[a.N] = ib;
+      if (NARROW) sm0[a.N] = is;
     }
   }
   __syncthreads();
@@ -142,9 +164,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const void* w, int
                                              (int)((unsigned)WR * K), kBufferFlags);
 }
 
-// One output tile: expert e, padded rows [p0, p1), weight n-tile nt.
+// One output tile: expert e, padded rows [p0, p1), weight n-tile nt; sub = -1, or the
+// half (0, 1) of the n-tile's weight rows a narrow tile covers.
 struct Tile {
-  int e, p0, p1, nt;
+  int e, p0, p1, nt, sub;
 };
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
@@ -176,8 +199,11 @@ __device__ __forceinline__ void lds_barrier() {
 //  - quarter (R <= 64): all 4 waves on the same 64 rows, each with 64 weight rows.
 // An output element's K order is the same in every mode (one MFMA chain over K in
 // ascending 16-wide steps), so the mode changes no output bit.
-template <int MODE, bool FP8>
+// NARROW (W2, bf16 weights only): small last m-tiles run as narrow tiles; see
+// run_tile_narrow.  A kernel of its own, so the others keep their register allocation.
+template <int MODE, bool FP8, bool NARROW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffn_gemm_bf16(FfnArgs a) {
+  static_assert(!NARROW || (MODE == 1 && !FP8), "narrow tiles: W2 with bf16 weights only");
   constexpr int TBN = BN;           // weight rows per tile
   constexpr int BJ = TBN / 32;      // weight-row DMA instructions (8 rows each) per wave and stage
   // Two stages, each its own array so the compiler can see that the tile being
@@ -186,7 +212,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ __attribute__((aligned(16))) char sB0[TBN * BK * 2];
   __shared__ __attribute__((aligned(16))) char sA1[BM * BK * 2];
   __shared__ __attribute__((aligned(16))) char sB1[TBN * BK * 2];
-  __shared__ int t_beg[kMaxExperts + 1], t_mt0[kMaxExperts + 1];
+  __shared__ int t_beg[kMaxExperts + 1], t_big0[kMaxExperts + 1], t_sm0[NARROW ? kMaxExperts + 1 : 1];
 
   // ---- persistent work.  Tiles in logical order: groups of kGroupN n-tiles, all
   // m-tiles of a group before the next group.  Hardware deals workgroups to the 8
@@ -196,10 +222,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // Dynamic schedule (a.work): workgroups claim the run's tiles in order from the
   // XCD's counter -- a workgroup claims its next tile when it starts the current
   // one, so tiles of unequal cost (full and half) balance across the XCD.
-  build_tile_table(a, t_beg, t_mt0);
+  build_tile_table<NARROW>(a, t_beg, t_big0, t_sm0);
   // values read from the table are the same in every lane; readfirstlane makes them
   // scalar, so the buffer resources built from them stay in SGPRs
-  const int total_m = __builtin_amdgcn_readfirstlane(t_mt0[a.N]);
+  constexpr bool kNarrow = NARROW;
+  const int total_big = __builtin_amdgcn_readfirstlane(t_big0[a.N]);
+  const int total_m = kNarrow ? total_big + __builtin_amdgcn_readfirstlane(t_sm0[a.N]) : total_big;
   const int G = total_m * a.ntiles;
   const int per_xcd = ceil_div(G, 8);
   const int slots = gridDim.x >> 3;
@@ -222,19 +250,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int idx = l - group * kGroupN * total_m;
     const int m = idx / gsize;
     t.nt = gn0 + idx % gsize;
-    int lo = 0, hi = a.N;  // last expert e with mt0[e] <= m (empty experts have no tiles)
+    const bool big = !kNarrow || m < total_big;
+    const int* pre = big ? t_big0 : t_sm0;
+    const int mm = big ? m : m - total_big;
+    int lo = 0, hi = a.N;  // last expert e with pre[e] <= mm (experts without such slots are skipped)
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (t_mt0[mid] <= m) lo = mid; else hi = mid;
+      if (pre[mid] <= mm) lo = mid; else hi = mid;
     }
     t.e = __builtin_amdgcn_readfirstlane(lo);
-    t.p0 = __builtin_amdgcn_readfirstlane(t_beg[lo] + (m - t_mt0[lo]) * BM);
+    const int j = mm - pre[lo], len = t_beg[lo + 1] - t_beg[lo], nf = ceil_div(len, BM);
+    // a big slot is m-tile j; a small slot is half j of the last m-tile
+    t.sub = __builtin_amdgcn_readfirstlane(!big && kNarrow ? j : -1);
+    t.p0 = __builtin_amdgcn_readfirstlane(t_beg[lo] + (big ? j : nf - 1) * BM);
     t.p1 = __builtin_amdgcn_readfirstlane(min(min(t_beg[lo + 1], t.p0 + BM), a.rows));
   };
-  // activation rows a tile mode covers: 256 (full), 128 (half) or 64 (quarter)
+  // tile mode: the activation rows it covers, 256 (full), 128 (half) or 64 (quarter);
+  // narrow tiles (128 weight rows, 128-deep stages) add 1: 129 or 65
   auto tile_rows = [&](const Tile& t) {
     const int r = __builtin_amdgcn_readfirstlane(t.p1 - t.p0);
-    return r <= BM / 4 ? BM / 4 : (r <= BM / 2 ? BM / 2 : BM);
+    const int rows = r <= BM / 4 ? BM / 4 : (r <= BM / 2 ? BM / 2 : BM);
+    return kNarrow && __builtin_amdgcn_readfirstlane(t.sub) >= 0 ? rows + 1 : rows;
   };
   Tile cur;
   decode(lid, cur);
@@ -273,6 +309,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // rows) or the tile's own act rows (MODE 1, contiguous from p0).  B: expert e.
   auto setup = [&](const Tile& t) {
     const int rows = tile_rows(t);
+    if (kNarrow && (rows & 1)) {
+      // narrow (W2): A rows [wave * R/4, +R/4) in R/16 DMAs of 4 rows; weight rows
+      // [32 wave, +32) of the tile's half in 8 DMAs.  Lane L lands in physical chunk
+      // L % 16 of row L / 16 of its group and fetches the logical chunk stored there.
+      const int R = rows - 1;
+      const int pc = lane & 15, gr = lane >> 4;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ar = wave * (R / 4) + j * 4 + gr;
+        const unsigned row = (j < R / 16 && t.p0 + ar < t.p1) ? (unsigned)ar : 0u;
+        aoff[j] = (row * (unsigned)K + swzn_chunk(ar, pc) * 8) * 2u;
+        const int br = wave * 32 + j * 4 + gr;
+        const int r = t.nt * TBN + t.sub * (TBN / 2) + br;
+        boff[j] = ((unsigned)(r < a.H ? r : 0) * (unsigned)K + swzn_chunk(br, pc) * 8) * 2u;
+      }
+      return;
+    }
     // Rows outside the tile or padding rows read a harmless valid row (token 0, or a
     // row of the tile's own act block); their results are never stored (rows never
     // interact in the product).  W13 gathers token rows: the eight route ids are loaded
@@ -341,15 +394,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     issue_part(rows_tag, t, sA, sB, k0, 0);
     issue_part(rows_tag, t, sA, sB, k0, 1);
   };
-  // the next tile's first copies, in its own mode (outside any scheduled region)
-  auto issue_loads_for = [&](const Tile& t, char* sA, char* sB, int k0) {
+  // narrow tiles: part 0 = the R/16 activation DMAs, part 1 = the 8 weight DMAs, 1 KB each
+  auto issue_part_narrow = [&](auto rows_tag, const Tile& t, char* sA, char* sB, int k0, int part) {
+    constexpr int NJ = decltype(rows_tag)::value / 16;
+    const __amdgpu_buffer_rsrc_t rsrcA = act_rsrc<MODE>(X, a.T, K, t.p0, t.p1);
+    const __amdgpu_buffer_rsrc_t rsrcB = weight_rsrc<FP8>(a.w, t.e, WR, K);
+    if (part == 0) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcA, LDS_PTR(sA + (wave * NJ + j) * 1024), 16, aoff[j], k0 * 2, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcB, LDS_PTR(sB + (wave * 8 + j) * 1024), 16, boff[j], k0 * 2, 0, 0);
+    }
+  };
+  // the next tile's first copies (its stage 0 or 1), in its own mode (outside any
+  // scheduled region)
+  auto issue_loads_for = [&](const Tile& t, char* sA, char* sB, int stage) {
     const int rows = tile_rows(t);
+    if constexpr (kNarrow) {
+      if (rows == BM / 4 + 1) {
+        issue_part_narrow(std::integral_constant<int, BM / 4>{}, t, sA, sB, stage * 2 * BK, 0);
+        issue_part_narrow(std::integral_constant<int, BM / 4>{}, t, sA, sB, stage * 2 * BK, 1);
+        return;
+      }
+      if (rows == BM / 2 + 1) {
+        issue_part_narrow(std::integral_constant<int, BM / 2>{}, t, sA, sB, stage * 2 * BK, 0);
+        issue_part_narrow(std::integral_constant<int, BM / 2>{}, t, sA, sB, stage * 2 * BK, 1);
+        return;
+      }
+    }
     if (rows == BM / 4)
-      issue_loads(std::integral_constant<int, BM / 4>{}, t, sA, sB, k0);
+      issue_loads(std::integral_constant<int, BM / 4>{}, t, sA, sB, stage * BK);
     else if (rows == BM / 2)
-      issue_loads(std::integral_constant<int, BM / 2>{}, t, sA, sB, k0);
+      issue_loads(std::integral_constant<int, BM / 2>{}, t, sA, sB, stage * BK);
     else
-      issue_loads(std::integral_constant<int, BM>{}, t, sA, sB, k0);
+      issue_loads(std::integral_constant<int, BM>{}, t, sA, sB, stage * BK);
   };
   // fp8 only: decode the staged codes, scale, round to bf16 and write the B tile
   auto store_fp8 = [&](char* sB) {
@@ -508,7 +589,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (more) {
       lds_barrier();
       store_fp8(sB0);
-      issue_loads_for(nxt, sA1, sB1, BK);
+      issue_loads_for(nxt, sA1, sB1, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
     mfma_step(fw[2], fx[2], false);
@@ -576,14 +657,161 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
   };
 
+  // ---- a narrow tile (W2, bf16 weights): R = 64 or 128 activation rows x one half
+  // (128 rows) of the weight n-tile, in 128-deep stages.  Small m-tiles are latency
+  // bound (a stage's copies have one stage of compute to arrive); a narrow tile has
+  // half the stages of the tile it replaces, and its two halves run on two CUs.  Wave
+  // w: weight rows [32 w, +32), all R rows.  Same K order per output element as every
+  // other mode (one MFMA chain over K in ascending 16-wide steps): no bit changes.
+  auto run_tile_narrow = [&](auto rows_tag, const Tile& t, bool& more, Tile& nxt) {
+    constexpr int R = decltype(rows_tag)::value;
+    constexpr int MSUB = R / 32;        // 32-row activation sub-tiles per wave
+    constexpr int NJ = R / 16;          // activation DMAs per wave and stage
+    constexpr int KS = 2 * BK;          // stage depth
+    int l32 = lane & 31;
+    asm volatile("" : "+v"(l32));
+    const int wrow = wave * 32 + l32;
+    auto load_frags = [&](const char* sA, const char* sB, int kk, bf16x8* wf, bf16x8* xf) {
+      const int ch = kk * 2 + khalf;
+      wf[0] = *reinterpret_cast<const bf16x8*>(sB + swzn(wrow, ch));
+#pragma unroll
+      for (int ms = 0; ms < MSUB; ++ms) xf[ms] = *reinterpret_cast<const bf16x8*>(sA + swzn(ms * 32 + l32, ch));
+    };
+    auto mfma_step = [&](const bf16x8* wf, const bf16x8* xf, bool first) {
+#pragma unroll
+      for (int ms = 0; ms < MSUB; ++ms)
+        acc[0][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0], xf[ms], first ? f32x16{} : acc[0][ms], 0, 0, 0);
+    };
+    // eight 16-wide steps per stage; fragments are read two steps ahead into four
+    // register sets (step i of a stage: MFMAs on set (i + 2) % 4, reads into set i % 4)
+    constexpr int MF = MSUB, RD = 1 + MSUB;
+    auto step = [&](int mset, const char* sA, const char* sB, int kk, int lset, bool first = false) {
+      load_frags(sA, sB, kk, fw[lset], fx[lset]);
+      mfma_step(fw[mset], fx[mset], first);
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+#pragma unroll
+        for (int c = (i * RD) / MF; c < ((i + 1) * RD) / MF; ++c) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto step_dma = [&](int mset, const char* sA, const char* sB, int kk, int lset, char* dA, char* dB, int k0,
+                        int part) {
+      load_frags(sA, sB, kk, fw[lset], fx[lset]);
+      issue_part_narrow(rows_tag, t, dA, dB, k0, part);
+      mfma_step(fw[mset], fx[mset], false);
+      const int VM = part == 0 ? NJ : 8;
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+#pragma unroll
+        for (int c = (i * RD) / MF; c < ((i + 1) * RD) / MF; ++c) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int c = (i * VM) / MF; c < ((i + 1) * VM) / MF; ++c) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // six plain steps 2..7 of a stage held in (sA, sB)
+    auto steps_2_7 = [&](const char* sA, const char* sB, bool first) {
+      step(0, sA, sB, 2, 2, first);
+      step(1, sA, sB, 3, 3);
+      step(2, sA, sB, 4, 0);
+      step(3, sA, sB, 5, 1);
+      step(0, sA, sB, 6, 2);
+      step(1, sA, sB, 7, 3);
+    };
+    const int KT = K / KS;  // even: K is a multiple of 256 for narrow tiles
+    dma_barrier();
+    int claim = 0;
+    if (dyn && threadIdx.x == 0) claim = atomicAdd(a.work + xcd, 1);
+    load_frags(sA0, sB0, 0, fw[0], fx[0]);
+    load_frags(sA0, sB0, 1, fw[1], fx[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    steps_2_7(sA0, sB0, true);
+    for (int kt = 0; kt < KT - 2; kt += 2) {
+      dma_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      step_dma(2, sA1, sB1, 0, 0, sA0, sB0, (kt + 2) * KS, 0);
+      step_dma(3, sA1, sB1, 1, 1, sA0, sB0, (kt + 2) * KS, 1);
+      steps_2_7(sA1, sB1, false);
+      dma_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      step_dma(2, sA0, sB0, 0, 0, sA1, sB1, (kt + 3) * KS, 0);
+      step_dma(3, sA0, sB0, 1, 1, sA1, sB1, (kt + 3) * KS, 1);
+      steps_2_7(sA0, sB0, false);
+    }
+    // stages KT-2 (steps 6, 7 in registers) and KT-1 (buffer 1)
+    if (dyn && threadIdx.x == 0) sh_claim = claim;
+    dma_barrier();
+    const int nlid = dyn ? run0 + __builtin_amdgcn_readfirstlane(sh_claim) : lid + slots;
+    next_lid = nlid;
+    more = nlid < lid_end;
+    if (more) {
+      decode(nlid, nxt);
+      setup(nxt);
+      issue_loads_for(nxt, sA0, sB0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    step(2, sA1, sB1, 0, 0);
+    step(3, sA1, sB1, 1, 1);
+    steps_2_7(sA1, sB1, false);
+    if (more) {
+      lds_barrier();
+      issue_loads_for(nxt, sA1, sB1, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(fw[2], fx[2], false);
+    mfma_step(fw[3], fx[3], false);
+    int erid[MSUB];
+#pragma unroll
+    for (int ms = 0; ms < MSUB; ++ms)
+      erid[ms] = a.sorted != nullptr ? a.sorted[min(t.p0 + ms * 32 + l32, t.p1 - 1)] : 0;
+    // epilogue: lane holds row (lane & 31) of each 32-row sub-tile and, per register
+    // group g, output columns 8 g + 4 (lane >> 5) + [0, 4) of the wave's 32
+    __bf16* y = (__bf16*)a.out;
+    const int cbase = t.nt * TBN + t.sub * (TBN / 2) + wave * 32;
+#pragma unroll
+    for (int ms = 0; ms < MSUB; ++ms) {
+      const int p = t.p0 + ms * 32 + l32;
+      if (p >= t.p1 || cbase >= a.H) continue;
+      int dest = p;
+      if (a.sorted != nullptr) {
+        const int r = erid[ms];
+        if ((unsigned)r >= (unsigned)a.sentinel) continue;
+        if (!a.dest_is_row) dest = r;
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = cbase + g * 8 + khalf * 4;
+        bf16x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = (__bf16)acc[0][ms][g * 4 + q];
+        *reinterpret_cast<bf16x4*>(y + (long)dest * a.H + col) = o;
+      }
+    }
+  };
+
   setup(cur);
   issue_loads_for(cur, sA0, sB0, 0);
   store_fp8(sB0);
-  issue_loads_for(cur, sA1, sB1, BK);
+  issue_loads_for(cur, sA1, sB1, 1);
   while (true) {
     bool more = false;
     Tile nxt = cur;
     const int rows = tile_rows(cur);
+    if constexpr (kNarrow) {
+      if (rows & 1) {
+        if (rows == BM / 4 + 1)
+          run_tile_narrow(std::integral_constant<int, BM / 4>{}, cur, more, nxt);
+        else
+          run_tile_narrow(std::integral_constant<int, BM / 2>{}, cur, more, nxt);
+        if (!more) break;
+        cur = nxt;
+        lid = next_lid;
+        continue;
+      }
+    }
     if (rows == BM / 4)
       run_tile(std::integral_constant<int, BM / 4>{}, cur, more, nxt);
     else if (rows == BM / 2)
@@ -661,7 +889,7 @@ int mtile_bound(const moe_config& c, bool identity) {
 
 // Persistent launch: one workgroup per CU (the kernel's LDS allows no more), at most
 // as many as there can be tiles, a multiple of the 8 XCDs.
-template <int MODE, bool FP8>
+template <int MODE, bool FP8, bool NARROW = false>
 hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
   int dev = 0, cus = 0;
   hipError_t err = hipGetDevice(&dev);
@@ -670,7 +898,7 @@ hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
   const int G = a.mtiles * a.ntiles;
   if (G == 0) return hipSuccess;  // no rows (an expert-choice capacity of 0)
   const int grid = ceil_div(min(G, max(cus, 8)), 8) * 8;
-  ffn_gemm_bf16<MODE, FP8><<<grid, kThreads, 0, s>>>(a);
+  ffn_gemm_bf16<MODE, FP8, NARROW><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -736,6 +964,21 @@ hipError_t launch_down(const moe_config& c, const void* act, const int32_t* sort
     return hipGetLastError();
   }
   a.ntiles = ceil_div(c.H, 256);
+  // Narrow tiles need 128-deep stages in pairs (K a multiple of 256).  They pay where the
+  // tiles make one to four rounds over the CUs: the short tiles, last in the order, then
+  // fill the final round (fewer tiles: the longest tile sets the time anyway; more: the
+  // last round is a small part, and keeping an expert's m-tiles together saves weight
+  // re-reads).  Each expert's last m-tile may take a second m-slot.
+  int dev = 0, cus = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  const long tiles = (long)a.mtiles * a.ntiles;
+  a.narrow = c.expert_dtype == MOE_BF16 && c.I % 256 == 0 && tiles > cus && tiles <= 4L * cus;
+  if (a.narrow) {
+    a.mtiles += a.N;
+    return launch_gemm<1, false, true>(a, s);
+  }
   return c.expert_dtype == MOE_FP8_E4M3 ? launch_gemm<1, true>(a, s) : launch_gemm<1, false>(a, s);
 }
 
