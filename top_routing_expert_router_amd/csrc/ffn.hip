@@ -182,6 +182,14 @@ __device__ __forceinline__ void dma_barrier() {
   __syncthreads();
 }
 
+// fp8 weights: the same, except that the newest BJ + 2 vector loads (the next stage's
+// weight codes and block scales, into registers) may still be in flight.  vmcnt(10):
+// imm 0x7A = vmcnt(10) expcnt(7) lgkmcnt(0).
+__device__ __forceinline__ void fp8_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x7A);
+  __syncthreads();
+}
+
 // Barrier after this wave's LDS reads have completed (lgkmcnt(0); vmcnt and expcnt
 // not waited: imm 0xC07F), so no wave's later DMA can overwrite what a read still needs.
 __device__ __forceinline__ void lds_barrier() {
@@ -204,6 +212,7 @@ __device__ __forceinline__ void lds_barrier() {
 template <int MODE, bool FP8, bool NARROW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffn_gemm_bf16(FfnArgs a) {
   static_assert(!NARROW || (MODE == 1 && !FP8), "narrow tiles: W2 with bf16 weights only");
+  static_assert(BN / 32 + 2 == 10, "fp8_barrier leaves BJ + 2 loads in flight");
   constexpr int TBN = BN;           // weight rows per tile
   constexpr int BJ = TBN / 32;      // weight-row DMA instructions (8 rows each) per wave and stage
   // Two stages, each its own array so the compiler can see that the tile being
@@ -433,10 +442,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       issue_loads(std::integral_constant<int, BM>{}, t, sA, sB, stage * BK);
   };
   // fp8 only: decode the staged codes, scale, round to bf16 and write the B tile
-  auto store_fp8 = [&](char* sB) {
+  // (part 0: rows rb + 32 i for i < BJ / 2; part 1: the rest; -1: all)
+  auto store_fp8 = [&](char* sB, int part = -1) {
     if constexpr (FP8) {
 #pragma unroll
       for (int i = 0; i < BJ; ++i) {
+        if ((part == 0 && i >= BJ / 2) || (part == 1 && i < BJ / 2)) continue;
         const u32x2 q = bq[i];
         const float s = i < 4 ? sc_lo : sc_hi;
         const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[0], false);
@@ -535,6 +546,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
       __builtin_amdgcn_sched_barrier(0);
     };
+    // fp8: the first two steps of a half.  dpart 0: the activation DMAs of the stage being
+    // filled and the decode of the first half of its codes; dpart 1: the decode of the
+    // second half, then the code (and scale) loads of the next stage at k0 = kcodes.
+    auto step_f8 = [&](int mset, const char* sA, const char* sB, int kk, int lset, char* dA, char* dB, int k0,
+                       int dpart, int kcodes) {
+      load_frags(sA, sB, kk, fw[lset], fx[lset]);
+      if (dpart == 0) issue_part(rows_tag, t, dA, dB, k0, 0);
+      store_fp8(dB, dpart);
+      if (dpart == 1) issue_part(rows_tag, t, dA, dB, kcodes, 1);
+      mfma_step(fw[mset], fx[mset], false);
+      const int VM = dpart == 0 ? AJ : BJ + 2;
+      constexpr int DW = BJ / 2;      // LDS writes of the decode
+      constexpr int VA = 16 * DW / MF + 1;  // its VALU work per MFMA (about 16 per row)
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           // MFMA
+        if ((i * RD) / MF != ((i + 1) * RD) / MF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, VA, 0);                          // VALU (decode)
+        if ((i * DW) / MF != ((i + 1) * DW) / MF) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+        if ((i * VM) / MF != ((i + 1) * VM) / MF) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // global load
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
 
     // Stage s of the K loop lives in buffer s & 1.  The DMA of stage s+2 is issued
     // right after the barrier that ends the reads of stage s, spread over the next
@@ -551,26 +585,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     __builtin_amdgcn_sched_barrier(0);
     step(0, sA0, sB0, 2, 2, true);
     step(1, sA0, sB0, 3, 3);
-    for (int kt = 0; kt < KT - 2; kt += 2) {
-      store_fp8(sB1);  // fp8: stage kt+1 into buffer 1 (codes fetched a stage earlier)
+    if constexpr (FP8) {
+      // fp8 weights.  The codes of a stage are loaded into registers one half-stage
+      // before they are decoded, and the decode (convert, scale, round, LDS write) of
+      // stage s+1 is spread over the MFMAs of the first two steps of the half that frees
+      // its buffer; the barrier then waits for all copies but the newest code loads.
+      store_fp8(sB1);  // stage 1 (its codes were staged with the tile's first copies)
+      issue_part(rows_tag, t, sA0, sB0, min(2, KT - 1) * BK, 1);
+      for (int kt = 0; kt < KT - 2; kt += 2) {
+        fp8_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        step_f8(2, sA1, sB1, 0, 0, sA0, sB0, (kt + 2) * BK, 0, 0);
+        step_f8(3, sA1, sB1, 1, 1, sA0, sB0, (kt + 2) * BK, 1, (kt + 3) * BK);
+        step(0, sA1, sB1, 2, 2);
+        step(1, sA1, sB1, 3, 3);
+        fp8_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        step_f8(2, sA0, sB0, 0, 0, sA1, sB1, (kt + 3) * BK, 0, 0);
+        step_f8(3, sA0, sB0, 1, 1, sA1, sB1, (kt + 3) * BK, 1, min(kt + 4, KT - 1) * BK);
+        step(0, sA0, sB0, 2, 2);
+        step(1, sA0, sB0, 3, 3);
+      }
+      // stage KT-1 is in buffer 1 (decoded above); the last code loads fetched nothing needed
+      if (dyn && threadIdx.x == 0) sh_claim = claim;
       dma_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      step_dma(2, sA1, sB1, 0, 0, sA0, sB0, (kt + 2) * BK, 0);
-      step_dma(3, sA1, sB1, 1, 1, sA0, sB0, (kt + 2) * BK, 1);
-      step(0, sA1, sB1, 2, 2);
-      step(1, sA1, sB1, 3, 3);
-      store_fp8(sB0);
+    } else {
+      for (int kt = 0; kt < KT - 2; kt += 2) {
+        dma_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        step_dma(2, sA1, sB1, 0, 0, sA0, sB0, (kt + 2) * BK, 0);
+        step_dma(3, sA1, sB1, 1, 1, sA0, sB0, (kt + 2) * BK, 1);
+        step(0, sA1, sB1, 2, 2);
+        step(1, sA1, sB1, 3, 3);
+        dma_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        step_dma(2, sA0, sB0, 0, 0, sA1, sB1, (kt + 3) * BK, 0);
+        step_dma(3, sA0, sB0, 1, 1, sA1, sB1, (kt + 3) * BK, 1);
+        step(0, sA0, sB0, 2, 2);
+        step(1, sA0, sB0, 3, 3);
+      }
+      // stages KT-2 (fragments 2, 3 in registers) and KT-1 (buffer 1)
+      if (dyn && threadIdx.x == 0) sh_claim = claim;
       dma_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      step_dma(2, sA0, sB0, 0, 0, sA1, sB1, (kt + 3) * BK, 0);
-      step_dma(3, sA0, sB0, 1, 1, sA1, sB1, (kt + 3) * BK, 1);
-      step(0, sA0, sB0, 2, 2);
-      step(1, sA0, sB0, 3, 3);
     }
-    // stages KT-2 (fragments 2, 3 in registers) and KT-1 (buffer 1)
-    if (dyn && threadIdx.x == 0) sh_claim = claim;
-    store_fp8(sB1);
-    dma_barrier();
     // buffer 0 is free: the next tile's stage 0 goes there now
     const int nlid = dyn ? run0 + __builtin_amdgcn_readfirstlane(sh_claim) : lid + slots;
     next_lid = nlid;
