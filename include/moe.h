@@ -79,7 +79,9 @@ enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 };
 /* moe_route flags (may be combined) */
 enum {
   MOE_ROUTE_LOGITS_IN = 1u, /* skip the projection: `logits` is an input (stored or replayed logits) */
-  MOE_ROUTE_IDS_IN = 2u     /* router replay: `topk_ids` is an input (recorded expert ids) */
+  MOE_ROUTE_IDS_IN = 2u,    /* router replay: `topk_ids` is an input (recorded expert ids) */
+  MOE_ROUTE_NO_LOGITS_OUT = 4u /* the logits are not written (`logits` may be NULL); bf16
+                                  activations only, not with MOE_ROUTE_LOGITS_IN */
 };
 
 /* moe_config.routing */
@@ -225,7 +227,9 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes);
  *   h          [T, H] act dtype (ignored with MOE_ROUTE_LOGITS_IN)
  *   w_gate     [N, H] act dtype (ignored with MOE_ROUTE_LOGITS_IN)
  *   logit_bias [N] float32, nullable (ignored with MOE_ROUTE_LOGITS_IN)
- *   logits     [T, N] float32: written, or read with MOE_ROUTE_LOGITS_IN
+ *   logits     [T, N] float32: written, or read with MOE_ROUTE_LOGITS_IN; with
+ *              MOE_ROUTE_NO_LOGITS_OUT nullable and not written (bf16 activations: the
+ *              logits stay on chip between the projection and the top-k)
  *   topk_ids   [T, k] int32, rank order;  topk_gates [T, k] float32
  *   margin     [T] float32, nullable: l_(k-1) - l_(k) in rank order, +inf when k = N
  * Logits are accumulated in fp32 over fixed 32-wide K steps in ascending K.

@@ -126,6 +126,12 @@ def test_host_validation_of_pointers_and_workspace():
     _expect("MOE_ERR_MISALIGNED", M.moe_route, cfg, ODD, A, None, A, A, A, None, 0, s)
     _expect("MOE_ERR_MISALIGNED", M.moe_route, cfg, A, A, None, A + 1, A, A, None, M.MOE_ROUTE_LOGITS_IN, s)
     _expect("MOE_ERR_UNSUPPORTED", M.moe_route, cfg, A, A, None, A, A, A, None, 0x10, s)
+    # no logits out: not with given logits, not on the fp32 path (it stages them in `logits`)
+    _expect("MOE_ERR_UNSUPPORTED", M.moe_route, cfg, A, A, None, A, A, A, None,
+            M.MOE_ROUTE_NO_LOGITS_OUT | M.MOE_ROUTE_LOGITS_IN, s)
+    _expect("MOE_ERR_UNSUPPORTED", M.moe_route, config(W.TOY_FP32), A, A, None, None, A, A, None,
+            M.MOE_ROUTE_NO_LOGITS_OUT, s)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_route, cfg, A, A, None, None, None, A, None, M.MOE_ROUTE_NO_LOGITS_OUT, s)
     # align
     _expect("MOE_ERR_NULL_POINTER", M.moe_align, cfg, A, A, A, A, A, None, None, A, 1 << 20, s)
     _expect("MOE_ERR_MISALIGNED", M.moe_align, cfg, A + 2, A, A, A, A, A, None, A, 1 << 20, s)
@@ -160,7 +166,7 @@ def test_host_validation_of_pointers_and_workspace():
     _expect("MOE_ERR_WORKSPACE_TOO_SMALL", M.moe_align_reroute, cs, A, A, A, A, A, A, A, A, None, A, 64, s)
     # route with recorded ids: the flag is known; unknown bits are not
     _expect("MOE_ERR_NULL_POINTER", M.moe_route, cfg, A, A, None, A, None, A, None, M.MOE_ROUTE_IDS_IN, s)
-    _expect("MOE_ERR_UNSUPPORTED", M.moe_route, cfg, A, A, None, A, A, A, None, 0x4 | M.MOE_ROUTE_IDS_IN, s)
+    _expect("MOE_ERR_UNSUPPORTED", M.moe_route, cfg, A, A, None, A, A, A, None, 0x8 | M.MOE_ROUTE_IDS_IN, s)
 
 
 def test_workspace_op_codes():

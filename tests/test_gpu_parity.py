@@ -354,6 +354,29 @@ def test_forward_end_to_end(name):
         assert torch.equal(out[idx], dv["residual"][idx])
 
 
+@pytest.mark.parametrize("name", ["mixtral_bf16", "qwen3moe_bf16", "deepseekv3_fp8"])
+def test_route_without_logits_out(name):
+    """MOE_ROUTE_NO_LOGITS_OUT: the same ids, gates and margins as with the logits written,
+    and the logits buffer untouched."""
+    w = SMALL[name]
+    _say("route without logits out", name)
+    h = W.hidden_states(w, device=DEV)
+    wg = W.router_weight(w, device=DEV)
+    cfg = Hn.config(w)
+    a, b = Hn.route_buffers(w), Hn.route_buffers(w)
+    M.moe_route(cfg, h, wg, None, a["logits"], a["ids"], a["gates"], a["margin"])
+    b["logits"].fill_(7.0)
+    M.moe_route(cfg, h, wg, None, b["logits"], b["ids"], b["gates"], b["margin"], flags=M.MOE_ROUTE_NO_LOGITS_OUT)
+    c = Hn.route_buffers(w)
+    M.moe_route(cfg, h, wg, None, None, c["ids"], c["gates"], c["margin"], flags=M.MOE_ROUTE_NO_LOGITS_OUT)
+    torch.cuda.synchronize()
+    assert torch.all(b["logits"] == 7.0)
+    for x in (b, c):
+        assert torch.equal(x["ids"], a["ids"])
+        assert torch.equal(x["gates"].view(torch.int32), a["gates"].view(torch.int32))
+        assert torch.equal(x["margin"].view(torch.int32), a["margin"].view(torch.int32))
+
+
 @pytest.mark.parametrize("T,N,H", [(300, 256, 1024), (777, 200, 2048), (16384, 256, 7168)])
 def test_route_projection_many_experts(T, N, H):
     """More than 128 experts take the kernel that stages W_g once per 32 or 64 tokens:

@@ -19,7 +19,8 @@ __all__ = [
     "moe_abi_version", "moe_status_str", "moe_validate_config", "moe_align_sizes",
     "moe_workspace_size", "moe_route", "moe_align", "moe_align_reroute", "moe_expert_ffn", "moe_expert_gate_up",
     "moe_expert_down", "moe_combine", "moe_forward", "moe_forward_replay", "moe_route_expert_choice",
-    "moe_align_expert_choice", "moe_combine_expert_choice", "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_IDS_IN", "MOE_OP_ALIGN",
+    "moe_align_expert_choice", "moe_combine_expert_choice", "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_IDS_IN", "MOE_ROUTE_NO_LOGITS_OUT",
+    "MOE_OP_ALIGN",
     "MOE_OP_FORWARD", "TRACE_EVENTS", "STATUS", "DTYPES", "ROUTING", "STATS_EXTRA", "STAT", "moe_expert_choice_sizes", "ec_capacity",
     "ec_segment",
 ]
@@ -28,6 +29,7 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3}
 MOE_ROUTE_LOGITS_IN = 1
 MOE_ROUTE_IDS_IN = 2
+MOE_ROUTE_NO_LOGITS_OUT = 4
 MOE_OP_ALIGN, MOE_OP_FORWARD = 1, 2
 ROUTING = {"token_choice": 0, "expert_choice": 1}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL_POINTER", 2: "MOE_ERR_INVALID_CONFIG", 3: "MOE_ERR_UNSUPPORTED",

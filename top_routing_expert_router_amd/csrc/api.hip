@@ -104,14 +104,18 @@ moe_status check_routing(const moe_config* c, bool want_expert_choice) {
 moe_status check_route_args(const moe_config& c, const void* h, const void* w_gate, const float* bias,
                             const float* logits, const int32_t* ids, const float* gates, const float* margin,
                             uint32_t flags) {
-  if (flags & ~(uint32_t)(MOE_ROUTE_LOGITS_IN | MOE_ROUTE_IDS_IN)) return MOE_ERR_UNSUPPORTED;
+  if (flags & ~(uint32_t)(MOE_ROUTE_LOGITS_IN | MOE_ROUTE_IDS_IN | MOE_ROUTE_NO_LOGITS_OUT))
+    return MOE_ERR_UNSUPPORTED;
   const bool in = flags & MOE_ROUTE_LOGITS_IN;
-  if (!logits || !ids || !gates) return MOE_ERR_NULL_POINTER;
+  const bool no_out = flags & MOE_ROUTE_NO_LOGITS_OUT;
+  // no logits out: the bf16 projection keeps them on chip; the fp32 path stages them in
+  // `logits` between its two kernels, and given logits are an input
+  if (no_out && (in || c.act_dtype != MOE_BF16)) return MOE_ERR_UNSUPPORTED;
+  if ((!logits && !no_out) || !ids || !gates) return MOE_ERR_NULL_POINTER;
   if (!in && (!h || !w_gate)) return MOE_ERR_NULL_POINTER;
-  if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4) || (margin && !aligned(margin, 4)))
+  if ((logits && !aligned(logits, 4)) || !aligned(ids, 4) || !aligned(gates, 4) || (margin && !aligned(margin, 4)))
     return MOE_ERR_MISALIGNED;
   if (!in && (!aligned(h, 16) || !aligned(w_gate, 16) || (bias && !aligned(bias, 4)))) return MOE_ERR_MISALIGNED;
-  (void)c;
   return MOE_OK;
 }
 
@@ -204,7 +208,8 @@ moe_status moe_route(const moe_config* cfg, const void* h, const void* w_gate, c
   int32_t* ids_out = replay ? nullptr : topk_ids;
   if (flags & MOE_ROUTE_LOGITS_IN)
     return hip_status(launch_topk(*cfg, logits, ids_out, topk_gates, margin, s, replay));
-  return hip_status(launch_router(*cfg, h, w_gate, logit_bias, logits, ids_out, topk_gates, margin, s, replay));
+  return hip_status(launch_router(*cfg, h, w_gate, logit_bias, (flags & MOE_ROUTE_NO_LOGITS_OUT) ? nullptr : logits,
+                                  ids_out, topk_gates, margin, s, replay));
 }
 
 moe_status moe_align(const moe_config* cfg, const int32_t* topk_ids, uint8_t* route_kept, int32_t* sorted_route_ids,

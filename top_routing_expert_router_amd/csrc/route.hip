@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
     for (int w = 1; w < kRouterWaves; ++w) v += part[w][e][t];
     if (bias) v += bias[e];
     lg[t][e] = v;
-    if (t0 + t < T) logits[(size_t)(t0 + t) * N + e] = v;
+    if (logits && t0 + t < T) logits[(size_t)(t0 + t) * N + e] = v;  // nullable: no logits out
   }
   __syncthreads();
   // fused top-k: one group of L lanes per token, 64 / L tokens per wave
@@ -384,9 +384,11 @@ __global__ __launch_bounds__(NW * 64) void router_bf16_wide(const __bf16* __rest
         lg[t * (NP + 1) + e] = v;
       }
   __syncthreads();
-  for (int i = tid; i < TW * N; i += NW * 64) {
-    const int t = i / N, e = i - t * N;
-    if (t0 + t < T) logits[(size_t)(t0 + t) * N + e] = lg[t * (NP + 1) + e];
+  if (logits) {  // nullable: no logits out
+    for (int i = tid; i < TW * N; i += NW * 64) {
+      const int t = i / N, e = i - t * N;
+      if (t0 + t < T) logits[(size_t)(t0 + t) * N + e] = lg[t * (NP + 1) + e];
+    }
   }
   const int L = topk_lanes(N);  // 64: one token per wave at a time
   for (int t = wave; t < TW; t += NW)
