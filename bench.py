@@ -34,8 +34,15 @@ def log(*a):
 
 
 def _ffn_source_hash() -> str:
+    """Hash of the GEMM source's code (comments and blank space removed), which the
+    committed traffic counters were taken on."""
+    import re
     p = os.path.join(ROOT, "top_routing_expert_router_amd", "csrc", "ffn.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    src = open(p).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    src = "\n".join(line.strip() for line in src.splitlines() if line.strip())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def _traffic(workload: str, launches_per_unit: float):

@@ -14,20 +14,25 @@
 // routes inside or across blocks leaves each row's bits unchanged.
 //
 // Kernel shape (bf16 / fp8-weight path):
-//   workgroup tile 256 rows x 256 weight rows, K step 64, 4 waves of 128 x 128,
-//   v_mfma_f32_32x32x16_bf16 with weights as the MFMA "A" operand, so each lane
-//   ends with 4 consecutive output columns of one row (8-byte stores);
+//   persistent: one workgroup per CU claims 256-row x 256-weight-row tiles (per-XCD
+//   counters, or a static stride without a workspace); K step 64, 4 waves of
+//   128 x 128, v_mfma_f32_32x32x16_bf16 with weights as the MFMA "A" operand, so
+//   each lane ends with 4 consecutive output columns of one row (8-byte stores);
 //   two LDS stages of (256 x 64) bf16 for each operand, 16-byte chunks XOR-swizzled
-//   by (row & 7) so 8 consecutive rows hit distinct banks;
-//   global -> register -> LDS staging, one barrier per K step;
-//   the A-row gather (route -> token row of h) is fused into the tile load;
+//   by (row >> 1) & 7 so the fragment reads are free of bank conflicts;
+//   global -> LDS copies by buffer loads with an LDS destination (the A-row gather,
+//   route -> token row of h, folded into their offsets), one barrier per K step,
+//   fragments read two 16-wide steps ahead of the MFMAs;
 //   W13 tiles hold 128 gate rows and the matching 128 up rows, so SwiGLU is a
 //   register-local epilogue; W2 writes each row straight to its route's y row;
 //   M tiles are 256-row slices of one expert's padded segment (a fixed constant,
-//   decoupled from B); workgroups map to XCDs so each XCD walks a contiguous
-//   run of (n-tile group, m-tile) pairs and shares weight tiles in its L2.
-// fp8 weights: E4M3FN codes are decoded with the hardware converter, multiplied
-// by their 128x128 block's bf16 scale in fp32, and rounded to bf16 on the way into LDS.
+//   decoupled from B), run in full, half or quarter mode by their valid rows; W2
+//   has narrow tiles (run_tile_narrow) for its small last m-tiles; workgroups map
+//   to XCDs so each XCD walks a contiguous run of (n-tile group, m-tile) pairs and
+//   shares weight tiles in its L2.
+// fp8 weights: E4M3FN codes are loaded into registers half a stage ahead, decoded
+// with the hardware converter, multiplied by their 128x128 block's bf16 scale in
+// fp32 and rounded to bf16 into LDS, spread over the MFMAs of the next half stage.
 #include <type_traits>
 
 #include "common.h"
