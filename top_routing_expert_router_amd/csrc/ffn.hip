@@ -321,6 +321,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   long srow_lo = 0, srow_hi = 0;
   // Buffers, offsets and weight rows of tile t.  A: all of h (MODE 0, gathered
   // rows) or the tile's own act rows (MODE 1, contiguous from p0).  B: expert e.
+  // Rows outside the tile or padding rows read a harmless valid row (token 0, or a
+  // row of the tile's own act block); their results are never stored (rows never
+  // interact in the product).  W13 gathers token rows: the eight route ids are loaded
+  // unconditionally (index clamped into the tile), so the loads are in flight together.
+  // W2 reads the tile's act rows in order and needs no route id.
+  int rid[8];
+  auto setup_ids = [&](const Tile& t) {
+    const int rows = tile_rows(t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      rid[j] = (MODE == 0 && a.sorted != nullptr) ? a.sorted[min(t.p0 + arow_of(rows, j), t.p1 - 1)] : 0;
+  };
+  // activation-row offsets of tile t (W13: from the route ids setup_ids loaded)
+  auto setup_a = [&](const Tile& t) {
+    const int rows = tile_rows(t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int ar = arow_of(rows, j);
+      const int p = t.p0 + ar;
+      unsigned row = 0;
+      if (p < t.p1) {
+        if (MODE == 1) row = p - t.p0;
+        else if (a.sorted == nullptr) row = p;
+        else if ((unsigned)rid[j] < (unsigned)a.sentinel) row = rid[j] / a.k;
+      }
+      aoff[j] = (row * (unsigned)K + swz_chunk(ar, lane & 7) * 8) * 2u;
+    }
+  };
+  // weight-row offsets of tile t (fp8: and its scale rows)
+  auto setup_b = [&](const Tile& t) {
+    const int n0 = MODE == 0 ? t.nt * (TBN / 2) : t.nt * TBN;
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int j = 0; j < BJ; ++j) {
+        const int r = weight_row(n0, brow_of(j));
+        boff[j] = ((unsigned)(r < 0 ? 0 : r) * (unsigned)K + swz_chunk(brow_of(j), lane & 7) * 8) * 2u;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < BJ; ++i) {
+        const int r = weight_row(n0, rb + 32 * i);
+        boff[i] = r < 0 ? 0x80000000u : (unsigned)r * (unsigned)K + chunk * 8;
+      }
+      const int kb = K / 128;
+      const int rhi = MODE == 0 ? a.I + n0 : n0 + 128;
+      srow_lo = ((long)t.e * (WR / 128) + n0 / 128) * kb;
+      srow_hi = ((long)t.e * (WR / 128) + min(rhi, WR - 1) / 128) * kb;
+    }
+  };
   auto setup = [&](const Tile& t) {
     const int rows = tile_rows(t);
     if (kNarrow && (rows & 1)) {
@@ -340,45 +389,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
       return;
     }
-    // Rows outside the tile or padding rows read a harmless valid row (token 0, or a
-    // row of the tile's own act block); their results are never stored (rows never
-    // interact in the product).  W13 gathers token rows: the eight route ids are loaded
-    // unconditionally (index clamped into the tile), so the loads are in flight together.
-    // W2 reads the tile's act rows in order and needs no route id.
-    int rid[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      rid[j] = (MODE == 0 && a.sorted != nullptr) ? a.sorted[min(t.p0 + arow_of(rows, j), t.p1 - 1)] : 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int ar = arow_of(rows, j);
-      const int p = t.p0 + ar;
-      unsigned row = 0;
-      if (p < t.p1) {
-        if (MODE == 1) row = p - t.p0;
-        else if (a.sorted == nullptr) row = p;
-        else if ((unsigned)rid[j] < (unsigned)a.sentinel) row = rid[j] / a.k;
-      }
-      aoff[j] = (row * (unsigned)K + swz_chunk(ar, lane & 7) * 8) * 2u;
-    }
-    const int n0 = MODE == 0 ? t.nt * (TBN / 2) : t.nt * TBN;
-    if constexpr (!FP8) {
-#pragma unroll
-      for (int j = 0; j < BJ; ++j) {
-        const int r = weight_row(n0, brow_of(j));
-        boff[j] = ((unsigned)(r < 0 ? 0 : r) * (unsigned)K + swz_chunk(brow_of(j), lane & 7) * 8) * 2u;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < BJ; ++i) {
-        const int r = weight_row(n0, rb + 32 * i);
-        boff[i] = r < 0 ? 0x80000000u : (unsigned)r * (unsigned)K + chunk * 8;
-      }
-      const int kb = K / 128;
-      const int rhi = MODE == 0 ? a.I + n0 : n0 + 128;
-      srow_lo = ((long)t.e * (WR / 128) + n0 / 128) * kb;
-      srow_hi = ((long)t.e * (WR / 128) + min(rhi, WR - 1) / 128) * kb;
-    }
+    setup_ids(t);
+    setup_a(t);
+    setup_b(t);
   };
   u32x2 bq[BJ];
   float sc_lo = 1.f, sc_hi = 1.f;
@@ -425,7 +438,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   };
   // the next tile's first copies (its stage 0 or 1), in its own mode (outside any
   // scheduled region)
-  auto issue_loads_for = [&](const Tile& t, char* sA, char* sB, int stage) {
+  auto issue_loads_for = [&](const Tile& t, char* sA, char* sB, int stage, int part = -1) {
     const int rows = tile_rows(t);
     if constexpr (kNarrow) {
       if (rows == BM / 4 + 1) {
@@ -439,12 +452,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         return;
       }
     }
+    auto go = [&](auto rows_tag) {
+      if (part < 0)
+        issue_loads(rows_tag, t, sA, sB, stage * BK);
+      else
+        issue_part(rows_tag, t, sA, sB, stage * BK, part);
+    };
     if (rows == BM / 4)
-      issue_loads(std::integral_constant<int, BM / 4>{}, t, sA, sB, stage * BK);
+      go(std::integral_constant<int, BM / 4>{});
     else if (rows == BM / 2)
-      issue_loads(std::integral_constant<int, BM / 2>{}, t, sA, sB, stage * BK);
+      go(std::integral_constant<int, BM / 2>{});
     else
-      issue_loads(std::integral_constant<int, BM>{}, t, sA, sB, stage * BK);
+      go(std::integral_constant<int, BM>{});
   };
   // fp8 only: decode the staged codes, scale, round to bf16 and write the B tile
   // (part 0: rows rb + 32 i for i < BJ / 2; part 1: the rest; -1: all)
@@ -637,16 +656,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int nlid = dyn ? run0 + __builtin_amdgcn_readfirstlane(sh_claim) : lid + slots;
     next_lid = nlid;
     more = nlid < lid_end;
+    // The next tile's stage 0 goes to buffer 0 (free now).  W13 with fp8 weights: the
+    // route ids are loaded first and the weight codes fetched, and the row offsets and
+    // activation copies follow the last stage's MFMAs, which hide the id loads' latency
+    // (3% on the DeepSeek shape; with bf16 weights it measured no different, and that
+    // kernel keeps the plain order).
+    constexpr bool kSplitSetup = MODE == 0 && FP8;
     if (more) {
       decode(nlid, nxt);
-      setup(nxt);
-      issue_loads_for(nxt, sA0, sB0, 0);
+      if constexpr (kSplitSetup) {
+        setup_ids(nxt);
+        setup_b(nxt);
+        issue_loads_for(nxt, sA0, sB0, 0, 1);
+      } else {
+        setup(nxt);
+        issue_loads_for(nxt, sA0, sB0, 0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     step(2, sA1, sB1, 0, 0);
     step(3, sA1, sB1, 1, 1);
     step(0, sA1, sB1, 2, 2);
     step(1, sA1, sB1, 3, 3);
+    if constexpr (kSplitSetup) {
+      if (more) {
+        setup_a(nxt);
+        issue_loads_for(nxt, sA0, sB0, 0, 0);
+      }
+    }
     // every wave has read buffer 1: the next tile's stage 1 goes there
     if (more) {
       lds_barrier();
