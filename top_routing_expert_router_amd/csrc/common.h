@@ -130,9 +130,11 @@ __device__ __forceinline__ float group_sum_f32(float v, int L) {
   return v;
 }
 
-// Lanes per token for the top-k: the smallest of 8, 16, 32, 64 that holds N experts
-// (N > 64: 64 lanes, up to 4 experts each).
-__host__ __device__ inline int topk_lanes(int N) { return N <= 8 ? 8 : (N <= 16 ? 16 : (N <= 32 ? 32 : 64)); }
+// Lanes per token for the top-k: the fewest of 8, 16, 32 that hold N experts at up to
+// kTopkPerLane each (N <= 64: 8, N <= 128: 16, N <= 256: 32), so that a wave ranks 8, 4 or
+// 2 tokens at once.
+constexpr int kTopkPerLane = 8;
+__host__ __device__ inline int topk_lanes(int N) { return N <= 64 ? 8 : (N <= 128 ? 16 : 32); }
 
 __device__ __forceinline__ int wave_sum_i32(int v) {
 #pragma unroll

@@ -18,10 +18,15 @@
 namespace moe {
 namespace {
 
-constexpr int kRouterTokens = 16;   // tokens per workgroup (one 16-wide MFMA column block)
+constexpr int kRouterTokens = 16;   // tokens per MFMA column block (a workgroup takes TB blocks)
 constexpr int kRouterWaves = 8;     // waves per workgroup; wave w takes K chunks w, w+8, ...
 constexpr int kRouterThreads = kRouterWaves * 64;
 constexpr int kChunkK = 64;         // K per chunk: lane group q = lane / 16 holds k in [16 q, 16 q + 16)
+
+// 16-token column blocks per workgroup: every workgroup reads all of W_g, so for
+// more than 64 experts two blocks share each weight load (half the W_g traffic)
+template <int NSUB>
+constexpr int kRouterTB = NSUB > 4 ? 2 : 1;
 
 // chunks in flight per wave: a CU's whole share of h for small expert counts
 template <int NSUB>
@@ -34,7 +39,7 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 // Top-k, gates and margin of one token from its N logits (global or LDS), by one
 // aligned group of L = topk_lanes(N) lanes; a wave ranks 64 / L tokens at once.
-// Lane g of the group holds experts g + L i.  k+1 rounds of a group max over
+// Lane g of the group holds experts g + L i, i < kTopkPerLane.  k+1 rounds of a group max over
 // (value, -index) keys give the ranked ids and the (k+1)-th logit for the margin.
 // Gate weight_j = exp(l_j - l_0) (0 for a NaN logit); divided by the sum over the
 // k chosen in rank order, or by the sum over all N experts without renormalisation.
@@ -54,10 +59,10 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
                                          float* __restrict__ scores) {
   const int lane = threadIdx.x & 63;
   const int g = lane & (L - 1), base = lane - g;
-  float lv[4];
-  uint64_t key[4];
+  float lv[kTopkPerLane];
+  uint64_t key[kTopkPerLane];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kTopkPerLane; ++i) {
     const int e = g + L * i;
     lv[i] = e < N ? row[e] : 0.f;
     key[i] = e < N ? rank_key(lv[i], e) : 0ull;
@@ -65,23 +70,23 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
   if (scores != nullptr) {
     uint64_t best = key[0];
 #pragma unroll
-    for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+    for (int i = 1; i < kTopkPerLane; ++i) best = key[i] > best ? key[i] : best;
     best = group_max_u64(best, L);
     const int e0 = (int)(0xFFFFFFFFu - (uint32_t)best);
     const int owner = e0 & (L - 1), slot = e0 / L;
     float mine = lv[0];
 #pragma unroll
-    for (int i = 1; i < 4; ++i) mine = slot == i ? lv[i] : mine;
+    for (int i = 1; i < kTopkPerLane; ++i) mine = slot == i ? lv[i] : mine;
     const float l0 = __shfl(mine, base + owner, kWave);
     float z = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kTopkPerLane; ++i) {
       const int e = g + L * i;
       if (e < N && lv[i] == lv[i]) z += expf(lv[i] - l0);
     }
     const float sum = group_sum_f32(z, L);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kTopkPerLane; ++i) {
       const int e = g + L * i;
       if (e < N) scores[(size_t)t * N + e] = (lv[i] == lv[i] ? expf(lv[i] - l0) : 0.f) / sum;
     }
@@ -97,18 +102,18 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
     if (j < rounds) {
       uint64_t best = key[0];
 #pragma unroll
-      for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+      for (int i = 1; i < kTopkPerLane; ++i) best = key[i] > best ? key[i] : best;
       best = group_max_u64(best, L);
       const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
       const int owner = e & (L - 1), slot = e / L;
       float mine = lv[0];
 #pragma unroll
-      for (int i = 1; i < 4; ++i) mine = slot == i ? lv[i] : mine;
+      for (int i = 1; i < kTopkPerLane; ++i) mine = slot == i ? lv[i] : mine;
       sl[j] = __shfl(mine, base + owner, kWave);
       sid[j] = e;
       if (g == owner) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kTopkPerLane; ++i)
           if (i == slot) key[i] = 0ull;
       }
     }
@@ -150,7 +155,7 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
   if (!renormalize) {
     float z = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kTopkPerLane; ++i) {
       const int e = g + L * i;
       if (e < N && lv[i] == lv[i]) z += expf(lv[i] - l0);
     }
@@ -178,50 +183,55 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
 // (the first and second 8 elements of its 16).  Wave w accumulates chunks w, w+4, ...
 // in ascending order; the eight wave partials are added in wave order; nothing depends
 // on T or on the other tokens.
-template <int NSUB>
+template <int NSUB, int TB>
 __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __restrict__ h, const __bf16* __restrict__ wg,
                                                    const float* __restrict__ bias, float* __restrict__ logits,
                                                    int32_t* __restrict__ ids, float* __restrict__ gates,
                                                    float* __restrict__ margin, int T, int H, int N, int k,
                                                    int renormalize, const int32_t* __restrict__ replay,
                                                    float* __restrict__ scores) {
-  constexpr int NP = NSUB * 16;
-  __shared__ float part[kRouterWaves][NP][kRouterTokens];
-  __shared__ float lg[kRouterTokens][NP + 1];
+  constexpr int NP = NSUB * 16, TW = TB * kRouterTokens;
+  __shared__ float part[kRouterWaves][NP][TW];
+  __shared__ float lg[TW][NP + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * kRouterTokens;
+  const int t0 = blockIdx.x * TW;
   const int col = lane & 15, kq = (lane >> 4) * 16;
   // Columns past T and expert rows past N read row 0: their products land only in
   // accumulator entries that are never written out, so no load needs a branch.
-  const __bf16* hrow = h + (size_t)(t0 + col < T ? t0 + col : 0) * H + kq;
+  const __bf16* hrow[TB];
+#pragma unroll
+  for (int b = 0; b < TB; ++b) hrow[b] = h + (size_t)(t0 + b * 16 + col < T ? t0 + b * 16 + col : 0) * H + kq;
   const __bf16* wrow[NSUB];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) wrow[s] = wg + (size_t)(s * 16 + col < N ? s * 16 + col : 0) * H + kq;
   const int nchunks = H / kChunkK;
 
-  f32x4 acc[NSUB];
+  f32x4 acc[NSUB][TB];
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int b = 0; b < TB; ++b) acc[s][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int kUnroll = RouterUnroll<NSUB>::value;
-  auto mfma2 = [&](int s, const bf16x16& wv, const bf16x16& hv) {
+  auto mfma2 = [&](f32x4& acc, const bf16x16& wv, const bf16x16& hv) {
     const bf16x8 hlo = __builtin_shufflevector(hv, hv, 0, 1, 2, 3, 4, 5, 6, 7);
     const bf16x8 hhi = __builtin_shufflevector(hv, hv, 8, 9, 10, 11, 12, 13, 14, 15);
     const bf16x8 wlo = __builtin_shufflevector(wv, wv, 0, 1, 2, 3, 4, 5, 6, 7);
     const bf16x8 whi = __builtin_shufflevector(wv, wv, 8, 9, 10, 11, 12, 13, 14, 15);
-    acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, hlo, acc[s], 0, 0, 0);
-    acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, hhi, acc[s], 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, hlo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, hhi, acc, 0, 0, 0);
   };
   const bf16x16 zero16 = bf16x16{};
   for (int c0 = wave; c0 < nchunks; c0 += kRouterWaves * kUnroll) {
     // Every load of this round is issued before the first MFMA.  A chunk slot past
     // the end of H (which slots exist depends on H only) re-reads the last chunk
     // and has its activations replaced by zeros, adding exact zeros to the sums.
-    bf16x16 hv[kUnroll];
+    bf16x16 hv[kUnroll][TB];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int c = min(c0 + u * kRouterWaves, nchunks - 1);
-      hv[u] = *reinterpret_cast<const bf16x16*>(hrow + c * kChunkK);
+#pragma unroll
+      for (int b = 0; b < TB; ++b) hv[u][b] = *reinterpret_cast<const bf16x16*>(hrow[b] + c * kChunkK);
     }
     if constexpr (NSUB <= 4) {
       bf16x16 wv[kUnroll][NSUB];
@@ -234,21 +244,25 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const bf16x16 x = (c0 + u * kRouterWaves < nchunks) ? hv[u] : zero16;
+        const bool in = c0 + u * kRouterWaves < nchunks;
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) mfma2(s, wv[u][s], x);
+        for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+          for (int b = 0; b < TB; ++b) mfma2(acc[s][b], wv[u][s], in ? hv[u][b] : zero16);
       }
     } else {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int c = min(c0 + u * kRouterWaves, nchunks - 1);
-        const bf16x16 x = (c0 + u * kRouterWaves < nchunks) ? hv[u] : zero16;
+        const bool in = c0 + u * kRouterWaves < nchunks;
         bf16x16 wv[NSUB];
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) wv[s] = *reinterpret_cast<const bf16x16*>(wrow[s] + c * kChunkK);
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) mfma2(s, wv[s], x);
+        for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+          for (int b = 0; b < TB; ++b) mfma2(acc[s][b], wv[s], in ? hv[u][b] : zero16);
       }
     }
   }
@@ -256,10 +270,12 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
 #pragma unroll
   for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part[wave][s * 16 + (lane >> 4) * 4 + r][col] = acc[s][r];
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[wave][s * 16 + (lane >> 4) * 4 + r][b * 16 + col] = acc[s][b][r];
   __syncthreads();
-  for (int i = threadIdx.x; i < NP * kRouterTokens; i += blockDim.x) {
-    const int e = i / kRouterTokens, t = i % kRouterTokens;
+  for (int i = threadIdx.x; i < NP * TW; i += blockDim.x) {
+    const int e = i / TW, t = i % TW;
     if (e >= N) continue;
     float v = part[0][e][t];
 #pragma unroll
@@ -272,7 +288,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
   // fused top-k: one group of L lanes per token, 64 / L tokens per wave
   const int L = topk_lanes(N);
   const int per_wave = kWave / L;
-  for (int t = wave * per_wave + lane / L; t < kRouterTokens; t += kRouterWaves * per_wave)
+  for (int t = wave * per_wave + lane / L; t < TW; t += kRouterWaves * per_wave)
     if (t0 + t < T) topk_one(&lg[t][0], t0 + t, N, k, renormalize, L, ids, gates, margin, replay, scores);
 }
 
@@ -390,8 +406,9 @@ __global__ __launch_bounds__(NW * 64) void router_bf16_wide(const __bf16* __rest
       if (t0 + t < T) logits[(size_t)(t0 + t) * N + e] = lg[t * (NP + 1) + e];
     }
   }
-  const int L = topk_lanes(N);  // 64: one token per wave at a time
-  for (int t = wave; t < TW; t += NW)
+  const int L = topk_lanes(N);  // one group of L lanes per token, 64 / L tokens per wave
+  const int per_wave = kWave / L;
+  for (int t = wave * per_wave + (tid & 63) / L; t < TW; t += NW * per_wave)
     if (t0 + t < T) topk_one(lg + t * (NP + 1), t0 + t, N, k, renormalize, L, ids, gates, margin, replay, scores);
 }
 
@@ -426,8 +443,9 @@ template <int NSUB>
 hipError_t launch_router_bf16(const moe_config& c, const void* h, const void* wg, const float* bias, float* logits,
                               int32_t* ids, float* gates, float* margin, hipStream_t s, const int32_t* replay,
                               float* scores) {
-  dim3 grid(ceil_div(c.T, kRouterTokens));
-  router_bf16<NSUB><<<grid, kRouterThreads, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits, ids, gates, margin, c.T,
+  constexpr int TB = kRouterTB<NSUB>;
+  dim3 grid(ceil_div(c.T, TB * kRouterTokens));
+  router_bf16<NSUB, TB><<<grid, kRouterThreads, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits, ids, gates, margin, c.T,
                                          c.H, c.N, c.k, c.renormalize, replay, scores);
   return hipGetLastError();
 }
@@ -472,11 +490,10 @@ hipError_t launch_router(const moe_config& c, const void* h, const void* w_gate,
 #define MOE_ROUTER_CASE(n) \
   case n:                  \
     return launch_router_bf16<n>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
-  switch (ceil_div(c.N, 16)) {
+  switch (ceil_div(c.N, 16)) {  // N <= 128 here
     MOE_ROUTER_CASE(1) MOE_ROUTER_CASE(2) MOE_ROUTER_CASE(3) MOE_ROUTER_CASE(4) MOE_ROUTER_CASE(5)
-    MOE_ROUTER_CASE(6) MOE_ROUTER_CASE(7) MOE_ROUTER_CASE(8) MOE_ROUTER_CASE(9) MOE_ROUTER_CASE(10)
-    MOE_ROUTER_CASE(11) MOE_ROUTER_CASE(12) MOE_ROUTER_CASE(13) MOE_ROUTER_CASE(14) MOE_ROUTER_CASE(15)
-    default: return launch_router_bf16<16>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
+    MOE_ROUTER_CASE(6) MOE_ROUTER_CASE(7)
+    default: return launch_router_bf16<8>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
   }
 #undef MOE_ROUTER_CASE
 }
