@@ -28,10 +28,11 @@ constexpr int kChunkK = 64;         // K per chunk: lane group q = lane / 16 hol
 template <int NSUB>
 constexpr int kRouterTB = NSUB > 4 ? 2 : 1;
 
-// chunks in flight per wave: a CU's whole share of h for small expert counts
+// chunks in flight per wave: a CU's whole share of h for small expert counts; one
+// (NSUB weight fragments of 8 VGPRs) above 64 experts
 template <int NSUB>
 struct RouterUnroll {
-  static constexpr int value = NSUB <= 1 ? 8 : (NSUB <= 4 ? 4 : 2);
+  static constexpr int value = NSUB <= 1 ? 8 : (NSUB <= 4 ? 4 : 1);
 };
 
 typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
@@ -233,37 +234,23 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
 #pragma unroll
       for (int b = 0; b < TB; ++b) hv[u][b] = *reinterpret_cast<const bf16x16*>(hrow[b] + c * kChunkK);
     }
-    if constexpr (NSUB <= 4) {
-      bf16x16 wv[kUnroll][NSUB];
+    bf16x16 wv[kUnroll][NSUB];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int c = min(c0 + u * kRouterWaves, nchunks - 1);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = min(c0 + u * kRouterWaves, nchunks - 1);
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) wv[u][s] = *reinterpret_cast<const bf16x16*>(wrow[s] + c * kChunkK);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int s = 0; s < NSUB; ++s) wv[u][s] = *reinterpret_cast<const bf16x16*>(wrow[s] + c * kChunkK);
+    }
+    // without this barrier the compiler moves each weight load next to the MFMAs that
+    // use it and waits for it there, one load in flight per wave
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const bool in = c0 + u * kRouterWaves < nchunks;
+    for (int u = 0; u < kUnroll; ++u) {
+      const bool in = c0 + u * kRouterWaves < nchunks;
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s)
+      for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-          for (int b = 0; b < TB; ++b) mfma2(acc[s][b], wv[u][s], in ? hv[u][b] : zero16);
-      }
-    } else {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int c = min(c0 + u * kRouterWaves, nchunks - 1);
-        const bool in = c0 + u * kRouterWaves < nchunks;
-        bf16x16 wv[NSUB];
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) wv[s] = *reinterpret_cast<const bf16x16*>(wrow[s] + c * kChunkK);
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-          for (int b = 0; b < TB; ++b) mfma2(acc[s][b], wv[s], in ? hv[u][b] : zero16);
-      }
+        for (int b = 0; b < TB; ++b) mfma2(acc[s][b], wv[u][s], in ? hv[u][b] : zero16);
     }
   }
   // lane holds token column (lane & 15), expert rows 4*(lane>>4) + r
