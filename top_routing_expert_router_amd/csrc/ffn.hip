@@ -30,7 +30,7 @@
 //   has narrow tiles (run_tile_narrow) for its small last m-tiles; workgroups map
 //   to XCDs so each XCD walks a contiguous run of (n-tile group, m-tile) pairs and
 //   shares weight tiles in its L2.
-// fp8 weights: E4M3FN codes are loaded into registers half a stage ahead, decoded
+// fp8 weights: E4M3FN codes are loaded into registers three MFMA steps ahead, decoded
 // with the hardware converter, multiplied by their 128x128 block's bf16 scale in
 // fp32 and rounded to bf16 into LDS, spread over the MFMAs of the next half stage.
 #include <type_traits>
@@ -394,7 +394,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     setup_b(t);
   };
   u32x2 bq[BJ];
-  float sc_lo = 1.f, sc_hi = 1.f;
+  // block scales of the staged codes, as raw bf16 bits: converted where the decode uses
+  // them, so that no conversion (and no wait for the load) lands in the step that
+  // issues the loads -- vmcnt counts in order, so waiting for a scale would also wait
+  // for the codes issued just before it
+  uint32_t sc_lo = 0x3F80u, sc_hi = 0x3F80u;
 
   // part 0: the activation-row DMAs (AJ of them); part 1: the weight-row DMAs
   // (bf16) or the weight-code loads into registers (fp8).
@@ -411,10 +415,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int j = 0; j < BJ; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcB, LDS_PTR(sB + (wave * BJ + j) * 1024), 16, boff[j], k0 * 2, 0, 0);
     } else {
+      // fp8 codes: part 1 all rows and both scales; 2: rows i < BJ / 2 and their scale;
+      // 3: the other rows and theirs
 #pragma unroll
-      for (int i = 0; i < BJ; ++i) bq[i] = __builtin_amdgcn_raw_buffer_load_b64(rsrcB, boff[i], k0, 0);
-      sc_lo = (float)a.wscale[srow_lo + k0 / 128];
-      sc_hi = (float)a.wscale[srow_hi + k0 / 128];
+      for (int i = 0; i < BJ; ++i)
+        if (part == 1 || (part == 2) == (i < BJ / 2)) bq[i] = __builtin_amdgcn_raw_buffer_load_b64(rsrcB, boff[i], k0, 0);
+      if (part != 3) sc_lo = reinterpret_cast<const uint16_t*>(a.wscale)[srow_lo + k0 / 128];
+      if (part != 2) sc_hi = reinterpret_cast<const uint16_t*>(a.wscale)[srow_hi + k0 / 128];
     }
   };
   auto issue_loads = [&](auto rows_tag, const Tile& t, char* sA, char* sB, int k0) {
@@ -473,7 +480,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int i = 0; i < BJ; ++i) {
         if ((part == 0 && i >= BJ / 2) || (part == 1 && i < BJ / 2)) continue;
         const u32x2 q = bq[i];
-        const float s = i < 4 ? sc_lo : sc_hi;
+        const float s = __uint_as_float((i < 4 ? sc_lo : sc_hi) << 16);  // bf16 -> fp32, exact
         const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[0], false);
         const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[0], true);
         const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[1], false);
@@ -571,16 +578,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       __builtin_amdgcn_sched_barrier(0);
     };
     // fp8: the first two steps of a half.  dpart 0: the activation DMAs of the stage being
-    // filled and the decode of the first half of its codes; dpart 1: the decode of the
-    // second half, then the code (and scale) loads of the next stage at k0 = kcodes.
+    // filled, the decode of the first half of its codes, then the next stage's codes of
+    // that half (and their scale) at k0 = kcodes; dpart 1: the same for the second half.
+    // Each half's registers are reloaded as soon as they are decoded, so the loads have
+    // three steps to arrive.
     auto step_f8 = [&](int mset, const char* sA, const char* sB, int kk, int lset, char* dA, char* dB, int k0,
                        int dpart, int kcodes) {
       load_frags(sA, sB, kk, fw[lset], fx[lset]);
       if (dpart == 0) issue_part(rows_tag, t, dA, dB, k0, 0);
       store_fp8(dB, dpart);
-      if (dpart == 1) issue_part(rows_tag, t, dA, dB, kcodes, 1);
+      issue_part(rows_tag, t, dA, dB, kcodes, 2 + dpart);
       mfma_step(fw[mset], fx[mset], false);
-      const int VM = dpart == 0 ? AJ : BJ + 2;
+      const int VM = dpart == 0 ? AJ + BJ / 2 + 1 : BJ / 2 + 1;
       constexpr int DW = BJ / 2;      // LDS writes of the decode
       constexpr int VA = 16 * DW / MF + 1;  // its VALU work per MFMA (about 16 per row)
 #pragma unroll
@@ -619,13 +628,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int kt = 0; kt < KT - 2; kt += 2) {
         fp8_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        step_f8(2, sA1, sB1, 0, 0, sA0, sB0, (kt + 2) * BK, 0, 0);
+        step_f8(2, sA1, sB1, 0, 0, sA0, sB0, (kt + 2) * BK, 0, (kt + 3) * BK);
         step_f8(3, sA1, sB1, 1, 1, sA0, sB0, (kt + 2) * BK, 1, (kt + 3) * BK);
         step(0, sA1, sB1, 2, 2);
         step(1, sA1, sB1, 3, 3);
         fp8_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        step_f8(2, sA0, sB0, 0, 0, sA1, sB1, (kt + 3) * BK, 0, 0);
+        step_f8(2, sA0, sB0, 0, 0, sA1, sB1, (kt + 3) * BK, 0, min(kt + 4, KT - 1) * BK);
         step_f8(3, sA0, sB0, 1, 1, sA1, sB1, (kt + 3) * BK, 1, min(kt + 4, KT - 1) * BK);
         step(0, sA0, sB0, 2, 2);
         step(1, sA0, sB0, 3, 3);
