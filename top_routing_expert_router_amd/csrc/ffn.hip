@@ -445,7 +445,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   };
   // the next tile's first copies (its stage 0 or 1), in its own mode (outside any
   // scheduled region)
-  auto issue_loads_for = [&](const Tile& t, char* sA, char* sB, int stage, int part = -1) {
+  auto issue_loads_for = [&](const Tile& t, char* sA, char* sB, int stage) {
     const int rows = tile_rows(t);
     if constexpr (kNarrow) {
       if (rows == BM / 4 + 1) {
@@ -459,12 +459,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         return;
       }
     }
-    auto go = [&](auto rows_tag) {
-      if (part < 0)
-        issue_loads(rows_tag, t, sA, sB, stage * BK);
-      else
-        issue_part(rows_tag, t, sA, sB, stage * BK, part);
-    };
+    auto go = [&](auto rows_tag) { issue_loads(rows_tag, t, sA, sB, stage * BK); };
     if (rows == BM / 4)
       go(std::integral_constant<int, BM / 4>{});
     else if (rows == BM / 2)
@@ -665,34 +660,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int nlid = dyn ? run0 + __builtin_amdgcn_readfirstlane(sh_claim) : lid + slots;
     next_lid = nlid;
     more = nlid < lid_end;
-    // The next tile's stage 0 goes to buffer 0 (free now).  W13 with fp8 weights: the
-    // route ids are loaded first and the weight codes fetched, and the row offsets and
-    // activation copies follow the last stage's MFMAs, which hide the id loads' latency
-    // (3% on the DeepSeek shape; with bf16 weights it measured no different, and that
-    // kernel keeps the plain order).
-    constexpr bool kSplitSetup = MODE == 0 && FP8;
+    // The next tile's stage 0 goes to buffer 0 (free now).
     if (more) {
       decode(nlid, nxt);
-      if constexpr (kSplitSetup) {
-        setup_ids(nxt);
-        setup_b(nxt);
-        issue_loads_for(nxt, sA0, sB0, 0, 1);
-      } else {
-        setup(nxt);
-        issue_loads_for(nxt, sA0, sB0, 0);
-      }
+      setup(nxt);
+      issue_loads_for(nxt, sA0, sB0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     step(2, sA1, sB1, 0, 0);
     step(3, sA1, sB1, 1, 1);
     step(0, sA1, sB1, 2, 2);
     step(1, sA1, sB1, 3, 3);
-    if constexpr (kSplitSetup) {
-      if (more) {
-        setup_a(nxt);
-        issue_loads_for(nxt, sA0, sB0, 0, 0);
-      }
-    }
     // every wave has read buffer 1: the next tile's stage 1 goes there
     if (more) {
       lds_barrier();
