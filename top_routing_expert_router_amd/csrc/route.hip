@@ -12,6 +12,8 @@
 // is reduced in a fixed order that depends only on H (64-wide K chunks dealt to
 // eight waves round-robin, each wave in ascending chunk order, then the eight wave
 // partials added in wave order).  Nothing depends on T or on the other tokens.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -319,9 +321,12 @@ __global__ __launch_bounds__(NW * 64) void router_bf16_wide(const __bf16* __rest
     src[i] = r < NP ? wg + (size_t)(r < N ? r : 0) * H : h + (size_t)(t0 + r - NP < T ? t0 + r - NP : 0) * H;
     src[i] += cchunk * 8;
   }
-  // two register buffers: chunk c + 2 is loaded while chunk c is multiplied, so each
-  // load has two chunks' time to arrive before it is stored to LDS
-  u32x4_t bufA[LOADS], bufB[LOADS];
+  // RB register buffers: chunk c + RB is loaded right after chunk c has been stored
+  // to LDS, so each load has RB - 1 chunks of MFMAs to arrive (one chunk is only a
+  // few hundred cycles of matrix work, far less than a memory round trip)
+  constexpr int RB = 4;
+  static_assert(RB == 4, "the chunk loop below is unrolled by hand for four buffers");
+  u32x4_t buf[RB][LOADS];
   auto load = [&](u32x4_t* buf, int c) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
@@ -356,20 +361,33 @@ __global__ __launch_bounds__(NW * 64) void router_bf16_wide(const __bf16* __rest
         for (int ts = 0; ts < TS; ++ts) acc[es][ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[es], hf[ts], acc[es][ts], 0, 0, 0);
     }
   };
-  load(bufA, 0);
-  if (nchunks > 1) load(bufB, 1);
-  store(bufA, stage[0]);
+  // Chunk c is multiplied from stage c & 1 and staged through register buffer c % RB.
+  // Loads and stores are unconditional: a load past the last chunk re-reads it, and a
+  // store past it fills the free stage; neither is multiplied.  (A guarded load is moved
+  // by the compiler next to the store that uses it, which leaves nothing in flight.)
+#pragma unroll
+  for (int j = 0; j < RB; ++j) load(buf[j], min(j, nchunks - 1));
+  store(buf[0], stage[0]);
   __syncthreads();
-  for (int c = 0; c < nchunks; c += 2) {  // chunk c in stage 0, chunk c + 1 in stage 1
-    if (c + 2 < nchunks) load(bufA, c + 2);
-    chunk_mfma(stage[0]);
-    if (c + 1 < nchunks) store(bufB, stage[1]);
+  auto chunk_step = [&](auto jt, int c) {
+    constexpr int j = decltype(jt)::value;
+    load(buf[j], min(c + RB, nchunks - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    chunk_mfma(stage[j & 1]);
+    store(buf[(j + 1) % RB], stage[(j + 1) & 1]);
     __syncthreads();
-    if (c + 1 >= nchunks) break;
-    if (c + 3 < nchunks) load(bufB, c + 3);
-    chunk_mfma(stage[1]);
-    if (c + 2 < nchunks) store(bufA, stage[0]);
-    __syncthreads();
+  };
+  const int nmain = nchunks - nchunks % RB;
+  for (int c0 = 0; c0 < nmain; c0 += RB) {
+    chunk_step(std::integral_constant<int, 0>{}, c0);
+    chunk_step(std::integral_constant<int, 1>{}, c0 + 1);
+    chunk_step(std::integral_constant<int, 2>{}, c0 + 2);
+    chunk_step(std::integral_constant<int, 3>{}, c0 + 3);
+  }
+  // H an odd multiple of 128: two chunks left, already in buffers 0 and 1
+  if (nmain < nchunks) {
+    chunk_step(std::integral_constant<int, 0>{}, nmain);
+    chunk_step(std::integral_constant<int, 1>{}, nmain + 1);
   }
   // logits of the TW tokens, [TW][NP + 1] floats over the staging buffers: lane holds
   // token (lane & 31) of each token sub-tile and experts 8 g + 4 (lane >> 5) + q
