@@ -12,6 +12,8 @@
 // Each thread owns 8 consecutive columns of one token (16-byte bf16 accesses).
 // A route whose kept flag is 0 contributes nothing: its y row (allocated, never
 // written) is loaded but not added.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -34,22 +36,26 @@ constexpr int kThreads = 256;
 constexpr int kColsPerBlock = kColsPerThread * kThreads;
 
 // One workgroup per (token, 2048-column slice): the token's gates and kept flags
-// are uniform (scalar loads); every y row is loaded unconditionally (all rows are
-// allocated) and the kept flag selects whether it enters the sum, so all loads of
-// a thread are in flight together.
-template <typename T>
+// are uniform (one per lane, read back with readlane); every y row is loaded
+// (all rows are allocated) and the kept flag selects whether it enters the sum, so
+// all loads of a thread are in flight together.
+template <typename T, int K>
 __global__ __launch_bounds__(kThreads) void combine_rows(const T* __restrict__ y, const float* __restrict__ gates,
                                                           const uint8_t* __restrict__ kept, const T* __restrict__ shared,
                                                           const T* __restrict__ residual, T* __restrict__ out, int H,
-                                                          int k, int slices) {
+                                                          int slices) {
   typedef typename Vec8<T>::type V;
   const int t = blockIdx.x / slices;
   const long col = (long)(blockIdx.x % slices) * kColsPerBlock + threadIdx.x * kColsPerThread;
   if (col >= H) return;
-  V yv[8];
+  // the token's k gates and kept flags, lane j holding route j, loaded before the rows
+  // (a flag loaded where it is used waits for every row load issued before it)
+  const int jl = (int)(threadIdx.x & 63) < K ? (int)(threadIdx.x & 63) : 0;
+  const float g_lane = gates[(long)t * K + jl];
+  const int on_lane = kept[(long)t * K + jl];
+  V yv[K];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j < k) yv[j] = *reinterpret_cast<const V*>(y + ((long)t * k + j) * H + col);
+  for (int j = 0; j < K; ++j) yv[j] = *reinterpret_cast<const V*>(y + ((long)t * K + j) * H + col);
   V sv, rv;
   if (shared) sv = *reinterpret_cast<const V*>(shared + (long)t * H + col);
   if (residual) rv = *reinterpret_cast<const V*>(residual + (long)t * H + col);
@@ -57,16 +63,13 @@ __global__ __launch_bounds__(kThreads) void combine_rows(const T* __restrict__ y
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = -0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j < k) {
-      const long r = (long)t * k + j;
-      const bool on = kept[r] != 0;
-      const float g = gates[r];
+  for (int j = 0; j < K; ++j) {
+    const bool on = __builtin_amdgcn_readlane(on_lane, j) != 0;
+    const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g_lane), j));
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float f = fmaf(g, (float)yv[j][q], acc[q]);
-        acc[q] = on ? f : acc[q];
-      }
+    for (int q = 0; q < 8; ++q) {
+      const float f = fmaf(g, (float)yv[j][q], acc[q]);
+      acc[q] = on ? f : acc[q];
     }
   }
   if (shared) {
@@ -161,12 +164,25 @@ hipError_t launch_combine(const moe_config& c, const void* y_route, const float*
                           const void* shared_out, const void* residual, void* out, hipStream_t s) {
   const int slices = ceil_div(c.H, kColsPerBlock);
   const dim3 grid((unsigned)c.T * slices);
-  if (c.act_dtype == MOE_F32) {
-    combine_rows<float><<<grid, kThreads, 0, s>>>((const float*)y_route, gates, kept, (const float*)shared_out,
-                                                  (const float*)residual, (float*)out, c.H, c.k, slices);
-  } else {
-    combine_rows<__bf16><<<grid, kThreads, 0, s>>>((const __bf16*)y_route, gates, kept, (const __bf16*)shared_out,
-                                                   (const __bf16*)residual, (__bf16*)out, c.H, c.k, slices);
+  auto go = [&](auto kt) {
+    constexpr int K = decltype(kt)::value;
+    if (c.act_dtype == MOE_F32)
+      combine_rows<float, K><<<grid, kThreads, 0, s>>>((const float*)y_route, gates, kept, (const float*)shared_out,
+                                                       (const float*)residual, (float*)out, c.H, slices);
+    else
+      combine_rows<__bf16, K><<<grid, kThreads, 0, s>>>((const __bf16*)y_route, gates, kept,
+                                                        (const __bf16*)shared_out, (const __bf16*)residual,
+                                                        (__bf16*)out, c.H, slices);
+  };
+  switch (c.k) {  // 1 <= k <= 8 (checked with the config)
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 3: go(std::integral_constant<int, 3>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    case 5: go(std::integral_constant<int, 5>{}); break;
+    case 6: go(std::integral_constant<int, 6>{}); break;
+    case 7: go(std::integral_constant<int, 7>{}); break;
+    default: go(std::integral_constant<int, 8>{}); break;
   }
   return hipGetLastError();
 }
