@@ -147,7 +147,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_bf16")
-    ap.add_argument("--cpu-sample", type=int, default=128, help="tokens of the workload the CPU oracle runs")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="tokens of the workload the CPU oracle runs (default 0: the whole batch, about 6 s of "
+                         "host work on the Mixtral-shaped layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timings")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -442,6 +444,7 @@ def cpu_baseline(w, d, sample: int):
         s13 = d["w13_scale"].float().cpu().double().numpy()
         s2 = d["w2_scale"].float().cpu().double().numpy()
     bias = None if d.get("bias") is None else d["bias"].double().cpu().numpy()
+    sample = w.T if sample <= 0 else min(sample, w.T)
     g = torch.Generator().manual_seed(1234)
     tokens = torch.randperm(w.T, generator=g)[:sample].sort().values.numpy()
     t0 = time.perf_counter()
