@@ -68,11 +68,15 @@ __global__ __launch_bounds__(kSelThreads) void ec_select(const float* __restrict
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const uint64_t lower = (1ull << lane) - 1ull;
 
+  // all J loads in flight together: the index is clamped rather than the load guarded
+  // (a guarded load gets its own branch and a wait of its own)
   uint32_t key[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int t = tid + j * kSelThreads;
-    key[j] = t < T ? float_order_key(scores[(size_t)t * N + e]) : 0u;
+    const float v = scores[(size_t)min(t, T - 1) * N + e];
+    key[j] = float_order_key(v) & (t < T ? 0xFFFFFFFFu : 0u);  // a mask, not a select: the
+                                                               // compiler sinks a load used on one side only
   }
 
   if (C == 0) {  // nothing to pick

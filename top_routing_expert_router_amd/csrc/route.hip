@@ -136,11 +136,14 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
   } else {
     float rl[8];
     float m = -__builtin_inff();
+    int rid[8];  // all recorded ids in flight together (index clamped into the token's k)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rid[j] = replay[(size_t)t * k + min(j, k - 1)];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       rl[j] = __builtin_nanf("");
       if (j < k) {
-        const int id = replay[(size_t)t * k + j];
+        const int id = rid[j];
         if ((unsigned)id < (unsigned)N) rl[j] = row[id];
         m = rl[j] > m ? rl[j] : m;  // NaN never wins
       }
@@ -263,13 +266,22 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
 #pragma unroll
       for (int r = 0; r < 4; ++r) part[wave][s * 16 + (lane >> 4) * 4 + r][b * 16 + col] = acc[s][b][r];
   __syncthreads();
-  for (int i = threadIdx.x; i < NP * TW; i += blockDim.x) {
+  // this thread's biases for its entries, all loads in flight together (index clamped)
+  constexpr int kPer = (NP * TW + kRouterThreads - 1) / kRouterThreads;
+  float bv[kPer];
+  if (bias) {
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) bv[m] = bias[min(((int)threadIdx.x + m * kRouterThreads) / TW, N - 1)];
+  }
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) {
+    const int i = threadIdx.x + m * kRouterThreads;
     const int e = i / TW, t = i % TW;
-    if (e >= N) continue;
+    if (i >= NP * TW || e >= N) continue;
     float v = part[0][e][t];
 #pragma unroll
     for (int w = 1; w < kRouterWaves; ++w) v += part[w][e][t];
-    if (bias) v += bias[e];
+    if (bias) v += bv[m];
     lg[t][e] = v;
     if (logits && t0 + t < T) logits[(size_t)(t0 + t) * N + e] = v;  // nullable: no logits out
   }
@@ -392,6 +404,14 @@ __global__ __launch_bounds__(NW * 64) void router_bf16_wide(const __bf16* __rest
   // logits of the TW tokens, [TW][NP + 1] floats over the staging buffers: lane holds
   // token (lane & 31) of each token sub-tile and experts 8 g + 4 (lane >> 5) + q
   float* lg = reinterpret_cast<float*>(&stage[0][0]);
+  // this lane's expert biases, all loads in flight together (index clamped into [0, N))
+  float bv[ES][16];
+  if (bias) {
+#pragma unroll
+    for (int es = 0; es < ES; ++es)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bv[es][i] = bias[min(e0 + es * 32 + 8 * (i / 4) + 4 * kh + (i % 4), N - 1)];
+  }
 #pragma unroll
   for (int es = 0; es < ES; ++es)
 #pragma unroll
@@ -401,7 +421,7 @@ __global__ __launch_bounds__(NW * 64) void router_bf16_wide(const __bf16* __rest
         const int e = e0 + es * 32 + 8 * (i / 4) + 4 * kh + (i % 4);
         const int t = ts * 32 + l32;
         float v = acc[es][ts][i];
-        if (bias && e < N) v += bias[e];
+        if (bias && e < N) v += bv[es][i];
         lg[t * (NP + 1) + e] = v;
       }
   __syncthreads();
