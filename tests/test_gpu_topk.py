@@ -83,3 +83,33 @@ def test_fused_topk_matches_standalone(N, renorm):
     assert torch.equal(a["margin"].view(torch.int32), b["margin"].view(torch.int32))
     # and the routes are a valid top-k of those logits
     assert Hn.topk_valid(a["logits"].cpu().double().numpy(), a["ids"].cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("N", [64, 100, 128, 200, 256])
+def test_router_bias_many_experts(N):
+    """The additive per-expert bias on the projection paths for more than 16 experts (the
+    16-token kernel with one or two column blocks, the wide kernel above 128): logits within
+    1e-5 x max|l| of the oracle, routes exact away from near ties, and the fused top-k bit
+    for bit against the standalone top-k on the biased logits."""
+    w = W.QWEN3MOE_BF16.with_(T=300, N=N, k=8, zipf_s=0.3)
+    _say("router with bias", N)
+    h = W.hidden_states(w, device=DEV)
+    wg = W.router_weight(w, device=DEV)
+    bias = W.logit_bias(w).to(DEV)
+    cfg = Hn.config(w)
+    a = Hn.route_buffers(w)
+    M.moe_route(cfg, h, wg, bias, a["logits"], a["ids"], a["gates"], a["margin"])
+    torch.cuda.synchronize()
+    l_ref = O.router_logits(Hn.f64(h), Hn.f64(wg), Hn.f64(bias))
+    l_gpu = a["logits"].cpu().double().numpy()
+    scale = np.max(np.abs(l_ref), axis=1)
+    assert (np.max(np.abs(l_gpu - l_ref), axis=1) / scale).max() <= 1e-5
+    ids_ref, _, margin_ref = O.topk_route(l_ref, w.k)
+    diff = np.any(a["ids"].cpu().numpy() != ids_ref, axis=1)
+    assert not np.any(diff & ~(margin_ref <= 2e-5 * scale))
+    b = Hn.route_buffers(w)
+    b["logits"].copy_(a["logits"])
+    M.moe_route(cfg, None, None, None, b["logits"], b["ids"], b["gates"], b["margin"], flags=M.MOE_ROUTE_LOGITS_IN)
+    torch.cuda.synchronize()
+    assert torch.equal(a["ids"], b["ids"])
+    assert torch.equal(a["gates"].view(torch.int32), b["gates"].view(torch.int32))
