@@ -68,12 +68,13 @@ _COUNTER_KERNELS = [("ffn_gemm_bf16<0", "gate_up_gemm"), ("ffn_gemm_bf16<1", "do
                     ("mfma_loop<1>", "ceiling_mfma_1wave"), ("mfma_loop<2>", "ceiling_mfma_2wave")]
 
 
-def summarize_counters(fetch_dir: str, write_dir: str, workload: str) -> int:
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, out_dir: str = None) -> int:
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; CSV
     output) into HBM bytes per launch.  Both counters are in KiB per dispatch; each is
     scaled by bytes / counter for the 1 GiB copy kernel the same runs launch (it reads
-    and writes exactly 2^30 bytes).  Writes profiles/gate_up_gemm_<workload>_traffic.json
-    (tagged with the hash of the GEMM source it was taken on) and prints a text summary."""
+    and writes exactly 2^30 bytes).  Writes gate_up_gemm_<workload>_traffic.json into
+    out_dir (default profiles/), tagged with the hash of the GEMM source it was taken on,
+    and prints a text summary."""
     import csv
     import statistics
 
@@ -104,7 +105,7 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str) -> int:
     out = {"workload": workload, "ffn_source_sha256_16": _ffn_source_hash(),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "hbm_bytes_per_launch": rows["gate_up_gemm"]["hbm_bytes"], "kernels": rows}
-    path = os.path.join(ROOT, "profiles", f"gate_up_gemm_{workload}_traffic.json")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"gate_up_gemm_{workload}_traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
@@ -114,7 +115,7 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str) -> int:
     for k, v in rows.items():
         print(f"{k:<20}{v['fetch_KiB']:>14,.0f}{v['write_KiB']:>14,.0f}{v['read_bytes'] / 1e9:>10.4f}"
               f"{v['write_bytes'] / 1e9:>10.4f}{v['hbm_bytes'] / 1e9:>10.4f}")
-    print(f"wrote {os.path.relpath(path, ROOT)}")
+    print(f"wrote {path}")
     return 0
 
 
@@ -258,13 +259,15 @@ def main() -> int:
         for ev in evs:
             M.moe_forward(cfg, wts, d["h"], d["residual"], out, {"stage_events": ev}, ws, stream=stream)
         torch.cuda.synchronize()
-        return [sum(ev[i].elapsed_time(ev[i + 1]) for ev in evs) / reps for i in range(M.TRACE_EVENTS - 1)]
+        stage = [sum(ev[i].elapsed_time(ev[i + 1]) for ev in evs) / reps for i in range(M.TRACE_EVENTS - 1)]
+        whole = sum(ev[0].elapsed_time(ev[-1]) for ev in evs) / reps
+        return stage, whole
 
     R, T, H, I, N, k = w.T * w.k, w.T, w.H, w.I, w.N, w.k
     stages = {}
     gate_up_flops = 4.0 * kept_routes * H * I
     down_flops = 2.0 * kept_routes * H * I
-    fwd_stage_ms = in_forward(max(args.steps, 5))
+    fwd_stage_ms, fwd_events_ms = in_forward(max(args.steps, 5))
     ms_gate_up, ms_down = fwd_stage_ms[2], fwd_stage_ms[3]
     stages["gate_up_gemm"] = {"us": ms_gate_up * 1e3, "TFLOP/s": gate_up_flops / (ms_gate_up * 1e-3) / 1e12}
     stages["down_gemm"] = {"us": ms_down * 1e3, "TFLOP/s": down_flops / (ms_down * 1e-3) / 1e12}
@@ -316,6 +319,21 @@ def main() -> int:
         for kname, v in stages.items():
             log(f"[bench] stage {kname}: " + ", ".join(f"{a} {b:,.2f}" for a, b in v.items()))
 
+    # the stage events themselves cost time: the sum of the stages equals the instrumented
+    # forward (first to last event), and that one is compared with the plain forward timed above
+    reconcile = {"stages_sum_us": round(sum(fwd_stage_ms) * 1e3, 2),
+                 "instrumented_forward_us": round(fwd_events_ms * 1e3, 2),
+                 "plain_forward_us": round(ms * 1e3, 2),
+                 "event_overhead_pct": round(100.0 * (fwd_events_ms - ms) / ms, 2)}
+    log(f"[bench] stage sum {reconcile['stages_sum_us']:.1f} us, instrumented forward "
+        f"{reconcile['instrumented_forward_us']:.1f} us, plain forward {reconcile['plain_forward_us']:.1f} us")
+    clocks = None
+    if not args.no_stages:
+        clocks = gfx_clock_report(step, tr, cfg, d, wts, act_t, stream)
+        if clocks:
+            log("[bench] shader clock (MHz, SMU samples while each runs back to back): "
+                + ", ".join(f"{k} {v}" for k, v in clocks.items()))
+
     achieved = stages["gate_up_gemm"]["TFLOP/s"]
     roofline = {"kernel": "ffn_gemm_bf16<W13+SwiGLU>", "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -340,6 +358,7 @@ def main() -> int:
                    "routing": w.routing, "n_shared": w.n_shared, "kept_routes": kept_routes,
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline, "stages": {k: {a: round(b, 3) for a, b in v.items()} for k, v in stages.items()},
+        "stage_reconciliation": reconcile, "sclk_MHz": clocks,
         "measured_ceilings": ceil,
         "cpu_baseline": cpu,
     }
@@ -391,6 +410,120 @@ def ceilings(stream):
     return {k: round(v, 1) for k, v in out.items()}
 
 
+class GfxClockSampler:
+    """The GPU's graphics (shader) clock as the SMU reports it (amdsmi GPU metrics, per XCD),
+    sampled from a host thread every ~2 ms while a workload runs back to back."""
+
+    def __init__(self):
+        import amdsmi
+        import torch
+        self.a = amdsmi
+        amdsmi.amdsmi_init()
+        hs = amdsmi.amdsmi_get_processor_handles()
+        self.h = hs[0]
+        if len(hs) > 1:  # the handle whose PCI address is torch's device 0
+            p = torch.cuda.get_device_properties(0)
+            want = (getattr(p, "pci_domain_id", 0), getattr(p, "pci_bus_id", -1), getattr(p, "pci_device_id", 0))
+            for h in hs:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self.h = h
+        self.sample()
+
+    def sample(self):
+        m = self.a.amdsmi_get_gpu_metrics_info(self.h)
+        v = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        if not v and isinstance(m.get("current_gfxclk"), (int, float)):
+            v = [m["current_gfxclk"]]
+        return sum(v) / len(v) if v else None
+
+    def during(self, fn, seconds: float = 0.6, batch: int = 8):
+        import statistics
+        import threading
+
+        import torch
+        got, stop = [], threading.Event()
+
+        def loop():
+            while not stop.is_set():
+                try:
+                    c = self.sample()
+                except Exception:  # pragma: no cover - reported as missing
+                    c = None
+                if c:
+                    got.append((time.perf_counter(), c))
+                time.sleep(0.002)
+
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
+        th = threading.Thread(target=loop, daemon=True)
+        t0 = time.perf_counter()
+        th.start()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(batch):
+                fn()
+            torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        stop.set()
+        th.join()
+        # leave out the first tenth (the clock settling) and anything after the work ended
+        vals = [c for t, c in got if t0 + 0.1 * (t1 - t0) <= t <= t1]
+        if not vals:
+            return None
+        return {"median": round(statistics.median(vals)), "min": round(min(vals)), "max": round(max(vals)),
+                "samples": len(vals)}
+
+
+def gfx_clock_report(step, tr, cfg, d, wts, act_t, stream):
+    """Sustained shader clock during the whole forward and during each expert GEMM alone (the
+    standalone entry points, run back to back), or None where the SMU metrics are unreadable."""
+    import top_routing_expert_router_amd as M
+    try:
+        smp = GfxClockSampler()
+    except Exception as e:  # pragma: no cover - depends on the box
+        log(f"[bench] shader clock unavailable: {e}")
+        return None
+    y = tr["y_route"]
+    out = {}
+    try:
+        out["forward"] = smp.during(step)
+        out["gate_up_gemm"] = smp.during(lambda: M.moe_expert_gate_up(
+            cfg, d["h"], tr["sorted_route_ids"], tr["expert_offsets"], wts["w13"], wts.get("w13_scale"), tr["act"],
+            None, stream=stream))
+        out["down_gemm"] = smp.during(lambda: M.moe_expert_down(
+            cfg, tr["act"], tr["sorted_route_ids"], tr["expert_offsets"], wts["w2"], wts.get("w2_scale"), y,
+            stream=stream))
+    except Exception as e:  # pragma: no cover
+        log(f"[bench] shader clock sampling failed: {e}")
+    return out or None
+
+
+def host_cpu() -> dict:
+    """The host's CPU model and core counts (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    info = {"model": None, "logical_cpus": os.cpu_count(), "physical_cores": None,
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+    try:
+        txt = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        kv = {a.strip(): b.strip() for a, _, b in (l.partition(":") for l in txt.splitlines())}
+        info["model"] = kv.get("Model name")
+        if kv.get("Core(s) per socket") and kv.get("Socket(s)"):
+            info["physical_cores"] = int(kv["Core(s) per socket"]) * int(kv["Socket(s)"])
+    except Exception:
+        pass
+    if info["model"] is None:
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    info["model"] = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
+    return info
+
+
 def ec_stages(stages, w, cfg, d, wts, tr, out, ws, C, p_max, n_blocks, asz, timed, reps, stream):
     """Per-stage timings of an expert-choice layer (scores + picks, picks alone, alignment, combine)."""
     import top_routing_expert_router_amd as M
@@ -420,8 +553,9 @@ def ec_stages(stages, w, cfg, d, wts, tr, out, ws, C, p_max, n_blocks, asz, time
     stages["combine"] = {"us": ms * 1e3, "GB/s": comb_bytes / (ms * 1e-3) / 1e9}
 
 
-def cpu_baseline(w, d, sample: int):
-    """The oracle (fp64 numpy) on this workload, restricted to a seeded token sample."""
+def cpu_baseline(w, d, sample: int, runs: int = 3):
+    """The oracle (fp64 numpy) on this workload, restricted to a seeded token sample: the
+    median of ``runs`` timed runs on the same host copies of the inputs."""
     import numpy as np
     import torch
 
@@ -447,7 +581,31 @@ def cpu_baseline(w, d, sample: int):
     sample = w.T if sample <= 0 else min(sample, w.T)
     g = torch.Generator().manual_seed(1234)
     tokens = torch.randperm(w.T, generator=g)[:sample].sort().values.numpy()
-    t0 = time.perf_counter()
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        res = _oracle_run(O, w, h_b, wg_b, w13_b, w2_b, s13 if fp8 else None, s2 if fp8 else None, fp8, bias, d,
+                          tokens)
+        times.append(time.perf_counter() - t0)
+        assert res["out"].shape[0] == sample
+    import statistics
+    dt = statistics.median(times)
+    log(f"[bench] cpu baseline: {sample} tokens, runs {' '.join(f'{t:.2f}' for t in times)} s")
+    cpu = host_cpu()
+    return {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "threads": int(threads), "cpu_model": cpu["model"], "host_logical_cpus": cpu["logical_cpus"],
+            "host_physical_cores": cpu["physical_cores"], "affinity_cpus": cpu["affinity_cpus"],
+            "runs_s": [round(t, 3) for t in times], "seconds": round(dt, 3),
+            "sample": f"median of {runs} runs; {sample} seeded tokens of the {w.T}-token batch: full routing, "
+                      f"capacity and alignment of all tokens, expert FFN (all experts' weights decoded to fp64) "
+                      f"and combine for the sampled tokens; 'cores' = BLAS threads the oracle's matrix "
+                      f"products ran on"}
+
+
+def _oracle_run(O, w, h_b, wg_b, w13_b, w2_b, s13, s2, fp8, bias, d, tokens):
+    """One oracle pass over the sampled tokens (decoding the stored inputs included)."""
+    import numpy as np
+    import torch
     h64 = O.decode_bf16(h_b)
 
     def expert(t, sc):
@@ -472,14 +630,7 @@ def cpu_baseline(w, d, sample: int):
         res = O.moe_forward(h64, O.decode_bf16(wg_b), expert(w13_b, s13 if fp8 else None),
                             expert(w2_b, s2 if fp8 else None), k=w.k, B=w.B, cap_num=w.cap_num, cap_den=w.cap_den,
                             residual=h64, tokens=tokens, bias=bias, reroute_depth=w.reroute_depth, **shared)
-    dt = time.perf_counter() - t0
-    assert res["out"].shape[0] == sample
-    log(f"[bench] cpu baseline: {sample} tokens in {dt:.2f} s")
-    return {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "host_cpus": len(os.sched_getaffinity(0)), "seconds": round(dt, 2),
-            "sample": f"{sample} seeded tokens of the {w.T}-token batch: full routing, capacity and alignment "
-                      f"of all tokens, expert FFN (all experts' weights decoded to fp64) and combine for the "
-                      f"sampled tokens"}
+    return res
 
 
 if __name__ == "__main__":

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef int32_t moe_status;
 enum {
@@ -202,6 +202,9 @@ typedef struct moe_trace {
    * consecutive events is that stage as it runs inside the layer.  A failed record is
    * returned as MOE_ERR_HIP. */
   void* const* stage_events;
+  /* Nullable: [P_max, 2I] act dtype, the routed W13 output before the activation (columns
+   * 0..I-1 the gate projection, I..2I-1 the up projection; see moe_expert_gate_up). */
+  void* w13_out;
 } moe_trace;
 
 #define MOE_TRACE_EVENTS 7
@@ -252,6 +255,17 @@ moe_status moe_route(const moe_config* cfg, const void* h, const void* w_gate, c
 /*
  * Capacity with the drop policy (whatever reroute_depth says; moe_align_reroute
  * applies the config's policy) and alignment (deterministic: no atomic decides any order).
+ *   capacity: "Mixture-of-experts routing & LLM repeatability", paragraph on expert
+ *     capacity (tokens / experts x factor, filled in batch order, overflow skips the
+ *     expert); "Mixture-of-Experts Routing at Inference Time", "Worked example" (the
+ *     capacity as the mean load times the factor, drops = overflow summed over experts)
+ *     and "The hard part", Figure 2 (drop branch: the token keeps only the residual path);
+ *   alignment: "Route-Block Membership Selects Packed-AWQ Arithmetic", "The bookkeeping
+ *     before the matrix multiplication" (rows grouped by expert, padded into fixed-size
+ *     blocks; membership = the valid flattened route ids of a block) and "Stable
+ *     construction selected a third trajectory" (order by expert id, then route id);
+ *   stats: "Mixture-of-Experts Routing at Inference Time", "Worked example" (per-expert
+ *     load = bincount of the flattened ids) and "The hard part" (the routing-stats probe).
  *   topk_ids         [T*k] int32 (from moe_route, or replayed by the caller)
  *   route_kept       [T*k] uint8 out: 1 = the route runs its expert, 0 = dropped or invalid id
  *   sorted_route_ids [P_max] int32 out: per expert (ascending), its kept route ids ascending,
@@ -287,7 +301,12 @@ moe_status moe_align_reroute(const moe_config* cfg, const int32_t* topk_ids, con
                              void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Grouped SwiGLU expert FFN over aligned rows.
+ * Grouped SwiGLU expert FFN over aligned rows ("Route-Block Membership Selects
+ * Packed-AWQ Arithmetic", "The boundary that mattered": an expert row passes through the
+ * fused first projection W13, the activation and the routed second projection W2; the
+ * page compares exactly these surfaces).  The FFN form is SwiGLU, the gate half through
+ * silu times the up half ("Mixture-of-Experts Routing at Inference Time", "How sparse
+ * routing works": each chosen expert is a feed-forward network applied to h).
  * Routed mode (sorted_route_ids != NULL): rows p in expert e's segment
  *   [expert_offsets[e], expert_offsets[e+1]) hold route r = sorted_route_ids[p]
  *   (token r / k); sentinel rows compute zeros and write no output row.
@@ -298,30 +317,42 @@ moe_status moe_align_reroute(const moe_config* cfg, const int32_t* topk_ids, con
  * act = silu(h W1^T) * (h W3^T) is stored in the act dtype (fp32 accumulation);
  * fp8 weights are decoded and scaled to bf16 before the bf16 MFMA.  Every row's
  * K order is fixed, so a row's results do not depend on the other rows.
+ *   w13_out  nullable debug surface [P_max, 2I] (identity mode [T, 2I]), act dtype: the W13
+ *            output before the activation, columns 0..I-1 = h W1^T, I..2I-1 = h W3^T, each
+ *            rounded once from its fp32 accumulator (the same accumulators act is made
+ *            from); rows as act.  Leaves act and y_out bit for bit unchanged.
  */
 moe_status moe_expert_ffn(const moe_config* cfg, const void* h, const int32_t* sorted_route_ids,
                           const int32_t* expert_offsets, const void* w13, const void* w2,
-                          const void* w13_scale, const void* w2_scale, void* act, void* y_out,
-                          void* stream);
+                          const void* w13_scale, const void* w2_scale, void* act, void* w13_out,
+                          void* y_out, void* stream);
 
 /*
  * The two halves of moe_expert_ffn, for callers that want the surfaces apart
  * (same row conventions and modes as moe_expert_ffn):
  *   moe_expert_gate_up: act = silu(x W1^T) * (x W3^T) from the fused W13 projection
  *                       ("Route-Block Membership Selects Packed-AWQ Arithmetic", "The
- *                       boundary that mattered": W13 and activation surfaces);
+ *                       boundary that mattered": W13 and activation surfaces); w13_out
+ *                       (nullable) as moe_expert_ffn's;
  *   moe_expert_down:    y rows = act W2^T (the routed second projection surface).
  */
 moe_status moe_expert_gate_up(const moe_config* cfg, const void* h, const int32_t* sorted_route_ids,
                               const int32_t* expert_offsets, const void* w13, const void* w13_scale, void* act,
-                              void* stream);
+                              void* w13_out, void* stream);
 moe_status moe_expert_down(const moe_config* cfg, const void* act, const int32_t* sorted_route_ids,
                            const int32_t* expert_offsets, const void* w2, const void* w2_scale, void* y_out,
                            void* stream);
 
 /*
- * Combine: out[t] = round( ((sum over kept j ascending of gate[t,j] * y_route[t*k+j])
- *                           + shared_out[t]) + residual[t] ), fp32 accumulation in exactly
+ * Combine ("Mixture-of-experts routing & LLM repeatability", the layer sketch: the output
+ * is the gate-weighted sum of the chosen experts' outputs, fed back into the residual
+ * stream; "Mixture-of-Experts Routing at Inference Time", "How sparse routing works",
+ * Figure 1, and "The hard part", Figure 2: a dropped route contributes nothing, the token
+ * keeps h and its surviving experts; "When Faster ≠ Identical: Numerical Pitfalls in
+ * Serving MoE Models", "Why This Matters": the always-on shared expert is added to the
+ * routed output):
+ *   out[t] = round( ((sum over kept j ascending of gate[t,j] * y_route[t*k+j])
+ *                    + shared_out[t]) + residual[t] ), fp32 accumulation in exactly
  * that order, one rounding to the act dtype.  Gates are not renormalised after a drop.
  * A token with no kept route, no shared expert and a residual outputs its residual bitwise.
  *   y_route [T*k, H], topk_gates [T, k] float32, route_kept [T*k] uint8,
@@ -332,7 +363,10 @@ moe_status moe_combine(const moe_config* cfg, const void* y_route, const float* 
                        void* out, void* stream);
 
 /*
- * The whole layer: moe_route -> moe_align -> moe_expert_ffn (routed, then the shared
+ * The whole layer ("Mixture-of-Experts Routing at Inference Time", "How sparse routing
+ * works", Figure 1: router, top-k, the chosen experts, weighted sum; "Mixture-of-experts
+ * routing & LLM repeatability", the layer sketch), as the entry points above compose it:
+ * moe_route -> moe_align -> moe_expert_ffn (routed, then the shared
  * expert in identity mode) -> moe_combine, on one stream, with no host synchronisation.
  *   h [T, H], residual [T, H] nullable (pass h for the usual h + MoE(h)), out [T, H].
  *   trace nullable (see moe_trace); ws of moe_workspace_size(MOE_OP_FORWARD) bytes.
@@ -433,6 +467,36 @@ moe_status moe_align_expert_choice(const moe_config* cfg, const int32_t* choice_
 moe_status moe_combine_expert_choice(const moe_config* cfg, const void* y_rows, const float* scores,
                                      const int32_t* choice_slot, const void* shared_out, const void* residual,
                                      void* out, void* stream);
+
+/* ---------------------------------------------------------------- routing health
+ *
+ * "Mixture-of-Experts Routing at Inference Time", "Worked example" (per-expert load and the
+ * dropped count) and "The hard part" (the per-pass routing-stats probe: largest and smallest
+ * expert load, imbalance = largest load over the mean load, dropped routes and their share
+ * of all routed ones, exported as a metric every forward pass).
+ */
+typedef struct moe_routing_health {
+  int32_t total_routes;     /* routes with an expert id in [0, N): the sum of the per-expert loads */
+  int32_t max_expert_load;  /* per-expert load before capacity */
+  int32_t min_expert_load;
+  int32_t dropped_routes;   /* valid routes that run no expert (MOE_STAT_DROPPED) */
+  int32_t kept_routes;      /* routes that run an expert (MOE_STAT_KEPT) */
+  int32_t invalid_routes;   /* ids outside [0, N) (MOE_STAT_INVALID) */
+  int32_t capacity;         /* per-expert capacity, -1 when dropless */
+  int32_t rerouted_routes;  /* reroute policy: kept on another expert (MOE_STAT_REROUTED) */
+  int32_t unpicked_tokens;  /* expert choice: tokens no expert picked (MOE_STAT_UNPICKED) */
+  int32_t reserved;         /* 0 */
+  double imbalance_ratio;   /* max_expert_load / (total_routes / N); 0 when total_routes = 0 */
+  double drop_fraction;     /* dropped_routes / total_routes; 0 when total_routes = 0 */
+} moe_routing_health;
+
+/* Host-only: the routing-health numbers of one pass from the stats array that moe_align,
+ * moe_align_reroute, moe_align_expert_choice or moe_forward (trace->stats) wrote, after the
+ * caller has copied it to host memory ([N + MOE_STATS_EXTRA] int32).  Reads nothing on the
+ * device and enqueues nothing.  MOE_ERR_NULL_POINTER for a NULL stats or out;
+ * MOE_ERR_INVALID_CONFIG for an invalid config, or a stats array that no alignment of this
+ * config can have written (a negative load or counter). */
+moe_status moe_routing_health_from_stats(const moe_config* cfg, const int32_t* stats, moe_routing_health* out);
 
 #ifdef __cplusplus
 }

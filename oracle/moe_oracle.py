@@ -34,6 +34,7 @@ import numpy as np
 __all__ = [
     "decode_bf16", "decode_e4m3", "round_bf16", "dequantize_blocks", "router_logits", "rank_experts",
     "topk_route", "replay_route", "capacity", "capacity_keep", "capacity_reroute", "align", "silu", "swiglu_expert",
+    "w13_projection", "swiglu_activation",
     "expert_ffn", "combine", "routing_stats", "moe_forward", "expert_scores", "expert_choice_capacity",
     "expert_choice_select", "expert_choice_align", "expert_choice_combine", "expert_choice_forward",
 ]
@@ -322,6 +323,28 @@ def swiglu_expert(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, stage_round=No
     u = x @ w13[:I].T
     v = x @ w13[I:].T
     return r(r(silu(u) * v) @ w2.T)
+
+
+def w13_projection(x: np.ndarray, w13: np.ndarray) -> np.ndarray:
+    """The fused first projection on rows x [M, H]: [W1 x ; W3 x] -> [M, 2I].
+
+    [RB] "The boundary that mattered" names the W13 output as the first of the four
+    surfaces an expert row passes through.  Columns 0..I-1 are the gate projection
+    (rows 0..I-1 of w13), columns I..2I-1 the up projection (rows I..2I-1).
+    """
+    return np.asarray(x, np.float64) @ np.asarray(w13, np.float64).T
+
+
+def swiglu_activation(x: np.ndarray, w13: np.ndarray) -> np.ndarray:
+    """The activation surface on rows x [M, H]: silu(W1 x) * (W3 x) -> [M, I].
+
+    [RB] "The boundary that mattered": the activation is the surface between the W13
+    output and the second projection; SwiGLU takes the gate half through silu and
+    multiplies it by the up half.
+    """
+    u = w13_projection(x, w13)
+    I = u.shape[1] // 2
+    return silu(u[:, :I]) * u[:, I:]
 
 
 def expert_ffn(h: np.ndarray, ids: np.ndarray, kept: np.ndarray, w13_of, w2_of, N: int,

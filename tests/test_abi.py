@@ -53,7 +53,7 @@ def test_ceiling_library_exports_and_rejects_bad_arguments():
 
 
 def test_abi_version_and_status_strings():
-    assert M.moe_abi_version() == 4
+    assert M.moe_abi_version() == 5
     for code, name in M.STATUS.items():
         assert M.moe_status_str(code).startswith(name)
     assert "unknown" in M.moe_status_str(99)
@@ -137,11 +137,14 @@ def test_host_validation_of_pointers_and_workspace():
     _expect("MOE_ERR_MISALIGNED", M.moe_align, cfg, A + 2, A, A, A, A, A, None, A, 1 << 20, s)
     _expect("MOE_ERR_WORKSPACE_TOO_SMALL", M.moe_align, cfg, A, A, A, A, A, A, None, A, 4, s)
     # expert ffn
-    _expect("MOE_ERR_NULL_POINTER", M.moe_expert_ffn, cfg, A, A, None, A, A, None, None, A, A, s)
-    _expect("MOE_ERR_NULL_POINTER", M.moe_expert_ffn, cfg, A, None, None, None, A, None, None, A, A, s)
-    _expect("MOE_ERR_MISALIGNED", M.moe_expert_ffn, cfg, A, None, None, A, A, None, None, A + 8, A, s)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_expert_ffn, cfg, A, A, None, A, A, None, None, A, None, A, s)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_expert_ffn, cfg, A, None, None, None, A, None, None, A, None, A, s)
+    _expect("MOE_ERR_MISALIGNED", M.moe_expert_ffn, cfg, A, None, None, A, A, None, None, A + 8, None, A, s)
+    _expect("MOE_ERR_MISALIGNED", M.moe_expert_ffn, cfg, A, None, None, A, A, None, None, A, A + 8, A, s)
+    _expect("MOE_ERR_MISALIGNED", M.moe_expert_gate_up, cfg, A, None, None, A, None, A, A + 2, s)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_expert_gate_up, cfg, A, A, None, A, None, A, A, s)
     cfg8 = config(W.DEEPSEEKV3_FP8)
-    _expect("MOE_ERR_NULL_POINTER", M.moe_expert_ffn, cfg8, A, None, None, A, A, None, None, A, A, s)
+    _expect("MOE_ERR_NULL_POINTER", M.moe_expert_ffn, cfg8, A, None, None, A, A, None, None, A, None, A, s)
     # combine
     _expect("MOE_ERR_NULL_POINTER", M.moe_combine, cfg, A, A, None, None, None, A, s)
     _expect("MOE_ERR_MISALIGNED", M.moe_combine, cfg, A, A, A, None, ODD, A, s)
@@ -229,7 +232,62 @@ def test_binding_structs_match_the_header():
     # the ctypes mirrors must list the C members in the same order (all pointer-sized here)
     assert [n for n, _ in M.moe_trace._fields_] == _header_fields("moe_trace")
     assert [n for n, _ in M.moe_weights._fields_] == _header_fields("moe_weights")
+    assert [n for n, _ in M.moe_routing_health._fields_] == _header_fields("moe_routing_health")
     assert M.TRACE_EVENTS == 7
+
+
+def _stats_array(N, load, kept, dropped, invalid, cap, rerouted=0, unpicked=0):
+    """A stats array laid out as the alignment writes it: per-expert load, then the counters."""
+    import numpy as np
+    st = np.zeros(N + M.STATS_EXTRA, np.int32)
+    st[:N] = load
+    x = N
+    st[x + M.STAT["kept"]], st[x + M.STAT["dropped"]], st[x + M.STAT["invalid"]] = kept, dropped, invalid
+    st[x + M.STAT["capacity"]] = cap
+    st[x + M.STAT["max_load"]], st[x + M.STAT["min_load"]] = max(load), min(load)
+    st[x + M.STAT["rerouted"]], st[x + M.STAT["unpicked"]] = rerouted, unpicked
+    return st
+
+
+def test_routing_health_from_stats_matches_the_oracle_probe():
+    # host-only helper: the numbers of the routing-stats probe from a stats array, against
+    # the oracle's routing_stats on the same routes (drop policy, with and without capacity)
+    import numpy as np
+    from oracle import moe_oracle as O
+    rng = np.random.default_rng(4)
+    for T, N, k, cf in ((64, 8, 2, None), (300, 16, 1, (5, 4)), (33, 6, 3, (1, 2)), (5, 4, 2, (1, 8))):
+        ids = rng.integers(-1, N + 1, size=(T, k)) if T == 33 else (rng.zipf(1.6, size=(T, k)) - 1) % N
+        cap = O.capacity(T, k, N, *(cf or (0, 0)))
+        kept = O.capacity_keep(ids, N, cap)
+        ref = O.routing_stats(ids, kept, N, cap)
+        cfg = config(W.MIXTRAL_BF16, T=T, N=N, k=k, cap_num=cf[0] if cf else 0, cap_den=cf[1] if cf else 0)
+        st = _stats_array(N, ref["load"], ref["kept_routes"], ref["dropped_tokens"], ref["invalid_routes"],
+                          ref["capacity"])
+        got = M.moe_routing_health_from_stats(cfg, st)
+        assert got["max_expert_load"] == ref["max_expert_load"] and got["min_expert_load"] == ref["min_expert_load"]
+        assert got["dropped_routes"] == ref["dropped_tokens"] and got["kept_routes"] == ref["kept_routes"]
+        assert got["invalid_routes"] == ref["invalid_routes"] and got["capacity"] == ref["capacity"]
+        assert got["total_routes"] == int(ref["load"].sum())
+        assert got["imbalance_ratio"] == pytest.approx(ref["imbalance_ratio"], rel=1e-15, abs=0)
+        assert got["drop_fraction"] == pytest.approx(ref["drop_fraction"], rel=1e-15, abs=0)
+    # no valid route: both ratios are 0
+    cfg = config(W.MIXTRAL_BF16, T=2, N=4, k=1)
+    z = M.moe_routing_health_from_stats(cfg, _stats_array(4, [0, 0, 0, 0], 0, 0, 2, -1))
+    assert z["imbalance_ratio"] == 0.0 and z["drop_fraction"] == 0.0 and z["invalid_routes"] == 2
+
+
+def test_routing_health_rejects_bad_arguments():
+    import numpy as np
+    cfg = config(W.MIXTRAL_BF16)
+    r = M.moe_routing_health()
+    L = M.lib()
+    st = np.zeros(cfg.N + M.STATS_EXTRA, np.int32)
+    assert L.moe_routing_health_from_stats(ctypes.byref(cfg), None, ctypes.byref(r)) == 1
+    assert L.moe_routing_health_from_stats(ctypes.byref(cfg), st.ctypes.data, None) == 1
+    st[0] = -3  # a negative load: no alignment writes that
+    assert L.moe_routing_health_from_stats(ctypes.byref(cfg), st.ctypes.data, ctypes.byref(r)) == 2
+    bad = config(W.MIXTRAL_BF16, k=0)
+    assert L.moe_routing_health_from_stats(ctypes.byref(bad), np.zeros(18, np.int32).ctypes.data, ctypes.byref(r)) == 2
 
 
 def test_stage_events_argument_checked_by_the_binding():

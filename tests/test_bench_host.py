@@ -28,16 +28,11 @@ def test_summaries_read_rocprof_csv(tmp_path):
     hdr = '"Kernel_Name","Counter_Name","Counter_Value"\n'
     (fetch / "run_counter_collection.csv").write_text(hdr + "".join(f'"{n}","FETCH_SIZE",{f / 2}\n' for n, f, _ in rows))
     (write / "run_counter_collection.csv").write_text(hdr + "".join(f'"{n}","WRITE_SIZE",{v}\n' for n, _, v in rows))
-    out = os.path.join(bench.ROOT, "profiles", "gate_up_gemm_unit_test_traffic.json")
-    try:
-        assert bench.summarize_counters(str(fetch), str(write), "unit_test") == 0
-        import json
-        dd = json.load(open(out))
-        assert dd["fetch_scale"] == 2.0 and dd["write_scale"] == 1.0
-        assert dd["hbm_bytes_per_launch"] == round(2000 * 1024 + 100 * 1024)
-    finally:
-        if os.path.exists(out):
-            os.remove(out)
+    assert bench.summarize_counters(str(fetch), str(write), "unit_test", out_dir=str(tmp_path)) == 0
+    import json
+    dd = json.load(open(tmp_path / "gate_up_gemm_unit_test_traffic.json"))
+    assert dd["fetch_scale"] == 2.0 and dd["write_scale"] == 1.0
+    assert dd["hbm_bytes_per_launch"] == round(2000 * 1024 + 100 * 1024)
     (trace / "run_kernel_trace.csv").write_text(
         '"Kernel_Name","Start_Timestamp","End_Timestamp"\n"copy16(x)",0,1000\n"router_bf16<1>(x)",0,3000\n')
     assert bench.summarize_trace(str(trace), "unit_test") == 0

@@ -309,7 +309,7 @@ def test_forward_trace_matches_standalone_calls_and_repeats(name):
     act = torch.zeros_like(tr["act"])
     y = torch.zeros_like(tr["y_route"])
     M.moe_expert_ffn(cfg, dv["h"], a["sorted"], a["offsets"], dv["w13"], dv["w2"], dv.get("w13_scale"),
-                     dv.get("w2_scale"), act, y)
+                     dv.get("w2_scale"), act, None, y)
     torch.cuda.synchronize()
     real = (a["sorted"][:P] < w.T)
     assert torch.equal(_bits(act[:P][real]), _bits(tr["act"][:P][real]))
@@ -320,7 +320,7 @@ def test_forward_trace_matches_standalone_calls_and_repeats(name):
         sact = torch.empty(w.T, w.I, dtype=act_t, device=DEV)
         shared = torch.empty(w.T, w.H, dtype=act_t, device=DEV)
         M.moe_expert_ffn(cfg, dv["h"], None, None, dv["shared_w13"], dv["shared_w2"], dv.get("shared_w13_scale"),
-                         dv.get("shared_w2_scale"), sact, shared)
+                         dv.get("shared_w2_scale"), sact, None, shared)
     out3 = torch.empty_like(out)
     M.moe_combine_expert_choice(cfg, y, b["scores"], b["slot"], shared, dv["h"], out3)
     torch.cuda.synchronize()

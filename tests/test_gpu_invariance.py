@@ -44,7 +44,8 @@ INV = {
     "toy_fp32": W.TOY_FP32.with_(T=4096),
     "mixtral_bf16": W.MIXTRAL_BF16,
     "qwen3moe_bf16": W.QWEN3MOE_BF16.with_(T=4096),
-    "deepseekv3_fp8": W.DEEPSEEKV3_FP8.with_(T=4096),
+    # the full 16384-token pool: probes are its first 16 rows, fillers come from all of it
+    "deepseekv3_fp8": W.DEEPSEEKV3_FP8,
 }
 
 
@@ -102,7 +103,7 @@ def test_route_permutation_within_and_across_blocks():
         act = torch.zeros(p_max, w.I, dtype=torch.bfloat16, device=DEV)
         y = torch.zeros(w.T * w.k, w.H, dtype=torch.bfloat16, device=DEV)
         M.moe_expert_ffn(cfg, d["h"], torch.from_numpy(sorted_ids.astype(np.int32)).to(DEV), offs, d["w13"], d["w2"],
-                         None, None, act, y)
+                         None, None, act, None, y)
         torch.cuda.synchronize()
         return act, y
 

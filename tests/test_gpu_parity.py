@@ -203,6 +203,9 @@ def _oracle_alignment(w, seed=0):
 
 @pytest.mark.parametrize("name", list(SMALL))
 def test_expert_ffn(name):
+    """Every stored surface of the routed expert path, element by element: the W13 output
+    (w13_out), the activation and the W2 output, each from the surface before it (bounds in
+    tests/harness.py); rows of dropped routes untouched; w13_out changes no other bit."""
     w = SMALL[name]
     d, dv = inputs(w)
     _say("expert_ffn", name, w)
@@ -214,19 +217,22 @@ def test_expert_ffn(name):
     offs_d = torch.from_numpy(al["expert_offsets"].astype(np.int32)).to(DEV)
     act = torch.zeros(p_max, w.I, dtype=act_t, device=DEV)
     y = torch.full((w.T * w.k, w.H), 7.0, dtype=act_t, device=DEV)
-    M.moe_expert_ffn(cfg, dv["h"], sorted_d, offs_d, dv["w13"], dv["w2"], dv["w13_scale"], dv["w2_scale"], act, y)
+    M.moe_expert_ffn(cfg, dv["h"], sorted_d, offs_d, dv["w13"], dv["w2"], dv["w13_scale"], dv["w2_scale"], act, None, y)
+    act2 = torch.zeros_like(act)
+    y2 = torch.full_like(y, 7.0)
+    w13o = torch.zeros(p_max, 2 * w.I, dtype=act_t, device=DEV)
+    M.moe_expert_ffn(cfg, dv["h"], sorted_d, offs_d, dv["w13"], dv["w2"], dv["w13_scale"], dv["w2_scale"], act2, w13o,
+                     y2)
     torch.cuda.synchronize()
-    h64 = Hn.f64(d["h"])
-    w13_of, w2_of = Hn.weights_f64(w, d, "w13"), Hn.weights_f64(w, d, "w2")
-    ref = O.expert_ffn(h64, ids.numpy(), kept, w13_of, w2_of, w.N)
-    rs = np.array(sorted(ref))
-    got = Hn.f64(y)[rs]
-    exact = np.stack([ref[r] for r in rs])
-    emul = None
-    if w.act_dtype != W.F32:
-        em = O.expert_ffn(h64, ids.numpy(), kept, w13_of, w2_of, w.N, stage_round=O.round_bf16)
-        emul = np.stack([em[r] for r in rs])
-    Hn.check_ffn_surface(w, got, exact, emul, _say)
+    bits = torch.int32 if act_t == torch.float32 else torch.int16
+    assert torch.equal(act.view(bits), act2.view(bits)) and torch.equal(y.view(bits), y2.view(bits))
+    sorted_h = al["sorted_route_ids"]
+    rows = np.nonzero(sorted_h < w.T * w.k)[0]          # padded rows that hold a kept route
+    routes = sorted_h[rows]
+    experts = ids.numpy().reshape(-1)[routes]
+    x = Hn.f64(d["h"])[routes // w.k]
+    Hn.check_expert_rows(w, x, experts, Hn.weights_f64(w, d, "w13"), Hn.weights_f64(w, d, "w2"),
+                         Hn.f64(act)[rows], Hn.f64(y)[routes], got_w13=Hn.f64(w13o)[rows], say=_say)
     # rows of dropped routes are untouched
     dropped = np.nonzero(~kept)[0]
     if dropped.size:
@@ -243,14 +249,14 @@ def test_shared_expert_identity_mode(name):
     cfg = Hn.config(w)
     act_t = torch.float32 if w.act_dtype == W.F32 else torch.bfloat16
     act = torch.zeros(w.T, w.I, dtype=act_t, device=DEV)
+    w13o = torch.zeros(w.T, 2 * w.I, dtype=act_t, device=DEV)
     y = torch.zeros(w.T, w.H, dtype=act_t, device=DEV)
     M.moe_expert_ffn(cfg, dv["h"], None, None, dv["shared_w13"], dv["shared_w2"], dv.get("shared_w13_scale"),
-                     dv.get("shared_w2_scale"), act, y)
+                     dv.get("shared_w2_scale"), act, w13o, y)
     torch.cuda.synchronize()
     s13, s2 = Hn.shared_f64(w, d, "w13"), Hn.shared_f64(w, d, "w2")
-    ref = O.swiglu_expert(Hn.f64(d["h"]), s13, s2)
-    emul = None if w.act_dtype == W.F32 else O.swiglu_expert(Hn.f64(d["h"]), s13, s2, stage_round=O.round_bf16)
-    Hn.check_ffn_surface(w, Hn.f64(y), ref, emul, _say)
+    Hn.check_expert_rows(w, Hn.f64(d["h"]), np.zeros(w.T, np.int64), lambda e: s13, lambda e: s2, Hn.f64(act),
+                         Hn.f64(y), got_w13=Hn.f64(w13o), say=_say)
 
 
 # ------------------------------------------------------------------ combine
@@ -337,11 +343,17 @@ def test_forward_end_to_end(name):
     diff = np.any(ids != res["ids"], axis=1)
     _say(f"  near-tie {near.sum()}, differing {diff.sum()}")
     assert not np.any(diff & ~near)
+    # capacity and alignment: the oracle's steps on the GPU's own ids, bit-exact, no exclusion
+    cap = O.capacity(w.T, w.k, w.N, w.cap_num, w.cap_den)
+    kept_ref = O.capacity_keep(ids.astype(np.int64), w.N, cap)
+    al = O.align(ids.astype(np.int64), kept_ref, w.N, w.B)
+    assert np.array_equal(tr["route_kept"].cpu().numpy().astype(bool), kept_ref)
+    assert np.array_equal(tr["sorted_route_ids"].cpu().numpy(), al["sorted_route_ids"])
+    assert np.array_equal(tr["expert_offsets"].cpu().numpy(), al["expert_offsets"])
+    assert np.array_equal(tr["block_expert"].cpu().numpy(), al["block_expert"])
+    assert int(tr["num_padded"].item()) == al["num_padded"]
     if not diff.any():
-        assert np.array_equal(tr["route_kept"].cpu().numpy().astype(bool), res["kept"])
-        assert np.array_equal(tr["sorted_route_ids"].cpu().numpy(), res["align"]["sorted_route_ids"])
-        assert np.array_equal(tr["expert_offsets"].cpu().numpy(), res["align"]["expert_offsets"])
-        assert np.array_equal(tr["block_expert"].cpu().numpy(), res["align"]["block_expert"])
+        assert np.array_equal(kept_ref, res["kept"])
     good = ~diff
     err = Hn.row_rel_err(Hn.f64(out)[good], res["out"][good])
     _say(f"  max out row err {err.max():.3e}")

@@ -190,7 +190,7 @@ def test_trace_export_matches_standalone_calls(name):
     kept = al["kept"].bool()
     y.index_fill_(0, torch.nonzero(kept).flatten(), 0)
     M.moe_expert_ffn(cfg, dv["h"], al["sorted"], al["offsets"], dv["w13"], dv["w2"], dv.get("w13_scale"),
-                     dv.get("w2_scale"), act, y)
+                     dv.get("w2_scale"), act, None, y)
     torch.cuda.synchronize()
     valid = al["sorted"][:npad] < w.T * w.k
     assert torch.equal(_bits(act[:npad][valid]), _bits(tr["act"][:npad][valid]))
@@ -200,7 +200,7 @@ def test_trace_export_matches_standalone_calls(name):
         sact = torch.empty(w.T, w.I, dtype=act_t, device=DEV)
         shared = torch.empty(w.T, w.H, dtype=act_t, device=DEV)
         M.moe_expert_ffn(cfg, dv["h"], None, None, dv["shared_w13"], dv["shared_w2"], dv.get("shared_w13_scale"),
-                         dv.get("shared_w2_scale"), sact, shared)
+                         dv.get("shared_w2_scale"), sact, None, shared)
     out2 = torch.empty_like(out)
     M.moe_combine(cfg, y, r["gates"], al["kept"], shared, dv["h"], out2)
     torch.cuda.synchronize()

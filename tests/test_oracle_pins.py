@@ -353,6 +353,25 @@ def test_silu_against_library():
     assert np.allclose(O.silu(x), ref, rtol=1e-15, atol=1e-300)
 
 
+def test_w13_projection_and_activation_against_library():
+    # [W1 x ; W3 x] is F.linear with the stacked weight; the activation is F.silu of the gate
+    # half times the up half; W2 applied to it is the whole expert (swiglu_expert, pinned
+    # below against an independent torch FFN).  H != I so that a transposed operand fails.
+    g = torch.Generator().manual_seed(12)
+    M, H, I = 7, 24, 40
+    x = torch.randn(M, H, generator=g, dtype=torch.float64)
+    w13 = torch.randn(2 * I, H, generator=g, dtype=torch.float64) / math.sqrt(H)
+    w2 = torch.randn(H, I, generator=g, dtype=torch.float64) / math.sqrt(I)
+    u = O.w13_projection(x.numpy(), w13.numpy())
+    assert u.shape == (M, 2 * I)
+    assert np.allclose(u[:, :I], F.linear(x, w13[:I]).numpy(), rtol=1e-14, atol=1e-14)
+    assert np.allclose(u[:, I:], F.linear(x, w13[I:]).numpy(), rtol=1e-14, atol=1e-14)
+    a = O.swiglu_activation(x.numpy(), w13.numpy())
+    want = F.silu(F.linear(x, w13[:I])) * F.linear(x, w13[I:])
+    assert a.shape == (M, I) and np.allclose(a, want.numpy(), rtol=1e-14, atol=1e-14)
+    assert np.allclose(a @ w2.numpy().T, O.swiglu_expert(x.numpy(), w13.numpy(), w2.numpy()), rtol=1e-13, atol=1e-13)
+
+
 def _torch_swiglu(x, w13, w2):
     I = w13.shape[0] // 2
     gate, up = w13[:I], w13[I:]
@@ -747,6 +766,43 @@ def test_expert_choice_align_invariants():
         for e in range(N):
             seg = al["sorted_tokens"][e * Cp:(e + 1) * Cp]
             assert seg[:C].tolist() == tokens[e].tolist() and np.all(seg[C:] == T)
+
+
+def test_golden_expert_choice_align():
+    d, _ = _read_fixture("expert_choice_align_T6_N3.txt")
+    T, N = int(d["T"]), int(d["N"])
+    for C, B in ((2, 4), (2, 8), (3, 2), (3, 3)):
+        tokens = _ints(d[f"picks_C{C}"]).reshape(N, C)
+        al = O.expert_choice_align(tokens, T, B)
+        tag = f"B{B}_C{C}"
+        assert al["sorted_tokens"].tolist() == _ints(d[tag + ".sorted"]).tolist(), tag
+        assert al["block_expert"].tolist() == _ints(d[tag + ".blocks"]).tolist(), tag
+        assert al["expert_offsets"].tolist() == _ints(d[tag + ".offsets"]).tolist(), tag
+        assert al["num_padded"] == int(d[tag + ".num_padded"]), tag
+
+
+def test_expert_choice_align_equals_token_choice_align_of_the_picks():
+    # The picks written as a token-choice route list: route r = e*C + j runs expert e and
+    # carries token tokens[e, j].  The token-choice alignment (pinned by brute force above)
+    # groups routes by expert in ascending route id, i.e. ascending token within an expert,
+    # and pads every expert's C routes to Cp rows, so its segments are the expert-choice
+    # segments with route ids in place of tokens.
+    rng = np.random.default_rng(11)
+    for T, N, C, B in ((9, 3, 4, 2), (40, 5, 13, 8), (7, 2, 7, 16), (64, 8, 16, 8), (33, 6, 1, 4), (6, 4, 0, 8)):
+        S = rng.random((T, N))
+        tokens, _, _ = O.expert_choice_select(S, C)
+        ec = O.expert_choice_align(tokens, T, B)
+        routes = np.repeat(np.arange(N), C)               # expert of route r = e*C + j
+        tc = O.align(routes.reshape(-1, 1), np.ones(N * C, bool), N, B)
+        P = ec["num_padded"]
+        assert tc["num_padded"] == P
+        assert tc["expert_offsets"].tolist() == ec["expert_offsets"].tolist()
+        assert tc["block_expert"][:P // B].tolist() == ec["block_expert"].tolist()
+        assert np.all(tc["block_expert"][P // B:] == -1)
+        r = tc["sorted_route_ids"][:P]
+        real = r < N * C
+        as_tokens = np.where(real, tokens.reshape(-1)[np.minimum(r, max(N * C - 1, 0))] if N * C else T, T)
+        assert as_tokens.tolist() == ec["sorted_tokens"].tolist()
 
 
 def _ec_layer(seed, T, H, I, N):

@@ -18,8 +18,10 @@ __all__ = [
     "MoeError", "moe_config", "moe_weights", "moe_trace", "make_config", "lib",
     "moe_abi_version", "moe_status_str", "moe_validate_config", "moe_align_sizes",
     "moe_workspace_size", "moe_route", "moe_align", "moe_align_reroute", "moe_expert_ffn", "moe_expert_gate_up",
-    "moe_expert_down", "moe_combine", "moe_forward", "moe_forward_replay", "moe_route_expert_choice",
-    "moe_align_expert_choice", "moe_combine_expert_choice", "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_IDS_IN", "MOE_ROUTE_NO_LOGITS_OUT",
+    "moe_expert_down", "moe_combine", "moe_forward", "moe_forward_replay",
+    "moe_route_expert_choice",
+    "moe_align_expert_choice", "moe_combine_expert_choice", "moe_routing_health_from_stats", "moe_routing_health",
+    "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_IDS_IN", "MOE_ROUTE_NO_LOGITS_OUT",
     "MOE_OP_ALIGN",
     "MOE_OP_FORWARD", "TRACE_EVENTS", "STATUS", "DTYPES", "ROUTING", "STATS_EXTRA", "STAT", "moe_expert_choice_sizes", "ec_capacity",
     "ec_segment",
@@ -63,7 +65,15 @@ class moe_trace(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "topk_ids", "topk_gates", "margin", "route_kept", "sorted_route_ids", "block_expert",
         "expert_offsets", "num_padded", "stats", "act", "y_route", "route_expert", "scores", "choice_tokens",
-        "choice_slot", "choice_margin")] + [("stage_events", ctypes.POINTER(ctypes.c_void_p))]
+        "choice_slot", "choice_margin")] + [("stage_events", ctypes.POINTER(ctypes.c_void_p)),
+                                             ("w13_out", ctypes.c_void_p)]
+
+
+class moe_routing_health(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "total_routes", "max_expert_load", "min_expert_load", "dropped_routes", "kept_routes", "invalid_routes",
+        "capacity", "rerouted_routes", "unpicked_tokens", "reserved")] + [
+        ("imbalance_ratio", ctypes.c_double), ("drop_fraction", ctypes.c_double)]
 
 
 TRACE_EVENTS = 7  # router, alignment, W13, W2, shared expert, combine: 7 boundaries
@@ -116,8 +126,8 @@ def lib() -> ctypes.CDLL:
             "moe_route": ([cfgp, P, P, P, P, P, P, P, U32, P], I32),
             "moe_align": ([cfgp, P, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_align_reroute": ([cfgp, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
-            "moe_expert_ffn": ([cfgp, P, P, P, P, P, P, P, P, P, P], I32),
-            "moe_expert_gate_up": ([cfgp, P, P, P, P, P, P, P], I32),
+            "moe_expert_ffn": ([cfgp, P, P, P, P, P, P, P, P, P, P, P], I32),
+            "moe_expert_gate_up": ([cfgp, P, P, P, P, P, P, P, P], I32),
             "moe_expert_down": ([cfgp, P, P, P, P, P, P, P], I32),
             "moe_combine": ([cfgp, P, P, P, P, P, P, P], I32),
             "moe_forward": ([cfgp, ctypes.POINTER(moe_weights), P, P, P, ctypes.POINTER(moe_trace), P, SZ, P], I32),
@@ -127,6 +137,7 @@ def lib() -> ctypes.CDLL:
             "moe_route_expert_choice": ([cfgp, P, P, P, P, P, P, P, P, U32, P], I32),
             "moe_align_expert_choice": ([cfgp, P, P, P, P, P, P, P, P], I32),
             "moe_combine_expert_choice": ([cfgp, P, P, P, P, P, P, P], I32),
+            "moe_routing_health_from_stats": ([cfgp, P, ctypes.POINTER(moe_routing_health)], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -219,16 +230,18 @@ def moe_align(cfg, topk_ids, route_kept, sorted_route_ids, block_expert, expert_
                                         _ptr(ws), nb, _stream(stream)))
 
 
-def moe_expert_ffn(cfg, h, sorted_route_ids, expert_offsets, w13, w2, w13_scale, w2_scale, act, y_out, stream=None):
+def moe_expert_ffn(cfg, h, sorted_route_ids, expert_offsets, w13, w2, w13_scale, w2_scale, act, w13_out, y_out,
+                   stream=None):
     _check("moe_expert_ffn", lib().moe_expert_ffn(ctypes.byref(cfg), _ptr(h), _ptr(sorted_route_ids),
                                                   _ptr(expert_offsets), _ptr(w13), _ptr(w2), _ptr(w13_scale),
-                                                  _ptr(w2_scale), _ptr(act), _ptr(y_out), _stream(stream)))
+                                                  _ptr(w2_scale), _ptr(act), _ptr(w13_out), _ptr(y_out),
+                                                  _stream(stream)))
 
 
-def moe_expert_gate_up(cfg, h, sorted_route_ids, expert_offsets, w13, w13_scale, act, stream=None):
+def moe_expert_gate_up(cfg, h, sorted_route_ids, expert_offsets, w13, w13_scale, act, w13_out=None, stream=None):
     _check("moe_expert_gate_up", lib().moe_expert_gate_up(ctypes.byref(cfg), _ptr(h), _ptr(sorted_route_ids),
                                                           _ptr(expert_offsets), _ptr(w13), _ptr(w13_scale),
-                                                          _ptr(act), _stream(stream)))
+                                                          _ptr(act), _ptr(w13_out), _stream(stream)))
 
 
 def moe_expert_down(cfg, act, sorted_route_ids, expert_offsets, w2, w2_scale, y_out, stream=None):
@@ -291,6 +304,18 @@ def moe_align_expert_choice(cfg, choice_tokens, choice_slot, sorted_route_ids, b
            lib().moe_align_expert_choice(ctypes.byref(cfg), _ptr(choice_tokens), _ptr(choice_slot),
                                          _ptr(sorted_route_ids), _ptr(block_expert), _ptr(expert_offsets),
                                          _ptr(num_padded), _ptr(stats), _stream(stream)))
+
+
+def moe_routing_health_from_stats(cfg, stats) -> dict:
+    """Routing-health numbers of one pass from a stats array (host copy, [N + STATS_EXTRA] int32)."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(stats, dtype=np.int32))
+    if a.size != cfg.N + STATS_EXTRA:
+        raise ValueError(f"stats: {cfg.N + STATS_EXTRA} int32 expected, got {a.size}")
+    r = moe_routing_health()
+    _check("moe_routing_health_from_stats",
+           lib().moe_routing_health_from_stats(ctypes.byref(cfg), a.ctypes.data, ctypes.byref(r)))
+    return {k: getattr(r, k) for k, _ in moe_routing_health._fields_ if k != "reserved"}
 
 
 def moe_combine_expert_choice(cfg, y_rows, scores, choice_slot, shared_out, residual, out, stream=None):

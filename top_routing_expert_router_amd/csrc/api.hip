@@ -130,12 +130,13 @@ moe_status check_align_args(const int32_t* ids, const uint8_t* kept, const int32
 
 moe_status check_ffn_args(const moe_config& c, const void* h, const int32_t* sorted, const int32_t* offsets,
                           const void* w13, const void* w2, const void* s13, const void* s2, const void* act,
-                          const void* y) {
+                          const void* w13_out, const void* y) {
   if (!h || !w13 || !w2 || !act || !y) return MOE_ERR_NULL_POINTER;
   if (sorted && !offsets) return MOE_ERR_NULL_POINTER;
   const bool fp8 = c.expert_dtype == MOE_FP8_E4M3;
   if (fp8 && (!s13 || !s2)) return MOE_ERR_NULL_POINTER;
-  if (!aligned(h, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(act, 16) || !aligned(y, 16))
+  if (!aligned(h, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(act, 16) || !aligned(y, 16) ||
+      (w13_out && !aligned(w13_out, 16)))
     return MOE_ERR_MISALIGNED;
   if ((sorted && !aligned(sorted, 4)) || (offsets && !aligned(offsets, 4))) return MOE_ERR_MISALIGNED;
   if (fp8 && (!aligned(s13, 2) || !aligned(s2, 2))) return MOE_ERR_MISALIGNED;
@@ -242,26 +243,27 @@ moe_status moe_align_reroute(const moe_config* cfg, const int32_t* topk_ids, con
 
 moe_status moe_expert_ffn(const moe_config* cfg, const void* h, const int32_t* sorted_route_ids,
                           const int32_t* expert_offsets, const void* w13, const void* w2, const void* w13_scale,
-                          const void* w2_scale, void* act, void* y_out, void* stream) {
+                          const void* w2_scale, void* act, void* w13_out, void* y_out, void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  st = check_ffn_args(*cfg, h, sorted_route_ids, expert_offsets, w13, w2, w13_scale, w2_scale, act, y_out);
+  st = check_ffn_args(*cfg, h, sorted_route_ids, expert_offsets, w13, w2, w13_scale, w2_scale, act, w13_out, y_out);
   if (st != MOE_OK) return st;
   return hip_status(launch_expert_ffn(*cfg, h, sorted_route_ids, expert_offsets, w13, w2, w13_scale, w2_scale, act,
-                                      y_out, sorted_route_ids == nullptr, (hipStream_t)stream));
+                                      w13_out, y_out, sorted_route_ids == nullptr, (hipStream_t)stream));
 }
 
 moe_status moe_expert_gate_up(const moe_config* cfg, const void* h, const int32_t* sorted_route_ids,
                               const int32_t* expert_offsets, const void* w13, const void* w13_scale, void* act,
-                              void* stream) {
+                              void* w13_out, void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   const bool fp8 = cfg->expert_dtype == MOE_FP8_E4M3;
   if (!h || !w13 || !act || (sorted_route_ids && !expert_offsets) || (fp8 && !w13_scale)) return MOE_ERR_NULL_POINTER;
   if (!aligned(h, 16) || !aligned(w13, 16) || !aligned(act, 16) || (sorted_route_ids && !aligned(sorted_route_ids, 4)) ||
-      (expert_offsets && !aligned(expert_offsets, 4)) || (fp8 && !aligned(w13_scale, 2)))
+      (expert_offsets && !aligned(expert_offsets, 4)) || (fp8 && !aligned(w13_scale, 2)) ||
+      (w13_out && !aligned(w13_out, 16)))
     return MOE_ERR_MISALIGNED;
-  return hip_status(launch_gate_up(*cfg, h, sorted_route_ids, expert_offsets, w13, w13_scale, act,
+  return hip_status(launch_gate_up(*cfg, h, sorted_route_ids, expert_offsets, w13, w13_scale, act, w13_out,
                                    sorted_route_ids == nullptr, (hipStream_t)stream));
 }
 
@@ -392,7 +394,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* wt, const void
   if (!aligned(rexp, 4)) return MOE_ERR_MISALIGNED;
   if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4) || !aligned(margin, 4) || !aligned(sorted, 4) ||
       !aligned(blocks, 4) || !aligned(offsets, 4) || !aligned(npad, 4) || !aligned(stats, 4) || !aligned(act, 16) ||
-      !aligned(y, 16))
+      !aligned(y, 16) || (tr.w13_out && !aligned(tr.w13_out, 16)))
     return MOE_ERR_MISALIGNED;
 
   hipStream_t s = (hipStream_t)stream;
@@ -403,14 +405,14 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* wt, const void
   // W13 then W2 of the routed experts, the shared expert, each followed by its event
   auto expert_stages = [&](hipError_t e, const void* shared_out_buf, const void** shared_out) -> hipError_t {
     if (e == hipSuccess)
-      e = launch_gate_up(c, h, sorted, offsets, wt->w13, wt->w13_scale, act, false, s, work);
+      e = launch_gate_up(c, h, sorted, offsets, wt->w13, wt->w13_scale, act, tr.w13_out, false, s, work);
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess)
       e = launch_down(c, act, sorted, offsets, wt->w2, wt->w2_scale, y, false, s, work + kGemmWorkWords);
     if (e == hipSuccess) e = mark(4);
     if (e == hipSuccess && c.n_shared) {
       e = launch_expert_ffn(c, h, nullptr, nullptr, wt->shared_w13, wt->shared_w2, wt->shared_w13_scale,
-                            wt->shared_w2_scale, base + L.sact, (void*)shared_out_buf, true, s,
+                            wt->shared_w2_scale, base + L.sact, nullptr, (void*)shared_out_buf, true, s,
                             work + 2 * kGemmWorkWords);
       *shared_out = shared_out_buf;
     }
@@ -460,6 +462,40 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* wt, const void
 moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void* h, const void* residual, void* out,
                        const moe_trace* trace, void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(cfg, wt, h, residual, nullptr, out, trace, ws, ws_bytes, stream);
+}
+
+moe_status moe_routing_health_from_stats(const moe_config* cfg, const int32_t* stats, moe_routing_health* out) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!stats || !out) return MOE_ERR_NULL_POINTER;
+  const int N = cfg->N;
+  const int32_t* x = stats + N;
+  long total = 0;
+  int32_t mx = 0, mn = 0;
+  for (int e = 0; e < N; ++e) {
+    if (stats[e] < 0) return MOE_ERR_INVALID_CONFIG;
+    total += stats[e];
+    mx = e == 0 || stats[e] > mx ? stats[e] : mx;
+    mn = e == 0 || stats[e] < mn ? stats[e] : mn;
+  }
+  if (x[MOE_STAT_KEPT] < 0 || x[MOE_STAT_DROPPED] < 0 || x[MOE_STAT_INVALID] < 0 || x[MOE_STAT_CAPACITY] < -1 ||
+      x[MOE_STAT_REROUTED] < 0 || x[MOE_STAT_UNPICKED] < 0 || total > INT32_MAX)
+    return MOE_ERR_INVALID_CONFIG;
+  moe_routing_health r{};
+  r.total_routes = (int32_t)total;
+  r.max_expert_load = mx;
+  r.min_expert_load = mn;
+  r.dropped_routes = x[MOE_STAT_DROPPED];
+  r.kept_routes = x[MOE_STAT_KEPT];
+  r.invalid_routes = x[MOE_STAT_INVALID];
+  r.capacity = x[MOE_STAT_CAPACITY];
+  r.rerouted_routes = x[MOE_STAT_REROUTED];
+  r.unpicked_tokens = x[MOE_STAT_UNPICKED];
+  // imbalance = largest load over the mean load of the N experts; drops over all routed
+  r.imbalance_ratio = total ? (double)mx * N / (double)total : 0.0;
+  r.drop_fraction = total ? (double)r.dropped_routes / (double)total : 0.0;
+  *out = r;
+  return MOE_OK;
 }
 
 moe_status moe_forward_replay(const moe_config* cfg, const moe_weights* wt, const void* h, const void* residual,

@@ -66,6 +66,7 @@ struct FfnArgs {
   int dest_is_row;        // W2: 1 = y row p (expert choice: sorted holds token ids), 0 = y row sorted[p]
   int narrow;             // W2, bf16 weights, K % 256 == 0, one to four rounds of tiles: small last
                           // m-tiles run as two narrow tiles, after all full-height tiles
+  void* w13_out;          // W13 only, nullable: [rows, 2I] gate then up projection, act dtype
 };
 
 // LDS tile layout: row-major 128-byte rows of 8 16-byte chunks, chunk index XORed
@@ -214,9 +215,13 @@ __device__ __forceinline__ void lds_barrier() {
 // ascending 16-wide steps), so the mode changes no output bit.
 // NARROW (W2, bf16 weights only): small last m-tiles run as narrow tiles; see
 // run_tile_narrow.  A kernel of its own, so the others keep their register allocation.
-template <int MODE, bool FP8, bool NARROW>
+// W13OUT (W13 only): the epilogue also stores the gate and up projections, each rounded
+// from its fp32 accumulator, to a.w13_out (the pre-activation surface); an instantiation
+// of its own, so the kernel the layer runs is unchanged.
+template <int MODE, bool FP8, bool NARROW, bool W13OUT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffn_gemm_bf16(FfnArgs a) {
   static_assert(!NARROW || (MODE == 1 && !FP8), "narrow tiles: W2 with bf16 weights only");
+  static_assert(!W13OUT || MODE == 0, "the pre-activation surface is the W13 GEMM's");
   static_assert(BN / 32 + 2 == 10, "fp8_barrier leaves BJ + 2 loads in flight");
   constexpr int TBN = BN;           // weight rows per tile
   constexpr int BJ = TBN / 32;      // weight-row DMA instructions (8 rows each) per wave and stage
@@ -711,6 +716,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
               o[q] = (__bf16)(silu_fast(gt) * up);
             }
             *reinterpret_cast<bf16x4*>(act + (long)p * a.I + col) = o;
+            if constexpr (W13OUT) {
+              bf16x4 og, ou;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                og[q] = (__bf16)acc[ns][ms][g * 4 + q];
+                ou[q] = (__bf16)acc[ns + NS / 2][ms][g * 4 + q];
+              }
+              __bf16* w13o = (__bf16*)a.w13_out + (long)p * 2 * a.I;
+              *reinterpret_cast<bf16x4*>(w13o + col) = og;
+              *reinterpret_cast<bf16x4*>(w13o + a.I + col) = ou;
+            }
           }
         }
       }
@@ -945,6 +961,11 @@ __global__ __launch_bounds__(256) void ffn_w13_f32(FfnArgs a, int rows) {
     v = fmaf(x[kk], w3[kk], v);
   }
   ((float*)a.out)[(long)p * a.I + col] = silu_f32(u) * v;
+  if (a.w13_out != nullptr) {  // the pre-activation surface
+    float* w13o = (float*)a.w13_out + (long)p * 2 * a.I;
+    w13o[col] = u;
+    w13o[a.I + col] = v;
+  }
 }
 
 __global__ __launch_bounds__(256) void ffn_w2_f32(FfnArgs a, int rows) {
@@ -975,7 +996,7 @@ int mtile_bound(const moe_config& c, bool identity) {
 
 // Persistent launch: one workgroup per CU (the kernel's LDS allows no more), at most
 // as many as there can be tiles, a multiple of the 8 XCDs.
-template <int MODE, bool FP8, bool NARROW = false>
+template <int MODE, bool FP8, bool NARROW = false, bool W13OUT = false>
 hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
   int dev = 0, cus = 0;
   hipError_t err = hipGetDevice(&dev);
@@ -984,7 +1005,7 @@ hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
   const int G = a.mtiles * a.ntiles;
   if (G == 0) return hipSuccess;  // no rows (an expert-choice capacity of 0)
   const int grid = ceil_div(min(G, max(cus, 8)), 8) * 8;
-  ffn_gemm_bf16<MODE, FP8, NARROW><<<grid, kThreads, 0, s>>>(a);
+  ffn_gemm_bf16<MODE, FP8, NARROW, W13OUT><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -1016,14 +1037,15 @@ FfnArgs base_args(const moe_config& c, const int32_t* sorted_ids, const int32_t*
 }  // namespace
 
 hipError_t launch_gate_up(const moe_config& c, const void* h, const int32_t* sorted_ids, const int32_t* offsets,
-                          const void* w13, const void* w13_scale, void* act, bool identity, hipStream_t s,
-                          int32_t* work) {
+                          const void* w13, const void* w13_scale, void* act, void* w13_out, bool identity,
+                          hipStream_t s, int32_t* work) {
   FfnArgs a = base_args(c, sorted_ids, offsets, identity);
   a.work = work;
   a.x = h;
   a.w = w13;
   a.wscale = (const __bf16*)w13_scale;
   a.out = act;
+  a.w13_out = w13_out;
   if (c.expert_dtype == MOE_F32) {
     const long n = (long)a.rows * c.I;
     if (n == 0) return hipSuccess;
@@ -1031,6 +1053,9 @@ hipError_t launch_gate_up(const moe_config& c, const void* h, const int32_t* sor
     return hipGetLastError();
   }
   a.ntiles = c.I / (BN / 2);
+  if (w13_out != nullptr)
+    return c.expert_dtype == MOE_FP8_E4M3 ? launch_gemm<0, true, false, true>(a, s)
+                                          : launch_gemm<0, false, false, true>(a, s);
   return c.expert_dtype == MOE_FP8_E4M3 ? launch_gemm<0, true>(a, s) : launch_gemm<0, false>(a, s);
 }
 
@@ -1070,8 +1095,8 @@ hipError_t launch_down(const moe_config& c, const void* act, const int32_t* sort
 
 hipError_t launch_expert_ffn(const moe_config& c, const void* h, const int32_t* sorted_ids, const int32_t* offsets,
                              const void* w13, const void* w2, const void* w13_scale, const void* w2_scale, void* act,
-                             void* y, bool identity, hipStream_t s, int32_t* work) {
-  hipError_t err = launch_gate_up(c, h, sorted_ids, offsets, w13, w13_scale, act, identity, s, work);
+                             void* w13_out, void* y, bool identity, hipStream_t s, int32_t* work) {
+  hipError_t err = launch_gate_up(c, h, sorted_ids, offsets, w13, w13_scale, act, w13_out, identity, s, work);
   if (err != hipSuccess) return err;
   return launch_down(c, act, sorted_ids, offsets, w2, w2_scale, y, identity, s,
                      work ? work + kGemmWorkWords : nullptr);

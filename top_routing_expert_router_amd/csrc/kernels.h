@@ -69,17 +69,18 @@ hipError_t launch_ec_align(const moe_config& c, const int32_t* tokens, const int
 // persistent workgroups claim tiles from per-XCD counters, without them each takes a
 // fixed share.  The schedule changes no output bit.
 constexpr int kGemmWorkWords = 8;
+// w13_out (nullable): also store the gate and up projections, [rows, 2I] act dtype
 hipError_t launch_gate_up(const moe_config& c, const void* h, const int32_t* sorted_ids, const int32_t* offsets,
-                          const void* w13, const void* w13_scale, void* act, bool identity, hipStream_t s,
-                          int32_t* work = nullptr);
+                          const void* w13, const void* w13_scale, void* act, void* w13_out, bool identity,
+                          hipStream_t s, int32_t* work = nullptr);
 hipError_t launch_down(const moe_config& c, const void* act, const int32_t* sorted_ids, const int32_t* offsets,
                        const void* w2, const void* w2_scale, void* y, bool identity, hipStream_t s,
                        int32_t* work = nullptr);
 // work: 2 * kGemmWorkWords ints (W13, then W2), or null
 hipError_t launch_expert_ffn(const moe_config& c, const void* h, const int32_t* sorted_ids,
                              const int32_t* offsets, const void* w13, const void* w2, const void* w13_scale,
-                             const void* w2_scale, void* act, void* y, bool identity, hipStream_t s,
-                             int32_t* work = nullptr);
+                             const void* w2_scale, void* act, void* w13_out, void* y, bool identity,
+                             hipStream_t s, int32_t* work = nullptr);
 
 // ---- combine (combine.hip)
 hipError_t launch_combine(const moe_config& c, const void* y_route, const float* gates, const uint8_t* kept,
