@@ -16,13 +16,14 @@
 extern "C" {
 #endif
 
-/* dst[0:bytes) = src[0:bytes): 16 bytes per lane, grid-stride.  bytes % 16 == 0,
- * both pointers 16-byte aligned.  Moves 2 * bytes through HBM when the buffers
- * exceed the caches; also the known-size reference for traffic counters. */
+/* dst[0:bytes) = src[0:bytes): a streaming copy (8 non-temporal 16-byte loads in flight
+ * per lane, then their stores; up to 8 workgroups of 256 lanes per CU).  bytes % 16 == 0,
+ * both pointers 16-byte aligned.  Moves 2 * bytes through HBM when the buffers exceed the
+ * caches; also the known-size reference for traffic counters. */
 int32_t moe_ceiling_copy(const void* src, void* dst, size_t bytes, void* stream);
 
-/* Reads src[0:bytes) (16 bytes per lane) and writes one float per workgroup to
- * sink[0:4096) only for a sentinel value, so the reads cannot be elided.
+/* Reads src[0:bytes) as a stream (the copy's access pattern, no stores) and writes one float
+ * per workgroup to sink[0:4096) only for a sentinel value, so the reads cannot be elided.
  * bytes % 16 == 0, src 16-byte aligned. */
 int32_t moe_ceiling_read(const void* src, size_t bytes, float* sink, void* stream);
 

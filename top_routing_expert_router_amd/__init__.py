@@ -147,10 +147,15 @@ def lib() -> ctypes.CDLL:
 
 
 def _ptr(x) -> Optional[int]:
+    """Device address of a tensor argument (None for NULL; an int is taken as an address).
+    Every tensor the C ABI reads or writes lives in device memory: a host tensor is refused
+    here, before any call (a kernel given a host address faults the GPU)."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not getattr(x, "is_cuda", False):
+        raise ValueError(f"a device tensor is required, got one on {getattr(x, 'device', type(x))}")
     return x.data_ptr()
 
 

@@ -9,9 +9,12 @@
 // in fp32 with fmaf for the weighted terms, in exactly this order, one rounding.
 // The accumulator starts at -0.0 (the IEEE additive identity), so a token with no
 // kept route and no shared expert outputs its residual bit for bit, -0 included.
-// Each thread owns 8 consecutive columns of one token (16-byte bf16 accesses).
-// A route whose kept flag is 0 contributes nothing: its y row (allocated, never
-// written) is loaded but not added.
+// Each thread owns 8 consecutive columns of one token in each of two 2048-column halves of
+// a 4096-column slice (16-byte bf16 accesses, each wave instruction 1 KB contiguous).
+// A route whose kept flag is 0 contributes nothing.  Without a capacity limit every valid
+// route is kept, and the y rows of all routes are loaded together with the flags (a row
+// whose flag is 0 -- an invalid replayed id -- is loaded but not added); with one, the
+// flags are read first and only kept routes' rows are loaded.
 #include <type_traits>
 
 #include "common.h"
@@ -33,57 +36,122 @@ struct Vec8<float> {
 
 constexpr int kColsPerThread = 8;
 constexpr int kThreads = 256;
-constexpr int kColsPerBlock = kColsPerThread * kThreads;
+constexpr int kColsPerBlock = kColsPerThread * kThreads;  // expert-choice combine: 2048 columns
+constexpr int kChunks = 2;                                 // token-choice combine: 2 x 2048 columns
+constexpr int kColsPerSlice = kColsPerBlock * kChunks;
 
-// One workgroup per (token, 2048-column slice): the token's gates and kept flags
-// are uniform (one per lane, read back with readlane); every y row is loaded
-// (all rows are allocated) and the kept flag selects whether it enters the sum, so
-// all loads of a thread are in flight together.
-template <typename T, int K>
+// One workgroup per (token, 4096-column slice).  The token's k gates and kept flags are
+// uniform (one per lane, read back with readlane).  Rows are read with buffer loads over
+// the token's own rows: a column past H, or a row left out, is an offset past the
+// resource, which reads zeros and no memory -- so no load sits under a branch (hipcc
+// waits for every load in flight at the joins of such branches).  DROPS = false: every y
+// row is loaded together with the flags, and a flag selects whether its row enters the
+// sum.  DROPS = true (a capacity limit, where many routes may be dropped): one wait for
+// the flags, then only the kept routes' rows are read.
+template <typename T, int K, bool DROPS>
 __global__ __launch_bounds__(kThreads) void combine_rows(const T* __restrict__ y, const float* __restrict__ gates,
                                                           const uint8_t* __restrict__ kept, const T* __restrict__ shared,
                                                           const T* __restrict__ residual, T* __restrict__ out, int H,
                                                           int slices) {
   typedef typename Vec8<T>::type V;
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int NP = sizeof(V) / 16;  // 16-byte pieces per 8 columns
   const int t = blockIdx.x / slices;
-  const long col = (long)(blockIdx.x % slices) * kColsPerBlock + threadIdx.x * kColsPerThread;
-  if (col >= H) return;
-  // the token's k gates and kept flags, lane j holding route j, loaded before the rows
-  // (a flag loaded where it is used waits for every row load issued before it)
+  const int slice = blockIdx.x % slices;
+  int col[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) col[c] = slice * kColsPerSlice + c * kColsPerBlock + threadIdx.x * kColsPerThread;
+  // the token's k gates and kept flags, lane j holding route j: with drops read first (they
+  // decide which rows are read), else after the rows are requested (vmcnt counts in order,
+  // so waiting for a flag loaded first would hold back the row loads issued behind it)
   const int jl = (int)(threadIdx.x & 63) < K ? (int)(threadIdx.x & 63) : 0;
-  const float g_lane = gates[(long)t * K + jl];
-  const int on_lane = kept[(long)t * K + jl];
-  V yv[K];
+  float g_lane = 0.f;
+  int on_lane = 0;
+  if constexpr (DROPS) {
+    g_lane = gates[(long)t * K + jl];
+    on_lane = kept[(long)t * K + jl];
+  }
+  const uint32_t row_bytes = (uint32_t)H * sizeof(T);
+  const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc((void*)(y + (long)t * K * H), (short)0,
+                                                                      (int)(K * row_bytes), kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(shared ? shared + (long)t * H : y),
+                                                                      (short)0, shared ? (int)row_bytes : 0,
+                                                                      kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void*)(residual ? residual + (long)t * H : y),
+                                                                      (short)0, residual ? (int)row_bytes : 0,
+                                                                      kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)(out + (long)t * H), (short)0,
+                                                                      (int)row_bytes, kRawBufferFlags);
+  const bool has_shared = shared != nullptr, has_residual = residual != nullptr;
+  bool on[K];
+  if constexpr (DROPS) {
 #pragma unroll
-  for (int j = 0; j < K; ++j) yv[j] = *reinterpret_cast<const V*>(y + ((long)t * K + j) * H + col);
-  V sv, rv;
-  if (shared) sv = *reinterpret_cast<const V*>(shared + (long)t * H + col);
-  if (residual) rv = *reinterpret_cast<const V*>(residual + (long)t * H + col);
-  float acc[8];
+    for (int j = 0; j < K; ++j) on[j] = __builtin_amdgcn_readlane(on_lane, j) != 0;
+  }
+  auto load8 = [&](__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    V v;
+    u32x4 p[NP];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) acc[q] = -0.0f;
+    for (int i = 0; i < NP; ++i)
+      p[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u * i, 0, 0));
+    __builtin_memcpy(&v, p, sizeof(V));
+    return v;
+  };
+  V yv[K][kChunks], sv[kChunks], rv[kChunks];
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const bool on = __builtin_amdgcn_readlane(on_lane, j) != 0;
-    const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g_lane), j));
+  for (int c = 0; c < kChunks; ++c) {
+    const uint32_t coff = col[c] < H ? (uint32_t)col[c] * sizeof(T) : kBufferOutOfRange;
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      yv[j][c] = load8(ry, (DROPS && !on[j]) || col[c] >= H ? kBufferOutOfRange : j * row_bytes + coff);
+    sv[c] = load8(rs, coff);
+    rv[c] = load8(rr, coff);
+  }
+  if constexpr (!DROPS) {
+    __builtin_amdgcn_sched_barrier(0);  // the row loads stay ahead of the flag loads
+    g_lane = gates[(long)t * K + jl];
+    on_lane = kept[(long)t * K + jl];
+#pragma unroll
+    for (int j = 0; j < K; ++j) on[j] = __builtin_amdgcn_readlane(on_lane, j) != 0;
+  }
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = -0.0f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g_lane), j));
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float f = fmaf(g, (float)yv[j][c][q], acc[q]);
+        acc[q] = on[j] ? f : acc[q];
+      }
+    }
+    // absent terms add nothing (selects, not branches, so no load sinks under a branch;
+    // adding a zero would turn an accumulator of -0 into +0)
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const float f = fmaf(g, (float)yv[j][q], acc[q]);
-      acc[q] = on ? f : acc[q];
+      const float f = acc[q] + (float)sv[c][q];
+      acc[q] = has_shared ? f : acc[q];
     }
-  }
-  if (shared) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] += (float)sv[q];
-  }
-  if (residual) {
+    for (int q = 0; q < 8; ++q) {
+      const float f = acc[q] + (float)rv[c][q];
+      acc[q] = has_residual ? f : acc[q];
+    }
+    V o;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] += (float)rv[q];
-  }
-  V o;
+    for (int q = 0; q < 8; ++q) o[q] = cvt_act<T>(acc[q]);
+    // a buffer store past the row's end writes nothing: no branch here either
+    const uint32_t ooff = col[c] < H ? (uint32_t)col[c] * sizeof(T) : kBufferOutOfRange;
+    u32x4 p[NP];
+    __builtin_memcpy(p, &o, sizeof(V));
 #pragma unroll
-  for (int q = 0; q < 8; ++q) o[q] = cvt_act<T>(acc[q]);
-  *reinterpret_cast<V*>(out + (long)t * H + col) = o;
+    for (int i = 0; i < NP; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, p[i]), ro,
+                                             ooff + 16u * i, 0, 0);
+  }
 }
 
 // Expert choice: out[t] = round(((sum over the experts e that picked t, ascending, of
@@ -162,17 +230,26 @@ __global__ __launch_bounds__(kThreads) void combine_ec_rows(const T* __restrict_
 
 hipError_t launch_combine(const moe_config& c, const void* y_route, const float* gates, const uint8_t* kept,
                           const void* shared_out, const void* residual, void* out, hipStream_t s) {
-  const int slices = ceil_div(c.H, kColsPerBlock);
+  const int slices = ceil_div(c.H, kColsPerSlice);
   const dim3 grid((unsigned)c.T * slices);
+  const bool drops = !(c.cap_num == 0 && c.cap_den == 0);
   auto go = [&](auto kt) {
     constexpr int K = decltype(kt)::value;
-    if (c.act_dtype == MOE_F32)
-      combine_rows<float, K><<<grid, kThreads, 0, s>>>((const float*)y_route, gates, kept, (const float*)shared_out,
-                                                       (const float*)residual, (float*)out, c.H, slices);
+    auto run = [&](auto dt) {
+      constexpr bool D = decltype(dt)::value;
+      if (c.act_dtype == MOE_F32)
+        combine_rows<float, K, D><<<grid, kThreads, 0, s>>>((const float*)y_route, gates, kept,
+                                                            (const float*)shared_out, (const float*)residual,
+                                                            (float*)out, c.H, slices);
+      else
+        combine_rows<__bf16, K, D><<<grid, kThreads, 0, s>>>((const __bf16*)y_route, gates, kept,
+                                                             (const __bf16*)shared_out, (const __bf16*)residual,
+                                                             (__bf16*)out, c.H, slices);
+    };
+    if (drops)
+      run(std::true_type{});
     else
-      combine_rows<__bf16, K><<<grid, kThreads, 0, s>>>((const __bf16*)y_route, gates, kept,
-                                                        (const __bf16*)shared_out, (const __bf16*)residual,
-                                                        (__bf16*)out, c.H, slices);
+      run(std::false_type{});
   };
   switch (c.k) {  // 1 <= k <= 8 (checked with the config)
     case 1: go(std::integral_constant<int, 1>{}); break;

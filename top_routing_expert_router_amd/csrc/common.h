@@ -155,6 +155,14 @@ __device__ __forceinline__ int wave_incl_scan_i32(int v) {
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Word 3 of a buffer resource for raw (untyped, stride 0) buffer loads on gfx9-family
+// parts.  A load whose byte offset is at or beyond the resource's size returns zeros
+// and touches no memory; a store there writes nothing.  kBufferOutOfRange is such an
+// offset for every resource under 2 GiB, with room to add a few 16-byte pieces to it
+// without wrapping around 2^32.
+constexpr int kRawBufferFlags = 0x00020000;
+constexpr uint32_t kBufferOutOfRange = 0x80000000u;
+
 // Position of this thread's key (0..N-1; -1 = none) among the keys of this chunk of NT
 // entries (one per thread of an NT-thread workgroup, in thread order) that come before
 // it, plus base[key]; afterwards base[key] has grown by the chunk's count of that key.
