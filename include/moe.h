@@ -376,6 +376,26 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* weights, const 
                        size_t ws_bytes, void* stream);
 
 /*
+ * moe_forward without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * composition, kernels and results bit for bit, with every intermediate in a static scratch
+ * array of MOE_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until the
+ * process ends.  The caller still passes inputs, outputs and (nullable) trace buffers.
+ *   Limit: configs whose forward workspace (moe_workspace_size, MOE_OP_FORWARD) exceeds
+ *   MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE_TOO_SMALL and enqueue nothing (it
+ *   holds, e.g., a Mixtral-shaped layer (H 4096, 8 experts, top-2, I 14336, B 64) up to 1622
+ *   tokens, a Qwen3-MoE-shaped one up to 2870, a DeepSeek-V3-shaped one up to 407).
+ *   The scratch is that of the current device (hipGetDevice); `stream` must belong to it.
+ *   Calls on one GPU share its scratch: calls that overlap on the GPU (on different streams,
+ *   or from different host threads without ordering) race.  Calls in one stream order are safe.
+ *   The first call on a device looks up the scratch's device address; no call allocates.
+ *   A failed lookup returns MOE_ERR_HIP.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (128u << 20)
+moe_status moe_forward_noalloc(const moe_config* cfg, const moe_weights* weights, const void* h,
+                               const void* residual, void* out, const moe_trace* trace, void* stream);
+
+/*
  * The whole layer with router replay ("Mixture-of-experts routing & LLM
  * repeatability", router replay paragraph): as moe_forward, but the experts are the
  * recorded ids instead of this run's top-k (moe_route with MOE_ROUTE_IDS_IN);

@@ -18,8 +18,8 @@ __all__ = [
     "MoeError", "moe_config", "moe_weights", "moe_trace", "make_config", "lib",
     "moe_abi_version", "moe_status_str", "moe_validate_config", "moe_align_sizes",
     "moe_workspace_size", "moe_route", "moe_align", "moe_align_reroute", "moe_expert_ffn", "moe_expert_gate_up",
-    "moe_expert_down", "moe_combine", "moe_forward", "moe_forward_replay",
-    "moe_route_expert_choice",
+    "moe_expert_down", "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_forward_replay",
+    "moe_route_expert_choice", "NOALLOC_SCRATCH_BYTES",
     "moe_align_expert_choice", "moe_combine_expert_choice", "moe_routing_health_from_stats", "moe_routing_health",
     "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_IDS_IN", "MOE_ROUTE_NO_LOGITS_OUT",
     "MOE_OP_ALIGN",
@@ -37,6 +37,7 @@ ROUTING = {"token_choice": 0, "expert_choice": 1}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL_POINTER", 2: "MOE_ERR_INVALID_CONFIG", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_MISALIGNED", 5: "MOE_ERR_WORKSPACE_TOO_SMALL", 6: "MOE_ERR_HIP"}
 STATS_EXTRA = 10
+NOALLOC_SCRATCH_BYTES = 128 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 STAT = {"kept": 0, "dropped": 1, "invalid": 2, "capacity": 3, "max_load": 4, "min_load": 5, "num_padded": 6,
         "rerouted": 7, "unpicked": 8, "max_picks": 9}
 
@@ -133,6 +134,7 @@ def lib() -> ctypes.CDLL:
             "moe_forward": ([cfgp, ctypes.POINTER(moe_weights), P, P, P, ctypes.POINTER(moe_trace), P, SZ, P], I32),
             "moe_forward_replay": ([cfgp, ctypes.POINTER(moe_weights), P, P, P, P, ctypes.POINTER(moe_trace), P, SZ,
                                     P], I32),
+            "moe_forward_noalloc": ([cfgp, ctypes.POINTER(moe_weights), P, P, P, ctypes.POINTER(moe_trace), P], I32),
             "moe_expert_choice_sizes": ([cfgp, ctypes.POINTER(I32), ctypes.POINTER(I32)], I32),
             "moe_route_expert_choice": ([cfgp, P, P, P, P, P, P, P, P, U32, P], I32),
             "moe_align_expert_choice": ([cfgp, P, P, P, P, P, P, P, P], I32),
@@ -269,6 +271,15 @@ def moe_forward(cfg, weights: dict, h, residual, out, trace: Optional[dict], ws,
     _check("moe_forward", lib().moe_forward(ctypes.byref(cfg), ctypes.byref(w), _ptr(h), _ptr(residual), _ptr(out),
                                             ctypes.byref(tr) if tr is not None else None, _ptr(ws), nb,
                                             _stream(stream)))
+
+
+def moe_forward_noalloc(cfg, weights: dict, h, residual, out, trace: Optional[dict] = None, stream=None):
+    """moe_forward with its intermediates in the library's static per-GPU scratch (no workspace)."""
+    w = moe_weights(**{k: _ptr(weights.get(k)) for k, _ in moe_weights._fields_})
+    tr, _events = _trace_struct(trace)
+    _check("moe_forward_noalloc",
+           lib().moe_forward_noalloc(ctypes.byref(cfg), ctypes.byref(w), _ptr(h), _ptr(residual), _ptr(out),
+                                     ctypes.byref(tr) if tr is not None else None, _stream(stream)))
 
 
 def moe_forward_replay(cfg, weights: dict, h, residual, replay_ids, out, trace: Optional[dict], ws,

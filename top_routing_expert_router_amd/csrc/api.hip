@@ -3,10 +3,18 @@
 // Validation runs before any HIP call, so every error path is host-only.
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
 using namespace moe;
+
+// Scratch of moe_forward_noalloc: every intermediate of one forward pass, for callers that
+// cannot allocate.  One copy per GPU, held until the process ends.  Host code never uses this
+// name as an address (on the host it is only a stand-in for the symbol): the device address
+// comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -496,6 +504,40 @@ moe_status moe_routing_health_from_stats(const moe_config* cfg, const int32_t* s
   r.drop_fraction = total ? (double)r.dropped_routes / (double)total : 0.0;
   *out = r;
   return MOE_OK;
+}
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxScratchDevices];  // device address of `scratch` on each device, once looked up
+
+// The device address of this device's `scratch` (looked up with the device current), or null.
+void* scratch_on(int dev) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+
+}  // namespace
+
+moe_status moe_forward_noalloc(const moe_config* cfg, const moe_weights* wt, const void* h, const void* residual,
+                               void* out, const moe_trace* trace, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (forward_layout(*cfg).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  void* ws = scratch_on(dev);
+  if (ws == nullptr) return MOE_ERR_HIP;
+  // the tile counters the GEMMs claim from are cleared by the alignment kernel inside the
+  // forward; nothing else in the scratch is read before it is written
+  return forward_impl(cfg, wt, h, residual, nullptr, out, trace, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 moe_status moe_forward_replay(const moe_config* cfg, const moe_weights* wt, const void* h, const void* residual,
