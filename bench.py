@@ -235,14 +235,18 @@ def main() -> int:
     torch.cuda.synchronize()
     kept_routes = w.N * C if ec else int(tr["route_kept"].sum().item())
     aws = torch.empty(M.moe_workspace_size(cfg, M.MOE_OP_ALIGN), dtype=torch.uint8, device=dev)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)  # larger than L2 + MALL
+    # cold runs: a read of 1 GiB (more than L2 and MALL together) before each timed launch
+    # evicts what the caches hold without leaving dirty lines for the timed kernel to write back
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    flush_sink = torch.zeros(4096, dtype=torch.float32, device=dev)
+    read_1gib = ceiling_reader(flush, flush_sink, stream)
 
     def timed(fn, reps, do_flush):
         es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         fn()
         for a, b in es:
             if do_flush:
-                flush.fill_(1)
+                read_1gib()
             a.record(stream)
             fn()
             b.record(stream)
@@ -327,12 +331,15 @@ def main() -> int:
                  "event_overhead_pct": round(100.0 * (fwd_events_ms - ms) / ms, 2)}
     log(f"[bench] stage sum {reconcile['stages_sum_us']:.1f} us, instrumented forward "
         f"{reconcile['instrumented_forward_us']:.1f} us, plain forward {reconcile['plain_forward_us']:.1f} us")
-    clocks = None
+    clocks = gemm_clock_report(cfg, wts, d, out, ws, stream, {"gate_up_gemm": ms_gate_up, "down_gemm": ms_down})
+    log("[bench] shader clock inside the GEMMs (core cycles / wall clock per workgroup): "
+        + ", ".join(f"{k} {v}" for k, v in clocks.items()))
     if not args.no_stages:
-        clocks = gfx_clock_report(step, tr, cfg, d, wts, act_t, stream)
-        if clocks:
-            log("[bench] shader clock (MHz, SMU samples while each runs back to back): "
-                + ", ".join(f"{k} {v}" for k, v in clocks.items()))
+        smu = gfx_clock_report(step, tr, cfg, d, wts, act_t, stream)
+        if smu:
+            clocks["smu_gfxclk_MHz"] = {k: (v or {}).get("median") for k, v in smu.items()}
+            log("[bench] SMU-reported gfx clock level (MHz, sampled while each runs back to back): "
+                + ", ".join(f"{k} {v}" for k, v in smu.items()))
 
     achieved = stages["gate_up_gemm"]["TFLOP/s"]
     roofline = {"kernel": "ffn_gemm_bf16<W13+SwiGLU>", "bound": "mfma", "achieved": round(achieved, 2),
@@ -474,6 +481,62 @@ class GfxClockSampler:
             return None
         return {"median": round(statistics.median(vals)), "min": round(min(vals)), "max": round(max(vals)),
                 "samples": len(vals)}
+
+
+def ceiling_reader(buf, sink, stream):
+    """A callable that enqueues the streaming read of buf (libmoe_ceiling.so) on stream."""
+    import ctypes
+
+    from top_routing_expert_router_amd.build import CEILING_LIB_PATH
+    L = ctypes.CDLL(CEILING_LIB_PATH)
+    L.moe_ceiling_read.argtypes, L.moe_ceiling_read.restype = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                                              ctypes.c_void_p], ctypes.c_int32
+    n, p, q, sp = buf.numel() * buf.element_size(), buf.data_ptr(), sink.data_ptr(), stream.cuda_stream
+
+    def go():
+        assert L.moe_ceiling_read(p, n, q, sp) == 0
+    return go
+
+
+def clock_rates():
+    """(wall-clock counter rate, peak shader clock) of the current device, in kHz."""
+    import ctypes
+
+    from top_routing_expert_router_amd.build import CEILING_LIB_PATH
+    L = ctypes.CDLL(CEILING_LIB_PATH)
+    wall, peak = ctypes.c_int32(), ctypes.c_int32()
+    assert L.moe_ceiling_clock_rates(ctypes.byref(wall), ctypes.byref(peak)) == 0
+    return wall.value, peak.value
+
+
+def gemm_clock_report(cfg, wts, d, out, ws, stream, stage_ms):
+    """The shader clock the routed expert GEMMs ran at inside one forward: each persistent
+    workgroup's core-cycle and wall-clock counters at its start and end (moe_trace.gemm_clocks);
+    clock = sum of cycles / sum of wall time over the workgroups.  The span from the first
+    start to the last end, in wall-clock time, is given beside the stage's event time."""
+    import numpy as np
+    import torch
+
+    import top_routing_expert_router_amd as M
+    wall_khz, peak_khz = clock_rates()
+    clk = torch.zeros(2 * M.CLOCK_SLOTS * 4, dtype=torch.int64, device="cuda")
+    M.moe_forward(cfg, wts, d["h"], d["residual"], out, {"gemm_clocks": clk}, ws, stream=stream)
+    torch.cuda.synchronize()
+    c = clk.view(2, M.CLOCK_SLOTS, 4).cpu().numpy().astype(np.float64)
+    res = {"peak_MHz": peak_khz / 1e3, "wall_clock_MHz": wall_khz / 1e3}
+    for i, name in enumerate(("gate_up_gemm", "down_gemm")):
+        x = c[i]
+        used = x[:, 3] > x[:, 1]
+        if not used.any():
+            continue
+        cyc, wall = x[used, 2] - x[used, 0], x[used, 3] - x[used, 1]
+        per = cyc / wall * wall_khz / 1e3
+        res[name] = {"MHz": round(float(cyc.sum() / wall.sum() * wall_khz / 1e3), 1),
+                     "per_workgroup_MHz_min": round(float(per.min()), 1),
+                     "per_workgroup_MHz_max": round(float(per.max()), 1), "workgroups": int(used.sum()),
+                     "span_us": round(float((x[used, 3].max() - x[used, 1].min()) / wall_khz * 1e3), 1),
+                     "event_us": round(stage_ms[name] * 1e3, 1)}
+    return res
 
 
 def gfx_clock_report(step, tr, cfg, d, wts, act_t, stream):

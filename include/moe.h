@@ -205,7 +205,17 @@ typedef struct moe_trace {
   /* Nullable: [P_max, 2I] act dtype, the routed W13 output before the activation (columns
    * 0..I-1 the gate projection, I..2I-1 the up projection; see moe_expert_gate_up). */
   void* w13_out;
+  /* Nullable, 8-byte aligned: [2][MOE_CLOCK_SLOTS][4] uint64, clock stamps of the routed W13
+   * ([0]) and W2 ([1]) GEMM launches.  Persistent workgroup b writes, at its start, the
+   * core-cycle counter (HIP clock64) and the constant-rate wall-clock counter (HIP
+   * wall_clock64, rate hipDeviceAttributeWallClockRate) into [.][b][0..1], and both again at
+   * its end into [.][b][2..3]: (t_end - t_start) / (r_end - r_start) times the wall-clock
+   * rate is the clock that workgroup ran at.  Slots of workgroups a launch does not have are
+   * not written. */
+  uint64_t* gemm_clocks;
 } moe_trace;
+
+#define MOE_CLOCK_SLOTS 1024
 
 #define MOE_TRACE_EVENTS 7
 

@@ -33,6 +33,11 @@ int32_t moe_ceiling_read(const void* src, size_t bytes, float* sink, void* strea
  * iters x 8 x 32768. */
 int32_t moe_ceiling_mfma_bf16(int32_t iters, int32_t waves_per_simd, float* sink, void* stream);
 
+/* Host only: the current device's wall-clock counter rate (the rate of HIP wall_clock64)
+ * and its peak shader clock, both in kHz (hipDeviceGetAttribute).  Returns 1 for a NULL
+ * pointer, 6 if the query fails. */
+int32_t moe_ceiling_clock_rates(int32_t* wall_khz, int32_t* peak_khz);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,7 @@ def test_ceiling_library_exports_and_rejects_bad_arguments():
     from top_routing_expert_router_amd.build import CEILING_LIB_PATH
     L = ctypes.CDLL(CEILING_LIB_PATH)
     names = _declared_functions("moe_ceiling.h")
-    assert names == ["moe_ceiling_copy", "moe_ceiling_mfma_bf16", "moe_ceiling_read"]
+    assert names == ["moe_ceiling_clock_rates", "moe_ceiling_copy", "moe_ceiling_mfma_bf16", "moe_ceiling_read"]
     for n in names:
         assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
     P, SZ, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
@@ -50,6 +50,8 @@ def test_ceiling_library_exports_and_rejects_bad_arguments():
     assert L.moe_ceiling_read(4096, 0, 4096, None) == 1
     assert L.moe_ceiling_mfma_bf16(10, 3, 4096, None) == 1
     assert L.moe_ceiling_mfma_bf16(0, 1, 4096, None) == 1
+    L.moe_ceiling_clock_rates.argtypes, L.moe_ceiling_clock_rates.restype = [P, P], I32
+    assert L.moe_ceiling_clock_rates(None, None) == 1
 
 
 def test_abi_version_and_status_strings():

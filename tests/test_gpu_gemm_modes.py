@@ -112,3 +112,39 @@ def test_forward_stage_events(name):
         assert torch.equal(out.view(torch.int16 if out.element_size() == 2 else torch.int32),
                            out0.view(torch.int16 if out0.element_size() == 2 else torch.int32))
     _say("  stage ms", [round(t, 4) for t in stages])
+
+
+@pytest.mark.parametrize("name", ["mixtral_bf16", "deepseekv3_fp8"])
+def test_forward_gemm_clock_stamps(name):
+    """Trace clock stamps of the routed W13 and W2 launches: every persistent workgroup of a
+    launch writes its start and end counters (end after start, within the real span of the
+    stage), the slots beyond the grid stay untouched, and stamping changes no output bit."""
+    import workloads as W
+    import harness as Hn
+    w = {"mixtral_bf16": W.MIXTRAL_BF16.with_(T=1024),
+         "deepseekv3_fp8": W.DEEPSEEKV3_FP8.with_(T=200, N=24, H=1024, I=512)}[name]
+    _say("gemm clock stamps", name)
+    d = W.layer_inputs(w)
+    dv = Hn.to_dev(d)
+    out0, _ = Hn.run_forward(w, dv, trace=False)
+    cfg = Hn.config(w)
+    ws = torch.empty(M.moe_workspace_size(cfg, M.MOE_OP_FORWARD), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(out0)
+    wts = {k: dv.get(k) for k in Hn.WEIGHT_KEYS}
+    wts["logit_bias"] = None if dv.get("bias") is None else dv["bias"].to(DEV)
+    clk = torch.full((2 * M.CLOCK_SLOTS * 4,), -1, dtype=torch.int64, device=DEV)
+    M.moe_forward(cfg, wts, dv["h"], dv["h"], out, {"gemm_clocks": clk}, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out0.view(torch.int16))
+    c = clk.view(2, M.CLOCK_SLOTS, 4).cpu()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for i in range(2):
+        used = c[i, :, 0] != -1
+        n = int(used.sum())
+        assert 8 <= n <= ((cus + 7) // 8) * 8 and bool(used[:n].all()), n  # slots 0..grid-1
+        x = c[i, :n]
+        assert bool((x[:, 2] >= x[:, 0]).all()) and bool((x[:, 3] >= x[:, 1]).all())
+        assert bool((c[i, n:] == -1).all())
+        mhz = float((x[:, 2] - x[:, 0]).sum()) / float((x[:, 3] - x[:, 1]).sum())
+        _say(f"  launch {i}: {n} workgroups, core cycles per wall-clock tick {mhz:.2f}")
+        assert 0.5 < mhz < 100  # a shader clock between 0.05 and 10 GHz against a 100 MHz wall clock

@@ -23,7 +23,7 @@ __all__ = [
     "moe_align_expert_choice", "moe_combine_expert_choice", "moe_routing_health_from_stats", "moe_routing_health",
     "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_IDS_IN", "MOE_ROUTE_NO_LOGITS_OUT",
     "MOE_OP_ALIGN",
-    "MOE_OP_FORWARD", "TRACE_EVENTS", "STATUS", "DTYPES", "ROUTING", "STATS_EXTRA", "STAT", "moe_expert_choice_sizes", "ec_capacity",
+    "MOE_OP_FORWARD", "TRACE_EVENTS", "CLOCK_SLOTS", "STATUS", "DTYPES", "ROUTING", "STATS_EXTRA", "STAT", "moe_expert_choice_sizes", "ec_capacity",
     "ec_segment",
 ]
 
@@ -67,7 +67,7 @@ class moe_trace(ctypes.Structure):
         "logits", "topk_ids", "topk_gates", "margin", "route_kept", "sorted_route_ids", "block_expert",
         "expert_offsets", "num_padded", "stats", "act", "y_route", "route_expert", "scores", "choice_tokens",
         "choice_slot", "choice_margin")] + [("stage_events", ctypes.POINTER(ctypes.c_void_p)),
-                                             ("w13_out", ctypes.c_void_p)]
+                                             ("w13_out", ctypes.c_void_p), ("gemm_clocks", ctypes.c_void_p)]
 
 
 class moe_routing_health(ctypes.Structure):
@@ -78,6 +78,7 @@ class moe_routing_health(ctypes.Structure):
 
 
 TRACE_EVENTS = 7  # router, alignment, W13, W2, shared expert, combine: 7 boundaries
+CLOCK_SLOTS = 1024  # MOE_CLOCK_SLOTS
 
 
 def _event_handle(e) -> int:

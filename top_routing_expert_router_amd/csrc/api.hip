@@ -402,7 +402,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* wt, const void
   if (!aligned(rexp, 4)) return MOE_ERR_MISALIGNED;
   if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4) || !aligned(margin, 4) || !aligned(sorted, 4) ||
       !aligned(blocks, 4) || !aligned(offsets, 4) || !aligned(npad, 4) || !aligned(stats, 4) || !aligned(act, 16) ||
-      !aligned(y, 16) || (tr.w13_out && !aligned(tr.w13_out, 16)))
+      !aligned(y, 16) || (tr.w13_out && !aligned(tr.w13_out, 16)) || !aligned(tr.gemm_clocks, 8))
     return MOE_ERR_MISALIGNED;
 
   hipStream_t s = (hipStream_t)stream;
@@ -413,10 +413,12 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* wt, const void
   // W13 then W2 of the routed experts, the shared expert, each followed by its event
   auto expert_stages = [&](hipError_t e, const void* shared_out_buf, const void** shared_out) -> hipError_t {
     if (e == hipSuccess)
-      e = launch_gate_up(c, h, sorted, offsets, wt->w13, wt->w13_scale, act, tr.w13_out, false, s, work);
+      e = launch_gate_up(c, h, sorted, offsets, wt->w13, wt->w13_scale, act, tr.w13_out, false, s, work,
+                         tr.gemm_clocks);
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess)
-      e = launch_down(c, act, sorted, offsets, wt->w2, wt->w2_scale, y, false, s, work + kGemmWorkWords);
+      e = launch_down(c, act, sorted, offsets, wt->w2, wt->w2_scale, y, false, s, work + kGemmWorkWords,
+                      tr.gemm_clocks ? tr.gemm_clocks + 4 * MOE_CLOCK_SLOTS : nullptr);
     if (e == hipSuccess) e = mark(4);
     if (e == hipSuccess && c.n_shared) {
       e = launch_expert_ffn(c, h, nullptr, nullptr, wt->shared_w13, wt->shared_w2, wt->shared_w13_scale,

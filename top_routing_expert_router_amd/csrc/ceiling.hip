@@ -108,6 +108,15 @@ int32_t moe_ceiling_read(const void* src, size_t bytes, float* sink, void* strea
   return status(hipGetLastError());
 }
 
+int32_t moe_ceiling_clock_rates(int32_t* wall_khz, int32_t* peak_khz) {
+  if (!wall_khz || !peak_khz) return 1;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(wall_khz, hipDeviceAttributeWallClockRate, dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(peak_khz, hipDeviceAttributeClockRate, dev);
+  return status(e);
+}
+
 int32_t moe_ceiling_mfma_bf16(int32_t iters, int32_t waves_per_simd, float* sink, void* stream) {
   if (!sink || iters <= 0 || (waves_per_simd != 1 && waves_per_simd != 2)) return 1;
   if (waves_per_simd == 1)

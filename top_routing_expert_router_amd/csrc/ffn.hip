@@ -67,7 +67,20 @@ struct FfnArgs {
   int narrow;             // W2, bf16 weights, K % 256 == 0, one to four rounds of tiles: small last
                           // m-tiles run as two narrow tiles, after all full-height tiles
   void* w13_out;          // W13 only, nullable: [rows, 2I] gate then up projection, act dtype
+  uint64_t* clk;          // nullable: per workgroup, shader-clock and real-time counters at its
+                          // start and its end (4 words at 4 * blockIdx.x)
 };
+
+// The core-cycle counter (clock64: it counts at whatever clock the shader runs at) and the
+// constant-rate wall-clock counter (wall_clock64, hipDeviceAttributeWallClockRate) now, into
+// p[0], p[1]: their ratio over a workgroup's life is the clock it ran at.  Counter reads and
+// a vector store, outside any K loop.
+__device__ __forceinline__ void clock_stamp(uint64_t* p) {
+  const uint64_t t = (uint64_t)clock64();
+  const uint64_t r = (uint64_t)wall_clock64();
+  p[0] = t;
+  p[1] = r;
+}
 
 // LDS tile layout: row-major 128-byte rows of 8 16-byte chunks, chunk index XORed
 // with (row >> 1) & 7.  A ds_read_b128 serves 16 lanes per cycle from 64 banks;
@@ -241,6 +254,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // Dynamic schedule (a.work): workgroups claim the run's tiles in order from the
   // XCD's counter -- a workgroup claims its next tile when it starts the current
   // one, so tiles of unequal cost (full and half) balance across the XCD.
+  if (a.clk != nullptr && threadIdx.x == 0) clock_stamp(a.clk + 4 * blockIdx.x);
   build_tile_table<NARROW>(a, t_beg, t_big0, t_sm0);
   // values read from the table are the same in every lane; readfirstlane makes them
   // scalar, so the buffer resources built from them stay in SGPRs
@@ -261,7 +275,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     __syncthreads();
     lid = run0 + __builtin_amdgcn_readfirstlane(sh_claim);
   }
-  if (lid >= lid_end) return;
+  if (lid >= lid_end) {
+    if (a.clk != nullptr && threadIdx.x == 0) clock_stamp(a.clk + 4 * blockIdx.x + 2);
+    return;
+  }
   auto decode = [&](int l, Tile& t) {
     const int group = l / (kGroupN * total_m);
     const int gn0 = group * kGroupN;
@@ -924,6 +941,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     cur = nxt;
     lid = next_lid;
   }
+  if (a.clk != nullptr && threadIdx.x == 0) clock_stamp(a.clk + 4 * blockIdx.x + 2);
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -997,7 +1015,7 @@ int mtile_bound(const moe_config& c, bool identity) {
 // Persistent launch: one workgroup per CU (the kernel's LDS allows no more), at most
 // as many as there can be tiles, a multiple of the 8 XCDs.
 template <int MODE, bool FP8, bool NARROW = false, bool W13OUT = false>
-hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_gemm(FfnArgs a, hipStream_t s) {
   int dev = 0, cus = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1005,6 +1023,7 @@ hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
   const int G = a.mtiles * a.ntiles;
   if (G == 0) return hipSuccess;  // no rows (an expert-choice capacity of 0)
   const int grid = ceil_div(min(G, max(cus, 8)), 8) * 8;
+  if (grid > MOE_CLOCK_SLOTS) a.clk = nullptr;  // more workgroups than stamp slots: none
   ffn_gemm_bf16<MODE, FP8, NARROW, W13OUT><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
@@ -1038,9 +1057,10 @@ FfnArgs base_args(const moe_config& c, const int32_t* sorted_ids, const int32_t*
 
 hipError_t launch_gate_up(const moe_config& c, const void* h, const int32_t* sorted_ids, const int32_t* offsets,
                           const void* w13, const void* w13_scale, void* act, void* w13_out, bool identity,
-                          hipStream_t s, int32_t* work) {
+                          hipStream_t s, int32_t* work, uint64_t* clk) {
   FfnArgs a = base_args(c, sorted_ids, offsets, identity);
   a.work = work;
+  a.clk = clk;
   a.x = h;
   a.w = w13;
   a.wscale = (const __bf16*)w13_scale;
@@ -1061,9 +1081,10 @@ hipError_t launch_gate_up(const moe_config& c, const void* h, const int32_t* sor
 
 hipError_t launch_down(const moe_config& c, const void* act, const int32_t* sorted_ids, const int32_t* offsets,
                        const void* w2, const void* w2_scale, void* y, bool identity, hipStream_t s,
-                       int32_t* work) {
+                       int32_t* work, uint64_t* clk) {
   FfnArgs a = base_args(c, sorted_ids, offsets, identity);
   a.work = work;
+  a.clk = clk;
   a.x = act;
   a.w = w2;
   a.wscale = (const __bf16*)w2_scale;

@@ -70,12 +70,13 @@ hipError_t launch_ec_align(const moe_config& c, const int32_t* tokens, const int
 // fixed share.  The schedule changes no output bit.
 constexpr int kGemmWorkWords = 8;
 // w13_out (nullable): also store the gate and up projections, [rows, 2I] act dtype
+// clk (nullable): MOE_CLOCK_SLOTS x 4 words, each persistent workgroup's clock stamps
 hipError_t launch_gate_up(const moe_config& c, const void* h, const int32_t* sorted_ids, const int32_t* offsets,
                           const void* w13, const void* w13_scale, void* act, void* w13_out, bool identity,
-                          hipStream_t s, int32_t* work = nullptr);
+                          hipStream_t s, int32_t* work = nullptr, uint64_t* clk = nullptr);
 hipError_t launch_down(const moe_config& c, const void* act, const int32_t* sorted_ids, const int32_t* offsets,
                        const void* w2, const void* w2_scale, void* y, bool identity, hipStream_t s,
-                       int32_t* work = nullptr);
+                       int32_t* work = nullptr, uint64_t* clk = nullptr);
 // work: 2 * kGemmWorkWords ints (W13, then W2), or null
 hipError_t launch_expert_ffn(const moe_config& c, const void* h, const int32_t* sorted_ids,
                              const int32_t* offsets, const void* w13, const void* w2, const void* w13_scale,
