@@ -148,3 +148,57 @@ def test_forward_gemm_clock_stamps(name):
         mhz = float((x[:, 2] - x[:, 0]).sum()) / float((x[:, 3] - x[:, 1]).sum())
         _say(f"  launch {i}: {n} workgroups, core cycles per wall-clock tick {mhz:.2f}")
         assert 0.5 < mhz < 100  # a shader clock between 0.05 and 10 GHz against a 100 MHz wall clock
+
+
+@pytest.mark.parametrize("expert_dtype", ["bf16", "fp8_e4m3"])
+def test_routed_tiles_match_quarter_tiles(expert_dtype):
+    """Experts of 1088, 1152, 448, 320, 576, 200 and 64 rows (full 256-row tiles followed by
+    partly filled full, half and quarter tiles) give, for every act and y row, the same bits as
+    the same rows computed 64 at a time in identity mode (quarter tiles only): every output
+    element is one MFMA chain over K whatever the tile and mode it lands in."""
+    import workloads as W
+    import harness as Hn
+    N, k, B = 8, 1, 64
+    loads = [1088, 1152, 448, 320, 576, 200, 64, 0]
+    T = sum(loads)
+    base = W.MIXTRAL_BF16 if expert_dtype == "bf16" else W.DEEPSEEKV3_FP8
+    w = base.with_(T=T, H=512, I=512, N=N, k=k, B=B, n_shared=0)
+    _say("routed tiles vs quarter tiles", expert_dtype, loads)
+    d = Hn.to_dev(W.layer_inputs(w))
+    cfg = Hn.config(w)
+    p_max, _ = M.moe_align_sizes(cfg)
+    g = torch.Generator().manual_seed(9)
+    perm = torch.randperm(T, generator=g).numpy()   # route r = token r (k = 1)
+    sorted_ids = np.full(p_max, T, dtype=np.int32)
+    offsets = np.zeros(N + 1, dtype=np.int32)
+    pos = 0
+    for e, n in enumerate(loads):
+        offsets[e + 1] = offsets[e] + -(-n // B) * B
+        sorted_ids[offsets[e]:offsets[e] + n] = np.sort(perm[pos:pos + n])
+        pos += n
+    sd, od = torch.from_numpy(sorted_ids).to(DEV), torch.from_numpy(offsets).to(DEV)
+    act = torch.zeros(p_max, w.I, dtype=torch.bfloat16, device=DEV)
+    y = torch.full((T, w.H), 7.0, dtype=torch.bfloat16, device=DEV)
+    M.moe_expert_ffn(cfg, d["h"], sd, od, d["w13"], d["w2"], d.get("w13_scale"), d.get("w2_scale"), act, None, y)
+    torch.cuda.synchronize()
+    checked = 0
+    for e, n in enumerate(loads):
+        if n == 0:
+            continue
+        routes = torch.from_numpy(sorted_ids[offsets[e]:offsets[e] + n].astype(np.int64)).to(DEV)
+        x = d["h"][routes].contiguous()
+        sc13 = None if d.get("w13_scale") is None else d["w13_scale"][e:e + 1].contiguous()
+        sc2 = None if d.get("w2_scale") is None else d["w2_scale"][e:e + 1].contiguous()
+        for c0 in range(0, n, 64):  # 64 rows at a time: one quarter tile per call
+            c1 = min(n, c0 + 64)
+            ce = Hn.config(w, T=c1 - c0, N=1)
+            ae = torch.empty(c1 - c0, w.I, dtype=torch.bfloat16, device=DEV)
+            ye = torch.empty(c1 - c0, w.H, dtype=torch.bfloat16, device=DEV)
+            M.moe_expert_ffn(ce, x[c0:c1].contiguous(), None, None, d["w13"][e:e + 1].contiguous(),
+                             d["w2"][e:e + 1].contiguous(), sc13, sc2, ae, None, ye)
+            torch.cuda.synchronize()
+            assert torch.equal(act[offsets[e] + c0:offsets[e] + c1].view(torch.int16), ae.view(torch.int16)), (e, c0)
+            assert torch.equal(y[routes[c0:c1]].view(torch.int16), ye.view(torch.int16)), (e, c0)
+            checked += c1 - c0
+    assert checked == T
+    _say(f"  {checked} act and y rows bitwise equal to quarter-tile results")
