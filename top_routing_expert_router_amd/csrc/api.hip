@@ -3,12 +3,43 @@
 // Validation runs before any HIP call, so every error path is host-only.
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "common.h"
 #include "kernels.h"
 
 using namespace moe;
+
+namespace moe {
+
+// Per-device compute-unit counts, looked up on the first launch on each device (the
+// persistent GEMMs and the router size their grids by it).  0 = not yet known.
+namespace {
+constexpr int kMaxCuDevices = 64;
+std::atomic<int> g_cus[kMaxCuDevices];
+}  // namespace
+
+hipError_t current_device_cus(int* cus) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev >= 0 && dev < kMaxCuDevices) {
+    const int known = g_cus[dev].load(std::memory_order_relaxed);
+    if (known > 0) {
+      *cus = known;
+      return hipSuccess;
+    }
+  }
+  int n = 0;
+  err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  if (dev >= 0 && dev < kMaxCuDevices) g_cus[dev].store(n, std::memory_order_relaxed);
+  *cus = n;
+  return hipSuccess;
+}
+
+}  // namespace moe
 
 // Scratch of moe_forward_noalloc: every intermediate of one forward pass, for callers that
 // cannot allocate.  One copy per GPU, held until the process ends.  Host code never uses this

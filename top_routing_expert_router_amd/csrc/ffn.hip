@@ -1016,9 +1016,8 @@ int mtile_bound(const moe_config& c, bool identity) {
 // as many as there can be tiles, a multiple of the 8 XCDs.
 template <int MODE, bool FP8, bool NARROW = false, bool W13OUT = false>
 hipError_t launch_gemm(FfnArgs a, hipStream_t s) {
-  int dev = 0, cus = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int cus = 0;
+  hipError_t err = current_device_cus(&cus);
   if (err != hipSuccess) return err;
   const int G = a.mtiles * a.ntiles;
   if (G == 0) return hipSuccess;  // no rows (an expert-choice capacity of 0)
@@ -1101,9 +1100,8 @@ hipError_t launch_down(const moe_config& c, const void* act, const int32_t* sort
   // fill the final round (fewer tiles: the longest tile sets the time anyway; more: the
   // last round is a small part, and keeping an expert's m-tiles together saves weight
   // re-reads).  Each expert's last m-tile may take a second m-slot.
-  int dev = 0, cus = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int cus = 0;
+  hipError_t err = current_device_cus(&cus);
   if (err != hipSuccess) return err;
   const long tiles = (long)a.mtiles * a.ntiles;
   a.narrow = c.expert_dtype == MOE_BF16 && c.I % 256 == 0 && tiles > cus && tiles <= 4L * cus;

@@ -63,6 +63,9 @@ hipError_t launch_ec_align(const moe_config& c, const int32_t* tokens, const int
                            int32_t* block_expert, int32_t* offsets, int32_t* num_padded, int32_t* stats,
                            hipStream_t s, int32_t* zero = nullptr, int nzero = 0);
 
+// Compute units of the current device: queried once per device, then cached (api.hip).
+hipError_t current_device_cus(int* cus);
+
 // ---- expert FFN (ffn.hip)
 // identity == true: one expert over T token rows (shared expert), offsets ignored.
 // work (nullable): kGemmWorkWords zeroed ints per GEMM launch; with them the

@@ -42,7 +42,7 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 // Top-k, gates and margin of one token from its N logits (global or LDS), by one
 // aligned group of L = topk_lanes(N) lanes; a wave ranks 64 / L tokens at once.
-// Lane g of the group holds experts g + L i, i < kTopkPerLane.  k+1 rounds of a group max over
+// Lane g of the group holds experts g + L i, i < P.  k+1 rounds of a group max over
 // (value, -index) keys give the ranked ids and the (k+1)-th logit for the margin.
 // Gate weight_j = exp(l_j - l_0) (0 for a NaN logit); divided by the sum over the
 // k chosen in rank order, or by the sum over all N experts without renormalisation.
@@ -55,17 +55,21 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 // paragraph on expert-choice routing): every expert's softmax value exp(l_e - l_0) / sum
 // over all N, written to scores[t, :] instead of ids, gates and margin -- the same
 // operations, so a token's top-k scores equal its gates with renormalize = 0 bit for bit.
-template <typename RowPtr>
-__device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int renormalize, int L,
-                                         int32_t* __restrict__ ids, float* __restrict__ gates,
-                                         float* __restrict__ margin, const int32_t* __restrict__ replay,
-                                         float* __restrict__ scores) {
+// P = experts per lane actually used (ceil(N / L), at most kTopkPerLane): slots past it
+// hold no expert, so they are left out at compile time (topk_one picks P); the result is
+// the same for every P that covers N.
+template <int P, typename RowPtr>
+__device__ __forceinline__ void topk_one_p(RowPtr row, int t, int N, int k, int renormalize, int L,
+                                           int32_t* __restrict__ ids, float* __restrict__ gates,
+                                           float* __restrict__ margin, const int32_t* __restrict__ replay,
+                                           float* __restrict__ scores) {
+  static_assert(P >= 1 && P <= kTopkPerLane, "experts per lane");
   const int lane = threadIdx.x & 63;
   const int g = lane & (L - 1), base = lane - g;
-  float lv[kTopkPerLane];
-  uint64_t key[kTopkPerLane];
+  float lv[P];
+  uint64_t key[P];
 #pragma unroll
-  for (int i = 0; i < kTopkPerLane; ++i) {
+  for (int i = 0; i < P; ++i) {
     const int e = g + L * i;
     lv[i] = e < N ? row[e] : 0.f;
     key[i] = e < N ? rank_key(lv[i], e) : 0ull;
@@ -73,23 +77,23 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
   if (scores != nullptr) {
     uint64_t best = key[0];
 #pragma unroll
-    for (int i = 1; i < kTopkPerLane; ++i) best = key[i] > best ? key[i] : best;
+    for (int i = 1; i < P; ++i) best = key[i] > best ? key[i] : best;
     best = group_max_u64(best, L);
     const int e0 = (int)(0xFFFFFFFFu - (uint32_t)best);
     const int owner = e0 & (L - 1), slot = e0 / L;
     float mine = lv[0];
 #pragma unroll
-    for (int i = 1; i < kTopkPerLane; ++i) mine = slot == i ? lv[i] : mine;
+    for (int i = 1; i < P; ++i) mine = slot == i ? lv[i] : mine;
     const float l0 = __shfl(mine, base + owner, kWave);
     float z = 0.f;
 #pragma unroll
-    for (int i = 0; i < kTopkPerLane; ++i) {
+    for (int i = 0; i < P; ++i) {
       const int e = g + L * i;
       if (e < N && lv[i] == lv[i]) z += expf(lv[i] - l0);
     }
     const float sum = group_sum_f32(z, L);
 #pragma unroll
-    for (int i = 0; i < kTopkPerLane; ++i) {
+    for (int i = 0; i < P; ++i) {
       const int e = g + L * i;
       if (e < N) scores[(size_t)t * N + e] = (lv[i] == lv[i] ? expf(lv[i] - l0) : 0.f) / sum;
     }
@@ -105,18 +109,18 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
     if (j < rounds) {
       uint64_t best = key[0];
 #pragma unroll
-      for (int i = 1; i < kTopkPerLane; ++i) best = key[i] > best ? key[i] : best;
+      for (int i = 1; i < P; ++i) best = key[i] > best ? key[i] : best;
       best = group_max_u64(best, L);
       const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
       const int owner = e & (L - 1), slot = e / L;
       float mine = lv[0];
 #pragma unroll
-      for (int i = 1; i < kTopkPerLane; ++i) mine = slot == i ? lv[i] : mine;
+      for (int i = 1; i < P; ++i) mine = slot == i ? lv[i] : mine;
       sl[j] = __shfl(mine, base + owner, kWave);
       sid[j] = e;
       if (g == owner) {
 #pragma unroll
-        for (int i = 0; i < kTopkPerLane; ++i)
+        for (int i = 0; i < P; ++i)
           if (i == slot) key[i] = 0ull;
       }
     }
@@ -161,7 +165,7 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
   if (!renormalize) {
     float z = 0.f;
 #pragma unroll
-    for (int i = 0; i < kTopkPerLane; ++i) {
+    for (int i = 0; i < P; ++i) {
       const int e = g + L * i;
       if (e < N && lv[i] == lv[i]) z += expf(lv[i] - l0);
     }
@@ -181,6 +185,22 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
       if (j == k && k < N) m = sl[j - 1] - sl[j];
     margin[t] = m;
   }
+}
+
+template <typename RowPtr>
+__device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int renormalize, int L,
+                                         int32_t* __restrict__ ids, float* __restrict__ gates,
+                                         float* __restrict__ margin, const int32_t* __restrict__ replay,
+                                         float* __restrict__ scores) {
+  const int per = ceil_div(N, L);  // uniform
+  if (per <= 1)
+    topk_one_p<1>(row, t, N, k, renormalize, L, ids, gates, margin, replay, scores);
+  else if (per <= 2)
+    topk_one_p<2>(row, t, N, k, renormalize, L, ids, gates, margin, replay, scores);
+  else if (per <= 4)
+    topk_one_p<4>(row, t, N, k, renormalize, L, ids, gates, margin, replay, scores);
+  else
+    topk_one_p<kTopkPerLane>(row, t, N, k, renormalize, L, ids, gates, margin, replay, scores);
 }
 
 // bf16 router on MFMA 16x16x32, with top-k fused: D[expert][token] = sum_k W_g[expert][k] h[token][k].
@@ -479,9 +499,8 @@ template <int NP>
 hipError_t launch_router_wide(const moe_config& c, const void* h, const void* wg, const float* bias, float* logits,
                               int32_t* ids, float* gates, float* margin, hipStream_t s, const int32_t* replay,
                               float* scores) {
-  int dev = 0, cus = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int cus = 0;
+  hipError_t err = current_device_cus(&cus);
   if (err != hipSuccess) return err;
   // 64 tokens per workgroup when that still gives every CU a workgroup, else 32
   constexpr int NW = 8;
