@@ -49,6 +49,8 @@ constexpr int kBufferFlags = 0x00020000;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 struct FfnArgs {
   const void* x;          // W13: h [T, H];  W2: act [rows, I]
@@ -507,8 +509,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[0], true);
         const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[1], false);
         const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[1], true);
+        // both products rounded to bf16 by one paired conversion (round to nearest even,
+        // as a scalar cast would), low half first
         auto pack = [&](float lo, float hi) {
-          return (unsigned)bf16_bits((__bf16)(lo * s)) | ((unsigned)bf16_bits((__bf16)(hi * s)) << 16);
+          return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo * s, hi * s}, bf16x2));
         };
         *reinterpret_cast<u32x4*>(sB + swz(rb + 32 * i, chunk)) =
             u32x4{pack(f0[0], f0[1]), pack(f1[0], f1[1]), pack(f2[0], f2[1]), pack(f3[0], f3[1])};
