@@ -317,10 +317,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int WR = MODE == 0 ? 2 * a.I : a.H;  // weight rows per expert
   // The wave index is uniform: made scalar, every per-wave LDS destination of a copy is an
   // SGPR sum (M0 set by scalar code, no VALU -> SGPR moves between the MFMAs), and the
-  // bf16 kernels then keep all their state in registers.  The fp8 kernels keep it in a
-  // VGPR: they stage weight codes in registers and would spill inside the K loop.
+  // kernels keep all their state in registers (no spills).
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = FP8 ? tid >> 6 : __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---- global -> LDS copy plan.  8 rows (1 KB) per DMA instruction; lane L lands
   // in physical 16-byte chunk L % 8 of its row, so it fetches the logical chunk that
