@@ -7,10 +7,12 @@ seeded synthetic inputs already resident in HBM.  Default workload: the
 Mixtral-shaped layer (T=4096, H=4096, 8 experts, top-2, SwiGLU I=14336, B=64,
 bf16).  Prints ONE JSON line on stdout; progress goes to stderr.
 
-Besides the headline rate it times every stage on its own with HIP events
-recorded on the stream each kernel is launched on (per launch, averaged), and
-reports the dominant kernel (the W13+SwiGLU grouped GEMM) against the bf16
-MFMA peak, plus the CPU oracle timed on a bounded token sample.
+The expert GEMMs are timed inside the timed steps themselves, by HIP events the
+forward records on its stream around them (its trace's stage events, at those
+boundaries only); the dominant one (the W13+SwiGLU grouped GEMM) is reported
+against the bf16 MFMA peak.  Every other stage is timed in forwards carrying all
+the stage events and on its own (cold), and the CPU oracle on a bounded token
+sample.
 """
 from __future__ import annotations
 
@@ -119,26 +121,51 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, out_dir: s
     return 0
 
 
-def summarize_trace(trace_dir: str, workload: str) -> int:
+def summarize_trace(trace_dir: str, workload: str, warmup: int = 0, steps: int = 0) -> int:
     """Per-kernel durations from a rocprofv3 --kernel-trace run of this script (CSV
     output): calls, average, min, max and share of GPU time, layer kernels by name
-    and torch's own kernels (input generation, cache-flush fills) lumped together."""
+    and torch's own kernels (input generation, cache-flush fills) lumped together.
+    With warmup and steps (those of the traced run), also the layer's kernels over the
+    timed steps alone, picked by dispatch order: the script's first calls of the layer are
+    the warmup forwards, then the timed ones.  With a shared expert each forward launches
+    each GEMM kernel twice (routed experts first, then the shared expert); the two are
+    reported apart."""
     import csv
     import statistics
 
-    per = {}
-    for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))):
+    import workloads as W
+
+    per, order = {}, {}
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    for r in rows:
         n = r["Kernel_Name"]
         name = next((st for frag, st in _COUNTER_KERNELS if frag in n), None)
         if name is None:
             name = "torch (inputs, flush fills)" if "at::native" in n else n.split("(")[0][-40:]
-        per.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per.setdefault(name, []).append(us)
     total = sum(sum(v) for v in per.values())
     print(f"# rocprofv3 kernel trace of bench.py, workload {workload}; durations in microseconds")
     print(f"{'kernel':<30}{'calls':>7}{'avg_us':>11}{'min_us':>11}{'max_us':>11}{'total_us':>12}{'pct':>8}")
     for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
         print(f"{k:<30}{len(v):>7}{statistics.mean(v):>11.2f}{min(v):>11.2f}{max(v):>11.2f}"
               f"{sum(v):>12.1f}{100 * sum(v) / total:>8.2f}")
+    if steps > 0:
+        shared = W.ALL[workload].n_shared > 0 if workload in W.ALL else False
+        print(f"# the {steps} timed steps alone (launches {warmup} .. {warmup + steps - 1} of each layer kernel, "
+              f"in dispatch order)")
+        print(f"{'kernel':<30}{'calls':>7}{'avg_us':>11}{'min_us':>11}{'max_us':>11}")
+        for k, v in per.items():
+            if k.startswith("ceiling") or k.startswith("torch") or k.startswith("__"):
+                continue
+            gemm = k in ("gate_up_gemm", "down_gemm")
+            per_fwd = 2 if gemm and shared else 1
+            sel = v[per_fwd * warmup: per_fwd * (warmup + steps)]
+            parts = [(k, sel)] if per_fwd == 1 else [(k + " (routed)", sel[0::2]), (k + " (shared)", sel[1::2])]
+            for name, x in parts:
+                if x:
+                    print(f"{name:<30}{len(x):>7}{statistics.mean(x):>11.2f}{min(x):>11.2f}{max(x):>11.2f}")
     return 0
 
 
@@ -156,10 +183,11 @@ def main() -> int:
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
-                    help="no GPU: per-kernel durations from a rocprofv3 --kernel-trace run of this script")
+                    help="no GPU: per-kernel durations from a rocprofv3 --kernel-trace run of this script "
+                         "(give that run's --steps and --warmup to also get its timed steps alone)")
     args = ap.parse_args()
     if args.summarize_trace:
-        return summarize_trace(args.summarize_trace, args.workload)
+        return summarize_trace(args.summarize_trace, args.workload, args.warmup, args.steps)
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters, args.workload)
 
@@ -195,22 +223,34 @@ def main() -> int:
     wts["logit_bias"] = None if d["bias"] is None else d["bias"].to(dev)
     stream = torch.cuda.current_stream()
 
-    def step():
-        M.moe_forward(cfg, wts, d["h"], d["residual"], out, None, ws, stream=stream)
+    def step(trace=None):
+        M.moe_forward(cfg, wts, d["h"], d["residual"], out, trace, ws, stream=stream)
 
+    # events around the expert GEMMs inside every timed step (boundaries: after the alignment,
+    # after W13, after W2, after the shared expert): the GEMM times come from the timed region
+    # itself, from the launches the step time covers
+    gemm_ev = [[None, None] + [torch.cuda.Event(enable_timing=True) for _ in range(4)] + [None]
+               for _ in range(args.steps)]
+    for evs in gemm_ev:
+        for e in evs:
+            if e is not None:
+                e.record(stream)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step({"stage_events": gemm_ev[i]})
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
     value = w.T / (ms / 1e3)
+    timed_gemm_ms = [sum(ev[b].elapsed_time(ev[b + 1]) for ev in gemm_ev) / args.steps for b in (2, 3, 4)]
     log(f"[bench] forward: {ms:.4f} ms/step, {value:,.0f} tokens/s")
+    log(f"[bench] inside the timed steps: W13 {timed_gemm_ms[0] * 1e3:,.1f} us, W2 {timed_gemm_ms[1] * 1e3:,.1f} us"
+        + (f", shared expert {timed_gemm_ms[2] * 1e3:,.1f} us" if w.n_shared else ""))
 
     # ---- per-stage timings through the individual entry points (same buffers)
     tr = dict(logits=torch.empty(w.T, w.N, device=dev),
@@ -272,13 +312,13 @@ def main() -> int:
     gate_up_flops = 4.0 * kept_routes * H * I
     down_flops = 2.0 * kept_routes * H * I
     fwd_stage_ms, fwd_events_ms = in_forward(max(args.steps, 5))
-    ms_gate_up, ms_down = fwd_stage_ms[2], fwd_stage_ms[3]
+    ms_gate_up, ms_down = timed_gemm_ms[0], timed_gemm_ms[1]
     stages["gate_up_gemm"] = {"us": ms_gate_up * 1e3, "TFLOP/s": gate_up_flops / (ms_gate_up * 1e-3) / 1e12}
     stages["down_gemm"] = {"us": ms_down * 1e3, "TFLOP/s": down_flops / (ms_down * 1e-3) / 1e12}
     if w.n_shared:
         sh_flops = 6.0 * T * H * I * w.n_shared
-        stages["shared_expert"] = {"us": fwd_stage_ms[4] * 1e3,
-                                   "TFLOP/s": sh_flops / (fwd_stage_ms[4] * 1e-3) / 1e12}
+        stages["shared_expert"] = {"us": timed_gemm_ms[2] * 1e3,
+                                   "TFLOP/s": sh_flops / (timed_gemm_ms[2] * 1e-3) / 1e12}
     if not args.no_stages and ec:
         ec_stages(stages, w, cfg, d, wts, tr, out, ws, C, p_max, n_blocks, asz, timed, max(args.steps, 5), stream)
         for name, ms_stage in (("route_expert_choice", fwd_stage_ms[0]), ("align_expert_choice", fwd_stage_ms[1]),
@@ -323,14 +363,20 @@ def main() -> int:
         for kname, v in stages.items():
             log(f"[bench] stage {kname}: " + ", ".join(f"{a} {b:,.2f}" for a, b in v.items()))
 
-    # the stage events themselves cost time: the sum of the stages equals the instrumented
-    # forward (first to last event), and that one is compared with the plain forward timed above
+    # the stage events themselves cost time: the sum of the stages equals the fully
+    # instrumented forward (first to last event), and that one is compared with the timed
+    # step (which records events at the GEMM boundaries only)
     reconcile = {"stages_sum_us": round(sum(fwd_stage_ms) * 1e3, 2),
                  "instrumented_forward_us": round(fwd_events_ms * 1e3, 2),
-                 "plain_forward_us": round(ms * 1e3, 2),
-                 "event_overhead_pct": round(100.0 * (fwd_events_ms - ms) / ms, 2)}
+                 "timed_step_us": round(ms * 1e3, 2),
+                 "event_overhead_pct": round(100.0 * (fwd_events_ms - ms) / ms, 2),
+                 "timed_step_gemm_us": {"gate_up_gemm": round(timed_gemm_ms[0] * 1e3, 2),
+                                        "down_gemm": round(timed_gemm_ms[1] * 1e3, 2)},
+                 "instrumented_gemm_us": {"gate_up_gemm": round(fwd_stage_ms[2] * 1e3, 2),
+                                          "down_gemm": round(fwd_stage_ms[3] * 1e3, 2)}}
     log(f"[bench] stage sum {reconcile['stages_sum_us']:.1f} us, instrumented forward "
-        f"{reconcile['instrumented_forward_us']:.1f} us, plain forward {reconcile['plain_forward_us']:.1f} us")
+        f"{reconcile['instrumented_forward_us']:.1f} us, timed step {reconcile['timed_step_us']:.1f} us; "
+        f"W13 {fwd_stage_ms[2] * 1e3:.1f} us instrumented vs {timed_gemm_ms[0] * 1e3:.1f} us in the timed steps")
     clocks = gemm_clock_report(cfg, wts, d, out, ws, stream, {"gate_up_gemm": ms_gate_up, "down_gemm": ms_down})
     log("[bench] shader clock inside the GEMMs (core cycles / wall clock per workgroup): "
         + ", ".join(f"{k} {v}" for k, v in clocks.items()))

@@ -36,3 +36,34 @@ def test_summaries_read_rocprof_csv(tmp_path):
     (trace / "run_kernel_trace.csv").write_text(
         '"Kernel_Name","Start_Timestamp","End_Timestamp"\n"copy16(x)",0,1000\n"router_bf16<1>(x)",0,3000\n')
     assert bench.summarize_trace(str(trace), "unit_test") == 0
+
+
+def test_trace_summary_timed_steps(tmp_path, capsys):
+    """Timed-step launches are picked by dispatch order after the warmup ones; with a shared
+    expert each forward's two GEMM launches are split into routed and shared."""
+    rows, t = [], 0
+    for fwd in range(5):  # 2 warmup, 2 timed, 1 after
+        for name, dur in (("router_bf16_wide<1>(x)", 10), ("void ffn_gemm_bf16<0, true>(a)", 1000 + fwd),
+                          ("void ffn_gemm_bf16<1, true>(a)", 500), ("void ffn_gemm_bf16<0, true>(a)", 100 + fwd),
+                          ("void ffn_gemm_bf16<1, true>(a)", 50), ("combine_rows<x>", 20)):
+            rows.append(f'"{name}",{t},{t + dur * 1000}\n')
+            t += dur * 1000 + 7
+    d = tmp_path / "t"
+    os.makedirs(d)
+    (d / "run_kernel_trace.csv").write_text('"Kernel_Name","Start_Timestamp","End_Timestamp"\n' + "".join(rows))
+    assert bench.summarize_trace(str(d), "deepseekv3_fp8", warmup=2, steps=2) == 0
+    out = capsys.readouterr().out
+    everything, timed = out.split("# the 2 timed steps")
+    def table(txt):
+        t = {}
+        for l in txt.splitlines():
+            f = l.split()
+            if not f or l.startswith("#") or f[0] == "kernel" or l.startswith(" "):
+                continue
+            key = f[0] + (" " + f[1] if len(f) > 1 and f[1].startswith("(") else "")
+            t[key] = f[2:] if key.endswith(")") else f[1:]
+        return t
+    a, b = table(everything), table(timed)
+    assert a["route_wide"][0] == "5" and a["gate_up_gemm"][0] == "10"
+    assert b["gate_up_gemm (routed)"][:2] == ["2", "1002.50"] and b["gate_up_gemm (shared)"][:2] == ["2", "102.50"]
+    assert b["route_wide"][:2] == ["2", "10.00"] and b["combine"][0] == "2"

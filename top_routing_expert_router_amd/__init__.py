@@ -81,8 +81,11 @@ TRACE_EVENTS = 7  # router, alignment, W13, W2, shared expert, combine: 7 bounda
 CLOCK_SLOTS = 1024  # MOE_CLOCK_SLOTS
 
 
-def _event_handle(e) -> int:
-    """Raw hipEvent_t of a torch.cuda.Event (created by one record on the current stream)."""
+def _event_handle(e) -> Optional[int]:
+    """Raw hipEvent_t of a torch.cuda.Event (created by one record on the current stream);
+    None for a boundary that records no event."""
+    if e is None:
+        return None
     if isinstance(e, int):
         return e
     if e.cuda_event == 0:
@@ -91,7 +94,8 @@ def _event_handle(e) -> int:
 
 
 def _trace_struct(trace: Optional[dict]):
-    """moe_trace for a dict of buffers; stage_events (optional) = TRACE_EVENTS timing events.
+    """moe_trace for a dict of buffers; stage_events (optional) = TRACE_EVENTS timing events
+    (None entries: no event at that boundary).
     Returns (struct or None, the event array, which must outlive the call)."""
     if not trace:
         return None, None
