@@ -107,6 +107,7 @@ __device__ __forceinline__ int swzn(int row, int chunk) { return row * (BK * 4) 
 // group the short tiles come last and fill the end of the schedule instead of pushing
 // full tiles into an extra round.  Identity rows: one expert, rows [0, T).
 constexpr int kMaxExperts = 256;
+constexpr int kEpiWaveBytes = 32 * (64 * 2 + 16);
 
 template <bool NARROW>
 __device__ void build_tile_table(const FfnArgs& a, int* beg, int* big0, int* sm0) {
@@ -247,6 +248,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ __attribute__((aligned(16))) char sA1[BM * BK * 2];
   __shared__ __attribute__((aligned(16))) char sB1[TBN * BK * 2];
   __shared__ int t_beg[kMaxExperts + 1], t_big0[kMaxExperts + 1], t_sm0[NARROW ? kMaxExperts + 1 : 1];
+  // each wave's epilogue staging area: 32 rows x up to 64 output columns (bf16), rows
+  // padded by 16 bytes so that the staging writes and the row reads spread over the banks
+  __shared__ __attribute__((aligned(16))) char s_epi[4 * kEpiWaveBytes];
 
   // ---- persistent work.  Tiles in logical order: groups of kGroupN n-tiles, all
   // m-tiles of a group before the next group.  Hardware deals workgroups to the 8
@@ -714,70 +718,95 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     int erid[4];
 #pragma unroll
     for (int ms = 0; ms < MSUB; ++ms)
-      erid[ms] = (!FP8 && a.sorted != nullptr) ? a.sorted[min(t.p0 + arow0 + ms * 32 + l32, t.p1 - 1)] : 0;
+      erid[ms] = a.sorted != nullptr ? a.sorted[min(t.p0 + arow0 + ms * 32 + l32, t.p1 - 1)] : 0;
 
     // ---- epilogue.  Lane holds row (lane & 31) of each 32-row sub-tile and, per
     // register group g, the 4 consecutive columns 8 g + 4 (lane >> 5) + [0, 4) of a
     // weight sub-tile (W2: output columns; W13: act columns of a gate sub-tile, its
     // up partner NS/2 sub-tiles later).
     const int n0 = MODE == 0 ? t.nt * (TBN / 2) : t.nt * TBN;
-    if (MODE == 0) {
+    if constexpr (MODE == 0 && W13OUT) {
+      // the pre-activation surface too: stored straight from the registers
       __bf16* act = (__bf16*)a.out;
 #pragma unroll
       for (int ms = 0; ms < MSUB; ++ms) {
         const int p = t.p0 + arow0 + ms * 32 + l32;
         bool ok = p < t.p1;
-        if (ok && a.sorted != nullptr) ok = (unsigned)(FP8 ? a.sorted[p] : erid[ms]) < (unsigned)a.sentinel;
+        if (ok && a.sorted != nullptr) ok = (unsigned)erid[ms] < (unsigned)a.sentinel;
         if (!ok) continue;
 #pragma unroll
         for (int ns = 0; ns < NS / 2; ++ns) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int col = n0 + br[ns] + g * 8 + khalf * 4;
-            bf16x4 o;
+            bf16x4 o, og, ou;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const float gt = acc[ns][ms][g * 4 + q], up = acc[ns + NS / 2][ms][g * 4 + q];
               o[q] = (__bf16)(silu_fast(gt) * up);
+              og[q] = (__bf16)gt;
+              ou[q] = (__bf16)up;
             }
             *reinterpret_cast<bf16x4*>(act + (long)p * a.I + col) = o;
-            if constexpr (W13OUT) {
-              bf16x4 og, ou;
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                og[q] = (__bf16)acc[ns][ms][g * 4 + q];
-                ou[q] = (__bf16)acc[ns + NS / 2][ms][g * 4 + q];
-              }
-              __bf16* w13o = (__bf16*)a.w13_out + (long)p * 2 * a.I;
-              *reinterpret_cast<bf16x4*>(w13o + col) = og;
-              *reinterpret_cast<bf16x4*>(w13o + a.I + col) = ou;
-            }
+            __bf16* w13o = (__bf16*)a.w13_out + (long)p * 2 * a.I;
+            *reinterpret_cast<bf16x4*>(w13o + col) = og;
+            *reinterpret_cast<bf16x4*>(w13o + a.I + col) = ou;
           }
         }
       }
     } else {
-      __bf16* y = (__bf16*)a.out;
+      // The wave's output columns are contiguous: W13 the act columns of its gate
+      // sub-tiles, W2 its weight sub-tiles.  Per 32-row sub-tile they go out in chunks of
+      // up to 64 columns through the wave's LDS area: staged in the accumulator layout,
+      // read back by row, and stored 16 B per lane with a row's chunk in consecutive lanes
+      // (whole 128-byte lines) -- instead of 8 B into 32 different rows per store.  Only
+      // this wave touches its area, and its LDS operations complete in order.
+      constexpr int SUBS = MODE == 0 ? NS / 2 : NS;  // 32-column sub-tiles of the wave
+      constexpr int CWS = SUBS >= 2 ? 2 : 1;          // of them per chunk
+      constexpr int CW = CWS * 32;                    // chunk width, columns
+      constexpr int RB = CW * 2 + 16;                 // staged row pitch, bytes
+      constexpr int LPR = CW / 8;                     // lanes per row on the way out
+      constexpr int RPI = kWave / LPR;                // rows per store
+      static_assert(32 * RB <= kEpiWaveBytes, "epilogue staging area");
+      char* stg = s_epi + wave * kEpiWaveBytes;
+      __bf16* outp = (__bf16*)a.out;
+      const long ld = MODE == 0 ? a.I : a.H;
 #pragma unroll
       for (int ms = 0; ms < MSUB; ++ms) {
-        const int p = t.p0 + arow0 + ms * 32 + l32;
-        if (p >= t.p1) continue;
-        int dest = p;
-        if (a.sorted != nullptr) {
-          const int r = FP8 ? a.sorted[p] : erid[ms];
-          if ((unsigned)r >= (unsigned)a.sentinel) continue;
-          if (!a.dest_is_row) dest = r;
-        }
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns) {
-          const int cbase = n0 + br[ns];
-          if (cbase >= a.H) continue;
+        for (int c = 0; c < SUBS / CWS; ++c) {
+          const int col0 = n0 + br[c * CWS];
+          // W2: a chunk past H (the last n-tile when H % 256 == 128) is staged but not stored
+          const bool cols_ok = MODE == 0 || col0 < a.H;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = cbase + g * 8 + khalf * 4;
-            bf16x4 o;
+          for (int nl = 0; nl < CWS; ++nl) {
+            const int ns = c * CWS + nl;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = (__bf16)acc[ns][ms][g * 4 + q];
-            *reinterpret_cast<bf16x4*>(y + (long)dest * a.H + col) = o;
+            for (int g = 0; g < 4; ++g) {
+              bf16x4 o;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                if constexpr (MODE == 0)
+                  o[q] = (__bf16)(silu_fast(acc[ns][ms][g * 4 + q]) * acc[ns + NS / 2][ms][g * 4 + q]);
+                else
+                  o[q] = (__bf16)acc[ns][ms][g * 4 + q];
+              }
+              *reinterpret_cast<bf16x4*>(stg + l32 * RB + (nl * 32 + g * 8 + khalf * 4) * 2) = o;
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 32 / RPI; ++i) {
+            const int rr = i * RPI + lane / LPR, c16 = lane % LPR;
+            const int eid = __shfl(erid[ms], rr, kWave);  // lane rr holds row rr's route id
+            const int p = t.p0 + arow0 + ms * 32 + rr;
+            bool ok = cols_ok && p < t.p1;
+            int dest = p;
+            if (a.sorted != nullptr) {
+              ok = ok && (unsigned)eid < (unsigned)a.sentinel;
+              if (MODE == 1 && !a.dest_is_row) dest = eid;
+            }
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rr * RB + c16 * 16);
+            if (ok) *reinterpret_cast<u32x4*>(outp + (long)dest * ld + col0 + c16 * 8) = v;
           }
         }
       }
