@@ -43,7 +43,12 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;  // BN: the W13 tile (128 gate + 128 up rows)
 constexpr int kThreads = 256;
-constexpr int kGroupN = 2;                        // n-tiles per raster group
+// n-tiles per raster group: 2 with bf16 weights; 8 with fp8 weights, whose stages take
+// longer (the decode) and whose workgroups then share each expert's activation rows across
+// more n-tiles (DeepSeek-V3 shape: W2 4.53 -> 4.37 ms; the bf16 shapes measured no faster
+// or slower with wider groups)
+template <bool FP8>
+constexpr int group_n() { return FP8 ? 8 : 2; }
 // buffer resource word 3 for raw (untyped, stride 0) buffer loads on gfx9-family parts
 constexpr int kBufferFlags = 0x00020000;
 
@@ -286,6 +291,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     return;
   }
   auto decode = [&](int l, Tile& t) {
+    constexpr int kGroupN = group_n<FP8>();
     const int group = l / (kGroupN * total_m);
     const int gn0 = group * kGroupN;
     const int gsize = min(kGroupN, a.ntiles - gn0);
