@@ -64,7 +64,7 @@ _COUNTER_KERNELS = [("ffn_gemm_bf16<0", "gate_up_gemm"), ("ffn_gemm_bf16<1", "do
                     ("router_bf16_wide", "route_wide"), ("router_bf16", "route"), ("topk_gates", "route_topk"),
                     ("align_hist", "align_hist"), ("align_scan", "align_scan"), ("align_scatter", "align_scatter"),
                     ("align_fused", "align_one_workgroup"), ("ec_select", "expert_choice_select"),
-                    ("ec_align", "align_expert_choice"), ("combine_ec_rows", "combine_expert_choice"),
+                    ("ec_align_init", "align_ec_init"), ("ec_align_rows", "align_ec_rows"), ("combine_ec_rows", "combine_expert_choice"),
                     ("reroute_capacity", "reroute"),
                     ("combine_rows", "combine"), ("copy16", "ceiling_copy_1GiB"), ("read16", "ceiling_read_1GiB"),
                     ("mfma_loop<1>", "ceiling_mfma_1wave"), ("mfma_loop<2>", "ceiling_mfma_2wave")]
@@ -161,6 +161,8 @@ def summarize_trace(trace_dir: str, workload: str, warmup: int = 0, steps: int =
                 continue
             gemm = k in ("gate_up_gemm", "down_gemm")
             per_fwd = 2 if gemm and shared else 1
+            if len(v) < per_fwd * (warmup + steps):
+                continue  # not launched by every forward (a standalone call elsewhere in the script)
             sel = v[per_fwd * warmup: per_fwd * (warmup + steps)]
             parts = [(k, sel)] if per_fwd == 1 else [(k + " (routed)", sel[0::2]), (k + " (shared)", sel[1::2])]
             for name, x in parts:

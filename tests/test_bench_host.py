@@ -48,6 +48,7 @@ def test_trace_summary_timed_steps(tmp_path, capsys):
                           ("void ffn_gemm_bf16<1, true>(a)", 50), ("combine_rows<x>", 20)):
             rows.append(f'"{name}",{t},{t + dur * 1000}\n')
             t += dur * 1000 + 7
+    rows.append(f'"topk_gates(x)",{t},{t + 4000}\n')  # a standalone launch, not part of each forward
     d = tmp_path / "t"
     os.makedirs(d)
     (d / "run_kernel_trace.csv").write_text('"Kernel_Name","Start_Timestamp","End_Timestamp"\n' + "".join(rows))
@@ -67,3 +68,4 @@ def test_trace_summary_timed_steps(tmp_path, capsys):
     assert a["route_wide"][0] == "5" and a["gate_up_gemm"][0] == "10"
     assert b["gate_up_gemm (routed)"][:2] == ["2", "1002.50"] and b["gate_up_gemm (shared)"][:2] == ["2", "102.50"]
     assert b["route_wide"][:2] == ["2", "10.00"] and b["combine"][0] == "2"
+    assert "route_topk" in a and "route_topk" not in b
