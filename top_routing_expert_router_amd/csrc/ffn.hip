@@ -800,19 +800,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
               *reinterpret_cast<bf16x4*>(stg + l32 * RB + (nl * 32 + g * 8 + khalf * 4) * 2) = o;
             }
           }
+          if constexpr (FP8 && MODE == 1) {
+            // fp8 W2: one LDS round trip pair per store (reading ahead, as below, takes
+            // registers that its K loop then spills)
 #pragma unroll
-          for (int i = 0; i < 32 / RPI; ++i) {
-            const int rr = i * RPI + lane / LPR, c16 = lane % LPR;
-            const int eid = __shfl(erid[ms], rr, kWave);  // lane rr holds row rr's route id
-            const int p = t.p0 + arow0 + ms * 32 + rr;
-            bool ok = cols_ok && p < t.p1;
-            int dest = p;
-            if (a.sorted != nullptr) {
-              ok = ok && (unsigned)eid < (unsigned)a.sentinel;
-              if (MODE == 1 && !a.dest_is_row) dest = eid;
+            for (int i = 0; i < 32 / RPI; ++i) {
+              const int rr = i * RPI + lane / LPR, c16 = lane % LPR;
+              const int eid = __shfl(erid[ms], rr, kWave);  // lane rr holds row rr's route id
+              const int p = t.p0 + arow0 + ms * 32 + rr;
+              bool ok = cols_ok && p < t.p1;
+              int dest = p;
+              if (a.sorted != nullptr) {
+                ok = ok && (unsigned)eid < (unsigned)a.sentinel;
+                if (!a.dest_is_row) dest = eid;
+              }
+              const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rr * RB + c16 * 16);
+              if (ok) *reinterpret_cast<u32x4*>(outp + (long)dest * ld + col0 + c16 * 8) = v;
             }
-            const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rr * RB + c16 * 16);
-            if (ok) *reinterpret_cast<u32x4*>(outp + (long)dest * ld + col0 + c16 * 8) = v;
+          } else {
+            // the chunk's route ids and staged rows are all read before the first store,
+            // so their LDS round trips overlap instead of one pair per store
+            constexpr int NR = 32 / RPI;
+            const int c16 = lane % LPR;
+            int eid[NR];
+            u32x4 v[NR];
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+              const int rr = i * RPI + lane / LPR;
+              eid[i] = __shfl(erid[ms], rr, kWave);  // lane rr holds row rr's route id
+              v[i] = *reinterpret_cast<const u32x4*>(stg + rr * RB + c16 * 16);
+            }
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+              const int rr = i * RPI + lane / LPR;
+              const int p = t.p0 + arow0 + ms * 32 + rr;
+              bool ok = cols_ok && p < t.p1;
+              int dest = p;
+              if (a.sorted != nullptr) {
+                ok = ok && (unsigned)eid[i] < (unsigned)a.sentinel;
+                if (MODE == 1 && !a.dest_is_row) dest = eid[i];
+              }
+              if (ok) *reinterpret_cast<u32x4*>(outp + (long)dest * ld + col0 + c16 * 8) = v[i];
+            }
           }
         }
       }
