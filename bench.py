@@ -229,10 +229,12 @@ def main() -> int:
         M.moe_forward(cfg, wts, d["h"], d["residual"], out, trace, ws, stream=stream)
 
     # events around the expert GEMMs inside every timed step (boundaries: after the alignment,
-    # after W13, after W2, after the shared expert): the GEMM times come from the timed region
-    # itself, from the launches the step time covers
-    gemm_ev = [[None, None] + [torch.cuda.Event(enable_timing=True) for _ in range(4)] + [None]
-               for _ in range(args.steps)]
+    # after W13, after W2, and after the shared expert when there is one): the GEMM times come
+    # from the timed region itself, from the launches the step time covers.  Each event is a
+    # packet of its own on the stream (about 5 us between the kernels around it), so no more
+    # are recorded than these times need.
+    gemm_ev = [[None, None] + [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+               + [torch.cuda.Event(enable_timing=True) if w.n_shared else None, None] for _ in range(args.steps)]
     for evs in gemm_ev:
         for e in evs:
             if e is not None:
@@ -249,7 +251,8 @@ def main() -> int:
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
     value = w.T / (ms / 1e3)
-    timed_gemm_ms = [sum(ev[b].elapsed_time(ev[b + 1]) for ev in gemm_ev) / args.steps for b in (2, 3, 4)]
+    timed_gemm_ms = [sum(ev[b].elapsed_time(ev[b + 1]) for ev in gemm_ev) / args.steps
+                     for b in ((2, 3, 4) if w.n_shared else (2, 3))]
     log(f"[bench] forward: {ms:.4f} ms/step, {value:,.0f} tokens/s")
     log(f"[bench] inside the timed steps: W13 {timed_gemm_ms[0] * 1e3:,.1f} us, W2 {timed_gemm_ms[1] * 1e3:,.1f} us"
         + (f", shared expert {timed_gemm_ms[2] * 1e3:,.1f} us" if w.n_shared else ""))
