@@ -35,6 +35,39 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence: recording it
+    does no system-scope cache write-back and invalidation (which a default event does, and
+    which costs the kernels around it several microseconds).  The library records it where a
+    trace's stage_events put it; elapsed() reads the time between two recorded events."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._hip is None:
+            TimingEvent._hip = ctypes.CDLL("libamdhip64.so")
+        self._ev = ctypes.c_void_p()
+        err = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(self._ev), self.DISABLE_SYSTEM_FENCE)
+        if err != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags: error {err}")
+        self.handle = self._ev.value
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        err = TimingEvent._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.handle),
+                                                   ctypes.c_void_p(end.handle))
+        if err != 0:
+            raise RuntimeError(f"hipEventElapsedTime: error {err}")
+        return ms.value
+
+    def __del__(self):
+        if TimingEvent._hip is not None and getattr(self, "handle", None):
+            import ctypes
+            TimingEvent._hip.hipEventDestroy(ctypes.c_void_p(self.handle))
+
+
 def _ffn_source_hash() -> str:
     """Hash of the GEMM source's code (comments and blank space removed), which the
     committed traffic counters were taken on."""
@@ -231,14 +264,10 @@ def main() -> int:
     # events around the expert GEMMs inside every timed step (boundaries: after the alignment,
     # after W13, after W2, and after the shared expert when there is one): the GEMM times come
     # from the timed region itself, from the launches the step time covers.  Each event is a
-    # packet of its own on the stream (about 5 us between the kernels around it), so no more
-    # are recorded than these times need.
-    gemm_ev = [[None, None] + [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-               + [torch.cuda.Event(enable_timing=True) if w.n_shared else None, None] for _ in range(args.steps)]
-    for evs in gemm_ev:
-        for e in evs:
-            if e is not None:
-                e.record(stream)
+    # packet of its own on the stream, so no more are recorded than these times need, and they
+    # are timing-only events (no system-scope fence).
+    gemm_ev = [[None, None] + [TimingEvent() for _ in range(3)] + [TimingEvent() if w.n_shared else None, None]
+               for _ in range(args.steps)]
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -246,7 +275,7 @@ def main() -> int:
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for i in range(args.steps):
-        step({"stage_events": gemm_ev[i]})
+        step({"stage_events": [None if e is None else e.handle for e in gemm_ev[i]]})
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
