@@ -114,6 +114,39 @@ def test_forward_stage_events(name):
     _say("  stage ms", [round(t, 4) for t in stages])
 
 
+def test_forward_timing_only_stage_events():
+    """The bench's in-step GEMM events: HIP events created for timing only (no system-scope
+    fence), passed as raw handles at the W13 and W2 boundaries with the other boundaries null.
+    Recorded in order inside the forward (between ordinary events recorded just before and
+    after it), the two GEMM times are positive and fit in the forward, and no output bit
+    changes."""
+    import bench
+    import workloads as W
+    import harness as Hn
+    w = W.MIXTRAL_BF16.with_(T=512)
+    d = W.layer_inputs(w)
+    dv = Hn.to_dev(d)
+    out0, _ = Hn.run_forward(w, dv, trace=False)
+    cfg = Hn.config(w)
+    ws = torch.empty(M.moe_workspace_size(cfg, M.MOE_OP_FORWARD), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(out0)
+    wts = {k: dv.get(k) for k in Hn.WEIGHT_KEYS}
+    wts["logit_bias"] = None if dv.get("bias") is None else dv["bias"].to(DEV)
+    ev = [bench.TimingEvent() for _ in range(3)]  # after the alignment, after W13, after W2
+    before, after = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for rep in range(2):
+        before.record()
+        M.moe_forward(cfg, wts, dv["h"], dv["h"], out,
+                      {"stage_events": [None, None] + [e.handle for e in ev] + [None, None]}, ws)
+        after.record()
+        torch.cuda.synchronize()
+        w13, w2 = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+        whole = before.elapsed_time(after)
+        assert 0 < w13 and 0 < w2 and w13 + w2 <= whole, (w13, w2, whole)
+        assert torch.equal(out.view(torch.int16), out0.view(torch.int16))
+    _say("  timing-only events: W13 %.4f ms, W2 %.4f ms of %.4f" % (w13, w2, whole))
+
+
 @pytest.mark.parametrize("name", ["mixtral_bf16", "deepseekv3_fp8"])
 def test_forward_gemm_clock_stamps(name):
     """Trace clock stamps of the routed W13 and W2 launches: every persistent workgroup of a
