@@ -336,9 +336,20 @@ def run_forward(w, dv, trace=True):
     return out, tr
 
 
-@pytest.mark.parametrize("name", list(SMALL))
+# degenerate shapes of the layer: one expert (a plain SwiGLU FFN per token), every token on
+# every expert (k = N, margin +inf), one token over 64 experts (56 of them empty), and fp8
+# weights with two experts and a shared expert
+DEGENERATE = {
+    "single_expert": W.MIXTRAL_BF16.with_(T=70, H=256, N=1, k=1, I=256, B=16),
+    "k_equals_n": W.MIXTRAL_BF16.with_(T=100, H=256, N=4, k=4, I=256, B=8),
+    "one_token_64_experts": W.QWEN3MOE_BF16.with_(T=1, H=512, N=64, k=8, I=384, B=16),
+    "fp8_two_experts_shared": W.DEEPSEEKV3_FP8.with_(T=33, H=256, N=2, k=2, I=256, B=64),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL) + list(DEGENERATE))
 def test_forward_end_to_end(name):
-    w = SMALL[name]
+    w = SMALL[name] if name in SMALL else DEGENERATE[name]
     d, dv = inputs(w)
     _say("forward", name, w)
     out, tr = run_forward(w, dv)
