@@ -72,10 +72,14 @@ def _check_alignment(w, tr):
     return kept
 
 
-@pytest.mark.parametrize("name", ["switch_capacity_bf16", "mixtral_bf16", "qwen3moe_bf16"])
+@pytest.mark.parametrize("name", ["switch_capacity_bf16", "mixtral_bf16", "qwen3moe_bf16", "mixtral_bf16@65536"])
 def test_full_size_layer(name):
-    w = W.ALL[name]
-    _say("full size", name)
+    """The whole layer at a workload's full size (and the Mixtral shape at the largest T the
+    ABI accepts): routing, capacity and alignment of every token, outputs on a sample."""
+    base, _, t = name.partition("@")
+    w = W.ALL[base] if not t else W.ALL[base].with_(T=int(t))
+    name = base
+    _say("full size", w.name, w.T)
     d = W.layer_inputs(w, device=DEV)
     out, tr = Hn.run_forward(w, d)
     ids_ref, diff = _check_routing(w, d, tr)
