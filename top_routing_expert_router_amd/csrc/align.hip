@@ -54,6 +54,11 @@ __global__ __launch_bounds__(kThreads) void align_hist(const int32_t* __restrict
 // capacity, padded segment sizes, expert offsets (exclusive scan over experts in
 // order), sentinel pads inside each segment, the block -> expert map, the stats, and
 // the zeroed words.  Returns expert e's offset; *total_out = padded row count.
+// The pads and block entries of each expert are written by a group of G threads, G the
+// largest power of two with G N <= NT (at least 1), striding over its rows and blocks:
+// with few experts one thread walking each expert's up to B - 1 pads and its blocks was
+// most of the one-workgroup alignment's time; with as many experts as threads (G = 1)
+// that walk is the fastest.
 template <int NT>
 __device__ int layout_experts(int load, int invalid, int N, int B, int cap, int n_blocks,
                               int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
@@ -63,6 +68,7 @@ __device__ int layout_experts(int load, int invalid, int N, int B, int cap, int 
   constexpr int NW = NT / kWave;
   __shared__ int wave_tot[NW];
   __shared__ int red[NW][3];
+  __shared__ int seg[2][256 + 1];  // per expert: first row of its segment (seg[0][N] = total), kept rows
   const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
   for (int i = e; i < nzero; i += NT) zero[i] = 0;
   const int kept = e < N ? (cap < 0 ? load : min(load, cap)) : 0;
@@ -92,13 +98,22 @@ __device__ int layout_experts(int load, int invalid, int N, int B, int cap, int 
   const int off = base + incl - padded;
   if (e < N) {
     offsets[e] = off;
-    for (int i = off + kept; i < off + padded; ++i) sorted_ids[i] = sentinel;
-    for (int b = off / B; b < (off + padded) / B; ++b) block_expert[b] = e;
+    seg[0][e] = off;
+    seg[1][e] = kept;
     if (stats && !stats_ready) stats[e] = load;
   }
   if (e == 0) {
     offsets[N] = total;
     *num_padded = total;
+    seg[0][N] = total;
+  }
+  __syncthreads();
+  int G = 1;
+  while (2 * G * N <= NT) G *= 2;
+  for (int x = e / G; x < N; x += NT / G) {
+    const int o = seg[0][x], o1 = seg[0][x + 1], kp = seg[1][x], sub = e % G;
+    for (int i = o + kp + sub; i < o1; i += G) sorted_ids[i] = sentinel;
+    for (int b = o / B + sub; b < o1 / B; b += G) block_expert[b] = x;
   }
   for (int b = total / B + e; b < n_blocks; b += NT) block_expert[b] = -1;
   if (stats && e == 0) {

@@ -39,6 +39,16 @@ struct RouterUnroll {
 
 typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x8_t __attribute__((ext_vector_type(8)));
+// buffer resource word 3 for raw (untyped, stride 0) buffer loads on gfx9-family parts
+constexpr int kRawBufferFlags = 0x00020000;
+
+// 32 bytes at byte offset off + soff of a raw buffer, as 16 bf16 (two 16-byte loads)
+__device__ __forceinline__ bf16x16 load32(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
+  const u32x4_t lo = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
+  const u32x4_t hi = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, soff, 0);
+  return __builtin_bit_cast(bf16x16, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 // Top-k, gates and margin of one token from its N logits (global or LDS), by one
 // aligned group of L = topk_lanes(N) lanes; a wave ranks 64 / L tokens at once.
@@ -58,12 +68,24 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 // P = experts per lane actually used (ceil(N / L), at most kTopkPerLane): slots past it
 // hold no expert, so they are left out at compile time (topk_one picks P); the result is
 // the same for every P that covers N.
-template <int P, typename RowPtr>
-__device__ __forceinline__ void topk_one_p(RowPtr row, int t, int N, int k, int renormalize, int L,
+// L, P and the mode (plain, replay, scores) are compile-time: each kernel then holds only
+// the code of its own case.  A kernel that carried every case was ~50 KB of code, and the
+// first pass of each CU through it (every launch, after the expert GEMMs have filled the
+// instruction caches) cost about 2 us of the Mixtral-shape router's 13.
+enum : int { kTopkPlain = 0, kTopkReplay = 1, kTopkScores = 2 };
+__host__ __device__ constexpr int topk_mode(const int32_t* replay, const float* scores) {
+  return scores != nullptr ? kTopkScores : (replay != nullptr ? kTopkReplay : kTopkPlain);
+}
+// smallest of 1, 2, 4, 8 that is at least v (v <= 8)
+constexpr int topk_slots(int v) { return v <= 1 ? 1 : (v <= 2 ? 2 : (v <= 4 ? 4 : 8)); }
+
+template <int P, int L, int MODE, typename RowPtr>
+__device__ __forceinline__ void topk_one_p(RowPtr row, int t, int N, int k, int renormalize,
                                            int32_t* __restrict__ ids, float* __restrict__ gates,
                                            float* __restrict__ margin, const int32_t* __restrict__ replay,
                                            float* __restrict__ scores) {
   static_assert(P >= 1 && P <= kTopkPerLane, "experts per lane");
+  static_assert(L == 8 || L == 16 || L == 32, "lanes per token");
   const int lane = threadIdx.x & 63;
   const int g = lane & (L - 1), base = lane - g;
   float lv[P];
@@ -74,7 +96,7 @@ __device__ __forceinline__ void topk_one_p(RowPtr row, int t, int N, int k, int 
     lv[i] = e < N ? row[e] : 0.f;
     key[i] = e < N ? rank_key(lv[i], e) : 0ull;
   }
-  if (scores != nullptr) {
+  if constexpr (MODE == kTopkScores) {
     uint64_t best = key[0];
 #pragma unroll
     for (int i = 1; i < P; ++i) best = key[i] > best ? key[i] : best;
@@ -128,7 +150,7 @@ __device__ __forceinline__ void topk_one_p(RowPtr row, int t, int N, int k, int 
   const float l0 = sl[0];
   float w[8];
   float s = 0.f;
-  if (replay == nullptr) {
+  if constexpr (MODE != kTopkReplay) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       w[j] = 0.f;
@@ -174,7 +196,7 @@ __device__ __forceinline__ void topk_one_p(RowPtr row, int t, int N, int k, int 
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (j < k && g == j) {
-      if (replay == nullptr) ids[(size_t)t * k + j] = sid[j];
+      if constexpr (MODE != kTopkReplay) ids[(size_t)t * k + j] = sid[j];
       gates[(size_t)t * k + j] = w[j] / s;
     }
   }
@@ -187,20 +209,22 @@ __device__ __forceinline__ void topk_one_p(RowPtr row, int t, int N, int k, int 
   }
 }
 
-template <typename RowPtr>
-__device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int renormalize, int L,
+// P = the smallest of 1, 2, 4, 8 that covers N; the caller's N lies where that choice is
+// one of [PMIN, PMAX], so only those are compiled.
+template <int L, int PMIN, int PMAX, int MODE, typename RowPtr>
+__device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int renormalize,
                                          int32_t* __restrict__ ids, float* __restrict__ gates,
                                          float* __restrict__ margin, const int32_t* __restrict__ replay,
                                          float* __restrict__ scores) {
+  static_assert(PMIN <= PMAX && PMAX <= kTopkPerLane, "slot window");
   const int per = ceil_div(N, L);  // uniform
-  if (per <= 1)
-    topk_one_p<1>(row, t, N, k, renormalize, L, ids, gates, margin, replay, scores);
-  else if (per <= 2)
-    topk_one_p<2>(row, t, N, k, renormalize, L, ids, gates, margin, replay, scores);
-  else if (per <= 4)
-    topk_one_p<4>(row, t, N, k, renormalize, L, ids, gates, margin, replay, scores);
-  else
-    topk_one_p<kTopkPerLane>(row, t, N, k, renormalize, L, ids, gates, margin, replay, scores);
+  if constexpr (PMIN <= 1 && 1 < PMAX)
+    if (per <= 1) return topk_one_p<1, L, MODE>(row, t, N, k, renormalize, ids, gates, margin, replay, scores);
+  if constexpr (PMIN <= 2 && 2 < PMAX)
+    if (per <= 2) return topk_one_p<2, L, MODE>(row, t, N, k, renormalize, ids, gates, margin, replay, scores);
+  if constexpr (PMIN <= 4 && 4 < PMAX)
+    if (per <= 4) return topk_one_p<4, L, MODE>(row, t, N, k, renormalize, ids, gates, margin, replay, scores);
+  topk_one_p<PMAX, L, MODE>(row, t, N, k, renormalize, ids, gates, margin, replay, scores);
 }
 
 // bf16 router on MFMA 16x16x32, with top-k fused: D[expert][token] = sum_k W_g[expert][k] h[token][k].
@@ -209,7 +233,7 @@ __device__ __forceinline__ void topk_one(RowPtr row, int t, int N, int k, int re
 // (the first and second 8 elements of its 16).  Wave w accumulates chunks w, w+4, ...
 // in ascending order; the eight wave partials are added in wave order; nothing depends
 // on T or on the other tokens.
-template <int NSUB, int TB>
+template <int NSUB, int TB, int MODE, int P>
 __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __restrict__ h, const __bf16* __restrict__ wg,
                                                    const float* __restrict__ bias, float* __restrict__ logits,
                                                    int32_t* __restrict__ ids, float* __restrict__ gates,
@@ -219,17 +243,27 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
   constexpr int NP = NSUB * 16, TW = TB * kRouterTokens;
   __shared__ float part[kRouterWaves][NP][TW];
   __shared__ float lg[TW][NP + 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index made scalar: the chunk offsets of the buffer loads below are then
+  // scalar operands (a vector one turns every load into a waterfall loop)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * TW;
   const int col = lane & 15, kq = (lane >> 4) * 16;
-  // Columns past T and expert rows past N read row 0: their products land only in
-  // accumulator entries that are never written out, so no load needs a branch.
-  const __bf16* hrow[TB];
+  // Buffer loads: token columns past T and expert rows past N (the padding of the last
+  // 16-expert block) start at the buffer's end, so they read zeros without a memory
+  // request (bounds-checked loads never fault); their accumulator entries are never
+  // written out.
+  const uint32_t hbytes = (uint32_t)T * H * 2u, wbytes = (uint32_t)N * H * 2u;  // T H < 2^31
+  const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc((void*)h, (short)0, (int)hbytes, kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)wg, (short)0, (int)wbytes, kRawBufferFlags);
+  uint32_t hoff[TB];
 #pragma unroll
-  for (int b = 0; b < TB; ++b) hrow[b] = h + (size_t)(t0 + b * 16 + col < T ? t0 + b * 16 + col : 0) * H + kq;
-  const __bf16* wrow[NSUB];
+  for (int b = 0; b < TB; ++b) {
+    const int t = t0 + b * 16 + col;
+    hoff[b] = t < T ? ((uint32_t)t * H + kq) * 2u : hbytes;
+  }
+  uint32_t woff[NSUB];
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) wrow[s] = wg + (size_t)(s * 16 + col < N ? s * 16 + col : 0) * H + kq;
+  for (int s = 0; s < NSUB; ++s) woff[s] = s * 16 + col < N ? ((uint32_t)(s * 16 + col) * H + kq) * 2u : wbytes;
   const int nchunks = H / kChunkK;
 
   f32x4 acc[NSUB][TB];
@@ -257,14 +291,14 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
     for (int u = 0; u < kUnroll; ++u) {
       const int c = min(c0 + u * kRouterWaves, nchunks - 1);
 #pragma unroll
-      for (int b = 0; b < TB; ++b) hv[u][b] = *reinterpret_cast<const bf16x16*>(hrow[b] + c * kChunkK);
+      for (int b = 0; b < TB; ++b) hv[u][b] = load32(hrs, hoff[b], c * kChunkK * 2);
     }
     bf16x16 wv[kUnroll][NSUB];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int c = min(c0 + u * kRouterWaves, nchunks - 1);
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) wv[u][s] = *reinterpret_cast<const bf16x16*>(wrow[s] + c * kChunkK);
+      for (int s = 0; s < NSUB; ++s) wv[u][s] = load32(wrs, woff[s], c * kChunkK * 2);
     }
     // without this barrier the compiler moves each weight load next to the MFMAs that
     // use it and waits for it there, one load in flight per wave
@@ -306,11 +340,13 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
     if (logits && t0 + t < T) logits[(size_t)(t0 + t) * N + e] = v;  // nullable: no logits out
   }
   __syncthreads();
-  // fused top-k: one group of L lanes per token, 64 / L tokens per wave
-  const int L = topk_lanes(N);
-  const int per_wave = kWave / L;
+  // fused top-k: one group of L lanes per token, 64 / L tokens per wave.  The launch
+  // takes NSUB = ceil(N / 16), so L = topk_lanes(N) follows from NSUB, and P =
+  // topk_slots(ceil(N / L)) (the launch picks the kernel).
+  constexpr int L = NSUB <= 4 ? 8 : 16;
+  constexpr int per_wave = kWave / L;
   for (int t = wave * per_wave + lane / L; t < TW; t += kRouterWaves * per_wave)
-    if (t0 + t < T) topk_one(&lg[t][0], t0 + t, N, k, renormalize, L, ids, gates, margin, replay, scores);
+    if (t0 + t < T) topk_one_p<P, L, MODE>(&lg[t][0], t0 + t, N, k, renormalize, ids, gates, margin, replay, scores);
 }
 
 // bf16 router for many experts (more than 128), top-k fused.  With one 16-token
@@ -324,7 +360,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
 // 16-wide steps, then the bias is added: the order depends only on H, not on T or TW.
 // LDS rows are 128 B (8 chunks of 16 B), chunk c of row r stored at c ^ ((r >> 1) & 7):
 // the 32-row fragment reads then hit all 64 banks.
-template <int NP, int TW, int NW>
+template <int NP, int TW, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64) void router_bf16_wide(const __bf16* __restrict__ h, const __bf16* __restrict__ wg,
                                                         const float* __restrict__ bias, float* __restrict__ logits,
                                                         int32_t* __restrict__ ids, float* __restrict__ gates,
@@ -451,10 +487,14 @@ __global__ __launch_bounds__(NW * 64) void router_bf16_wide(const __bf16* __rest
       if (t0 + t < T) logits[(size_t)(t0 + t) * N + e] = lg[t * (NP + 1) + e];
     }
   }
-  const int L = topk_lanes(N);  // one group of L lanes per token, 64 / L tokens per wave
-  const int per_wave = kWave / L;
+  // one group of L lanes per token, 64 / L tokens per wave; launched for 128 < N <= NP = 256
+  // only, so L = topk_lanes(N) = 32 and 5 to 8 experts per lane
+  static_assert(NP == 256, "lanes per token below assume 128 < N <= 256");
+  constexpr int L = 32;
+  constexpr int per_wave = kWave / L;
   for (int t = wave * per_wave + (tid & 63) / L; t < TW; t += NW * per_wave)
-    if (t0 + t < T) topk_one(lg + t * (NP + 1), t0 + t, N, k, renormalize, L, ids, gates, margin, replay, scores);
+    if (t0 + t < T)
+      topk_one<L, 8, 8, MODE>(lg + t * (NP + 1), t0 + t, N, k, renormalize, ids, gates, margin, replay, scores);
 }
 
 // fp32 projection: one thread per (token, expert), fmaf over H in ascending order.
@@ -473,29 +513,55 @@ __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict
 }
 
 // Standalone top-k over stored logits (fp32 path and routing from given logits):
-// 256 threads, one group of L lanes per token, 256 / L tokens per workgroup.
+// 256 threads, one group of L = topk_lanes(N) lanes per token, 256 / L tokens per
+// workgroup.  L = 8 covers 1 to 64 experts (1 to 8 per lane); 16 and 32 take 65 to 128
+// and 129 to 256 experts, 5 to 8 per lane.
+template <int L, int MODE>
 __global__ __launch_bounds__(256) void topk_gates(const float* __restrict__ logits, int32_t* __restrict__ ids,
                                                    float* __restrict__ gates, float* __restrict__ margin,
                                                    int T, int N, int k, int renormalize,
                                                    const int32_t* __restrict__ replay, float* __restrict__ scores) {
-  const int L = topk_lanes(N);
   const int t = blockIdx.x * (256 / L) + threadIdx.x / L;
   if (t >= T) return;
-  topk_one(logits + (size_t)t * N, t, N, k, renormalize, L, ids, gates, margin, replay, scores);
+  topk_one<L, L == 8 ? 1 : 8, 8, MODE>(logits + (size_t)t * N, t, N, k, renormalize, ids, gates, margin, replay,
+                                       scores);
 }
 
-template <int NSUB>
+template <int NSUB, int MODE>
 hipError_t launch_router_bf16(const moe_config& c, const void* h, const void* wg, const float* bias, float* logits,
                               int32_t* ids, float* gates, float* margin, hipStream_t s, const int32_t* replay,
                               float* scores) {
   constexpr int TB = kRouterTB<NSUB>;
+  constexpr int L = NSUB <= 4 ? 8 : 16;
+  // the slots per lane for N in (16 (NSUB - 1), 16 NSUB]: two choices for NSUB = 1, one above
+  constexpr int PMIN = topk_slots((16 * (NSUB - 1) + L) / L), PMAX = topk_slots((16 * NSUB + L - 1) / L);
+  static_assert(PMIN == PMAX || (NSUB == 1 && PMIN == 1 && PMAX == 2), "slot choices");
   dim3 grid(ceil_div(c.T, TB * kRouterTokens));
-  router_bf16<NSUB, TB><<<grid, kRouterThreads, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits, ids, gates, margin, c.T,
-                                         c.H, c.N, c.k, c.renormalize, replay, scores);
+  if (PMIN != PMAX && topk_slots(ceil_div(c.N, L)) == PMIN)
+    router_bf16<NSUB, TB, MODE, PMIN><<<grid, kRouterThreads, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits,
+                                                                     ids, gates, margin, c.T, c.H, c.N, c.k,
+                                                                     c.renormalize, replay, scores);
+  else
+    router_bf16<NSUB, TB, MODE, PMAX><<<grid, kRouterThreads, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits,
+                                                                     ids, gates, margin, c.T, c.H, c.N, c.k,
+                                                                     c.renormalize, replay, scores);
   return hipGetLastError();
 }
+template <int NSUB>
+hipError_t launch_router_bf16(const moe_config& c, const void* h, const void* wg, const float* bias, float* logits,
+                              int32_t* ids, float* gates, float* margin, hipStream_t s, const int32_t* replay,
+                              float* scores) {
+  switch (topk_mode(replay, scores)) {
+    case kTopkScores:
+      return launch_router_bf16<NSUB, kTopkScores>(c, h, wg, bias, logits, ids, gates, margin, s, replay, scores);
+    case kTopkReplay:
+      return launch_router_bf16<NSUB, kTopkReplay>(c, h, wg, bias, logits, ids, gates, margin, s, replay, scores);
+    default:
+      return launch_router_bf16<NSUB, kTopkPlain>(c, h, wg, bias, logits, ids, gates, margin, s, replay, scores);
+  }
+}
 
-template <int NP>
+template <int NP, int MODE>
 hipError_t launch_router_wide(const moe_config& c, const void* h, const void* wg, const float* bias, float* logits,
                               int32_t* ids, float* gates, float* margin, hipStream_t s, const int32_t* replay,
                               float* scores) {
@@ -505,11 +571,11 @@ hipError_t launch_router_wide(const moe_config& c, const void* h, const void* wg
   // 64 tokens per workgroup when that still gives every CU a workgroup, else 32
   constexpr int NW = 8;
   if (ceil_div(c.T, 64) >= cus)
-    router_bf16_wide<NP, 64, NW><<<ceil_div(c.T, 64), NW * 64, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits,
+    router_bf16_wide<NP, 64, NW, MODE><<<ceil_div(c.T, 64), NW * 64, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits,
                                                                         ids, gates, margin, c.T, c.H, c.N, c.k,
                                                                         c.renormalize, replay, scores);
   else
-    router_bf16_wide<NP, 32, NW><<<ceil_div(c.T, 32), NW * 64, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits,
+    router_bf16_wide<NP, 32, NW, MODE><<<ceil_div(c.T, 32), NW * 64, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits,
                                                                         ids, gates, margin, c.T, c.H, c.N, c.k,
                                                                         c.renormalize, replay, scores);
   return hipGetLastError();
@@ -530,7 +596,16 @@ hipError_t launch_router(const moe_config& c, const void* h, const void* w_gate,
   }
   // more than 128 experts: W_g staged once per 64 tokens (for up to 128 the 16-token
   // kernel below measured faster)
-  if (c.N > 128) return launch_router_wide<256>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
+  if (c.N > 128) {
+    switch (topk_mode(replay, scores)) {
+      case kTopkScores:
+        return launch_router_wide<256, kTopkScores>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
+      case kTopkReplay:
+        return launch_router_wide<256, kTopkReplay>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
+      default:
+        return launch_router_wide<256, kTopkPlain>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
+    }
+  }
 #define MOE_ROUTER_CASE(n) \
   case n:                  \
     return launch_router_bf16<n>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
@@ -544,8 +619,25 @@ hipError_t launch_router(const moe_config& c, const void* h, const void* w_gate,
 
 hipError_t launch_topk(const moe_config& c, const float* logits, int32_t* ids, float* gates, float* margin,
                        hipStream_t s, const int32_t* replay, float* scores) {
-  dim3 grid(ceil_div(c.T, 256 / topk_lanes(c.N)));
-  topk_gates<<<grid, 256, 0, s>>>(logits, ids, gates, margin, c.T, c.N, c.k, c.renormalize, replay, scores);
+  const int L = topk_lanes(c.N);
+  dim3 grid(ceil_div(c.T, 256 / L));
+  auto go = [&](auto lanes, auto mode) {
+    topk_gates<decltype(lanes)::value, decltype(mode)::value><<<grid, 256, 0, s>>>(logits, ids, gates, margin, c.T, c.N,
+                                                                                 c.k, c.renormalize, replay, scores);
+  };
+  auto by_mode = [&](auto lanes) {
+    switch (topk_mode(replay, scores)) {
+      case kTopkScores: go(lanes, std::integral_constant<int, kTopkScores>{}); break;
+      case kTopkReplay: go(lanes, std::integral_constant<int, kTopkReplay>{}); break;
+      default: go(lanes, std::integral_constant<int, kTopkPlain>{}); break;
+    }
+  };
+  if (L == 8)
+    by_mode(std::integral_constant<int, 8>{});
+  else if (L == 16)
+    by_mode(std::integral_constant<int, 16>{});
+  else
+    by_mode(std::integral_constant<int, 32>{});
   return hipGetLastError();
 }
 
