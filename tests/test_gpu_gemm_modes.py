@@ -1,11 +1,13 @@
 """Tile modes of the grouped down-projection GEMM give the same bits.
 
 On the Mixtral-shaped layer the down projection makes one to four rounds of 256x256
-tiles over the CUs, so an expert's last m-tile of at most 128 rows runs as two narrow
-tiles (128 weight rows each, 128-deep stages), scheduled after the full-height tiles.
-Every output element is still one MFMA chain over K in ascending 16-wide steps, so each
-y row must equal, bit for bit, the same row computed in a problem small enough that no
-narrow tile is used (one expert's rows in identity mode: full, half or quarter tiles).
+tiles over the CUs, so an expert's last m-tile of at most 128 rows runs as micro tiles
+(up to 64 rows x 64 weight rows, 128-deep stages in a four-buffer ring: four of them for
+a last m-tile of up to 64 rows, eight for 65 to 128), scheduled after the full-height
+tiles.  Every output element is still one MFMA chain over K in ascending 16-wide steps,
+so each y row must equal, bit for bit, the same row computed in a problem small enough
+that no micro tile is used (one expert's rows in identity mode: full, half or quarter
+tiles).
 """
 import sys
 
@@ -31,13 +33,13 @@ def _gpu():
     M.lib()
 
 
-def test_w2_narrow_tiles_match_standard_tiles():
+def test_w2_micro_tiles_match_standard_tiles():
     T, H, N, k, I, B = 4096, 4096, 8, 2, 14336, 64
-    # expert loads: last m-tiles of 64 (expert 1) and 128 rows (expert 2) become narrow
-    # tiles; 1000 and 952 leave padded, partly empty last tiles of 256 and 192 rows
+    # expert loads: last m-tiles of 64 (expert 1) and 128 rows (expert 2) become four and
+    # eight micro tiles per weight n-tile; 1000 and 952 leave padded, partly empty last tiles of 256 and 192 rows
     loads = [1024, 1088, 1152, 1024, 1000, 1000, 952, 952]
     assert sum(loads) == T * k
-    _say("w2 narrow tiles vs standard tiles, loads", loads)
+    _say("w2 micro tiles vs standard tiles, loads", loads)
     g = torch.Generator().manual_seed(5)
     perm = torch.randperm(T * k, generator=g).numpy()
     cfg = M.make_config(T, H, N, k, I, B)
@@ -61,7 +63,7 @@ def test_w2_narrow_tiles_match_standard_tiles():
     checked = 0
     for e, n in enumerate(loads):
         seg = -(-n // B) * B
-        # one expert's padded rows alone, identity rows: at most 5 x 16 tiles, no narrow tiles
+        # one expert's padded rows alone, identity rows: at most 5 x 16 tiles, no micro tiles
         ce = M.make_config(seg, H, 1, 1, I, B)
         ye = torch.empty(seg, H, dtype=torch.bfloat16, device=DEV)
         M.moe_expert_down(ce, act[offsets[e]:offsets[e] + seg].contiguous(), None, None, w2[e:e + 1].contiguous(),

@@ -203,10 +203,10 @@ def _oracle_alignment(w, seed=0):
 
 # H an odd multiple of 128: the W2 tiles of the last weight n-tile are half past H, and the
 # epilogue must store none of those columns (each chunk past H is staged, not stored); with
-# I % 256 == 0 and one to four rounds of W2 tiles the narrow down-projection kernel runs too
+# I % 256 == 0 and one to four rounds of W2 tiles the micro-tile down-projection kernel runs too
 ODD_H = {
     "odd_h_bf16": W.MIXTRAL_BF16.with_(T=300, H=640, I=384),
-    "odd_h_bf16_narrow": W.MIXTRAL_BF16.with_(T=12000, H=640, I=512),
+    "odd_h_bf16_micro": W.MIXTRAL_BF16.with_(T=12000, H=640, I=512),
     "odd_h_fp8": W.DEEPSEEKV3_FP8.with_(T=200, N=24, H=896, I=384),
 }
 

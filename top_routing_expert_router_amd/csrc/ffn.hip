@@ -27,7 +27,7 @@
 //   register-local epilogue; W2 writes each row straight to its route's y row;
 //   M tiles are 256-row slices of one expert's padded segment (a fixed constant,
 //   decoupled from B), run in full, half or quarter mode by their valid rows; W2
-//   has narrow tiles (run_tile_narrow) for its small last m-tiles; workgroups map
+//   has micro tiles (run_tile_micro) for its small last m-tiles; workgroups map
 //   to XCDs so each XCD walks a contiguous run of (n-tile group, m-tile) pairs and
 //   shares weight tiles in its L2.
 // fp8 weights: E4M3FN codes are loaded into registers three MFMA steps ahead, decoded
@@ -71,8 +71,8 @@ struct FfnArgs {
   int ntiles;
   int32_t* work;          // nullable: 8 zeroed per-XCD tile counters (dynamic schedule)
   int dest_is_row;        // W2: 1 = y row p (expert choice: sorted holds token ids), 0 = y row sorted[p]
-  int narrow;             // W2, bf16 weights, K % 256 == 0, one to four rounds of tiles: small last
-                          // m-tiles run as two narrow tiles, after all full-height tiles
+  int micro;              // W2, bf16 weights, K % 256 == 0, one to four rounds of tiles: small last
+                          // m-tiles run as micro tiles, after all full-height tiles
   void* w13_out;          // W13 only, nullable: [rows, 2I] gate then up projection, act dtype
   uint64_t* clk;          // nullable: per workgroup, shader-clock and real-time counters at its
                           // start and its end (4 words at 4 * blockIdx.x)
@@ -96,7 +96,7 @@ __device__ __forceinline__ void clock_stamp(uint64_t* p) {
 // the bank half, rows 2m.. in the chunk).
 __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * (BK * 2) + (swz_chunk(row, chunk) << 4); }
-// Narrow tiles: 128-deep stages, rows of 256 B (16 chunks); chunk index XORed with
+// Micro tiles: 128-deep stages, rows of 256 B (16 chunks); chunk index XORed with
 // row & 15, so the 16 consecutive rows a 16-lane group reads at one logical chunk
 // land in 16 different chunks, i.e. all 64 banks.
 __device__ __forceinline__ int swzn_chunk(int row, int chunk) { return chunk ^ (row & 15); }
@@ -106,15 +106,18 @@ __device__ __forceinline__ int swzn(int row, int chunk) { return row * (BK * 4) 
 // e (beg[N] = end of the last).  Each expert's padded segment is cut into
 // ceil(len / BM) m-tiles; m-slots are numbered in expert order, big0[e] = m-slots of
 // the experts before e (big0[N] = all of them), so an expert's m-tiles stay together
-// and share its weight tiles in L2.  Narrow kernels: a last m-tile of at most BM / 2
-// rows is "small": it takes two m-slots (one per half of the weight n-tile), numbered
-// after all other m-tiles (sm0[e] = small m-slots before e), so within each raster
-// group the short tiles come last and fill the end of the schedule instead of pushing
-// full tiles into an extra round.  Identity rows: one expert, rows [0, T).
+// and share its weight tiles in L2.  Micro-tile kernels: a last m-tile of at most BM / 2
+// rows is "small": it runs as micro tiles of up to 64 of its rows and a quarter (64
+// rows) of the weight n-tile, so it takes four m-slots (up to 64 rows) or eight (65 to
+// 128 rows: row half j / 4, weight quarter j % 4), numbered after all other m-tiles
+// (sm0[e] = small m-slots before e), so within each raster group the short tiles come
+// last and fill the end of the schedule instead of pushing full tiles into an extra
+// round.  Identity rows: one expert, rows [0, T).
 constexpr int kMaxExperts = 256;
 constexpr int kEpiWaveBytes = 32 * (64 * 2 + 16);
+constexpr int kMicroB = 16384;  // micro tiles: byte offset of the weight rows in a stage buffer
 
-template <bool NARROW>
+template <bool MICRO>
 __device__ void build_tile_table(const FfnArgs& a, int* beg, int* big0, int* sm0) {
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
@@ -128,14 +131,15 @@ __device__ void build_tile_table(const FfnArgs& a, int* beg, int* big0, int* sm0
       const int end = !ok ? 0 : (a.sorted == nullptr ? a.T : a.offsets[ee + 1]);
       const int len = end - b[i];
       const int nf = ok ? ceil_div(len, BM) : 0;
-      const bool small = NARROW && nf > 0 && len - (nf - 1) * BM <= BM / 2;
+      const int last = len - (nf - 1) * BM;  // rows of the last m-tile (nf > 0)
+      const bool small = MICRO && nf > 0 && last <= BM / 2;
       nb[i] = small ? nf - 1 : nf;
-      ns[i] = small ? 2 : 0;
+      ns[i] = small ? (last > BM / 4 ? 8 : 4) : 0;
       sb += nb[i];
       ss += ns[i];
     }
     const int ib = wave_incl_scan_i32(sb);
-    const int is = NARROW ? wave_incl_scan_i32(ss) : 0;
+    const int is = MICRO ? wave_incl_scan_i32(ss) : 0;
     int pb = ib - sb, ps = is - ss;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -143,7 +147,7 @@ __device__ void build_tile_table(const FfnArgs& a, int* beg, int* big0, int* sm0
       if (ee < a.N) {
         beg[ee] = b[i];
         big0[ee] = pb;
-        if (NARROW) sm0[ee] = ps;
+        if (MICRO) sm0[ee] = ps;
       }
       pb += nb[i];
       ps += ns[i];
@@ -151,7 +155,7 @@ __device__ void build_tile_table(const FfnArgs& a, int* beg, int* big0, int* sm0
     if (lane == kWave - 1) {
       beg[a.N] = a.sorted == nullptr ? a.T : a.offsets[a.N];
       big0[a.N] = ib;
-      if (NARROW) sm0[a.N] = is;
+      if (MICRO) sm0[a.N] = is;
     }
   }
   __syncthreads();
@@ -192,12 +196,36 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const void* w, int
 }
 
 // One output tile: expert e, padded rows [p0, p1), weight n-tile nt; sub = -1, or the
-// half (0, 1) of the n-tile's weight rows a narrow tile covers.
+// quarter (sub & 3) of the n-tile's weight rows a micro tile covers.
 struct Tile {
   int e, p0, p1, nt, sub;
 };
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// LDS byte address of a shared-memory array (its address-space cast folds to a constant)
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
+// One global -> LDS copy (buffer_load_dwordx4 ... lds): lane L's 16 bytes at buffer offset
+// voff + soff land at LDS byte address m0 + 16 L.  Written as inline assembly, so that the
+// only waits for it are the kernel's own: the compiler's wait-count pass does not tell
+// apart the LDS arrays the builtin form writes once several stages of copies are in
+// flight, and made every fragment read wait for all of them.  The copy reads M0 one wait
+// state after the scalar write (s_nop 0).
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t m0, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(r), "s"(soff)
+               : "m0");
+}
+
+// Workgroup barrier without a memory fence: the caller has already waited for what the
+// other waves need (__syncthreads() would also wait for every LDS copy in flight, which
+// its workgroup fence counts as LDS writes).  The memory clobber keeps the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Barrier that publishes LDS written by global->LDS DMA.  The DMA is counted by
 // vmcnt, and a workgroup fence does not wait for it (the compiler treats it as a
@@ -234,14 +262,14 @@ __device__ __forceinline__ void lds_barrier() {
 //  - quarter (R <= 64): all 4 waves on the same 64 rows, each with 64 weight rows.
 // An output element's K order is the same in every mode (one MFMA chain over K in
 // ascending 16-wide steps), so the mode changes no output bit.
-// NARROW (W2, bf16 weights only): small last m-tiles run as narrow tiles; see
-// run_tile_narrow.  A kernel of its own, so the others keep their register allocation.
+// MICRO (W2, bf16 weights only): small last m-tiles run as micro tiles; see
+// run_tile_micro.  A kernel of its own, so the others keep their register allocation.
 // W13OUT (W13 only): the epilogue also stores the gate and up projections, each rounded
 // from its fp32 accumulator, to a.w13_out (the pre-activation surface); an instantiation
 // of its own, so the kernel the layer runs is unchanged.
-template <int MODE, bool FP8, bool NARROW, bool W13OUT = false>
+template <int MODE, bool FP8, bool MICRO, bool W13OUT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffn_gemm_bf16(FfnArgs a) {
-  static_assert(!NARROW || (MODE == 1 && !FP8), "narrow tiles: W2 with bf16 weights only");
+  static_assert(!MICRO || (MODE == 1 && !FP8), "micro tiles: W2 with bf16 weights only");
   static_assert(!W13OUT || MODE == 0, "the pre-activation surface is the W13 GEMM's");
   static_assert(BN / 32 + 2 == 10, "fp8_barrier leaves BJ + 2 loads in flight");
   constexpr int TBN = BN;           // weight rows per tile
@@ -252,7 +280,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ __attribute__((aligned(16))) char sB0[TBN * BK * 2];
   __shared__ __attribute__((aligned(16))) char sA1[BM * BK * 2];
   __shared__ __attribute__((aligned(16))) char sB1[TBN * BK * 2];
-  __shared__ int t_beg[kMaxExperts + 1], t_big0[kMaxExperts + 1], t_sm0[NARROW ? kMaxExperts + 1 : 1];
+  __shared__ int t_beg[kMaxExperts + 1], t_big0[kMaxExperts + 1], t_sm0[MICRO ? kMaxExperts + 1 : 1];
   // each wave's epilogue staging area: 32 rows x up to 64 output columns (bf16), rows
   // padded by 16 bytes so that the staging writes and the row reads spread over the banks
   __shared__ __attribute__((aligned(16))) char s_epi[4 * kEpiWaveBytes];
@@ -266,12 +294,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // XCD's counter -- a workgroup claims its next tile when it starts the current
   // one, so tiles of unequal cost (full and half) balance across the XCD.
   if (a.clk != nullptr && threadIdx.x == 0) clock_stamp(a.clk + 4 * blockIdx.x);
-  build_tile_table<NARROW>(a, t_beg, t_big0, t_sm0);
+  build_tile_table<MICRO>(a, t_beg, t_big0, t_sm0);
   // values read from the table are the same in every lane; readfirstlane makes them
   // scalar, so the buffer resources built from them stay in SGPRs
-  constexpr bool kNarrow = NARROW;
+  constexpr bool kMicro = MICRO;
   const int total_big = __builtin_amdgcn_readfirstlane(t_big0[a.N]);
-  const int total_m = kNarrow ? total_big + __builtin_amdgcn_readfirstlane(t_sm0[a.N]) : total_big;
+  const int total_m = kMicro ? total_big + __builtin_amdgcn_readfirstlane(t_sm0[a.N]) : total_big;
   const int G = total_m * a.ntiles;
   const int per_xcd = ceil_div(G, 8);
   const int slots = gridDim.x >> 3;
@@ -298,7 +326,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int idx = l - group * kGroupN * total_m;
     const int m = idx / gsize;
     t.nt = gn0 + idx % gsize;
-    const bool big = !kNarrow || m < total_big;
+    const bool big = !kMicro || m < total_big;
     const int* pre = big ? t_big0 : t_sm0;
     const int mm = big ? m : m - total_big;
     int lo = 0, hi = a.N;  // last expert e with pre[e] <= mm (experts without such slots are skipped)
@@ -308,17 +336,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
     t.e = __builtin_amdgcn_readfirstlane(lo);
     const int j = mm - pre[lo], len = t_beg[lo + 1] - t_beg[lo], nf = ceil_div(len, BM);
-    // a big slot is m-tile j; a small slot is half j of the last m-tile
-    t.sub = __builtin_amdgcn_readfirstlane(!big && kNarrow ? j : -1);
-    t.p0 = __builtin_amdgcn_readfirstlane(t_beg[lo] + (big ? j : nf - 1) * BM);
-    t.p1 = __builtin_amdgcn_readfirstlane(min(min(t_beg[lo + 1], t.p0 + BM), a.rows));
+    // a big slot is m-tile j; a small slot j is row half j / 4 and weight quarter j % 4 of
+    // the last m-tile
+    t.sub = __builtin_amdgcn_readfirstlane(!big && kMicro ? j : -1);
+    const int mrow = big ? j * BM : (nf - 1) * BM + (j >> 2) * (BM / 4);
+    t.p0 = __builtin_amdgcn_readfirstlane(t_beg[lo] + mrow);
+    t.p1 = __builtin_amdgcn_readfirstlane(min(min(t_beg[lo + 1], t.p0 + (big ? BM : BM / 4)), a.rows));
   };
   // tile mode: the activation rows it covers, 256 (full), 128 (half) or 64 (quarter);
-  // narrow tiles (128 weight rows, 128-deep stages) add 1: 129 or 65
+  // micro tiles (64 weight rows, 128-deep stages, up to 64 rows): 65
   auto tile_rows = [&](const Tile& t) {
     const int r = __builtin_amdgcn_readfirstlane(t.p1 - t.p0);
     const int rows = r <= BM / 4 ? BM / 4 : (r <= BM / 2 ? BM / 2 : BM);
-    return kNarrow && __builtin_amdgcn_readfirstlane(t.sub) >= 0 ? rows + 1 : rows;
+    return kMicro && __builtin_amdgcn_readfirstlane(t.sub) >= 0 ? BM / 4 + 1 : rows;
   };
   Tile cur;
   decode(lid, cur);
@@ -410,20 +440,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   };
   auto setup = [&](const Tile& t) {
     const int rows = tile_rows(t);
-    if (kNarrow && (rows & 1)) {
-      // narrow (W2): A rows [wave * R/4, +R/4) in R/16 DMAs of 4 rows; weight rows
-      // [32 wave, +32) of the tile's half in 8 DMAs.  Lane L lands in physical chunk
-      // L % 16 of row L / 16 of its group and fetches the logical chunk stored there.
-      const int R = rows - 1;
+    if (kMicro && (rows & 1)) {
+      // micro (W2): activation rows [16 wave, +16) of the tile's 64 and weight rows [16 wave,
+      // +16) of its quarter, each in 4 DMAs of 4 rows.  Lane L lands in physical chunk L % 16
+      // of row L / 16 of its group and fetches the logical chunk stored there.  Rows past the
+      // tile read its first row (never stored); weight rows past H read row 0 (a column past H
+      // is never stored either).
       const int pc = lane & 15, gr = lane >> 4;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int ar = wave * (R / 4) + j * 4 + gr;
-        const unsigned row = (j < R / 16 && t.p0 + ar < t.p1) ? (unsigned)ar : 0u;
-        aoff[j] = (row * (unsigned)K + swzn_chunk(ar, pc) * 8) * 2u;
-        const int br = wave * 32 + j * 4 + gr;
-        const int r = t.nt * TBN + t.sub * (TBN / 2) + br;
-        boff[j] = ((unsigned)(r < a.H ? r : 0) * (unsigned)K + swzn_chunk(br, pc) * 8) * 2u;
+      for (int j = 0; j < 4; ++j) {
+        const int r = wave * 16 + j * 4 + gr;
+        const unsigned row = t.p0 + r < t.p1 ? (unsigned)r : 0u;
+        aoff[j] = (row * (unsigned)K + swzn_chunk(r, pc) * 8) * 2u;
+        const int wr = t.nt * TBN + (t.sub & 3) * (TBN / 4) + r;
+        boff[j] = ((unsigned)(wr < a.H ? wr : 0) * (unsigned)K + swzn_chunk(r, pc) * 8) * 2u;
       }
       return;
     }
@@ -466,36 +496,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     issue_part(rows_tag, t, sA, sB, k0, 0);
     issue_part(rows_tag, t, sA, sB, k0, 1);
   };
-  // narrow tiles: part 0 = the R/16 activation DMAs, part 1 = the 8 weight DMAs, 1 KB each
-  auto issue_part_narrow = [&](auto rows_tag, const Tile& t, char* sA, char* sB, int k0, int part) {
-    constexpr int NJ = decltype(rows_tag)::value / 16;
+  // micro tiles: one 128-deep stage (K columns [k0, k0 + 128)) into the 32 KB buffer dst:
+  // the 64 activation rows at byte 0, the 64 weight rows at 16 KB; 4 + 4 DMAs of 1 KB per
+  // wave
+  auto issue_micro = [&](const Tile& t, char* dst, int k0) {
     const __amdgpu_buffer_rsrc_t rsrcA = act_rsrc<MODE>(X, a.T, K, t.p0, t.p1);
     const __amdgpu_buffer_rsrc_t rsrcB = weight_rsrc<FP8>(a.w, t.e, WR, K);
-    if (part == 0) {
+    const uint32_t base = lds_addr(dst) + wave * 4 * 1024;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcA, LDS_PTR(sA + (wave * NJ + j) * 1024), 16, aoff[j], k0 * 2, 0, 0);
-    } else {
+    for (int j = 0; j < 4; ++j) lds_copy16(rsrcA, base + j * 1024, aoff[j], k0 * 2);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcB, LDS_PTR(sB + (wave * 8 + j) * 1024), 16, boff[j], k0 * 2, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j) lds_copy16(rsrcB, base + kMicroB + j * 1024, boff[j], k0 * 2);
   };
   // the next tile's first copies (its stage 0 or 1), in its own mode (outside any
-  // scheduled region)
+  // scheduled region); a micro tile issues its own first stages
   auto issue_loads_for = [&](const Tile& t, char* sA, char* sB, int stage) {
     const int rows = tile_rows(t);
-    if constexpr (kNarrow) {
-      if (rows == BM / 4 + 1) {
-        issue_part_narrow(std::integral_constant<int, BM / 4>{}, t, sA, sB, stage * 2 * BK, 0);
-        issue_part_narrow(std::integral_constant<int, BM / 4>{}, t, sA, sB, stage * 2 * BK, 1);
-        return;
-      }
-      if (rows == BM / 2 + 1) {
-        issue_part_narrow(std::integral_constant<int, BM / 2>{}, t, sA, sB, stage * 2 * BK, 0);
-        issue_part_narrow(std::integral_constant<int, BM / 2>{}, t, sA, sB, stage * 2 * BK, 1);
-        return;
-      }
+    if constexpr (kMicro) {
+      if (rows & 1) return;
     }
     auto go = [&](auto rows_tag) { issue_loads(rows_tag, t, sA, sB, stage * BK); };
     if (rows == BM / 4)
@@ -848,93 +866,71 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
   };
 
-  // ---- a narrow tile (W2, bf16 weights): R = 64 or 128 activation rows x one half
-  // (128 rows) of the weight n-tile, in 128-deep stages.  Small m-tiles are latency
-  // bound (a stage's copies have one stage of compute to arrive); a narrow tile has
-  // half the stages of the tile it replaces, and its two halves run on two CUs.  Wave
-  // w: weight rows [32 w, +32), all R rows.  Same K order per output element as every
-  // other mode (one MFMA chain over K in ascending 16-wide steps): no bit changes.
-  auto run_tile_narrow = [&](auto rows_tag, const Tile& t, bool& more, Tile& nxt) {
-    constexpr int R = decltype(rows_tag)::value;
-    constexpr int MSUB = R / 32;        // 32-row activation sub-tiles per wave
-    constexpr int NJ = R / 16;          // activation DMAs per wave and stage
-    constexpr int KS = 2 * BK;          // stage depth
+  // ---- a micro tile (W2, bf16 weights): up to 64 activation rows x one quarter (64 rows)
+  // of the weight n-tile, in 128-deep stages (32 KB: activation rows, then weight rows).
+  // A small m-tile's K loop is latency-bound: with two stages its copies had one stage of
+  // compute to arrive.  A micro tile's stages rotate through all four LDS arrays (stage s
+  // in buffer s % 4), so the copies of three stages are in flight while one is multiplied;
+  // and a small m-tile becomes four or eight micro tiles, spread over as many CUs.  Wave w
+  // computes the 32 x 32 output block (activation rows 32 (w & 1), weight rows 32 (w >> 1)).
+  // Same K order per output element as every other mode (one MFMA chain over K in
+  // ascending 16-wide steps): no bit changes.
+  auto run_tile_micro = [&](const Tile& t, bool& more, Tile& nxt) {
+    constexpr int KS = 2 * BK;  // stage depth
     int l32 = lane & 31;
     asm volatile("" : "+v"(l32));
-    const int wrow = wave * 32 + l32;
-    auto load_frags = [&](const char* sA, const char* sB, int kk, bf16x8* wf, bf16x8* xf) {
-      const int ch = kk * 2 + khalf;
-      wf[0] = *reinterpret_cast<const bf16x8*>(sB + swzn(wrow, ch));
-#pragma unroll
-      for (int ms = 0; ms < MSUB; ++ms) xf[ms] = *reinterpret_cast<const bf16x8*>(sA + swzn(ms * 32 + l32, ch));
-    };
-    auto mfma_step = [&](const bf16x8* wf, const bf16x8* xf, bool first) {
-#pragma unroll
-      for (int ms = 0; ms < MSUB; ++ms)
-        acc[0][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0], xf[ms], first ? f32x16{} : acc[0][ms], 0, 0, 0);
-    };
-    // eight 16-wide steps per stage; fragments are read two steps ahead into four
-    // register sets (step i of a stage: MFMAs on set (i + 2) % 4, reads into set i % 4)
-    constexpr int MF = MSUB, RD = 1 + MSUB;
-    auto step = [&](int mset, const char* sA, const char* sB, int kk, int lset, bool first = false) {
-      load_frags(sA, sB, kk, fw[lset], fx[lset]);
-      mfma_step(fw[mset], fx[mset], first);
-#pragma unroll
-      for (int i = 0; i < MF; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-#pragma unroll
-        for (int c = (i * RD) / MF; c < ((i + 1) * RD) / MF; ++c) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    auto step_dma = [&](int mset, const char* sA, const char* sB, int kk, int lset, char* dA, char* dB, int k0,
-                        int part) {
-      load_frags(sA, sB, kk, fw[lset], fx[lset]);
-      issue_part_narrow(rows_tag, t, dA, dB, k0, part);
-      mfma_step(fw[mset], fx[mset], false);
-      const int VM = part == 0 ? NJ : 8;
-#pragma unroll
-      for (int i = 0; i < MF; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-#pragma unroll
-        for (int c = (i * RD) / MF; c < ((i + 1) * RD) / MF; ++c) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-        for (int c = (i * VM) / MF; c < ((i + 1) * VM) / MF; ++c) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // six plain steps 2..7 of a stage held in (sA, sB)
-    auto steps_2_7 = [&](const char* sA, const char* sB, bool first) {
-      step(0, sA, sB, 2, 2, first);
-      step(1, sA, sB, 3, 3);
-      step(2, sA, sB, 4, 0);
-      step(3, sA, sB, 5, 1);
-      step(0, sA, sB, 6, 2);
-      step(1, sA, sB, 7, 3);
-    };
-    const int KT = K / KS;  // even: K is a multiple of 256 for narrow tiles
-    dma_barrier();
+    const int arow = (wave & 1) * 32 + l32, wrow = (wave >> 1) * 32 + l32;
+    const int KT = K / KS;  // even, >= 2: K is a multiple of 256 for micro tiles
+    // every wave is done with the LDS of the previous tile: its last stage's fragment reads
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    bare_barrier();
     int claim = 0;
     if (dyn && threadIdx.x == 0) claim = atomicAdd(a.work + xcd, 1);
-    load_frags(sA0, sB0, 0, fw[0], fx[0]);
-    load_frags(sA0, sB0, 1, fw[1], fx[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    steps_2_7(sA0, sB0, true);
-    for (int kt = 0; kt < KT - 2; kt += 2) {
-      dma_barrier();
+    issue_micro(t, sA0, 0);
+    issue_micro(t, sB0, KS);
+    if (KT > 2) issue_micro(t, sA1, 2 * KS);
+    acc[0][0] = f32x16{};
+    // Stage s from buffer cur: its head waits for this wave's copies of stage s (the 8
+    // copies of each later stage already issued may stay in flight) and for its own LDS
+    // reads, then the barrier; the copies of stage s + 3 then go to buffer fill, the
+    // buffer of stage s - 1, which every wave has finished reading.
+    auto stage = [&](int s, const char* cur, char* fill) {
+      if (s + 2 < KT)
+        __builtin_amdgcn_s_waitcnt(0x4070);  // vmcnt(16) expcnt(7) lgkmcnt(0)
+      else if (s + 1 < KT)
+        __builtin_amdgcn_s_waitcnt(0x78);    // vmcnt(8)
+      else
+        __builtin_amdgcn_s_waitcnt(0x70);    // vmcnt(0)
+      bare_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      step_dma(2, sA1, sB1, 0, 0, sA0, sB0, (kt + 2) * KS, 0);
-      step_dma(3, sA1, sB1, 1, 1, sA0, sB0, (kt + 2) * KS, 1);
-      steps_2_7(sA1, sB1, false);
-      dma_barrier();
+      if (s + 3 < KT) issue_micro(t, fill, (s + 3) * KS);
       __builtin_amdgcn_sched_barrier(0);
-      step_dma(2, sA0, sB0, 0, 0, sA1, sB1, (kt + 3) * KS, 0);
-      step_dma(3, sA0, sB0, 1, 1, sA1, sB1, (kt + 3) * KS, 1);
-      steps_2_7(sA0, sB0, false);
+      bf16x8 wf[8], xf[8];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int ch = kk * 2 + khalf;
+        wf[kk] = *reinterpret_cast<const bf16x8*>(cur + kMicroB + swzn(wrow, ch));
+        xf[kk] = *reinterpret_cast<const bf16x8*>(cur + swzn(arow, ch));
+      }
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk], xf[kk], acc[0][0], 0, 0, 0);
+      // all 16 fragment reads first, then the MFMAs (each waits only for its own two)
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int s0 = 0; s0 < KT; s0 += 4) {
+      stage(s0, sA0, sB1);
+      stage(s0 + 1, sB0, sA0);
+      if (s0 + 2 < KT) {
+        stage(s0 + 2, sA1, sB0);
+        stage(s0 + 3, sB1, sA1);
+      }
     }
-    // stages KT-2 (steps 6, 7 in registers) and KT-1 (buffer 1)
+    // every wave has read its last stage: the next tile's first two stages (a full-height
+    // tile's; a micro tile issues its own) may go to the buffers now
     if (dyn && threadIdx.x == 0) sh_claim = claim;
-    dma_barrier();
+    __syncthreads();
     const int nlid = dyn ? run0 + __builtin_amdgcn_readfirstlane(sh_claim) : lid + slots;
     next_lid = nlid;
     more = nlid < lid_end;
@@ -942,43 +938,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       decode(nlid, nxt);
       setup(nxt);
       issue_loads_for(nxt, sA0, sB0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    step(2, sA1, sB1, 0, 0);
-    step(3, sA1, sB1, 1, 1);
-    steps_2_7(sA1, sB1, false);
-    if (more) {
-      lds_barrier();
       issue_loads_for(nxt, sA1, sB1, 1);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step(fw[2], fx[2], false);
-    mfma_step(fw[3], fx[3], false);
-    int erid[MSUB];
-#pragma unroll
-    for (int ms = 0; ms < MSUB; ++ms)
-      erid[ms] = a.sorted != nullptr ? a.sorted[min(t.p0 + ms * 32 + l32, t.p1 - 1)] : 0;
-    // epilogue: lane holds row (lane & 31) of each 32-row sub-tile and, per register
-    // group g, output columns 8 g + 4 (lane >> 5) + [0, 4) of the wave's 32
+    // epilogue: lane holds activation row (lane & 31) of the wave's block and, per register
+    // group g, weight rows (output columns) 8 g + 4 (lane >> 5) + [0, 4) of its 32
+    const int p = t.p0 + arow;
+    const int erid = a.sorted != nullptr ? a.sorted[min(p, t.p1 - 1)] : 0;
     __bf16* y = (__bf16*)a.out;
-    const int cbase = t.nt * TBN + t.sub * (TBN / 2) + wave * 32;
-#pragma unroll
-    for (int ms = 0; ms < MSUB; ++ms) {
-      const int p = t.p0 + ms * 32 + l32;
-      if (p >= t.p1 || cbase >= a.H) continue;
-      int dest = p;
-      if (a.sorted != nullptr) {
-        const int r = erid[ms];
-        if ((unsigned)r >= (unsigned)a.sentinel) continue;
-        if (!a.dest_is_row) dest = r;
-      }
+    const int cbase = t.nt * TBN + (t.sub & 3) * (TBN / 4) + (wave >> 1) * 32;
+    bool ok = p < t.p1 && cbase < a.H;
+    int dest = p;
+    if (a.sorted != nullptr) {
+      ok = ok && (unsigned)erid < (unsigned)a.sentinel;
+      if (!a.dest_is_row) dest = erid;
+    }
+    if (ok) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int col = cbase + g * 8 + khalf * 4;
         bf16x4 o;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = (__bf16)acc[0][ms][g * 4 + q];
-        *reinterpret_cast<bf16x4*>(y + (long)dest * a.H + col) = o;
+        for (int q = 0; q < 4; ++q) o[q] = (__bf16)acc[0][0][g * 4 + q];
+        *reinterpret_cast<bf16x4*>(y + (long)dest * a.H + cbase + g * 8 + khalf * 4) = o;
       }
     }
   };
@@ -991,12 +971,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     bool more = false;
     Tile nxt = cur;
     const int rows = tile_rows(cur);
-    if constexpr (kNarrow) {
+    if constexpr (kMicro) {
       if (rows & 1) {
-        if (rows == BM / 4 + 1)
-          run_tile_narrow(std::integral_constant<int, BM / 4>{}, cur, more, nxt);
-        else
-          run_tile_narrow(std::integral_constant<int, BM / 2>{}, cur, more, nxt);
+        run_tile_micro(cur, more, nxt);
         if (!more) break;
         cur = nxt;
         lid = next_lid;
@@ -1086,7 +1063,7 @@ int mtile_bound(const moe_config& c, bool identity) {
 
 // Persistent launch: one workgroup per CU (the kernel's LDS allows no more), at most
 // as many as there can be tiles, a multiple of the 8 XCDs.
-template <int MODE, bool FP8, bool NARROW = false, bool W13OUT = false>
+template <int MODE, bool FP8, bool MICRO = false, bool W13OUT = false>
 hipError_t launch_gemm(FfnArgs a, hipStream_t s) {
   int cus = 0;
   hipError_t err = current_device_cus(&cus);
@@ -1095,7 +1072,7 @@ hipError_t launch_gemm(FfnArgs a, hipStream_t s) {
   if (G == 0) return hipSuccess;  // no rows (an expert-choice capacity of 0)
   const int grid = ceil_div(min(G, max(cus, 8)), 8) * 8;
   if (grid > MOE_CLOCK_SLOTS) a.clk = nullptr;  // more workgroups than stamp slots: none
-  ffn_gemm_bf16<MODE, FP8, NARROW, W13OUT><<<grid, kThreads, 0, s>>>(a);
+  ffn_gemm_bf16<MODE, FP8, MICRO, W13OUT><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -1167,18 +1144,18 @@ hipError_t launch_down(const moe_config& c, const void* act, const int32_t* sort
     return hipGetLastError();
   }
   a.ntiles = ceil_div(c.H, 256);
-  // Narrow tiles need 128-deep stages in pairs (K a multiple of 256).  They pay where the
+  // Micro tiles need 128-deep stages in pairs (K a multiple of 256).  They pay where the
   // tiles make one to four rounds over the CUs: the short tiles, last in the order, then
   // fill the final round (fewer tiles: the longest tile sets the time anyway; more: the
   // last round is a small part, and keeping an expert's m-tiles together saves weight
-  // re-reads).  Each expert's last m-tile may take a second m-slot.
+  // re-reads).  Each expert's last m-tile may take eight m-slots instead of one.
   int cus = 0;
   hipError_t err = current_device_cus(&cus);
   if (err != hipSuccess) return err;
   const long tiles = (long)a.mtiles * a.ntiles;
-  a.narrow = c.expert_dtype == MOE_BF16 && c.I % 256 == 0 && tiles > cus && tiles <= 4L * cus;
-  if (a.narrow) {
-    a.mtiles += a.N;
+  a.micro = c.expert_dtype == MOE_BF16 && c.I % 256 == 0 && tiles > cus && tiles <= 4L * cus;
+  if (a.micro) {
+    a.mtiles += 7 * a.N;
     return launch_gemm<1, false, true>(a, s);
   }
   return c.expert_dtype == MOE_FP8_E4M3 ? launch_gemm<1, true>(a, s) : launch_gemm<1, false>(a, s);
