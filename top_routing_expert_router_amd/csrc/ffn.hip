@@ -228,10 +228,10 @@ __device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t m0
 __device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Barrier that publishes LDS written by global->LDS DMA.  The DMA is counted by
-// vmcnt, and a workgroup fence does not wait for it (the compiler treats it as a
-// load), so every wave waits for its own DMA *before* the barrier; only then are
-// all waves' rows in LDS when any wave passes it.  s_waitcnt imm 0x70 =
-// vmcnt(0) expcnt(7) lgkmcnt(0).
+// vmcnt, so every wave waits for its own DMA *before* the barrier; only then are all
+// waves' rows in LDS when any wave passes it.  s_waitcnt imm 0x70 = vmcnt(0) expcnt(7)
+// lgkmcnt(0).  (The workgroup fence of __syncthreads() would wait for all of them too: it
+// counts LDS copies as LDS writes.)
 __device__ __forceinline__ void dma_barrier() {
   __builtin_amdgcn_s_waitcnt(0x70);
   __syncthreads();
@@ -245,8 +245,10 @@ __device__ __forceinline__ void fp8_barrier() {
   __syncthreads();
 }
 
-// Barrier after this wave's LDS reads have completed (lgkmcnt(0); vmcnt and expcnt
-// not waited: imm 0xC07F), so no wave's later DMA can overwrite what a read still needs.
+// Barrier after this wave's LDS reads have completed (lgkmcnt(0): imm 0xC07F), so no
+// wave's later DMA can overwrite what a read still needs.  The workgroup fence of
+// __syncthreads() also makes it wait for the copies in flight (the next tile's first
+// stage, issued a few steps earlier); a bare barrier here measured no faster.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __syncthreads();
