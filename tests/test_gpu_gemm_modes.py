@@ -33,13 +33,16 @@ def _gpu():
     M.lib()
 
 
-def test_w2_micro_tiles_match_standard_tiles():
-    T, H, N, k, I, B = 4096, 4096, 8, 2, 14336, 64
+@pytest.mark.parametrize("I", [14336, 768, 256])
+def test_w2_micro_tiles_match_standard_tiles(I):
+    # I = 14336: 112 stages of 128 (whole groups of four); 768: six (the last group has
+    # two); 256: two (no stage issued from inside the ring)
+    T, H, N, k, B = 4096, 4096, 8, 2, 64
     # expert loads: last m-tiles of 64 (expert 1) and 128 rows (expert 2) become four and
     # eight micro tiles per weight n-tile; 1000 and 952 leave padded, partly empty last tiles of 256 and 192 rows
     loads = [1024, 1088, 1152, 1024, 1000, 1000, 952, 952]
     assert sum(loads) == T * k
-    _say("w2 micro tiles vs standard tiles, loads", loads)
+    _say("w2 micro tiles vs standard tiles, I", I, "loads", loads)
     g = torch.Generator().manual_seed(5)
     perm = torch.randperm(T * k, generator=g).numpy()
     cfg = M.make_config(T, H, N, k, I, B)
