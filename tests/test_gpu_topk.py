@@ -64,8 +64,11 @@ def test_route_from_logits_expert_counts(N, k, renorm):
         assert np.all(np.abs(gm - margin) <= 1e-6 * np.maximum(scale, 1.0))
 
 
+# each router kernel's top-k case: 16-token kernel with 1 to 8 column blocks of 16 experts
+# (8 lanes per token and 1, 2, 4 or 8 experts per lane up to 64 experts, 16 lanes above),
+# and the wide kernel above 128
 @pytest.mark.parametrize("renorm", [1, 0])
-@pytest.mark.parametrize("N", [16, 64, 65, 128, 129, 256])
+@pytest.mark.parametrize("N", [8, 16, 24, 40, 64, 65, 100, 128, 129, 256])
 def test_fused_topk_matches_standalone(N, renorm):
     w = W.QWEN3MOE_BF16.with_(T=300, N=N, k=8, renormalize=renorm)
     _say("fused vs standalone top-k", N, "renormalize", renorm)
