@@ -82,6 +82,31 @@ def test_w2_micro_tiles_match_standard_tiles(I):
     _say(f"  {checked} y rows bitwise equal to the standard-tile results")
 
 
+def test_w2_micro_tiles_identity_rows():
+    """Identity rows (no routing: the shared-expert form) with micro tiles: T = 4160 tokens
+    make 17 x 16 down-projection tiles, so the last m-tile (64 rows) runs as micro tiles;
+    every y row must equal, bit for bit, the same row computed in two smaller calls whose
+    tiles do not use them (2048 and 2112 tokens: 128 and 144 tiles)."""
+    T, H, I = 4160, 4096, 14336
+    cfg = M.make_config(T, H, 1, 1, I, 64)
+    gd = torch.Generator(device=DEV).manual_seed(11)
+    act = (torch.randn(T, I, device=DEV, generator=gd) * 0.05).to(torch.bfloat16)
+    w2 = (torch.randn(1, H, I, device=DEV, generator=gd) / I ** 0.5).to(torch.bfloat16)
+    y = torch.full((T, H), 7.0, dtype=torch.bfloat16, device=DEV)
+    M.moe_expert_down(cfg, act, None, None, w2, None, y)
+    parts = []
+    for r0, r1 in ((0, 2048), (2048, T)):
+        c = M.make_config(r1 - r0, H, 1, 1, I, 64)
+        yp = torch.empty(r1 - r0, H, dtype=torch.bfloat16, device=DEV)
+        M.moe_expert_down(c, act[r0:r1].contiguous(), None, None, w2, None, yp)
+        parts.append(yp)
+    torch.cuda.synchronize()
+    want = torch.cat(parts)
+    bad = (y.view(torch.int16) != want.view(torch.int16)).any(dim=1).nonzero().flatten()
+    assert bad.numel() == 0, bad[:8].tolist()
+    _say(f"  {T} identity y rows bitwise equal without micro tiles")
+
+
 @pytest.mark.parametrize("name", ["toy_fp32", "mixtral_bf16", "mixtral_ec_bf16", "deepseekv3_fp8"])
 def test_forward_stage_events(name):
     """Trace stage events: recorded in order on the forward's stream, the stage times add
