@@ -94,7 +94,7 @@ def _traffic(workload: str, launches_per_unit: float):
 
 # rocprofv3 kernel-name fragments -> stage names used in the counter summary
 _COUNTER_KERNELS = [("ffn_gemm_bf16<0", "gate_up_gemm"), ("ffn_gemm_bf16<1", "down_gemm"),
-                    ("router_bf16_wide", "route_wide"), ("router_bf16", "route"), ("topk_gates", "route_topk"),
+                    ("router_ring", "route_ring"), ("router_bf16", "route"), ("topk_gates", "route_topk"),
                     ("align_hist", "align_hist"), ("align_scan", "align_scan"), ("align_scatter", "align_scatter"),
                     ("align_fused", "align_one_workgroup"), ("ec_select", "expert_choice_select"),
                     ("ec_align_init", "align_ec_init"), ("ec_align_rows", "align_ec_rows"), ("combine_ec_rows", "combine_expert_choice"),

@@ -43,7 +43,7 @@ def test_trace_summary_timed_steps(tmp_path, capsys):
     expert each forward's two GEMM launches are split into routed and shared."""
     rows, t = [], 0
     for fwd in range(5):  # 2 warmup, 2 timed, 1 after
-        for name, dur in (("router_bf16_wide<1>(x)", 10), ("void ffn_gemm_bf16<0, true>(a)", 1000 + fwd),
+        for name, dur in (("router_ring<256, 64, 3, 0>(x)", 10), ("void ffn_gemm_bf16<0, true>(a)", 1000 + fwd),
                           ("void ffn_gemm_bf16<1, true>(a)", 500), ("void ffn_gemm_bf16<0, true>(a)", 100 + fwd),
                           ("void ffn_gemm_bf16<1, true>(a)", 50), ("combine_rows<x>", 20)):
             rows.append(f'"{name}",{t},{t + dur * 1000}\n')
@@ -65,7 +65,7 @@ def test_trace_summary_timed_steps(tmp_path, capsys):
             t[key] = f[2:] if key.endswith(")") else f[1:]
         return t
     a, b = table(everything), table(timed)
-    assert a["route_wide"][0] == "5" and a["gate_up_gemm"][0] == "10"
+    assert a["route_ring"][0] == "5" and a["gate_up_gemm"][0] == "10"
     assert b["gate_up_gemm (routed)"][:2] == ["2", "1002.50"] and b["gate_up_gemm (shared)"][:2] == ["2", "102.50"]
-    assert b["route_wide"][:2] == ["2", "10.00"] and b["combine"][0] == "2"
+    assert b["route_ring"][:2] == ["2", "10.00"] and b["combine"][0] == "2"
     assert "route_topk" in a and "route_topk" not in b

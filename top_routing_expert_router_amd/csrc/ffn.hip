@@ -203,29 +203,6 @@ struct Tile {
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-// LDS byte address of a shared-memory array (its address-space cast folds to a constant)
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
-}
-
-// One global -> LDS copy (buffer_load_dwordx4 ... lds): lane L's 16 bytes at buffer offset
-// voff + soff land at LDS byte address m0 + 16 L.  Written as inline assembly, so that the
-// only waits for it are the kernel's own: the compiler's wait-count pass does not tell
-// apart the LDS arrays the builtin form writes once several stages of copies are in
-// flight, and made every fragment read wait for all of them.  The copy reads M0 one wait
-// state after the scalar write (s_nop 0).
-__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t m0, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(m0), "v"(voff), "s"(r), "s"(soff)
-               : "m0");
-}
-
-// Workgroup barrier without a memory fence: the caller has already waited for what the
-// other waves need (__syncthreads() would also wait for every LDS copy in flight, which
-// its workgroup fence counts as LDS writes).  The memory clobber keeps the compiler from
-// moving memory operations across it.
-__device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Barrier that publishes LDS written by global->LDS DMA.  The DMA is counted by
 // vmcnt, so every wave waits for its own DMA *before* the barrier; only then are all

@@ -9,9 +9,11 @@
 //
 // Batch invariance ("Why temperature=0 Still Gives Different Answers: Batch
 // Invariance", "How do I make LLM inference reproducible?", tier 2): each logit
-// is reduced in a fixed order that depends only on H (64-wide K chunks dealt to
-// eight waves round-robin, each wave in ascending chunk order, then the eight wave
-// partials added in wave order).  Nothing depends on T or on the other tokens.
+// is reduced in a fixed order that depends only on H and on N's kernel (up to 64
+// experts: 64-wide K chunks dealt to eight waves round-robin, each wave in ascending
+// chunk order, then the eight wave partials added in wave order; more than 64: one
+// MFMA chain over K in ascending 32-wide steps).  Nothing depends on T or on the
+// other tokens.
 #include <type_traits>
 
 #include "common.h"
@@ -25,16 +27,11 @@ constexpr int kRouterWaves = 8;     // waves per workgroup; wave w takes K chunk
 constexpr int kRouterThreads = kRouterWaves * 64;
 constexpr int kChunkK = 64;         // K per chunk: lane group q = lane / 16 holds k in [16 q, 16 q + 16)
 
-// 16-token column blocks per workgroup: every workgroup reads all of W_g, so for
-// more than 64 experts two blocks share each weight load (half the W_g traffic)
-template <int NSUB>
-constexpr int kRouterTB = NSUB > 4 ? 2 : 1;
-
-// chunks in flight per wave: a CU's whole share of h for small expert counts; one
-// (NSUB weight fragments of 8 VGPRs) above 64 experts
+// chunks in flight per wave: a CU's whole share of h for 16 experts, four for up to 64
 template <int NSUB>
 struct RouterUnroll {
-  static constexpr int value = NSUB <= 1 ? 8 : (NSUB <= 4 ? 4 : 1);
+  static_assert(NSUB >= 1 && NSUB <= 4, "the 16-token router takes up to 64 experts");
+  static constexpr int value = NSUB <= 1 ? 8 : 4;
 };
 
 typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
@@ -341,144 +338,133 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16(const __bf16* __re
   }
   __syncthreads();
   // fused top-k: one group of L lanes per token, 64 / L tokens per wave.  The launch
-  // takes NSUB = ceil(N / 16), so L = topk_lanes(N) follows from NSUB, and P =
-  // topk_slots(ceil(N / L)) (the launch picks the kernel).
-  constexpr int L = NSUB <= 4 ? 8 : 16;
+  // takes NSUB = ceil(N / 16) <= 4, so L = topk_lanes(N) = 8, and P = topk_slots(ceil(N /
+  // 8)) (the launch picks the kernel).
+  constexpr int L = 8;
   constexpr int per_wave = kWave / L;
   for (int t = wave * per_wave + lane / L; t < TW; t += kRouterWaves * per_wave)
     if (t0 + t < T) topk_one_p<P, L, MODE>(&lg[t][0], t0 + t, N, k, renormalize, ids, gates, margin, replay, scores);
 }
 
-// bf16 router for many experts (more than 128), top-k fused.  With one 16-token
-// workgroup per CU, every workgroup would read all of W_g (3.7 MB for 256 experts of
-// 7168), 16 tokens at a time -- the weights, not h, would set the time.  Here a
-// workgroup of NW waves takes TW = 32 or 64 tokens, and each 64-wide K chunk of W_g (all
-// NP padded experts) and of the tokens' rows is staged once in LDS for all waves (loads
-// for chunk c + 2 in flight while chunk c is multiplied).  Wave w computes experts
-// [w NP/NW, (w+1) NP/NW) for all TW tokens with 32x32x16 MFMAs (W_g rows as the A
-// operand, token rows as B), so each logit is one MFMA chain over K in ascending
-// 16-wide steps, then the bias is added: the order depends only on H, not on T or TW.
-// LDS rows are 128 B (8 chunks of 16 B), chunk c of row r stored at c ^ ((r >> 1) & 7):
-// the 32-row fragment reads then hit all 64 banks.
-template <int NP, int TW, int NW, int MODE>
-__global__ __launch_bounds__(NW * 64) void router_bf16_wide(const __bf16* __restrict__ h, const __bf16* __restrict__ wg,
-                                                        const float* __restrict__ bias, float* __restrict__ logits,
-                                                        int32_t* __restrict__ ids, float* __restrict__ gates,
-                                                        float* __restrict__ margin, int T, int H, int N, int k,
-                                                        int renormalize, const int32_t* __restrict__ replay,
-                                                        float* __restrict__ scores) {
-  constexpr int ROWS = NP + TW;                 // staged rows per chunk: experts, then tokens
-  constexpr int STAGE = ROWS * 128;             // bytes per stage
-  constexpr int RPL = NW * 8;                   // staged rows per load instruction of the workgroup
-  constexpr int LOADS = (ROWS + RPL - 1) / RPL; // 16-byte loads per thread per chunk (the last may be partial)
-  constexpr int ES = NP / NW / 32;              // 32-expert sub-tiles per wave
-  constexpr int TS = TW / 32;                   // 32-token sub-tiles
-  static_assert(ES >= 1, "tile shape");
-  static_assert(2 * STAGE >= TW * (NP + 1) * 4, "the logit rows reuse the staging buffers");
-  __shared__ __attribute__((aligned(16))) char stage[2][STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// bf16 router for more than 64 experts, top-k fused: the K chunks stream through an LDS
+// ring.  A workgroup of 8 waves takes TW tokens; each 64-wide K chunk of all NP (padded)
+// expert rows of W_g and of the TW token rows is copied global -> LDS as one stage of RS
+// rows (NP + TW rounded up to 64: 128-byte rows, 16-byte chunks XORed with (row >> 1) & 7),
+// S stages in the ring, so the copies of S - 1 chunks are in flight while one is multiplied.
+// Wave w owns expert blocks [w EPW, (w + 1) EPW) of 16 for all TW tokens: its logits are
+// one 16x16x32 MFMA chain over K in ascending 32-wide steps (W_g rows as the A operand),
+// then the bias is added.  No partial sums cross waves, and nothing depends on T or TW.
+// The copies are inline assembly and the stage heads bare barriers with the ring's own
+// waits (the compiler's wait-count pass cannot tell the stages apart).  Expert rows past
+// N, token rows past T and the padding rows start at their buffer's end: zeros, no fetch.
+template <int NP, int TW, int S, int MODE>
+__global__ __launch_bounds__(512) void router_ring(const __bf16* __restrict__ h, const __bf16* __restrict__ wg,
+                                                   const float* __restrict__ bias, float* __restrict__ logits,
+                                                   int32_t* __restrict__ ids, float* __restrict__ gates,
+                                                   float* __restrict__ margin, int T, int H, int N, int k,
+                                                   int renormalize, const int32_t* __restrict__ replay,
+                                                   float* __restrict__ scores) {
+  constexpr int NW = 8;
+  constexpr int RS = (NP + TW + 63) / 64 * 64;  // rows per stage
+  constexpr int SB = RS * 128;                   // bytes per stage
+  constexpr int IPW = RS / 64;                   // copies (8 rows each) per wave and stage
+  constexpr int EB = NP / 16, TB = TW / 16;      // 16-row expert blocks, 16-token blocks
+  constexpr int EPW = EB / NW;                   // expert blocks per wave
+  static_assert(EPW >= 1 && EB % NW == 0 && TW % 16 == 0 && S >= 3, "tile shape");
+  static_assert(S * SB >= TW * (NP + 1) * 4, "the logit rows reuse the ring");
+  static_assert(S - 2 <= 3, "head waits below cover up to three later stages");
+  __shared__ __attribute__((aligned(16))) char ring[S * SB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.x * TW;
-  auto swz = [](int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); };
-  // copy plan: load i of thread tid moves chunk (tid & 7) of staged row RPL i + (tid >> 3);
-  // expert rows past N and token rows past T read row 0 (their results are never used)
-  const int crow = tid >> 3, cchunk = tid & 7;
-  const __bf16* src[LOADS];
+  const uint32_t hbytes = (uint32_t)T * H * 2u, wbytes = (uint32_t)N * H * 2u;  // T H < 2^31
+  const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc((void*)h, (short)0, (int)hbytes, kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)wg, (short)0, (int)wbytes, kRawBufferFlags);
+  // copy plan: copy i of wave w moves rows [8 (w IPW + i), +8); lane L lands in physical
+  // chunk L % 8 of row 8 (w IPW + i) + L / 8 and fetches the logical chunk stored there.
+  // A copy's 8 rows are all expert rows or all token (or padding) rows: NP and TW are
+  // multiples of 16.
+  uint32_t voff[IPW];
+  bool wrow[IPW];
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int r = RPL * i + crow;
-    src[i] = r < NP ? wg + (size_t)(r < N ? r : 0) * H : h + (size_t)(t0 + r - NP < T ? t0 + r - NP : 0) * H;
-    src[i] += cchunk * 8;
-  }
-  // RB register buffers: chunk c + RB is loaded right after chunk c has been stored
-  // to LDS, so each load has RB - 1 chunks of MFMAs to arrive (one chunk is only a
-  // few hundred cycles of matrix work, far less than a memory round trip)
-  constexpr int RB = 4;
-  static_assert(RB == 4, "the chunk loop below is unrolled by hand for four buffers");
-  u32x4_t buf[RB][LOADS];
-  auto load = [&](u32x4_t* buf, int c) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      if (ROWS % RPL == 0 || RPL * i + crow < ROWS) buf[i] = *reinterpret_cast<const u32x4_t*>(src[i] + c * 64);
-  };
-  auto store = [&](const u32x4_t* buf, char* st) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      if (ROWS % RPL == 0 || RPL * i + crow < ROWS) *reinterpret_cast<u32x4_t*>(st + swz(RPL * i + crow, cchunk)) = buf[i];
-  };
-  f32x16 acc[ES][TS];
-#pragma unroll
-  for (int es = 0; es < ES; ++es)
-#pragma unroll
-    for (int ts = 0; ts < TS; ++ts) acc[es][ts] = f32x16{};
-  const int l32 = lane & 31, kh = lane >> 5;
-  const int e0 = wave * (NP / NW);
-  const int nchunks = H / 64;
-  auto chunk_mfma = [&](const char* st) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 wf[ES], hf[TS];
-#pragma unroll
-      for (int es = 0; es < ES; ++es)
-        wf[es] = *reinterpret_cast<const bf16x8*>(st + swz(e0 + es * 32 + l32, kk * 2 + kh));
-#pragma unroll
-      for (int ts = 0; ts < TS; ++ts)
-        hf[ts] = *reinterpret_cast<const bf16x8*>(st + swz(NP + ts * 32 + l32, kk * 2 + kh));
-#pragma unroll
-      for (int es = 0; es < ES; ++es)
-#pragma unroll
-        for (int ts = 0; ts < TS; ++ts) acc[es][ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[es], hf[ts], acc[es][ts], 0, 0, 0);
+  for (int i = 0; i < IPW; ++i) {
+    const int g = wave * IPW + i;              // copy group, uniform
+    const int r = g * 8 + (lane >> 3);
+    const int lchunk = (lane & 7) ^ ((r >> 1) & 7);
+    wrow[i] = g * 8 < NP;
+    if (wrow[i]) {
+      voff[i] = r < N ? ((uint32_t)r * H + lchunk * 8) * 2u : wbytes;
+    } else {
+      const int t = t0 + r - NP;
+      voff[i] = (r < NP + TW && t < T) ? ((uint32_t)t * H + lchunk * 8) * 2u : hbytes;
     }
-  };
-  // Chunk c is multiplied from stage c & 1 and staged through register buffer c % RB.
-  // Loads and stores are unconditional: a load past the last chunk re-reads it, and a
-  // store past it fills the free stage; neither is multiplied.  (A guarded load is moved
-  // by the compiler next to the store that uses it, which leaves nothing in flight.)
+  }
+  const uint32_t ring0 = lds_addr(ring);
+  auto issue = [&](int c, int b) {
 #pragma unroll
-  for (int j = 0; j < RB; ++j) load(buf[j], min(j, nchunks - 1));
-  store(buf[0], stage[0]);
+    for (int i = 0; i < IPW; ++i)
+      lds_copy16(wrow[i] ? wrs : hrs, ring0 + b * SB + (wave * IPW + i) * 1024, voff[i], c * 128);
+  };
+  const int nchunks = H / 64;
+  f32x4 acc[EPW][TB];
+#pragma unroll
+  for (int eb = 0; eb < EPW; ++eb)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[eb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // this wave's biases (index clamped into [0, N)), loaded before the loop
+  float bv[EPW][4];
+#pragma unroll
+  for (int eb = 0; eb < EPW; ++eb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      bv[eb][r] = bias ? bias[min((wave * EPW + eb) * 16 + 4 * (lane >> 4) + r, N - 1)] : 0.f;
+  auto swz = [](int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); };
+  const int l16 = lane & 15, q = lane >> 4;
+  for (int c = 0; c < S - 1 && c < nchunks; ++c) issue(c, c);
+  for (int c = 0; c < nchunks; ++c) {
+    // head: this wave's copies of chunk c have landed (those of the later chunks already
+    // issued may be in flight) and its reads of chunk c - 1 are done; then the barrier,
+    // and chunk c + S - 1 goes to the buffer of chunk c - 1
+    const int later = min(S - 2, nchunks - 1 - c);
+    if (later >= 3)
+      __builtin_amdgcn_s_waitcnt((3 * IPW & 15) | ((3 * IPW >> 4) << 14) | 0x70);
+    else if (later == 2)
+      __builtin_amdgcn_s_waitcnt((2 * IPW & 15) | ((2 * IPW >> 4) << 14) | 0x70);
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt((IPW & 15) | ((IPW >> 4) << 14) | 0x70);
+    else
+      __builtin_amdgcn_s_waitcnt(0x70);
+    bare_barrier();
+    if (c + S - 1 < nchunks) issue(c + S - 1, (c + S - 1) % S);
+    const char* st = ring + (c % S) * SB;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {  // 32-wide K steps: lane group q holds k in [32 s + 8 q, +8)
+      bf16x8 wf[EPW], tf[TB];
+#pragma unroll
+      for (int eb = 0; eb < EPW; ++eb)
+        wf[eb] = *reinterpret_cast<const bf16x8*>(st + swz((wave * EPW + eb) * 16 + l16, 4 * s + q));
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) tf[tb] = *reinterpret_cast<const bf16x8*>(st + swz(NP + tb * 16 + l16, 4 * s + q));
+#pragma unroll
+      for (int eb = 0; eb < EPW; ++eb)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) acc[eb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[eb], tf[tb], acc[eb][tb], 0, 0, 0);
+    }
+  }
+  // logits of the TW tokens, [TW][NP + 1] floats over the ring: lane holds token l16 of
+  // each token block and experts 4 q + r of each of its expert blocks
   __syncthreads();
-  auto chunk_step = [&](auto jt, int c) {
-    constexpr int j = decltype(jt)::value;
-    load(buf[j], min(c + RB, nchunks - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    chunk_mfma(stage[j & 1]);
-    store(buf[(j + 1) % RB], stage[(j + 1) & 1]);
-    __syncthreads();
-  };
-  const int nmain = nchunks - nchunks % RB;
-  for (int c0 = 0; c0 < nmain; c0 += RB) {
-    chunk_step(std::integral_constant<int, 0>{}, c0);
-    chunk_step(std::integral_constant<int, 1>{}, c0 + 1);
-    chunk_step(std::integral_constant<int, 2>{}, c0 + 2);
-    chunk_step(std::integral_constant<int, 3>{}, c0 + 3);
-  }
-  // H an odd multiple of 128: two chunks left, already in buffers 0 and 1
-  if (nmain < nchunks) {
-    chunk_step(std::integral_constant<int, 0>{}, nmain);
-    chunk_step(std::integral_constant<int, 1>{}, nmain + 1);
-  }
-  // logits of the TW tokens, [TW][NP + 1] floats over the staging buffers: lane holds
-  // token (lane & 31) of each token sub-tile and experts 8 g + 4 (lane >> 5) + q
-  float* lg = reinterpret_cast<float*>(&stage[0][0]);
-  // this lane's expert biases, all loads in flight together (index clamped into [0, N))
-  float bv[ES][16];
-  if (bias) {
+  float* lg = reinterpret_cast<float*>(ring);
 #pragma unroll
-    for (int es = 0; es < ES; ++es)
+  for (int eb = 0; eb < EPW; ++eb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) bv[es][i] = bias[min(e0 + es * 32 + 8 * (i / 4) + 4 * kh + (i % 4), N - 1)];
-  }
+    for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-  for (int es = 0; es < ES; ++es)
-#pragma unroll
-    for (int ts = 0; ts < TS; ++ts)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int e = e0 + es * 32 + 8 * (i / 4) + 4 * kh + (i % 4);
-        const int t = ts * 32 + l32;
-        float v = acc[es][ts][i];
-        if (bias && e < N) v += bv[es][i];
-        lg[t * (NP + 1) + e] = v;
+      for (int r = 0; r < 4; ++r) {
+        const int e = (wave * EPW + eb) * 16 + 4 * q + r;
+        float v = acc[eb][tb][r];
+        if (bias && e < N) v += bv[eb][r];
+        lg[(tb * 16 + l16) * (NP + 1) + e] = v;
       }
   __syncthreads();
   if (logits) {  // nullable: no logits out
@@ -487,14 +473,14 @@ __global__ __launch_bounds__(NW * 64) void router_bf16_wide(const __bf16* __rest
       if (t0 + t < T) logits[(size_t)(t0 + t) * N + e] = lg[t * (NP + 1) + e];
     }
   }
-  // one group of L lanes per token, 64 / L tokens per wave; launched for 128 < N <= NP = 256
-  // only, so L = topk_lanes(N) = 32 and 5 to 8 experts per lane
-  static_assert(NP == 256, "lanes per token below assume 128 < N <= 256");
-  constexpr int L = 32;
+  // one group of L lanes per token, 64 / L tokens per wave: N in (64, NP] with NP = 128 or
+  // 256 gives L = topk_lanes(N) = NP / 8 and 5 to 8 experts per lane
+  constexpr int L = NP / 8;
+  static_assert(NP == 128 || NP == 256, "lanes per token below");
   constexpr int per_wave = kWave / L;
-  for (int t = wave * per_wave + (tid & 63) / L; t < TW; t += NW * per_wave)
+  for (int t = wave * per_wave + lane / L; t < TW; t += NW * per_wave)
     if (t0 + t < T)
-      topk_one<L, 8, 8, MODE>(lg + t * (NP + 1), t0 + t, N, k, renormalize, ids, gates, margin, replay, scores);
+      topk_one_p<8, L, MODE>(lg + t * (NP + 1), t0 + t, N, k, renormalize, ids, gates, margin, replay, scores);
 }
 
 // fp32 projection: one thread per (token, expert), fmaf over H in ascending order.
@@ -531,8 +517,8 @@ template <int NSUB, int MODE>
 hipError_t launch_router_bf16(const moe_config& c, const void* h, const void* wg, const float* bias, float* logits,
                               int32_t* ids, float* gates, float* margin, hipStream_t s, const int32_t* replay,
                               float* scores) {
-  constexpr int TB = kRouterTB<NSUB>;
-  constexpr int L = NSUB <= 4 ? 8 : 16;
+  constexpr int TB = 1;
+  constexpr int L = 8;
   // the slots per lane for N in (16 (NSUB - 1), 16 NSUB]: two choices for NSUB = 1, one above
   constexpr int PMIN = topk_slots((16 * (NSUB - 1) + L) / L), PMAX = topk_slots((16 * NSUB + L - 1) / L);
   static_assert(PMIN == PMAX || (NSUB == 1 && PMIN == 1 && PMAX == 2), "slot choices");
@@ -562,22 +548,29 @@ hipError_t launch_router_bf16(const moe_config& c, const void* h, const void* wg
 }
 
 template <int NP, int MODE>
-hipError_t launch_router_wide(const moe_config& c, const void* h, const void* wg, const float* bias, float* logits,
+hipError_t launch_router_ring(const moe_config& c, const void* h, const void* wg, const float* bias, float* logits,
                               int32_t* ids, float* gates, float* margin, hipStream_t s, const int32_t* replay,
                               float* scores) {
   int cus = 0;
   hipError_t err = current_device_cus(&cus);
   if (err != hipSuccess) return err;
-  // 64 tokens per workgroup when that still gives every CU a workgroup, else 32
-  constexpr int NW = 8;
-  if (ceil_div(c.T, 64) >= cus)
-    router_bf16_wide<NP, 64, NW, MODE><<<ceil_div(c.T, 64), NW * 64, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits,
-                                                                        ids, gates, margin, c.T, c.H, c.N, c.k,
-                                                                        c.renormalize, replay, scores);
-  else
-    router_bf16_wide<NP, 32, NW, MODE><<<ceil_div(c.T, 32), NW * 64, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits,
-                                                                        ids, gates, margin, c.T, c.H, c.N, c.k,
-                                                                        c.renormalize, replay, scores);
+  // 256 experts: 64 tokens per workgroup when that still gives every CU a workgroup, else
+  // 32; stages of 40 KB, three in the ring.  128 experts: 32 tokens, stages of 24 KB, five.
+  if constexpr (NP == 256) {
+    if (ceil_div(c.T, 64) >= cus) {
+      router_ring<256, 64, 3, MODE><<<ceil_div(c.T, 64), 512, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits,
+                                                                       ids, gates, margin, c.T, c.H, c.N, c.k,
+                                                                       c.renormalize, replay, scores);
+      return hipGetLastError();
+    }
+    router_ring<256, 32, 3, MODE><<<ceil_div(c.T, 32), 512, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits,
+                                                                     ids, gates, margin, c.T, c.H, c.N, c.k,
+                                                                     c.renormalize, replay, scores);
+  } else {
+    router_ring<128, 32, 5, MODE><<<ceil_div(c.T, 32), 512, 0, s>>>((const __bf16*)h, (const __bf16*)wg, bias, logits,
+                                                                     ids, gates, margin, c.T, c.H, c.N, c.k,
+                                                                     c.renormalize, replay, scores);
+  }
   return hipGetLastError();
 }
 
@@ -594,27 +587,30 @@ hipError_t launch_router(const moe_config& c, const void* h, const void* w_gate,
     if (err != hipSuccess) return err;
     return launch_topk(c, logits, ids, gates, margin, s, replay, scores);
   }
-  // more than 128 experts: W_g staged once per 64 tokens (for up to 128 the 16-token
-  // kernel below measured faster)
-  if (c.N > 128) {
-    switch (topk_mode(replay, scores)) {
-      case kTopkScores:
-        return launch_router_wide<256, kTopkScores>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
-      case kTopkReplay:
-        return launch_router_wide<256, kTopkReplay>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
-      default:
-        return launch_router_wide<256, kTopkPlain>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
-    }
+  // more than 64 experts: every workgroup reads all of W_g, so it streams through an LDS
+  // ring shared by the waves, 32 or 64 tokens per workgroup (Qwen shape: 32.8 -> 23.7 us
+  // against the 16-token kernel with two column blocks; DeepSeek shape: 123 -> 120.5 us
+  // against a register-staged kernel)
+  if (c.N > 64) {
+    auto ring = [&](auto np) {
+      constexpr int NP = decltype(np)::value;
+      switch (topk_mode(replay, scores)) {
+        case kTopkScores:
+          return launch_router_ring<NP, kTopkScores>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
+        case kTopkReplay:
+          return launch_router_ring<NP, kTopkReplay>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
+        default:
+          return launch_router_ring<NP, kTopkPlain>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
+      }
+    };
+    return c.N > 128 ? ring(std::integral_constant<int, 256>{}) : ring(std::integral_constant<int, 128>{});
   }
-#define MOE_ROUTER_CASE(n) \
-  case n:                  \
-    return launch_router_bf16<n>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
-  switch (ceil_div(c.N, 16)) {  // N <= 128 here
-    MOE_ROUTER_CASE(1) MOE_ROUTER_CASE(2) MOE_ROUTER_CASE(3) MOE_ROUTER_CASE(4) MOE_ROUTER_CASE(5)
-    MOE_ROUTER_CASE(6) MOE_ROUTER_CASE(7)
-    default: return launch_router_bf16<8>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
+  switch (ceil_div(c.N, 16)) {  // N <= 64 here: the 16-token kernel
+    case 1: return launch_router_bf16<1>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
+    case 2: return launch_router_bf16<2>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
+    case 3: return launch_router_bf16<3>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
+    default: return launch_router_bf16<4>(c, h, w_gate, bias, logits, ids, gates, margin, s, replay, scores);
   }
-#undef MOE_ROUTER_CASE
 }
 
 hipError_t launch_topk(const moe_config& c, const float* logits, int32_t* ids, float* gates, float* margin,
