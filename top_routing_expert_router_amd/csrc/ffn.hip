@@ -357,6 +357,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const __bf16* X = (const __bf16*)a.x;
   uint32_t aoff[8];                              // byte offset of each of the lane's A rows
   uint32_t boff[8];                              // byte offset of each of the lane's weight rows
+  uint32_t poff = 0x80000000u;                   // W2 prefetch: activation row 64 wave + lane (or none)
   auto weight_row = [&](int n0, int j) {  // j = tile row
     const int r = MODE == 0 ? (j < TBN / 2 ? n0 + j : a.I + n0 + (j - TBN / 2)) : n0 + j;
     return (MODE == 1 && r >= a.H) ? -1 : r;
@@ -394,6 +395,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         else if ((unsigned)rid[j] < (unsigned)a.sentinel) row = rid[j] / a.k;
       }
       aoff[j] = (row * (unsigned)K + swz_chunk(ar, lane & 7) * 8) * 2u;
+    }
+    if constexpr (MODE == 1) {
+      // one lane per activation row of the tile; lanes past its rows fetch nothing
+      // (an offset beyond the buffer's size)
+      const int pr = wave * 64 + lane;
+      poff = pr < rows && t.p0 + pr < t.p1 ? (unsigned)pr * (unsigned)K * 2u : 0x80000000u;
     }
   };
   // weight-row offsets of tile t (fp8: and its scale rows)
@@ -675,20 +682,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       if (dyn && threadIdx.x == 0) sh_claim = claim;
       dma_barrier();
     } else {
+      // W2 also touches the activation rows of the stage after next: one 4-byte load per
+      // row (lane) brings that row's 128-byte line into L2, so the stage's copies, issued
+      // one stage later, find it there instead of going to memory.  The loads land in
+      // registers nobody reads; each stage head then waits for all loads but the newest
+      // (the prefetch issued after the copies it needs), as a bare barrier, since the
+      // workgroup fence of __syncthreads() would wait for the prefetch too.  W13's
+      // gathered token rows and the weight rows were measured slower with the same.
+      auto prefetch = [&](int k0) {
+        return __builtin_amdgcn_raw_buffer_load_b32(act_rsrc<MODE>(X, a.T, K, t.p0, t.p1), poff, k0 * 2, 0);
+      };
+      auto head = [&](int pf) {
+        if constexpr (MODE == 1) {
+          __builtin_amdgcn_s_waitcnt(0x71);  // vmcnt(1) expcnt(7) lgkmcnt(0)
+          bare_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          asm volatile("" ::"v"(pf));  // the previous prefetch has arrived: its register is free
+        } else {
+          dma_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      int pf0 = 0, pf1 = 0;
       for (int kt = 0; kt < KT - 2; kt += 2) {
-        dma_barrier();
-        __builtin_amdgcn_sched_barrier(0);
+        head(pf0);
         step_dma(2, sA1, sB1, 0, 0, sA0, sB0, (kt + 2) * BK, 0);
         step_dma(3, sA1, sB1, 1, 1, sA0, sB0, (kt + 2) * BK, 1);
+        if constexpr (MODE == 1) pf0 = prefetch((kt + 3) * BK);
         step(0, sA1, sB1, 2, 2);
         step(1, sA1, sB1, 3, 3);
-        dma_barrier();
-        __builtin_amdgcn_sched_barrier(0);
+        head(pf1);
         step_dma(2, sA0, sB0, 0, 0, sA1, sB1, (kt + 3) * BK, 0);
         step_dma(3, sA0, sB0, 1, 1, sA1, sB1, (kt + 3) * BK, 1);
+        if constexpr (MODE == 1) pf1 = prefetch(min(kt + 4, KT - 1) * BK);
         step(0, sA0, sB0, 2, 2);
         step(1, sA0, sB0, 3, 3);
       }
+      asm volatile("" ::"v"(pf0), "v"(pf1));
       // stages KT-2 (fragments 2, 3 in registers) and KT-1 (buffer 1)
       if (dyn && threadIdx.x == 0) sh_claim = claim;
       dma_barrier();
