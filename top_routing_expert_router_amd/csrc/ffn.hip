@@ -357,7 +357,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const __bf16* X = (const __bf16*)a.x;
   uint32_t aoff[8];                              // byte offset of each of the lane's A rows
   uint32_t boff[8];                              // byte offset of each of the lane's weight rows
-  uint32_t poff = 0x80000000u;                   // W2 prefetch: activation row 64 wave + lane (or none)
+  // prefetch (bf16 W2, fp8 W13): byte offset of activation row 64 wave + lane (or none), and
+  // that row's route id (W13)
+  uint32_t poff = 0x80000000u;
+  int prid = 0;
   auto weight_row = [&](int n0, int j) {  // j = tile row
     const int r = MODE == 0 ? (j < TBN / 2 ? n0 + j : a.I + n0 + (j - TBN / 2)) : n0 + j;
     return (MODE == 1 && r >= a.H) ? -1 : r;
@@ -380,6 +383,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       rid[j] = (MODE == 0 && a.sorted != nullptr) ? a.sorted[min(t.p0 + arow_of(rows, j), t.p1 - 1)] : 0;
+    if constexpr (MODE == 0 && FP8)
+      prid = a.sorted != nullptr ? a.sorted[min(t.p0 + wave * 64 + lane, t.p1 - 1)] : 0;
   };
   // activation-row offsets of tile t (W13: from the route ids setup_ids loaded)
   auto setup_a = [&](const Tile& t) {
@@ -396,11 +401,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
       aoff[j] = (row * (unsigned)K + swz_chunk(ar, lane & 7) * 8) * 2u;
     }
-    if constexpr (MODE == 1) {
-      // one lane per activation row of the tile; lanes past its rows fetch nothing
-      // (an offset beyond the buffer's size)
+    if constexpr (MODE == 1 || FP8) {
+      // one lane per activation row of the tile; lanes past its rows, and padding rows,
+      // fetch nothing (an offset beyond the buffer's size)
       const int pr = wave * 64 + lane;
-      poff = pr < rows && t.p0 + pr < t.p1 ? (unsigned)pr * (unsigned)K * 2u : 0x80000000u;
+      const int p = t.p0 + pr;
+      poff = 0x80000000u;
+      if (pr < rows && p < t.p1) {
+        if (MODE == 1) poff = (unsigned)pr * (unsigned)K * 2u;
+        else if (a.sorted == nullptr) poff = (unsigned)p * (unsigned)K * 2u;
+        else if ((unsigned)prid < (unsigned)a.sentinel) poff = (unsigned)(prid / a.k) * (unsigned)K * 2u;
+      }
     }
   };
   // weight-row offsets of tile t (fp8: and its scale rows)
@@ -664,20 +675,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       // its buffer; the barrier then waits for all copies but the newest code loads.
       store_fp8(sB1);  // stage 1 (its codes were staged with the tile's first copies)
       issue_part(rows_tag, t, sA0, sB0, min(2, KT - 1) * BK, 1);
+      // W13 also touches the token rows of the stage after next, as W2 with bf16 weights
+      // does below (the loads after the next stage's codes: each head then leaves 11 loads
+      // in flight).  fp8 W2 measured no faster with it.
+      auto prefetch8 = [&](int k0) {
+        return __builtin_amdgcn_raw_buffer_load_b32(act_rsrc<MODE>(X, a.T, K, t.p0, t.p1), poff, k0 * 2, 0);
+      };
+      auto head8 = [&](int pf) {
+        if constexpr (MODE == 0) {
+          __builtin_amdgcn_s_waitcnt(0x7B);  // vmcnt(11) expcnt(7) lgkmcnt(0)
+          __syncthreads();
+          __builtin_amdgcn_sched_barrier(0);
+          asm volatile("" ::"v"(pf));  // the previous prefetch has arrived: its register is free
+        } else {
+          fp8_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      int pf0 = 0, pf1 = 0;
       for (int kt = 0; kt < KT - 2; kt += 2) {
-        fp8_barrier();
-        __builtin_amdgcn_sched_barrier(0);
+        head8(pf0);
         step_f8(2, sA1, sB1, 0, 0, sA0, sB0, (kt + 2) * BK, 0, (kt + 3) * BK);
         step_f8(3, sA1, sB1, 1, 1, sA0, sB0, (kt + 2) * BK, 1, (kt + 3) * BK);
+        if constexpr (MODE == 0) pf0 = prefetch8((kt + 3) * BK);
         step(0, sA1, sB1, 2, 2);
         step(1, sA1, sB1, 3, 3);
-        fp8_barrier();
-        __builtin_amdgcn_sched_barrier(0);
+        head8(pf1);
         step_f8(2, sA0, sB0, 0, 0, sA1, sB1, (kt + 3) * BK, 0, min(kt + 4, KT - 1) * BK);
         step_f8(3, sA0, sB0, 1, 1, sA1, sB1, (kt + 3) * BK, 1, min(kt + 4, KT - 1) * BK);
+        if constexpr (MODE == 0) pf1 = prefetch8(min(kt + 4, KT - 1) * BK);
         step(0, sA0, sB0, 2, 2);
         step(1, sA0, sB0, 3, 3);
       }
+      asm volatile("" ::"v"(pf0), "v"(pf1));
       // stage KT-1 is in buffer 1 (decoded above); the last code loads fetched nothing needed
       if (dyn && threadIdx.x == 0) sh_claim = claim;
       dma_barrier();
@@ -687,8 +717,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       // one stage later, find it there instead of going to memory.  The loads land in
       // registers nobody reads; each stage head then waits for all loads but the newest
       // (the prefetch issued after the copies it needs), as a bare barrier, since the
-      // workgroup fence of __syncthreads() would wait for the prefetch too.  W13's
-      // gathered token rows and the weight rows were measured slower with the same.
+      // workgroup fence of __syncthreads() would wait for the prefetch too.  With bf16
+      // weights, W13's gathered token rows and the weight rows measured slower with the same.
       auto prefetch = [&](int k0) {
         return __builtin_amdgcn_raw_buffer_load_b32(act_rsrc<MODE>(X, a.T, K, t.p0, t.p1), poff, k0 * 2, 0);
       };
