@@ -16,11 +16,15 @@
 //     candidate with its original gate.
 // Depth 1 is the literal "second choice"; depth N - k walks the whole ranking.
 //
-// One workgroup does it all: the decisions chain through the remaining capacity,
+// Each token's ranking of all its experts is computed first, spread over the GPU
+// (reroute_rank); a round then takes a token's next candidate from it in constant time.
+// One workgroup does the rest: the decisions chain through the remaining capacity,
 // round after round.  Every position in token or route order is a prefix count --
 // ballot peer masks inside a wave, waves added in order -- so no atomic decides an
 // order; LDS atomics only add up totals.  The alignment proper then runs on the
 // experts the routes ended up with (dropless: every route with an expert runs it).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -30,11 +34,36 @@ namespace {
 constexpr int kRThreads = 1024;
 constexpr int kRWaves = kRThreads / kWave;
 
+// order[t * N + r] = the expert of rank r in token t's ranking of its logits (value
+// descending, lower index first, NaN last, -0 == +0: the order of rank_key).  A group of L
+// lanes per token (N rounded up to a power of two, at most 64): the token's keys are staged
+// in LDS, and a lane ranks experts l, l + L, ... by counting the keys above each.  Keys are
+// distinct (they hold the index), so the ranks are a permutation.
+template <int L>
+__global__ __launch_bounds__(256) void reroute_rank(const float* __restrict__ logits, int T, int N,
+                                                    uint8_t* __restrict__ order) {
+  constexpr int TPB = 256 / L;  // tokens per workgroup; TPB * N <= 1024
+  __shared__ uint64_t key[1024];
+  const long t0 = (long)blockIdx.x * TPB;
+  const int nt = (int)min((long)TPB, (long)T - t0);
+  for (int i = threadIdx.x; i < nt * N; i += 256) key[i] = rank_key(logits[t0 * N + i], i % N);
+  __syncthreads();
+  const int g = threadIdx.x / L, l = threadIdx.x % L;
+  if (g >= nt) return;
+  const uint64_t* kt = key + g * N;
+  for (int e = l; e < N; e += L) {
+    const uint64_t ke = kt[e];
+    int r = 0;
+    for (int j = 0; j < N; ++j) r += kt[j] > ke ? 1 : 0;
+    order[(t0 + g) * N + r] = (uint8_t)e;
+  }
+}
+
 __global__ __launch_bounds__(kRThreads) void reroute_capacity(const int32_t* __restrict__ ids,
-                                                              const float* __restrict__ logits, int T, int N,
+                                                              const uint8_t* __restrict__ order, int T, int N,
                                                               int k, int cap, int depth,
                                                               int32_t* __restrict__ route_expert,
-                                                              uint64_t* __restrict__ offered,
+                                                              int32_t* __restrict__ next,
                                                               int32_t* __restrict__ stats) {
   __shared__ int base[256], room[256];
   __shared__ int cnt[kRWaves][256];
@@ -66,7 +95,7 @@ __global__ __launch_bounds__(kRThreads) void reroute_capacity(const int32_t* __r
     atomicMin(&sh_min, base[e]);
     if (stats) stats[e] = base[e];
   }
-  for (int t = tid; t < T; t += kRThreads) offered[t] = ~0ull;  // nothing offered yet
+  for (int t = tid; t < T; t += kRThreads) next[t] = 0;  // rank of the next candidate to look at
   __syncthreads();
 
   // 2. rounds
@@ -87,36 +116,21 @@ __global__ __launch_bounds__(kRThreads) void reroute_capacity(const int32_t* __r
           }
         }
         if (route >= 0) {
-          const uint64_t last = offered[t];
-          uint64_t best = 0;
-          const float* lt = logits + (size_t)t * N;
+          // the next candidate: the next expert down the token's ranking that is not one
+          // of its own (none once the ranking is used up)
           int own[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) own[j] = j < k ? tid_ids[j] : -1;
-          // the next candidate: the largest key below the last one offered, among the
-          // experts that are not the token's own (4 logits per load when N allows)
-          auto consider = [&](float v, int e) {
+          const uint8_t* ot = order + (size_t)t * N;
+          int r = next[t];
+          while (r < N && want < 0) {
+            const int e = ot[r++];
             bool mine = false;
 #pragma unroll
             for (int j = 0; j < 8; ++j) mine |= own[j] == e;
-            const uint64_t key = rank_key(v, e);
-            if (!mine && key < last && key > best) {
-              best = key;
-              want = e;
-            }
-          };
-          if ((N & 3) == 0 && ((uintptr_t)logits & 15) == 0) {
-            for (int e = 0; e < N; e += 4) {
-              const float4 v = *reinterpret_cast<const float4*>(lt + e);
-              consider(v.x, e);
-              consider(v.y, e + 1);
-              consider(v.z, e + 2);
-              consider(v.w, e + 3);
-            }
-          } else {
-            for (int e = 0; e < N; ++e) consider(lt[e], e);
+            if (!mine) want = e;
           }
-          if (want >= 0) offered[t] = best;
+          next[t] = r;
         }
       }
       const int pos = chunk_position<kRThreads>(want, N, base, cnt);
@@ -160,7 +174,11 @@ __global__ __launch_bounds__(kRThreads) void reroute_capacity(const int32_t* __r
 
 }  // namespace
 
-size_t reroute_workspace_bytes(const moe_config& c) { return ((size_t)c.T * 8 + 255) & ~(size_t)255; }
+// the rankings (T x N bytes) and the walk positions (T ints)
+size_t reroute_workspace_bytes(const moe_config& c) {
+  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  return up((size_t)c.T * c.N) + up((size_t)c.T * 4);
+}
 
 hipError_t launch_align_reroute(const moe_config& c, const int32_t* ids, const float* logits, int32_t* route_expert,
                                 uint8_t* kept, int32_t* sorted_ids, int32_t* block_expert, int32_t* offsets,
@@ -171,8 +189,21 @@ hipError_t launch_align_reroute(const moe_config& c, const int32_t* ids, const f
     const long long cl = ((long long)c.T * c.k * c.cap_num) / ((long long)c.N * c.cap_den);
     cap = cl > 0x7fffffffLL ? 0x7fffffff : (int)cl;
   }
-  uint64_t* offered = (uint64_t*)ws;
-  reroute_capacity<<<1, kRThreads, 0, s>>>(ids, logits, c.T, c.N, c.k, cap, c.reroute_depth, route_expert, offered,
+  uint8_t* order = (uint8_t*)ws;
+  int32_t* next = (int32_t*)((char*)ws + (((size_t)c.T * c.N + 255) & ~(size_t)255));
+  if (cap >= 0 && c.reroute_depth > 0 && c.T > 0) {
+    auto rank = [&](auto lanes) {
+      constexpr int L = decltype(lanes)::value;
+      reroute_rank<L><<<(c.T + 256 / L - 1) / (256 / L), 256, 0, s>>>(logits, c.T, c.N, order);
+    };
+    if (c.N <= 2) rank(std::integral_constant<int, 2>{});
+    else if (c.N <= 4) rank(std::integral_constant<int, 4>{});
+    else if (c.N <= 8) rank(std::integral_constant<int, 8>{});
+    else if (c.N <= 16) rank(std::integral_constant<int, 16>{});
+    else if (c.N <= 32) rank(std::integral_constant<int, 32>{});
+    else rank(std::integral_constant<int, 64>{});
+  }
+  reroute_capacity<<<1, kRThreads, 0, s>>>(ids, order, c.T, c.N, c.k, cap, c.reroute_depth, route_expert, next,
                                            stats);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
