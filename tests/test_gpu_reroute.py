@@ -100,6 +100,9 @@ CASES = [
     (40000, 128, 8, 9, 10, 4, 0.0, 4),  # large: 320k routes through the one-workgroup pass
     (5, 4, 1, 1, 1, 3, 0.0, 5),         # tiny
     (1, 8, 2, 1, 1, 6, 0.0, 6),         # one token: cap = 0, nothing can be placed
+    (1000, 2, 1, 1, 1, 1, 0.0, 7),      # two experts: 2 lanes per token in the ranking kernel
+    (2500, 24, 3, 1, 1, 21, 0.01, 8),   # 24 experts (32 lanes per token), whole ranking
+    (300, 256, 8, 1, 1, 248, 0.0, 9),   # 256 experts, whole ranking (4 ranks per lane)
 ]
 
 
