@@ -98,7 +98,7 @@ _COUNTER_KERNELS = [("ffn_gemm_bf16<0", "gate_up_gemm"), ("ffn_gemm_bf16<1", "do
                     ("align_hist", "align_hist"), ("align_scan", "align_scan"), ("align_scatter", "align_scatter"),
                     ("align_fused", "align_one_workgroup"), ("ec_select", "expert_choice_select"),
                     ("ec_align_init", "align_ec_init"), ("ec_align_rows", "align_ec_rows"), ("combine_ec_rows", "combine_expert_choice"),
-                    ("reroute_capacity", "reroute"),
+                    ("reroute_rank", "reroute_rank"), ("reroute_capacity", "reroute"),
                     ("combine_rows", "combine"), ("copy16", "ceiling_copy_1GiB"), ("read16", "ceiling_read_1GiB"),
                     ("mfma_loop<1>", "ceiling_mfma_1wave"), ("mfma_loop<2>", "ceiling_mfma_2wave")]
 

@@ -69,3 +69,18 @@ def test_trace_summary_timed_steps(tmp_path, capsys):
     assert b["gate_up_gemm (routed)"][:2] == ["2", "1002.50"] and b["gate_up_gemm (shared)"][:2] == ["2", "102.50"]
     assert b["route_ring"][:2] == ["2", "10.00"] and b["combine"][0] == "2"
     assert "route_topk" in a and "route_topk" not in b
+
+
+def test_trace_summary_names_the_reroute_kernels(tmp_path, capsys):
+    """The reroute policy's two kernels (the ranking, then the one-workgroup rounds) get
+    stage names of their own in the trace summary."""
+    d = tmp_path / "r"
+    os.makedirs(d)
+    (d / "run_kernel_trace.csv").write_text(
+        '"Kernel_Name","Start_Timestamp","End_Timestamp"\n'
+        '"void moe::(anonymous namespace)::reroute_rank<16>(float const*, int, int, unsigned char*)",0,4000\n'
+        '"moe::(anonymous namespace)::reroute_capacity(int const*, unsigned char const*)",5000,65000\n')
+    assert bench.summarize_trace(str(d), "switch_reroute_bf16") == 0
+    out = capsys.readouterr().out
+    names = {l.split()[0] for l in out.splitlines() if l and not l.startswith("#")}
+    assert {"reroute_rank", "reroute"} <= names
