@@ -394,7 +394,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* weights, const 
  *   Limit: configs whose forward workspace (moe_workspace_size, MOE_OP_FORWARD) exceeds
  *   MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE_TOO_SMALL and enqueue nothing (it
  *   holds, e.g., a Mixtral-shaped layer (H 4096, 8 experts, top-2, I 14336, B 64) up to 1622
- *   tokens, a Qwen3-MoE-shaped one up to 2870, a DeepSeek-V3-shaped one up to 407).
+ *   tokens, a Qwen3-MoE-shaped one up to 2871, a DeepSeek-V3-shaped one up to 407).
  *   The scratch is that of the current device (hipGetDevice); `stream` must belong to it.
  *   Calls on one GPU share its scratch: calls that overlap on the GPU (on different streams,
  *   or from different host threads without ordering) race.  Calls in one stream order are safe.

@@ -174,10 +174,12 @@ __global__ __launch_bounds__(kRThreads) void reroute_capacity(const int32_t* __r
 
 }  // namespace
 
-// the rankings (T x N bytes) and the walk positions (T ints)
+// the rankings (T x N bytes, with reroute rounds only) and the walk positions (T ints)
+static size_t ranking_bytes(const moe_config& c) {
+  return c.reroute_depth > 0 ? (((size_t)c.T * c.N + 255) & ~(size_t)255) : 0;
+}
 size_t reroute_workspace_bytes(const moe_config& c) {
-  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
-  return up((size_t)c.T * c.N) + up((size_t)c.T * 4);
+  return ranking_bytes(c) + (((size_t)c.T * 4 + 255) & ~(size_t)255);
 }
 
 hipError_t launch_align_reroute(const moe_config& c, const int32_t* ids, const float* logits, int32_t* route_expert,
@@ -190,7 +192,7 @@ hipError_t launch_align_reroute(const moe_config& c, const int32_t* ids, const f
     cap = cl > 0x7fffffffLL ? 0x7fffffff : (int)cl;
   }
   uint8_t* order = (uint8_t*)ws;
-  int32_t* next = (int32_t*)((char*)ws + (((size_t)c.T * c.N + 255) & ~(size_t)255));
+  int32_t* next = (int32_t*)((char*)ws + ranking_bytes(c));
   if (cap >= 0 && c.reroute_depth > 0 && c.T > 0) {
     auto rank = [&](auto lanes) {
       constexpr int L = decltype(lanes)::value;
