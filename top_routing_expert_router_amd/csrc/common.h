@@ -187,35 +187,4 @@ __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / 
 constexpr int kRawBufferFlags = 0x00020000;
 constexpr uint32_t kBufferOutOfRange = 0x80000000u;
 
-// Position of this thread's key (0..N-1; -1 = none) among the keys of this chunk of NT
-// entries (one per thread of an NT-thread workgroup, in thread order) that come before
-// it, plus base[key]; afterwards base[key] has grown by the chunk's count of that key.
-// Peer masks from ballots within a wave, per-key wave counts added in wave order: no
-// atomic decides a position.  Called by every thread; cnt is [NT / 64][256] ints of LDS.
-template <int NT>
-__device__ int chunk_position(int key, int N, int* base, int (*cnt)[256]) {
-  constexpr int NW = NT / kWave;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  for (int i = tid; i < NW * N; i += NT) cnt[i / N][i % N] = 0;
-  __syncthreads();
-  const bool valid = key >= 0;
-  const uint64_t peers = peer_mask(valid ? key : 256);
-  if (valid && (peers & lt) == 0) cnt[wave][key] = __popcll(peers);  // one writer per (wave, key)
-  __syncthreads();
-  for (int e = tid; e < N; e += NT) {
-    int acc = base[e];
-    for (int w = 0; w < NW; ++w) {
-      const int c = cnt[w][e];
-      cnt[w][e] = acc;
-      acc += c;
-    }
-    base[e] = acc;
-  }
-  __syncthreads();
-  const int pos = valid ? cnt[wave][key] + __popcll(peers & lt) : -1;
-  __syncthreads();
-  return pos;
-}
-
 }  // namespace moe

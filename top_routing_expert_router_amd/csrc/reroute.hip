@@ -59,6 +59,45 @@ __global__ __launch_bounds__(256) void reroute_rank(const float* __restrict__ lo
   }
 }
 
+// Position of each of this thread's C keys (0..N-1; -1 = none) among the keys before it,
+// plus base[key]; afterwards base[key] has grown by the count of that key.  Thread i's key
+// c is entry c * NT + i of the run (chunk c of NT entries, in thread order).  Peer masks
+// from ballots within a wave; per key, the wave counts of chunk 0, then of chunk 1, ...,
+// added in that order: no atomic decides a position.  Called by every thread of the
+// NT-thread workgroup; cnt is [C * NT / 64][256] ints of LDS.
+template <int NT, int C>
+__device__ void chunk_positions(const int (&key)[C], int (&pos)[C], int N, int* base, int (*cnt)[256]) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int i = tid; i < C * NW * N; i += NT) cnt[i / N][i % N] = 0;
+  __syncthreads();
+  uint64_t peers[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const bool valid = key[c] >= 0;
+    peers[c] = peer_mask(valid ? key[c] : 256);
+    if (valid && (peers[c] & lt) == 0) cnt[c * NW + wave][key[c]] = __popcll(peers[c]);  // one writer
+  }
+  __syncthreads();
+  for (int e = tid; e < N; e += NT) {
+    int acc = base[e];
+    for (int w = 0; w < C * NW; ++w) {
+      const int x = cnt[w][e];
+      cnt[w][e] = acc;
+      acc += x;
+    }
+    base[e] = acc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < C; ++c) pos[c] = key[c] >= 0 ? cnt[c * NW + wave][key[c]] + __popcll(peers[c] & lt) : -1;
+  __syncthreads();
+}
+
+// Two chunks of tokens (or routes) per step: half the barriers of one chunk at a time.
+constexpr int kRChunks = 2;
+
 __global__ __launch_bounds__(kRThreads) void reroute_capacity(const int32_t* __restrict__ ids,
                                                               const uint8_t* __restrict__ order, int T, int N,
                                                               int k, int cap, int depth,
@@ -66,7 +105,7 @@ __global__ __launch_bounds__(kRThreads) void reroute_capacity(const int32_t* __r
                                                               int32_t* __restrict__ next,
                                                               int32_t* __restrict__ stats) {
   __shared__ int base[256], room[256];
-  __shared__ int cnt[kRWaves][256];
+  __shared__ int cnt[kRChunks * kRWaves][256];
   __shared__ int sh_any, sh_kept, sh_rer, sh_invalid, sh_max, sh_min;
   const int tid = threadIdx.x;
   const int R = T * k;
@@ -81,12 +120,20 @@ __global__ __launch_bounds__(kRThreads) void reroute_capacity(const int32_t* __r
   __syncthreads();
 
   // 1. drop-policy fill in route-id order
-  for (int r0 = 0; r0 < R; r0 += kRThreads) {
-    const int r = r0 + tid;
-    const int e = r < R ? ids[r] : -1;
-    const bool valid = e >= 0 && e < N;
-    const int pos = chunk_position<kRThreads>(valid ? e : -1, N, base, cnt);
-    if (r < R) route_expert[r] = (valid && (cap < 0 || pos < cap)) ? e : -1;
+  for (int r0 = 0; r0 < R; r0 += kRChunks * kRThreads) {
+    int key[kRChunks], pos[kRChunks];
+#pragma unroll
+    for (int c = 0; c < kRChunks; ++c) {
+      const int r = r0 + c * kRThreads + tid;
+      const int e = r < R ? ids[r] : -1;
+      key[c] = e >= 0 && e < N ? e : -1;
+    }
+    chunk_positions<kRThreads, kRChunks>(key, pos, N, base, cnt);
+#pragma unroll
+    for (int c = 0; c < kRChunks; ++c) {
+      const int r = r0 + c * kRThreads + tid;
+      if (r < R) route_expert[r] = (key[c] >= 0 && (cap < 0 || pos[c] < cap)) ? key[c] : -1;
+    }
   }
   // base[e] is now expert e's routed load (before capacity)
   for (int e = tid; e < N; e += kRThreads) {
@@ -103,40 +150,48 @@ __global__ __launch_bounds__(kRThreads) void reroute_capacity(const int32_t* __r
     for (int e = tid; e < N; e += kRThreads) base[e] = 0;
     if (tid == 0) sh_any = 0;
     __syncthreads();
-    for (int t0 = 0; t0 < T; t0 += kRThreads) {
-      const int t = t0 + tid;
-      int want = -1, route = -1;
-      if (t < T) {
-        const int32_t* tid_ids = ids + (size_t)t * k;
-        for (int j = 0; j < k; ++j) {
-          const int e = tid_ids[j];
-          if (e >= 0 && e < N && route_expert[t * k + j] < 0) {
-            route = t * k + j;
-            break;
-          }
-        }
-        if (route >= 0) {
-          // the next candidate: the next expert down the token's ranking that is not one
-          // of its own (none once the ranking is used up)
-          int own[8];
+    for (int t00 = 0; t00 < T; t00 += kRChunks * kRThreads) {
+      int want[kRChunks], route[kRChunks], pos[kRChunks];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) own[j] = j < k ? tid_ids[j] : -1;
-          const uint8_t* ot = order + (size_t)t * N;
-          int r = next[t];
-          while (r < N && want < 0) {
-            const int e = ot[r++];
-            bool mine = false;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) mine |= own[j] == e;
-            if (!mine) want = e;
+      for (int c = 0; c < kRChunks; ++c) {
+        const int t = t00 + c * kRThreads + tid;
+        want[c] = -1;
+        route[c] = -1;
+        if (t < T) {
+          const int32_t* tid_ids = ids + (size_t)t * k;
+          for (int j = 0; j < k; ++j) {
+            const int e = tid_ids[j];
+            if (e >= 0 && e < N && route_expert[t * k + j] < 0) {
+              route[c] = t * k + j;
+              break;
+            }
           }
-          next[t] = r;
+          if (route[c] >= 0) {
+            // the next candidate: the next expert down the token's ranking that is not one
+            // of its own (none once the ranking is used up)
+            int own[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) own[j] = j < k ? tid_ids[j] : -1;
+            const uint8_t* ot = order + (size_t)t * N;
+            int r = next[t];
+            while (r < N && want[c] < 0) {
+              const int e = ot[r++];
+              bool mine = false;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) mine |= own[j] == e;
+              if (!mine) want[c] = e;
+            }
+            next[t] = r;
+          }
         }
       }
-      const int pos = chunk_position<kRThreads>(want, N, base, cnt);
-      if (want >= 0) {
-        sh_any = 1;
-        if (pos < room[want]) route_expert[route] = want;
+      chunk_positions<kRThreads, kRChunks>(want, pos, N, base, cnt);
+#pragma unroll
+      for (int c = 0; c < kRChunks; ++c) {
+        if (want[c] >= 0) {
+          sh_any = 1;
+          if (pos[c] < room[want[c]]) route_expert[route[c]] = want[c];
+        }
       }
     }
     __syncthreads();
