@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void align_scan(int32_t* __restrict__ cou
                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ num_padded,
                                                        int32_t* __restrict__ stats, int sentinel,
                                                        int32_t* __restrict__ zero, int nzero, int stats_ready) {
-  constexpr int kBatch = 16;  // chunk counts loaded together (clamped index: no branch, no serial waits)
+  constexpr int kBatch = 32;  // chunk counts loaded together (clamped index: no branch, no serial waits)
   __shared__ int s_inv[kThreads / kWave];
   const int e = threadIdx.x;
   int load = 0;
