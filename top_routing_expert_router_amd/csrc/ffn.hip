@@ -872,11 +872,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 if (!a.dest_is_row) dest = eid;
               }
               const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rr * RB + c16 * 16);
-              if (ok) *reinterpret_cast<u32x4*>(outp + (long)dest * ld + col0 + c16 * 8) = v;
+              if (ok) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(outp + (long)dest * ld + col0 + c16 * 8));
             }
           } else {
             // the chunk's route ids and staged rows are all read before the first store,
-            // so their LDS round trips overlap instead of one pair per store
+            // so their LDS round trips overlap instead of one pair per store.  The stores
+            // are non-temporal: this kernel never reads its output, and the output lines
+            // then displace less of the operand tiles the XCD's workgroups share in L2
             constexpr int NR = 32 / RPI;
             const int c16 = lane % LPR;
             int eid[NR];
@@ -897,7 +899,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 ok = ok && (unsigned)eid[i] < (unsigned)a.sentinel;
                 if (MODE == 1 && !a.dest_is_row) dest = eid[i];
               }
-              if (ok) *reinterpret_cast<u32x4*>(outp + (long)dest * ld + col0 + c16 * 8) = v[i];
+              if (ok) __builtin_nontemporal_store(v[i], reinterpret_cast<u32x4*>(outp + (long)dest * ld + col0 + c16 * 8));
             }
           }
         }
